@@ -1,0 +1,372 @@
+"""Pins of the CPU oracle against facts fixed outside it (CPU only).
+
+Each test ties an oracle function to something other than its own formula:
+the OCP MX element tables, hand-derived bit patterns, torch's bf16 rounding,
+brute force on tiny inputs, closed-form special cases and algebraic
+identities.  Planted-mistake variants of the oracle show that the parity bar
+(normwise 1e-2) would catch each defect class the pages warn about.
+"""
+
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+from scipy.special import expit, softmax
+
+from oracle import mxfp4_moe as O
+from mxfp4_quantized_expert_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- encodings
+
+def test_e2m1_matches_ocp_table():
+    # OCP Microscaling Formats v1.0, FP4 (E2M1) element: the eight magnitudes.
+    spec = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    assert list(O.E2M1_VALUES[:8]) == spec
+    assert list(O.E2M1_VALUES[8:]) == [-v for v in spec]
+    assert math.copysign(1.0, O.E2M1_VALUES[8]) == -1.0  # code 0x8 is -0
+
+
+def test_e8m0_values():
+    assert O.e8m0_value(127) == 1.0
+    assert O.e8m0_value(128) == 2.0
+    assert O.e8m0_value(0) == math.ldexp(1.0, -127)
+    assert O.e8m0_value(254) == math.ldexp(1.0, 127)
+    assert np.isnan(O.e8m0_value(255))
+
+
+def test_bf16_encoder_matches_torch_on_float32_values():
+    rng = np.random.default_rng(7)
+    # random bit patterns cover normals, subnormals, ties and near-overflow
+    bits = rng.integers(0, 2 ** 32, size=200000, dtype=np.uint64).astype(np.uint32)
+    f = bits.view(np.float32)
+    f = f[np.isfinite(f)]
+    extra = np.array([0.0, -0.0, 1.0, 2.0 ** -133, 2.0 ** -134, 3 * 2.0 ** -134,
+                      (2 - 2 ** -8) * 2.0 ** 127, 3.3e38, 1 + 2 ** -8, 1 + 3 * 2 ** -8],
+                     dtype=np.float32)
+    f = np.concatenate([f, extra, -extra])
+    ref = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = O.bf16_encode_rne(f.astype(np.float64))
+    assert np.array_equal(got, ref)
+
+
+def test_bf16_encoder_special_bits():
+    enc = lambda v: int(O.bf16_encode_rne(np.array([v]))[0])  # noqa: E731
+    assert enc(1.0) == 0x3F80
+    assert enc(-0.0) == 0x8000
+    assert enc(2.0 ** -133) == 0x0001
+    assert enc(2.0 ** -134) == 0x0000  # tie to even (zero)
+    assert enc(3 * 2.0 ** -134) == 0x0002  # 1.5 quanta: tie to even (2)
+    assert enc(float("inf")) == 0x7F80
+    assert enc(float("nan")) == 0x7FC0
+    assert enc(2.0 ** 128) == 0x7F80
+    assert enc((2 - 2 ** -7) * 2.0 ** 127) == 0x7F7F
+
+
+def _golden_cases():
+    rows = []
+    with open(os.path.join(GOLDEN, "dequant_cases.txt")) as fh:
+        for line in fh:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                c, s, b = line.split()
+                rows.append((int(c, 16), int(s), int(b, 16)))
+    return rows
+
+
+def test_dequant_golden_cases():
+    for code, s, bits in _golden_cases():
+        # one 32-element group whose element 0 carries the code (low nibble of byte 0)
+        blocks = np.zeros((1, 16), np.uint8)
+        blocks[0, 0] = code
+        out = O.mxfp4_dequantize(blocks, np.array([[s]], np.uint8))
+        assert out[0, 0] == bits, (hex(code), s, hex(out[0, 0]), hex(bits))
+        assert O.bf16_encode_rne(O.dequantize_f64(blocks, np.array([[s]], np.uint8)))[0, 0] == bits
+
+
+def test_dequant_exhaustive_against_spec_table_and_torch():
+    # All 16 codes x 256 scale bytes.  Values from the OCP table literal times
+    # 2^(s-127) computed by math.ldexp, rounded by torch (float32 -> bf16 RNE).
+    spec = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    codes = np.arange(16, dtype=np.uint8)
+    blocks = np.zeros((256, 16), np.uint8)
+    blocks[:, :8] = (codes[0::2] | (codes[1::2] << 4))[None, :]
+    scales = np.arange(256, dtype=np.uint8)[:, None]
+    out = O.mxfp4_dequantize(blocks, scales)
+    for s in range(256):
+        for c in range(16):
+            got = int(out[s, c])
+            if s == 255:
+                assert got == 0x7FC0
+                continue
+            v = math.ldexp(spec[c & 7], s - 127)
+            v = -v if c & 8 else v
+            with np.errstate(over="ignore"):
+                f32 = np.array([v], dtype=np.float32)
+            ref = int(torch.from_numpy(f32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)[0])
+            assert got == ref, (c, s, hex(got), hex(ref))
+
+
+def test_nibble_order_and_group_axis():
+    # Reading: element 2i is the low nibble of byte i; element k uses scale k // 32.
+    blocks = np.zeros((1, 32), np.uint8)
+    blocks[0, 0] = 0x21   # k=0 -> code 1 (0.5), k=1 -> code 2 (1.0)
+    blocks[0, 16] = 0x73  # k=32 -> code 3 (1.5), k=33 -> code 7 (6.0)
+    scales = np.array([[127, 128]], np.uint8)
+    v = O.dequantize_f64(blocks, scales)
+    assert v[0, 0] == 0.5 and v[0, 1] == 1.0
+    assert v[0, 32] == 3.0 and v[0, 33] == 12.0
+    assert np.all(v[0, 2:32] == 0) and np.all(v[0, 34:] == 0)
+
+
+# ---------------------------------------------------------------- routing
+
+def test_route_against_python_brute_force():
+    rng = np.random.default_rng(3)
+    for T, E, k in [(16, 4, 2), (9, 32, 4), (5, 128, 4), (3, 7, 7), (4, 5, 1)]:
+        logits = rng.standard_normal((T, E)).astype(np.float32)
+        logits[0, :] = np.round(logits[0, :])  # plenty of ties
+        ids, w = O.route(logits, k)
+        for t in range(T):
+            order = sorted(range(E), key=lambda e: (-float(logits[t, e]), e))[:k]
+            assert list(ids[t]) == order
+            sel = [float(logits[t, e]) for e in order]
+            ex = [math.exp(v - sel[0]) for v in sel]
+            assert np.allclose(w[t], [v / sum(ex) for v in ex], rtol=0, atol=1e-15)
+        assert np.all(np.abs(w.sum(1) - 1.0) <= 1e-12)
+
+
+def test_route_softmax_over_selected_equals_renormalised_full_softmax():
+    rng = np.random.default_rng(4)
+    logits = (rng.standard_normal((64, 32)) * 2).astype(np.float32)
+    ids, w = O.route(logits, 4)
+    full = softmax(logits.astype(np.float64), axis=1)
+    sel = np.take_along_axis(full, ids, axis=1)
+    assert np.allclose(w, sel / sel.sum(1, keepdims=True), rtol=1e-12, atol=0)
+
+
+def test_route_tie_rule():
+    ids, w = O.route(np.array([[1.0, 3.0, 3.0, 0.0]], np.float32), 2)
+    assert list(ids[0]) == [1, 2]
+    assert np.allclose(w[0], [0.5, 0.5])
+
+
+def test_group_against_brute_force():
+    rng = np.random.default_rng(5)
+    for T, E, k in [(16, 4, 2), (33, 32, 4), (50, 128, 4)]:
+        ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+        counts, offsets, perm = O.group_by_expert(ids, E)
+        flat = ids.ravel()
+        bf = [p for e in range(E) for p in range(T * k) if flat[p] == e]
+        assert list(perm) == bf
+        assert list(counts) == [int((flat == e).sum()) for e in range(E)]
+        assert offsets[0] == 0 and offsets[-1] == T * k
+
+
+# ---------------------------------------------------------------- SwiGLU
+
+def test_swiglu_special_cases():
+    g = np.linspace(-30, 30, 241)
+    a = O.swiglu_clamped(g, -np.ones_like(g))
+    assert np.all(a == 0)  # up = -1 kills the unit, saturated gate or not
+    u = np.linspace(-30, 30, 241)
+    assert np.all(O.swiglu_clamped(np.zeros_like(u), u) == 0)
+    # gate clamp from above only, up clamp on both sides
+    for gv in [7.0, 7.5, 100.0, 1e6]:
+        assert O.swiglu_clamped(gv, 0.3) == O.swiglu_clamped(7.0, 0.3)
+    for uv in [7.0, 8.0, 1e5]:
+        assert O.swiglu_clamped(0.9, uv) == O.swiglu_clamped(0.9, 7.0)
+    for uv in [-7.0, -8.0, -1e5]:
+        assert O.swiglu_clamped(0.9, uv) == O.swiglu_clamped(0.9, -7.0)
+    assert abs(O.swiglu_clamped(-60.0, 3.0)) < 1e-40
+    assert math.isclose(O.swiglu_clamped(7.0, 7.0), 7.0 * 8.0 * expit(1.702 * 7.0), rel_tol=1e-15)
+
+
+def test_swiglu_odd_even_identities():
+    # g*s(ag) - (-g)*s(-ag) = g and g*s(ag) + (-g)*s(-ag) = g*tanh(a*g/2)
+    g = np.linspace(-6.9, 6.9, 139)
+    for uv in [-0.5, 0.0, 2.0]:
+        u = np.full_like(g, uv)
+        d = O.swiglu_clamped(g, u) - O.swiglu_clamped(-g, u)
+        assert np.allclose(d, g * (uv + 1), rtol=1e-12, atol=1e-12)
+    s = O.swiglu_clamped(g, np.zeros_like(g)) + O.swiglu_clamped(-g, np.zeros_like(g))
+    assert np.allclose(s, g * np.tanh(1.702 * g / 2), rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------- whole layer
+
+def _tiny(seed, **kw):
+    spec = W.LAYERS["tiny"].with_(**kw) if kw else W.LAYERS["tiny"]
+    return W.make_layer(spec, seed=seed), spec
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_grouped_equals_dense_brute_force(seed):
+    L, spec = _tiny(seed)
+    y = O.moe_forward(L, spec.top_k)
+    yd = O.moe_forward_dense(L, spec.top_k)
+    rel, mx = O.parity_errors(y, yd)
+    assert rel <= 1e-12 and mx <= 1e-12
+
+
+def test_dense_matches_float64_loops_on_one_token():
+    # Scalar loops over one token, against the oracle's vectorised path.
+    L, spec = _tiny(0, T=3, H=32, I=32, E=3)
+    y = O.moe_forward(L, spec.top_k)
+    x = O.bf16_decode(L["x"])
+    ids, w = O.route(L["router_logits"], spec.top_k)
+    t = 1
+    acc = np.zeros(spec.H)
+    for j in range(spec.top_k):
+        e = ids[t, j]
+        W13 = O.dequantize_f64(L["w13_blocks"][e], L["w13_scales"][e])
+        b13 = O.bf16_decode(L["w13_bias"][e])
+        W2 = O.dequantize_f64(L["w2_blocks"][e], L["w2_scales"][e])
+        b2 = O.bf16_decode(L["w2_bias"][e])
+        a = np.zeros(spec.I)
+        for i in range(spec.I):
+            hg = sum(W13[2 * i, c] * x[t, c] for c in range(spec.H)) + b13[2 * i]
+            hu = sum(W13[2 * i + 1, c] * x[t, c] for c in range(spec.H)) + b13[2 * i + 1]
+            a[i] = O.swiglu_clamped(hg, hu)
+        for n in range(spec.H):
+            acc[n] += w[t, j] * (sum(W2[n, i] * a[i] for i in range(spec.I)) + b2[n])
+    assert np.allclose(acc, y[t], rtol=1e-12, atol=1e-9)
+
+
+def test_zero_down_weights_give_weighted_down_bias():
+    # All w2 codes zero: z = b2 exactly, so y_t = sum_j w_tj * b2[e_tj]; a
+    # down bias added after the routing weight would give sum_j b2 instead.
+    L, spec = _tiny(0)
+    L["w2_blocks"][:] = 0
+    y = O.moe_forward(L, spec.top_k)
+    ids, w = O.route(L["router_logits"], spec.top_k)
+    b2 = O.bf16_decode(L["w2_bias"])
+    ref = (w[:, :, None] * b2[ids]).sum(1)
+    assert np.allclose(y, ref, rtol=1e-14, atol=0)
+
+
+def test_one_hot_weights_closed_form():
+    # W13 row n holds code 0x2 (1.0) at column pi(n), W2 row m at column sig(m):
+    # the GEMMs become gathers, which fixes orientation, interleave and biases.
+    rng = np.random.default_rng(11)
+    L, spec = _tiny(0, T=5, H=64, I=32, E=3)
+    E, H, I = spec.E, spec.H, spec.I
+    pi = rng.integers(0, H, size=(E, 2 * I))
+    sg = rng.integers(0, I, size=(E, H))
+    L["w13_blocks"][:] = 0
+    L["w2_blocks"][:] = 0
+    for e in range(E):
+        for n in range(2 * I):
+            c = pi[e, n]
+            L["w13_blocks"][e, n, c // 2] |= np.uint8(0x2 << (4 * (c % 2)))
+        for m in range(H):
+            c = sg[e, m]
+            L["w2_blocks"][e, m, c // 2] |= np.uint8(0x2 << (4 * (c % 2)))
+    y = O.moe_forward(L, spec.top_k)
+    x = O.bf16_decode(L["x"])
+    ids, w = O.route(L["router_logits"], spec.top_k)
+    ref = np.zeros((spec.T, H))
+    for t in range(spec.T):
+        for j in range(spec.top_k):
+            e = ids[t, j]
+            s13 = 2.0 ** (L["w13_scales"][e].astype(np.int64) - 127)  # [2I, H/32]
+            h = np.array([x[t, pi[e, n]] * s13[n, pi[e, n] // 32] for n in range(2 * I)])
+            h = h + O.bf16_decode(L["w13_bias"][e])
+            a = O.swiglu_clamped(h[0::2], h[1::2])  # even rows gate, odd rows up
+            s2 = 2.0 ** (L["w2_scales"][e].astype(np.int64) - 127)
+            z = np.array([a[sg[e, m]] * s2[m, sg[e, m] // 32] for m in range(H)])
+            ref[t] += w[t, j] * (z + O.bf16_decode(L["w2_bias"][e]))
+    assert np.allclose(y, ref, rtol=1e-13, atol=1e-13)
+
+
+def test_bias_after_scale_identity():
+    # All w2 scale bytes = c: z(c) = 2^(c-127) * z(127, b2=0) + b2 exactly
+    # (power-of-two scaling commutes with rounding when nothing over- or underflows).
+    L, spec = _tiny(0, I=64, H=64, scale_lo=112, scale_hi=120, bias_std=1.0)
+    c = 120
+    Lc = {k: v.copy() for k, v in L.items()}
+    Lc["w2_scales"][:] = c
+    L0 = {k: v.copy() for k, v in L.items()}
+    L0["w2_scales"][:] = 127
+    L0["w2_bias"][:] = 0
+    yc = O.moe_forward(Lc, spec.top_k)
+    ids, w = O.route(L["router_logits"], spec.top_k)
+    x = O.bf16_decode(L["x"])
+    ref = np.zeros_like(yc)
+    for t in range(spec.T):
+        for j in range(spec.top_k):
+            e = ids[t, j]
+            z0 = O.expert_ffn(x[t:t + 1], L0["w13_blocks"][e], L0["w13_scales"][e], L0["w13_bias"][e],
+                              L0["w2_blocks"][e], L0["w2_scales"][e], L0["w2_bias"][e])[0]
+            ref[t] += w[t, j] * (2.0 ** (c - 127) * z0 + O.bf16_decode(L["w2_bias"][e]))
+    assert np.array_equal(yc, ref) or O.parity_errors(yc, ref)[0] <= 1e-15
+    # the scaled-bias variant sum w*s*(z0 + b) must miss the 1e-2 bar by >= 10x
+    bad = np.zeros_like(yc)
+    for t in range(spec.T):
+        for j in range(spec.top_k):
+            e = ids[t, j]
+            z0 = O.expert_ffn(x[t:t + 1], L0["w13_blocks"][e], L0["w13_scales"][e], L0["w13_bias"][e],
+                              L0["w2_blocks"][e], L0["w2_scales"][e], L0["w2_bias"][e])[0]
+            bad[t] += w[t, j] * 2.0 ** (c - 127) * (z0 + O.bf16_decode(L["w2_bias"][e]))
+    assert O.parity_errors(bad, yc)[0] >= 0.1
+
+
+# ------------------------------------------------------- non-vacuity controls
+
+def _variant_forward(L, k, defect):
+    """The oracle with one planted defect (CPU only), for the non-vacuity checks."""
+    x = O.bf16_decode(L["x"])
+    lg = L["router_logits"].astype(np.float64)
+    ids, w = O.route(L["router_logits"], k)
+    if defect == "no_softmax":
+        w = np.take_along_axis(lg, ids, axis=1)
+    T, H = x.shape
+    y = np.zeros((T, H))
+
+    def deq(b, s):
+        if defect == "high_nibble_first":
+            b = ((b & 0x0F) << 4) | (b >> 4)
+        if defect == "e8m0_bias_128":
+            return O.dequantize_f64(b, s) / 2.0
+        return O.dequantize_f64(b, s)
+
+    for t in range(T):
+        for j in range(k):
+            e = ids[t, j]
+            xin = x[t] * (w[t, j] if defect == "weight_on_input" else 1.0)
+            W13 = deq(L["w13_blocks"][e], L["w13_scales"][e])
+            h = W13 @ xin + O.bf16_decode(L["w13_bias"][e])
+            gate, up = h[0::2], h[1::2]
+            if defect == "gate_up_swap":
+                gate, up = up, gate
+            if defect == "no_clamp":
+                a = gate * expit(1.702 * gate) * (up + 1)
+            else:
+                a = O.swiglu_clamped(gate, up)
+            W2 = deq(L["w2_blocks"][e], L["w2_scales"][e])
+            b2 = O.bf16_decode(L["w2_bias"][e])
+            z = W2 @ a
+            if defect != "no_bias":
+                z = z + b2
+            y[t] += z if defect == "weight_on_input" else w[t, j] * z
+    return y
+
+
+@pytest.mark.parametrize("defect,case", [
+    ("high_nibble_first", "live"), ("e8m0_bias_128", "live"), ("gate_up_swap", "live"),
+    ("no_clamp", "saturated"), ("no_softmax", "live"), ("weight_on_input", "live"),
+    ("no_bias", "live")])
+def test_planted_defects_fail_parity(defect, case):
+    # "live": small scales keep the SwiGLU unsaturated and the biases significant;
+    # "saturated": the gpt-oss-shaped scale range [118,132], where the clamps bite.
+    base = W.LAYERS["20b_live"] if case == "live" else W.LAYERS["20b_decode"]
+    spec = base.with_(H=256, I=256, E=8, T=6)
+    L = W.make_layer(spec)
+    ref = O.moe_forward(L, spec.top_k)
+    assert O.parity_errors(_variant_forward(L, spec.top_k, "none"), ref)[0] <= 1e-12
+    rel, _ = O.parity_errors(_variant_forward(L, spec.top_k, defect), ref)
+    assert rel > 1e-2, (defect, rel)
