@@ -1,0 +1,160 @@
+/*
+ * mxfp4moe.h - C ABI of libmxfp4moe.so, the MI355X (gfx950) MXFP4
+ * mixture-of-experts expert FFN and the standalone MXFP4 dequant.
+ *
+ * All tensors are row-major and contiguous.  Every pointer argument that names
+ * a tensor is DEVICE memory owned by the caller; the library never allocates,
+ * frees or keeps a pointer after a call returns.  `stream` is a hipStream_t
+ * (NULL = the default stream).  Every call only enqueues work on `stream` and
+ * returns without synchronising; results are valid once the caller has
+ * synchronised that stream.  Arguments are checked on the host before any
+ * launch: on a non-zero return nothing was launched and nothing was written.
+ * Faults inside kernels surface at the caller's next synchronisation.
+ *
+ * Formats (OCP Microscaling Formats v1.0):
+ *   blocks : uint8, two E2M1 codes per byte; element 2i of a row is the low
+ *            nibble of byte i, element 2i+1 the high nibble.  E2M1 magnitudes
+ *            are 0, 0.5, 1, 1.5, 2, 3, 4, 6 for codes 0..7, bit 3 is the sign.
+ *   scales : uint8 E8M0, one per 32 consecutive elements of a row (one
+ *            16-byte block); value 2^(s-127).  0xFF means NaN.
+ *   bf16   : uint16 bit patterns.
+ */
+#ifndef MXFP4MOE_H
+#define MXFP4MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define MXFP4MOE_OK 0
+#define MXFP4MOE_ERR_ARG (-1)       /* NULL pointer or otherwise invalid argument          */
+#define MXFP4MOE_ERR_SHAPE (-2)     /* sizes out of range or not multiples of 32           */
+#define MXFP4MOE_ERR_WORKSPACE (-3) /* workspace smaller than the size the query returned   */
+#define MXFP4MOE_ERR_ALIGN (-4)     /* a pointer is not 16-byte aligned                    */
+#define MXFP4MOE_ERR_HIP (-5)       /* the HIP runtime rejected a launch                   */
+
+/* Largest supported expert count and top_k. */
+#define MXFP4MOE_MAX_EXPERTS 512
+#define MXFP4MOE_MAX_TOPK 32
+
+/*
+ * mxfp4_dequantize - "dequant-on-copy": expand packed MXFP4 rows to bf16.
+ *
+ * Defined by "feat(gpt-oss): expert offloading Phase 2 - MXFP4 dequant-on-copy
+ * execution" (MoE-Infinity PR #152), Changes: packed experts are dequantized
+ * to bf16, bit-exactly (its golden test reports relative error 0.0); the row
+ * layout is [N, K//2] (numerical review).  Block layout [E, N, K/32, 16] with
+ * one E8M0 byte per block: "Add native GPT-OSS MXFP4 QMoE export" (mobius
+ * PR #719), Summary.
+ *
+ *   blocks   [N, K/2]  uint8, 16-byte aligned
+ *   scales   [N, K/32] uint8
+ *   out_bf16 [N, K]    uint16 (bf16 bits), 16-byte aligned, must not overlap the inputs
+ *   N >= 0 rows (leading dimensions flatten into N: a bank [E, Nr, K/2] passes N = E*Nr);
+ *   K > 0, a multiple of 32.
+ *
+ * out[n, k] = bf16_rne(E2M1(code[n, k]) * 2^(scales[n, k/32] - 127)).  This is
+ * exact for scale bytes up to 252; 253 and 254 overflow the largest codes to
+ * +-inf; 0xFF writes 0x7FC0 for the whole 32-element group.  N == 0 is a no-op.
+ * Returns MXFP4MOE_OK or a negative status.
+ */
+int mxfp4_dequantize(const uint8_t* blocks, const uint8_t* scales, uint16_t* out_bf16,
+                     int64_t N, int64_t K, void* stream);
+
+/*
+ * moe_mxfp4_route - the routing data the MXFP4 experts consume: top-k
+ * selection, softmax over the k selected logits, and the tokens grouped by
+ * expert.
+ *
+ * Defined by "Restore GPT-OSS's router-masked expert-parallel plan"
+ * (transformers PR #49431), description: MXFP4 experts take routing data and
+ * route their tokens themselves; and by "feat(gguf): serve gpt-oss gguf
+ * checkpoints on gpt_oss" (FreeToken PR #838), "What it does": the
+ * expert-ordered prefill views.
+ *
+ *   router_logits  [T, E] float32 (post router bias)
+ *   topk_ids       [T, top_k] int32 out: experts by descending logit; equal
+ *                  logits are ordered by the lower expert index
+ *   topk_weights   [T, top_k] float32 out: exp(l_j - l_0) / sum_i exp(l_i - l_0)
+ *   expert_offsets [E + 1] int32 out: exclusive prefix sum of tokens per expert
+ *   sorted_pairs   [T * top_k] int32 out: pair ids p = t*top_k + j sorted by
+ *                  (expert, p); expert e owns sorted_pairs[offsets[e] .. offsets[e+1])
+ *   1 <= top_k <= min(E, MXFP4MOE_MAX_TOPK), 1 <= E <= MXFP4MOE_MAX_EXPERTS, T >= 0.
+ * T == 0 writes offsets of zeros only.  NaN logits give unspecified ids.
+ */
+int moe_mxfp4_route(const float* router_logits, int64_t T, int64_t E, int64_t top_k,
+                    int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets,
+                    int32_t* sorted_pairs, void* stream);
+
+/*
+ * moe_mxfp4_forward - one gpt-oss MXFP4 MoE expert layer:
+ *
+ *   (ids, w) = top-k of router_logits, softmax over the k selected logits
+ *   for each pair (t, j), e = ids[t, j]:
+ *     h    = x[t] W13_e^T + b13_e                 (bias before the activation)
+ *     gate = h[0::2], up = h[1::2]                (interleaved rows)
+ *     a    = min(gate,7) * sigmoid(1.702*min(gate,7)) * (clamp(up,-7,7) + 1)
+ *     z    = a W2_e^T + b2_e                      (bias before the routing weight)
+ *   y[t] = bf16_rne( sum_j w[t, j] * z_(t,j) )
+ *
+ * Defined by "feat(gguf): serve gpt-oss gguf checkpoints on gpt_oss"
+ * (FreeToken PR #838): "What it does" (alpha 1.702 and limit 7, interleaved
+ * gate/up, gate/up bias before the gated activation, down bias before the
+ * routing weight, required biases) and review items 3 and 4 (sum w*(s*y + b),
+ * router weight applied to the output); "feat(gpt-oss): expert offloading
+ * Phase 2" (MoE-Infinity PR #152), numerical review (scales, bias, [N, K//2]
+ * layout, gate/up split, clamped SwiGLU, fp32 accumulation); the six packed
+ * components per layer of "feat(gpt-oss): expert offloading Phase 3"
+ * (MoE-Infinity PR #153), description.
+ *
+ *   x             [T, H] bf16, 16-byte aligned
+ *   router_logits [T, E] float32
+ *   w13_blocks    [E, 2I, H/2] uint8, 16-byte aligned   (row 2i = gate i, row 2i+1 = up i)
+ *   w13_scales    [E, 2I, H/32] uint8
+ *   w13_bias      [E, 2I] bf16
+ *   w2_blocks     [E, H, I/2] uint8, 16-byte aligned
+ *   w2_scales     [E, H, I/32] uint8
+ *   w2_bias       [E, H] bf16
+ *   y             [T, H] bf16 out, 16-byte aligned, must not alias any input
+ *   H, I > 0 and multiples of 32; 1 <= E <= MXFP4MOE_MAX_EXPERTS;
+ *   1 <= top_k <= min(E, MXFP4MOE_MAX_TOPK); T >= 0.
+ *   workspace     device scratch of at least *workspace_bytes bytes, 256-byte aligned.
+ *                 If workspace == NULL the call only stores the required size in
+ *                 *workspace_bytes and returns MXFP4MOE_OK without launching anything.
+ *
+ * Biases are required (a NULL bias is MXFP4MOE_ERR_ARG); there is no mode that
+ * applies the routing weight to the input.  Accumulation is fp32; the SwiGLU
+ * output is rounded to bf16 before the down GEMM.  T == 0 is a no-op.
+ * The environment variable MXFP4MOE_PATH=small|wide forces one of the two tile
+ * configurations (default: chosen from the average tokens per expert).
+ */
+int moe_mxfp4_forward(const uint16_t* x, const float* router_logits,
+                      const uint8_t* w13_blocks, const uint8_t* w13_scales, const uint16_t* w13_bias,
+                      const uint8_t* w2_blocks, const uint8_t* w2_scales, const uint16_t* w2_bias,
+                      uint16_t* y, int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k,
+                      void* workspace, size_t* workspace_bytes, void* stream);
+
+/* Short English text for a status code (static storage). */
+const char* mxfp4moe_status_string(int status);
+
+/*
+ * Kernel timing hook for benchmarks.  mxfp4moe_profile_begin(stage, max_calls)
+ * makes the next max_calls launches of one kernel stage record a pair of HIP
+ * events around that launch, on the stream the kernel runs on.  Stages:
+ * 1 route, 2 group, 3 gate_up GEMM, 4 down GEMM, 5 combine, 6 dequant.
+ * mxfp4moe_profile_end(ms, capacity) synchronises on the recorded events,
+ * stores up to `capacity` per-launch durations in milliseconds (host array),
+ * releases the events and returns how many were stored (negative on error).
+ */
+int mxfp4moe_profile_begin(int stage, int max_calls);
+int mxfp4moe_profile_end(float* ms, int capacity);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXFP4MOE_H */

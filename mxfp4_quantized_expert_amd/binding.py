@@ -1,0 +1,211 @@
+"""ctypes binding of libmxfp4moe.so.
+
+Argument marshalling only: dtype/device/shape checks, output allocation with
+torch, and the raw C call on torch's current HIP stream.  Every step of the
+computation runs in the library's HIP kernels; there is no other code path.
+The C ABI is declared in include/mxfp4moe.h.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmxfp4moe.so")
+
+STATUS = {
+    0: "ok",
+    -1: "invalid argument",
+    -2: "unsupported shape",
+    -3: "workspace too small",
+    -4: "pointer not 16-byte aligned",
+    -5: "HIP launch error",
+}
+
+STAGES = {"route": 1, "group": 2, "gate_up": 3, "down": 4, "combine": 5, "dequant": 6}
+
+_lib: Optional[ctypes.CDLL] = None
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+
+
+class MXFP4MoEError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: status {status} ({STATUS.get(status, 'unknown')})")
+        self.status = status
+
+
+def load() -> ctypes.CDLL:
+    """Load the HIP library; raises if it has not been built (no fallback exists)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                           "or python -m mxfp4_quantized_expert_amd.build")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.mxfp4_dequantize.argtypes = [_vp, _vp, _vp, _i64, _i64, _vp]
+    lib.mxfp4_dequantize.restype = ctypes.c_int
+    lib.moe_mxfp4_route.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp]
+    lib.moe_mxfp4_route.restype = ctypes.c_int
+    lib.moe_mxfp4_forward.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                      _i64, _i64, _i64, _i64, _i64, _vp,
+                                      ctypes.POINTER(ctypes.c_size_t), _vp]
+    lib.moe_mxfp4_forward.restype = ctypes.c_int
+    lib.mxfp4moe_status_string.argtypes = [ctypes.c_int]
+    lib.mxfp4moe_status_string.restype = ctypes.c_char_p
+    lib.mxfp4moe_profile_begin.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.mxfp4moe_profile_begin.restype = ctypes.c_int
+    lib.mxfp4moe_profile_end.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_int]
+    lib.mxfp4moe_profile_end.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _check(t: torch.Tensor, name: str, dtype: torch.dtype, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _raise(fn: str, st: int):
+    if st != 0:
+        raise MXFP4MoEError(fn, st)
+
+
+def mxfp4_dequantize(blocks: torch.Tensor, scales: torch.Tensor, out: Optional[torch.Tensor] = None,
+                     stream=None) -> torch.Tensor:
+    """blocks [..., N, K/2] uint8 + scales [..., N, K/32] uint8 -> [..., N, K] bfloat16."""
+    lib = load()
+    half_k = blocks.shape[-1]
+    K = 2 * half_k
+    lead = tuple(blocks.shape[:-1])
+    _check(blocks, "blocks", torch.uint8)
+    _check(scales, "scales", torch.uint8, lead + (K // 32,))
+    if out is None:
+        out = torch.empty(lead + (K,), dtype=torch.bfloat16, device=blocks.device)
+    _check(out, "out", torch.bfloat16, lead + (K,))
+    N = 1
+    for d in lead:
+        N *= d
+    st = lib.mxfp4_dequantize(blocks.data_ptr(), scales.data_ptr(), out.data_ptr(), N, K, _stream(stream))
+    _raise("mxfp4_dequantize", st)
+    return out
+
+
+def moe_mxfp4_route(router_logits: torch.Tensor, top_k: int, stream=None):
+    """Returns (topk_ids [T,k] int32, topk_weights [T,k] float32, expert_offsets [E+1] int32,
+    sorted_pairs [T*k] int32)."""
+    lib = load()
+    _check(router_logits, "router_logits", torch.float32)
+    T, E = router_logits.shape
+    dev = router_logits.device
+    ids = torch.empty((T, top_k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, top_k), dtype=torch.float32, device=dev)
+    offsets = torch.empty((E + 1,), dtype=torch.int32, device=dev)
+    pairs = torch.empty((T * top_k,), dtype=torch.int32, device=dev)
+    st = lib.moe_mxfp4_route(router_logits.data_ptr(), T, E, top_k, ids.data_ptr(), w.data_ptr(),
+                             offsets.data_ptr(), pairs.data_ptr(), _stream(stream))
+    _raise("moe_mxfp4_route", st)
+    return ids, w, offsets, pairs
+
+
+def workspace_bytes(T: int, H: int, I: int, E: int, top_k: int) -> int:
+    """Device workspace moe_mxfp4_forward needs for these sizes."""
+    lib = load()
+    n = ctypes.c_size_t(0)
+    st = lib.moe_mxfp4_forward(None, None, None, None, None, None, None, None, None,
+                               T, H, I, E, top_k, None, ctypes.byref(n), None)
+    _raise("moe_mxfp4_forward(workspace query)", st)
+    return int(n.value)
+
+
+def moe_mxfp4_forward(x: torch.Tensor, router_logits: torch.Tensor,
+                      w13_blocks: torch.Tensor, w13_scales: torch.Tensor, w13_bias: torch.Tensor,
+                      w2_blocks: torch.Tensor, w2_scales: torch.Tensor, w2_bias: torch.Tensor,
+                      top_k: int, out: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """One MXFP4 MoE expert layer; returns y [T, H] bfloat16."""
+    lib = load()
+    T, H = x.shape
+    E = router_logits.shape[1]
+    I = w2_blocks.shape[-1] * 2
+    _check(x, "x", torch.bfloat16, (T, H))
+    _check(router_logits, "router_logits", torch.float32, (T, E))
+    _check(w13_blocks, "w13_blocks", torch.uint8, (E, 2 * I, H // 2))
+    _check(w13_scales, "w13_scales", torch.uint8, (E, 2 * I, H // 32))
+    _check(w13_bias, "w13_bias", torch.bfloat16, (E, 2 * I))
+    _check(w2_blocks, "w2_blocks", torch.uint8, (E, H, I // 2))
+    _check(w2_scales, "w2_scales", torch.uint8, (E, H, I // 32))
+    _check(w2_bias, "w2_bias", torch.bfloat16, (E, H))
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    _check(out, "out", torch.bfloat16, (T, H))
+    need = workspace_bytes(T, H, I, E, top_k)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
+    _check(workspace, "workspace", torch.uint8)
+    n = ctypes.c_size_t(workspace.numel())
+    st = lib.moe_mxfp4_forward(x.data_ptr(), router_logits.data_ptr(),
+                               w13_blocks.data_ptr(), w13_scales.data_ptr(), w13_bias.data_ptr(),
+                               w2_blocks.data_ptr(), w2_scales.data_ptr(), w2_bias.data_ptr(),
+                               out.data_ptr(), T, H, I, E, top_k, workspace.data_ptr(),
+                               ctypes.byref(n), _stream(stream))
+    _raise("moe_mxfp4_forward", st)
+    return out
+
+
+def profile_begin(stage: str, max_calls: int) -> None:
+    """Record HIP events around the next ``max_calls`` launches of one kernel stage."""
+    st = load().mxfp4moe_profile_begin(STAGES[stage], max_calls)
+    _raise("mxfp4moe_profile_begin", st)
+
+
+def profile_end(capacity: int):
+    """Per-launch durations (ms) recorded since profile_begin."""
+    buf = (ctypes.c_float * max(capacity, 1))()
+    n = load().mxfp4moe_profile_end(buf, capacity)
+    if n < 0:
+        raise MXFP4MoEError("mxfp4moe_profile_end", n)
+    return [float(buf[i]) for i in range(n)]
+
+
+def layer_to_device(layer, device="cuda"):
+    """Host numpy layer (workloads.make_layer) -> device tensors with the binding's dtypes."""
+    import numpy as np
+
+    def dev(a, dtype):
+        a = np.ascontiguousarray(a)
+        if dtype == torch.bfloat16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+        return torch.from_numpy(a).to(device)
+
+    return {
+        "x": dev(layer["x"], torch.bfloat16),
+        "router_logits": dev(layer["router_logits"], torch.float32),
+        "w13_blocks": dev(layer["w13_blocks"], torch.uint8),
+        "w13_scales": dev(layer["w13_scales"], torch.uint8),
+        "w13_bias": dev(layer["w13_bias"], torch.bfloat16),
+        "w2_blocks": dev(layer["w2_blocks"], torch.uint8),
+        "w2_scales": dev(layer["w2_scales"], torch.uint8),
+        "w2_bias": dev(layer["w2_bias"], torch.bfloat16),
+    }

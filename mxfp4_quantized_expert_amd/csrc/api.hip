@@ -1,0 +1,271 @@
+// C ABI of libmxfp4moe.so: argument checks, workspace carving, tile
+// configuration choice and the launch sequence on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "../../include/mxfp4moe.h"
+#include "internal.h"
+
+namespace mxfp4moe {
+
+// ---------------------------------------------------------------- profiling
+
+namespace {
+std::mutex g_prof_mu;
+std::atomic<int> g_prof_stage{kStageNone};
+int g_prof_next = 0;
+std::vector<hipEvent_t> g_prof_start, g_prof_stop;
+}  // namespace
+
+ProfileScope::ProfileScope(int stage, hipStream_t stream) : slot_(-1), stream_(stream) {
+  if (g_prof_stage.load(std::memory_order_relaxed) == kStageNone) return;  // hook off: no lock
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (stage != g_prof_stage || g_prof_next >= (int)g_prof_start.size()) return;
+  slot_ = g_prof_next++;
+  (void)hipEventRecord(g_prof_start[slot_], stream_);
+}
+
+ProfileScope::~ProfileScope() {
+  if (slot_ < 0) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  (void)hipEventRecord(g_prof_stop[slot_], stream_);
+}
+
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    cached[dev] = cus;
+  }
+  return cached[dev];
+}
+
+// ---------------------------------------------------------------- workspace
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+  size_t ids, weights, offsets, sorted, num_tiles, tiles, act, zw, total;
+  int max_tiles;
+};
+
+int max_tiles_for(int64_t P, int64_t E, int tile_tokens) {
+  const int64_t active = E < P ? E : P;
+  return (int)((P + tile_tokens - 1) / tile_tokens + active);
+}
+
+Layout make_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k) {
+  const int64_t P = T * top_k;
+  Layout L;
+  // Size the tile table for the smallest token tile so every configuration fits.
+  L.max_tiles = max_tiles_for(P, E, gemm_tile_tokens(kGemmSmall));
+  size_t off = 0;
+  L.ids = off;       off = align_up(off + (size_t)P * 4);
+  L.weights = off;   off = align_up(off + (size_t)P * 4);
+  L.offsets = off;   off = align_up(off + (size_t)(E + 1) * 4);
+  L.sorted = off;    off = align_up(off + (size_t)P * 4);
+  L.num_tiles = off; off = align_up(off + 4);
+  L.tiles = off;     off = align_up(off + (size_t)L.max_tiles * 16);
+  L.act = off;       off = align_up(off + (size_t)P * (size_t)I * 2);
+  L.zw = off;        off = align_up(off + (size_t)P * (size_t)H * 4);
+  L.total = off;
+  return L;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+GemmConfig choose_config(int64_t P, int64_t E) {
+  const char* env = std::getenv("MXFP4MOE_PATH");
+  if (env != nullptr) {
+    if (std::strcmp(env, "small") == 0) return kGemmSmall;
+    if (std::strcmp(env, "wide") == 0) return kGemmWide;
+  }
+  const int64_t active = E < P ? E : P;
+  const int64_t per_expert = active > 0 ? P / active : 0;
+  return per_expert >= 64 ? kGemmWide : kGemmSmall;
+}
+
+int check_route_shape(int64_t T, int64_t E, int64_t top_k) {
+  if (T < 0 || E < 1 || E > MXFP4MOE_MAX_EXPERTS) return MXFP4MOE_ERR_SHAPE;
+  if (top_k < 1 || top_k > E || top_k > MXFP4MOE_MAX_TOPK) return MXFP4MOE_ERR_SHAPE;
+  if (T * top_k > (int64_t)0x7fffffff) return MXFP4MOE_ERR_SHAPE;
+  return MXFP4MOE_OK;
+}
+
+}  // namespace
+}  // namespace mxfp4moe
+
+using namespace mxfp4moe;
+
+extern "C" {
+
+const char* mxfp4moe_status_string(int status) {
+  switch (status) {
+    case MXFP4MOE_OK: return "ok";
+    case MXFP4MOE_ERR_ARG: return "invalid argument (NULL pointer)";
+    case MXFP4MOE_ERR_SHAPE: return "unsupported shape";
+    case MXFP4MOE_ERR_WORKSPACE: return "workspace too small";
+    case MXFP4MOE_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case MXFP4MOE_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int mxfp4_dequantize(const uint8_t* blocks, const uint8_t* scales, uint16_t* out_bf16, int64_t N, int64_t K,
+                     void* stream) {
+  if (N < 0 || K <= 0 || (K & 31) != 0) return MXFP4MOE_ERR_SHAPE;
+  if (N > 0 && K > ((int64_t)1 << 62) / N) return MXFP4MOE_ERR_SHAPE;
+  if (N == 0) return MXFP4MOE_OK;
+  if (blocks == nullptr || scales == nullptr || out_bf16 == nullptr) return MXFP4MOE_ERR_ARG;
+  if (!aligned16(blocks) || !aligned16(out_bf16)) return MXFP4MOE_ERR_ALIGN;
+  hipError_t err = launch_dequant(blocks, scales, out_bf16, N, K, (hipStream_t)stream);
+  return err == hipSuccess ? MXFP4MOE_OK : MXFP4MOE_ERR_HIP;
+}
+
+int moe_mxfp4_route(const float* router_logits, int64_t T, int64_t E, int64_t top_k, int32_t* topk_ids,
+                    float* topk_weights, int32_t* expert_offsets, int32_t* sorted_pairs, void* stream) {
+  int st = check_route_shape(T, E, top_k);
+  if (st != MXFP4MOE_OK) return st;
+  if (expert_offsets == nullptr) return MXFP4MOE_ERR_ARG;
+  if (T > 0 && (router_logits == nullptr || topk_ids == nullptr || topk_weights == nullptr ||
+                sorted_pairs == nullptr))
+    return MXFP4MOE_ERR_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t err = launch_route(router_logits, (int)T, (int)E, (int)top_k, topk_ids, topk_weights, s);
+  if (err == hipSuccess)
+    err = launch_group(topk_ids, (int)(T * top_k), (int)E, expert_offsets, sorted_pairs, nullptr, nullptr, 32, s);
+  return err == hipSuccess ? MXFP4MOE_OK : MXFP4MOE_ERR_HIP;
+}
+
+int moe_mxfp4_forward(const uint16_t* x, const float* router_logits, const uint8_t* w13_blocks,
+                      const uint8_t* w13_scales, const uint16_t* w13_bias, const uint8_t* w2_blocks,
+                      const uint8_t* w2_scales, const uint16_t* w2_bias, uint16_t* y, int64_t T, int64_t H,
+                      int64_t I, int64_t E, int64_t top_k, void* workspace, size_t* workspace_bytes,
+                      void* stream) {
+  if (workspace_bytes == nullptr) return MXFP4MOE_ERR_ARG;
+  int st = check_route_shape(T, E, top_k);
+  if (st != MXFP4MOE_OK) return st;
+  if (H <= 0 || I <= 0 || (H & 31) != 0 || (I & 31) != 0) return MXFP4MOE_ERR_SHAPE;
+  if (H > (1 << 20) || I > (1 << 20)) return MXFP4MOE_ERR_SHAPE;
+  const Layout L = make_layout(T, H, I, E, top_k);
+  if (workspace == nullptr) {
+    *workspace_bytes = L.total;
+    return MXFP4MOE_OK;
+  }
+  if (w13_blocks == nullptr || w13_scales == nullptr || w13_bias == nullptr || w2_blocks == nullptr ||
+      w2_scales == nullptr || w2_bias == nullptr)
+    return MXFP4MOE_ERR_ARG;
+  if (T > 0 && (x == nullptr || router_logits == nullptr || y == nullptr)) return MXFP4MOE_ERR_ARG;
+  if (*workspace_bytes < L.total) return MXFP4MOE_ERR_WORKSPACE;
+  if (((uintptr_t)workspace & (kAlign - 1)) != 0) return MXFP4MOE_ERR_ALIGN;
+  if (!aligned16(w13_blocks) || !aligned16(w2_blocks)) return MXFP4MOE_ERR_ALIGN;
+  if (T > 0 && (!aligned16(x) || !aligned16(y))) return MXFP4MOE_ERR_ALIGN;
+  if (T == 0) return MXFP4MOE_OK;
+
+  char* ws = static_cast<char*>(workspace);
+  int32_t* ids = reinterpret_cast<int32_t*>(ws + L.ids);
+  float* weights = reinterpret_cast<float*>(ws + L.weights);
+  int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+  int32_t* sorted = reinterpret_cast<int32_t*>(ws + L.sorted);
+  int32_t* num_tiles = reinterpret_cast<int32_t*>(ws + L.num_tiles);
+  int32_t* tiles = reinterpret_cast<int32_t*>(ws + L.tiles);
+  uint16_t* act = reinterpret_cast<uint16_t*>(ws + L.act);
+  float* zw = reinterpret_cast<float*>(ws + L.zw);
+
+  const int64_t P = T * top_k;
+  const GemmConfig cfg = choose_config(P, E);
+  const int tile_tokens = gemm_tile_tokens(cfg);
+  hipStream_t s = (hipStream_t)stream;
+
+  hipError_t err = launch_route(router_logits, (int)T, (int)E, (int)top_k, ids, weights, s);
+  if (err == hipSuccess)
+    err = launch_group(ids, (int)P, (int)E, offsets, sorted, tiles, num_tiles, tile_tokens, s);
+  GemmArgs g{};
+  g.sorted_pairs = sorted;
+  g.tiles = tiles;
+  g.num_tiles = num_tiles;
+  g.topk_weights = weights;
+  g.top_k = (int)top_k;
+  g.max_tiles = max_tiles_for(P, E, tile_tokens);
+  if (err == hipSuccess) {
+    g.wblocks = w13_blocks;
+    g.wscales = w13_scales;
+    g.bias = w13_bias;
+    g.act = x;
+    g.out = act;
+    g.N = (int)(2 * I);
+    g.K = (int)H;
+    err = launch_gate_up(g, cfg, s);
+  }
+  if (err == hipSuccess) {
+    g.wblocks = w2_blocks;
+    g.wscales = w2_scales;
+    g.bias = w2_bias;
+    g.act = act;
+    g.out = zw;
+    g.N = (int)H;
+    g.K = (int)I;
+    err = launch_down(g, cfg, s);
+  }
+  if (err == hipSuccess) err = launch_combine(zw, y, (int)T, (int)H, (int)top_k, s);
+  return err == hipSuccess ? MXFP4MOE_OK : MXFP4MOE_ERR_HIP;
+}
+
+int mxfp4moe_profile_begin(int stage, int max_calls) {
+  if (stage < kStageRoute || stage > kStageDequant || max_calls < 1 || max_calls > 100000)
+    return MXFP4MOE_ERR_ARG;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (hipEvent_t ev : g_prof_start) (void)hipEventDestroy(ev);
+  for (hipEvent_t ev : g_prof_stop) (void)hipEventDestroy(ev);
+  g_prof_start.assign(max_calls, nullptr);
+  g_prof_stop.assign(max_calls, nullptr);
+  for (int i = 0; i < max_calls; ++i) {
+    if (hipEventCreate(&g_prof_start[i]) != hipSuccess || hipEventCreate(&g_prof_stop[i]) != hipSuccess) {
+      g_prof_stage = kStageNone;
+      return MXFP4MOE_ERR_HIP;
+    }
+  }
+  g_prof_next = 0;
+  g_prof_stage = stage;
+  return MXFP4MOE_OK;
+}
+
+int mxfp4moe_profile_end(float* ms, int capacity) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  const int n = g_prof_next;
+  int stored = 0;
+  int status = MXFP4MOE_OK;
+  for (int i = 0; i < n; ++i) {
+    if (hipEventSynchronize(g_prof_stop[i]) != hipSuccess) {
+      status = MXFP4MOE_ERR_HIP;
+      break;
+    }
+    float t = 0.f;
+    if (hipEventElapsedTime(&t, g_prof_start[i], g_prof_stop[i]) != hipSuccess) {
+      status = MXFP4MOE_ERR_HIP;
+      break;
+    }
+    if (ms != nullptr && stored < capacity) ms[stored++] = t;
+  }
+  for (hipEvent_t ev : g_prof_start) (void)hipEventDestroy(ev);
+  for (hipEvent_t ev : g_prof_stop) (void)hipEventDestroy(ev);
+  g_prof_start.clear();
+  g_prof_stop.clear();
+  g_prof_stage = kStageNone;
+  g_prof_next = 0;
+  return status == MXFP4MOE_OK ? stored : status;
+}
+
+}  // extern "C"

@@ -1,0 +1,209 @@
+// Routing data for the MXFP4 experts: top-k with softmax over the selected
+// logits, then the pairs grouped by expert ("Restore GPT-OSS's router-masked
+// expert-parallel plan", transformers PR #49431, description: the experts
+// consume routing data and route their tokens themselves; "feat(gguf): serve
+// gpt-oss gguf checkpoints on gpt_oss", FreeToken PR #838, "What it does":
+// expert-ordered views of the tokens).
+#include "../../include/mxfp4moe.h"
+#include "internal.h"
+#include "mx_device.h"
+
+namespace {
+
+constexpr int kRouteThreads = 256;  // four tokens per block, one wave each
+constexpr int kPerLane = MXFP4MOE_MAX_EXPERTS / 64;
+
+// One wave per token.  Lane l holds logits l, l+64, ...; k rounds of a
+// wave-wide argmax (ties to the lower expert index) pick the experts in
+// descending order; lane j keeps the j-th pick.  The softmax runs over the
+// picks relative to the largest one.
+__global__ __launch_bounds__(kRouteThreads) void route_kernel(const float* __restrict__ logits, int T, int E,
+                                                              int top_k, int32_t* __restrict__ ids,
+                                                              float* __restrict__ weights) {
+  const int lane = mx::lane_id();
+  const int t = blockIdx.x * (kRouteThreads / 64) + (threadIdx.x >> 6);
+  if (t >= T) return;  // uniform per wave
+  const float* row = logits + (size_t)t * E;
+  float v[kPerLane];
+  uint32_t avail = 0;
+#pragma unroll
+  for (int i = 0; i < kPerLane; ++i) {
+    const int e = lane + 64 * i;
+    v[i] = 0.f;
+    if (e < E) {
+      v[i] = row[e];
+      avail |= 1u << i;
+    }
+  }
+  float my_v = 0.f, v0 = 0.f;
+  int my_e = 0;
+  for (int j = 0; j < top_k; ++j) {
+    bool have = false;
+    float bv = 0.f;
+    int be = 0;
+#pragma unroll
+    for (int i = 0; i < kPerLane; ++i) {
+      if ((avail >> i) & 1u) {
+        if (!have || v[i] > bv) {  // strict: the lower index wins ties inside a lane
+          bv = v[i];
+          be = lane + 64 * i;
+          have = true;
+        }
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off, 64);
+      const int oe = __shfl_xor(be, off, 64);
+      const int oh = __shfl_xor((int)have, off, 64);
+      if (oh && (!have || ov > bv || (ov == bv && oe < be))) {
+        bv = ov;
+        be = oe;
+        have = true;
+      }
+    }
+    if ((be & 63) == lane) avail &= ~(1u << (be >> 6));
+    if (lane == j) {
+      my_v = bv;
+      my_e = be;
+    }
+    if (j == 0) v0 = bv;
+  }
+  float ex = lane < top_k ? expf(my_v - v0) : 0.f;
+  float sum = ex;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
+  if (lane < top_k) {
+    ids[(size_t)t * top_k + lane] = my_e;
+    weights[(size_t)t * top_k + lane] = ex / sum;
+  }
+}
+
+constexpr int kGroupThreads = 1024;
+constexpr int kGroupWaves = kGroupThreads / 64;
+
+// Exclusive prefix sum of vals[0..n) into out[0..n) by wave 0; returns the
+// total to every thread of the block (after the trailing barrier).
+__device__ int block_exclusive_scan_wave0(const int* vals, int* out, int n, int* total_slot) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int carry = 0;
+    for (int c0 = 0; c0 < n; c0 += 64) {
+      const int e = c0 + lane;
+      const int x = e < n ? vals[e] : 0;
+      int incl = x;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += y;
+      }
+      if (e < n) out[e] = carry + incl - x;
+      carry += __shfl(incl, 63, 64);
+    }
+    if (lane == 0) *total_slot = carry;
+  }
+  __syncthreads();
+  return *total_slot;
+}
+
+// Single workgroup: histogram of experts, exclusive scan into offsets, a
+// stable scatter of pair ids into expert order, and the GEMM tile table.
+// The scatter walks the pairs in chunks of 1024; inside a wave the lanes with
+// the same expert are found by matching the expert id bit by bit with
+// ballots, and the per-wave counts are turned into positions wave by wave, so
+// pairs keep ascending id order inside every expert.
+__global__ __launch_bounds__(kGroupThreads) void group_kernel(const int32_t* __restrict__ ids, int P, int E,
+                                                              int32_t* __restrict__ offsets,
+                                                              int32_t* __restrict__ sorted_pairs,
+                                                              int32_t* __restrict__ tiles,
+                                                              int32_t* __restrict__ num_tiles, int tile_tokens) {
+  extern __shared__ int smem[];
+  int* cnt = smem;                 // [E]
+  int* base = cnt + E;             // [E]
+  int* tile_base = base + E;       // [E]
+  int* ntile = tile_base + E;      // [E]
+  int* wave_cnt = ntile + E;       // [kGroupWaves][E]
+  __shared__ int total_slot;
+
+  for (int e = threadIdx.x; e < E; e += kGroupThreads) cnt[e] = 0;
+  __syncthreads();
+  for (int p = threadIdx.x; p < P; p += kGroupThreads) atomicAdd(&cnt[ids[p]], 1);
+  __syncthreads();
+  block_exclusive_scan_wave0(cnt, base, E, &total_slot);
+  for (int e = threadIdx.x; e < E; e += kGroupThreads) offsets[e] = base[e];
+  if (threadIdx.x == 0) offsets[E] = P;
+
+  if (tiles != nullptr) {
+    for (int e = threadIdx.x; e < E; e += kGroupThreads) ntile[e] = (cnt[e] + tile_tokens - 1) / tile_tokens;
+    __syncthreads();
+    const int n_tiles = block_exclusive_scan_wave0(ntile, tile_base, E, &total_slot);
+    if (threadIdx.x == 0) *num_tiles = n_tiles;
+    for (int e = threadIdx.x; e < E; e += kGroupThreads) {
+      for (int i = 0; i < ntile[e]; ++i) {
+        int4 tl;
+        tl.x = e;
+        tl.y = base[e] + i * tile_tokens;
+        tl.z = min(tile_tokens, cnt[e] - i * tile_tokens);
+        tl.w = 0;
+        reinterpret_cast<int4*>(tiles)[tile_base[e] + i] = tl;
+      }
+    }
+  }
+
+  const int wave = threadIdx.x >> 6;
+  int nbits = 1;
+  while ((1 << nbits) < E) ++nbits;
+  for (int c0 = 0; c0 < P; c0 += kGroupThreads) {
+    for (int i = threadIdx.x; i < kGroupWaves * E; i += kGroupThreads) wave_cnt[i] = 0;
+    __syncthreads();
+    const int p = c0 + threadIdx.x;
+    const bool valid = p < P;
+    const int e = valid ? ids[p] : 0;
+    uint64_t match = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t ones = __ballot(valid && bit);
+      match &= bit ? ones : ~ones;
+    }
+    const int rank = mx::lanes_below(match);
+    if (valid && rank == 0) wave_cnt[wave * E + e] = __popcll(match);
+    __syncthreads();
+    for (int ee = threadIdx.x; ee < E; ee += kGroupThreads) {
+      int run = base[ee];
+      for (int w = 0; w < kGroupWaves; ++w) {
+        const int c = wave_cnt[w * E + ee];
+        wave_cnt[w * E + ee] = run;
+        run += c;
+      }
+      base[ee] = run;
+    }
+    __syncthreads();
+    if (valid) sorted_pairs[wave_cnt[wave * E + e] + rank] = p;
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+namespace mxfp4moe {
+
+hipError_t launch_route(const float* logits, int T, int E, int top_k, int32_t* ids, float* weights,
+                        hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  const int per_block = kRouteThreads / 64;
+  const unsigned grid = (unsigned)((T + per_block - 1) / per_block);
+  ProfileScope prof(kStageRoute, stream);
+  route_kernel<<<grid, kRouteThreads, 0, stream>>>(logits, T, E, top_k, ids, weights);
+  return hipGetLastError();
+}
+
+hipError_t launch_group(const int32_t* ids, int P, int E, int32_t* offsets, int32_t* sorted_pairs,
+                        int32_t* tiles, int32_t* num_tiles, int tile_tokens, hipStream_t stream) {
+  const size_t smem = (size_t)(4 + kGroupWaves) * E * sizeof(int);
+  ProfileScope prof(kStageGroup, stream);
+  group_kernel<<<1, kGroupThreads, smem, stream>>>(ids, P, E, offsets, sorted_pairs, tiles, num_tiles,
+                                                   tile_tokens);
+  return hipGetLastError();
+}
+
+}  // namespace mxfp4moe

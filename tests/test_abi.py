@@ -1,0 +1,101 @@
+"""The C-ABI library: it loads, exports every declared entry point, and
+rejects bad arguments on the host before any HIP call (CPU only; no kernel runs)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from mxfp4_quantized_expert_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxfp4moe.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        from mxfp4_quantized_expert_amd import build
+        build.build(verbose=False)
+    return binding.load()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+
+
+def test_exports_every_declared_function(lib):
+    names = _declared()
+    assert {"mxfp4_dequantize", "moe_mxfp4_route", "moe_mxfp4_forward"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    assert lib.mxfp4moe_status_string(0) == b"ok"
+    assert b"shape" in lib.mxfp4moe_status_string(-2)
+
+
+A = 0x100000  # a 256-byte aligned fake address: never dereferenced, every call fails before use
+
+
+def test_dequant_argument_checks(lib):
+    f = lib.mxfp4_dequantize
+    assert f(A, A, A, 10, 33, None) == -2
+    assert f(A, A, A, -1, 32, None) == -2
+    assert f(A, A, A, 10, 0, None) == -2
+    assert f(None, A, A, 10, 32, None) == -1
+    assert f(A, None, A, 10, 32, None) == -1
+    assert f(A, A, None, 10, 32, None) == -1
+    assert f(A + 1, A, A, 10, 32, None) == -4
+    assert f(A, A, A + 8, 10, 32, None) == -4
+    assert f(None, None, None, 0, 32, None) == 0  # empty: no-op
+
+
+def _fwd(lib, T=4, H=64, I=64, E=4, k=2, ws=A, ws_bytes=1 << 30, x=A, lg=A, b13=A, b2=A, y=A,
+         wb=A):
+    n = ctypes.c_size_t(ws_bytes)
+    return lib.moe_mxfp4_forward(x, lg, wb, A, b13, wb, A, b2, y, T, H, I, E, k, ws,
+                                 ctypes.byref(n), None), n.value
+
+
+def test_forward_workspace_query(lib):
+    st, n = _fwd(lib, ws=None, ws_bytes=0)
+    assert st == 0 and n > 0
+    P, H, I = 8, 64, 64
+    assert n >= P * I * 2 + P * H * 4  # activations in bf16 and per-pair rows in fp32
+    st2, n2 = _fwd(lib, T=4096, H=2880, I=2880, E=128, k=4, ws=None, ws_bytes=0)
+    assert st2 == 0 and n2 >= 16384 * 2880 * 6
+    assert binding.workspace_bytes(4, 64, 64, 4, 2) == n
+
+
+def test_forward_argument_checks(lib):
+    assert _fwd(lib, T=-1)[0] == -2
+    assert _fwd(lib, k=5)[0] == -2            # top_k > E
+    assert _fwd(lib, k=0)[0] == -2
+    assert _fwd(lib, E=513, k=2)[0] == -2     # more experts than supported
+    assert _fwd(lib, E=64, k=33)[0] == -2     # top_k above the maximum
+    assert _fwd(lib, H=48)[0] == -2           # not a multiple of 32
+    assert _fwd(lib, I=40)[0] == -2
+    assert _fwd(lib, b13=None)[0] == -1       # biases are required
+    assert _fwd(lib, b2=None)[0] == -1
+    assert _fwd(lib, x=None)[0] == -1
+    assert _fwd(lib, ws_bytes=16)[0] == -3
+    assert _fwd(lib, ws=A + 16)[0] == -4
+    assert _fwd(lib, x=A + 2)[0] == -4
+    assert _fwd(lib, wb=A + 4)[0] == -4
+    n = ctypes.c_size_t(0)
+    assert lib.moe_mxfp4_forward(A, A, A, A, A, A, A, A, A, 4, 64, 64, 4, 2, A, None, None) == -1
+    assert _fwd(lib, T=0, x=None, lg=None, y=None)[0] == 0  # empty batch: nothing to do
+    del n
+
+
+def test_route_argument_checks(lib):
+    f = lib.moe_mxfp4_route
+    assert f(A, 4, 0, 1, A, A, A, A, None) == -2
+    assert f(A, 4, 8, 9, A, A, A, A, None) == -2
+    assert f(A, 4, 8, 2, A, A, None, A, None) == -1
+    assert f(None, 4, 8, 2, A, A, A, A, None) == -1

@@ -1,0 +1,50 @@
+"""moe_mxfp4_route on the GPU against the oracle: ids, offsets and the
+expert-ordered pair list bit-exact, weights within 1e-6."""
+
+import numpy as np
+import pytest
+import torch
+
+from mxfp4_quantized_expert_amd import workloads as W
+from oracle import mxfp4_moe as O
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(gpu, logits: np.ndarray, k: int):
+    T, E = logits.shape
+    ids, w, offsets, pairs = gpu.moe_mxfp4_route(torch.from_numpy(logits).cuda(), k)
+    torch.cuda.synchronize()
+    rids, rw = O.route(logits, k)
+    counts, roff, rperm = O.group_by_expert(rids, E)
+    assert np.array_equal(ids.cpu().numpy(), rids)
+    assert np.max(np.abs(w.cpu().numpy() - rw), initial=0.0) <= 1e-6
+    assert np.array_equal(offsets.cpu().numpy(), roff)
+    assert np.array_equal(pairs.cpu().numpy(), rperm)
+
+
+@pytest.mark.parametrize("name", ["tiny", "20b_decode", "20b_prefill", "120b_prefill"])
+def test_route_layers(gpu, name):
+    spec = W.LAYERS[name]
+    _, logits = W.make_routing_inputs(spec)
+    _check(gpu, logits, spec.top_k)
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 1, 1), (3, 7, 7), (77, 512, 32), (5000, 64, 1), (2048, 128, 8),
+                                   (1, 65, 4)])
+def test_route_shapes(gpu, T, E, k):
+    rng = np.random.default_rng(T + E + k)
+    _check(gpu, rng.standard_normal((T, E)).astype(np.float32), k)
+
+
+def test_route_ties_go_to_lower_index(gpu):
+    rng = np.random.default_rng(1)
+    logits = np.round(rng.standard_normal((300, 40)) * 2).astype(np.float32)  # many equal logits
+    _check(gpu, logits, 6)
+
+
+def test_route_empty(gpu):
+    logits = torch.zeros((0, 8), dtype=torch.float32, device="cuda")
+    ids, w, offsets, pairs = gpu.moe_mxfp4_route(logits, 2)
+    torch.cuda.synchronize()
+    assert np.array_equal(offsets.cpu().numpy(), np.zeros(9, np.int32))
