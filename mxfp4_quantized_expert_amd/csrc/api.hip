@@ -86,15 +86,21 @@ Layout make_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-GemmConfig choose_config(int64_t P, int64_t E) {
+GemmConfig choose_config(int64_t P, int64_t E, int64_t H, int64_t I) {
+  // The wide loader/compute kernel stages every scale byte of its weight rows
+  // in LDS, which bounds K (= H for gate_up, I for down) at 4096.
+  const bool wide_ok = H <= 4096 && I <= 4096;
   const char* env = std::getenv("MXFP4MOE_PATH");
   if (env != nullptr) {
     if (std::strcmp(env, "small") == 0) return kGemmSmall;
-    if (std::strcmp(env, "wide") == 0) return kGemmWide;
+    if (std::strcmp(env, "mid") == 0) return kGemmMid;
+    if (std::strcmp(env, "wide") == 0) return wide_ok ? kGemmWide : kGemmMid;
   }
   const int64_t active = E < P ? E : P;
   const int64_t per_expert = active > 0 ? P / active : 0;
-  return per_expert >= 64 ? kGemmWide : kGemmSmall;
+  if (per_expert >= 96 && wide_ok) return kGemmWide;
+  if (per_expert >= 16) return kGemmMid;
+  return kGemmSmall;
 }
 
 int check_route_shape(int64_t T, int64_t E, int64_t top_k) {
@@ -185,7 +191,7 @@ int moe_mxfp4_forward(const uint16_t* x, const float* router_logits, const uint8
   float* zw = reinterpret_cast<float*>(ws + L.zw);
 
   const int64_t P = T * top_k;
-  const GemmConfig cfg = choose_config(P, E);
+  const GemmConfig cfg = choose_config(P, E, H, I);
   const int tile_tokens = gemm_tile_tokens(cfg);
   hipStream_t s = (hipStream_t)stream;
 

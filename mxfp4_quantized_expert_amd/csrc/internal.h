@@ -37,7 +37,8 @@ int device_cu_count();
 // same token tile (the tile table is shared).
 enum GemmConfig : int {
   kGemmSmall = 0,  // 32 token columns per tile: decode-sized expert groups
-  kGemmWide = 1,   // 128 token columns per tile: prefill-sized expert groups
+  kGemmMid = 1,    // 64 token columns per tile
+  kGemmWide = 2,   // 256 token columns per tile: prefill-sized expert groups
 };
 int gemm_tile_tokens(GemmConfig cfg);
 
