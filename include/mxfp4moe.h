@@ -40,6 +40,7 @@ extern "C" {
 /* Largest supported expert count and top_k. */
 #define MXFP4MOE_MAX_EXPERTS 512
 #define MXFP4MOE_MAX_TOPK 32
+#define MXFP4MOE_MAX_HIDDEN 4096 /* bound on H and I: the GEMMs stage a tile's scale rows in LDS */
 
 /*
  * mxfp4_dequantize - "dequant-on-copy": expand packed MXFP4 rows to bf16.
@@ -120,7 +121,7 @@ int moe_mxfp4_route(const float* router_logits, int64_t T, int64_t E, int64_t to
  *   w2_scales     [E, H, I/32] uint8
  *   w2_bias       [E, H] bf16
  *   y             [T, H] bf16 out, 16-byte aligned, must not alias any input
- *   H, I > 0 and multiples of 32; 1 <= E <= MXFP4MOE_MAX_EXPERTS;
+ *   H, I multiples of 32 in [32, MXFP4MOE_MAX_HIDDEN]; 1 <= E <= MXFP4MOE_MAX_EXPERTS;
  *   1 <= top_k <= min(E, MXFP4MOE_MAX_TOPK); T >= 0.
  *   workspace     device scratch of at least *workspace_bytes bytes, 256-byte aligned.
  *                 If workspace == NULL the call only stores the required size in
@@ -129,8 +130,10 @@ int moe_mxfp4_route(const float* router_logits, int64_t T, int64_t E, int64_t to
  * Biases are required (a NULL bias is MXFP4MOE_ERR_ARG); there is no mode that
  * applies the routing weight to the input.  Accumulation is fp32; the SwiGLU
  * output is rounded to bf16 before the down GEMM.  T == 0 is a no-op.
- * The environment variable MXFP4MOE_PATH=small|wide forces one of the two tile
- * configurations (default: chosen from the average tokens per expert).
+ * Each expert's pairs are cut into full tiles of 128 (one GEMM kernel
+ * configuration) and a remainder in tiles of 32 (a streaming configuration
+ * that is also the whole decode path); MXFP4MOE_PATH=stream in the environment
+ * sends every pair through the streaming configuration.
  */
 int moe_mxfp4_forward(const uint16_t* x, const float* router_logits,
                       const uint8_t* w13_blocks, const uint8_t* w13_scales, const uint16_t* w13_bias,

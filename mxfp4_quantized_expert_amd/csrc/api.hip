@@ -57,27 +57,31 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t ids, weights, offsets, sorted, num_tiles, tiles, act, zw, total;
-  int max_tiles;
+  size_t ids, weights, offsets, sorted, counts, big, small, act, zw, total;
+  int max_big, max_small;
 };
 
-int max_tiles_for(int64_t P, int64_t E, int tile_tokens) {
+// Tile table bounds: the full tiles of all experts hold at most P pairs; every
+// expert with pairs adds at most one partial small tile on top of P/32 full ones.
+int max_big_tiles(int64_t P) { return (int)(P / kWideTokens); }
+int max_small_tiles(int64_t P, int64_t E) {
   const int64_t active = E < P ? E : P;
-  return (int)((P + tile_tokens - 1) / tile_tokens + active);
+  return (int)((P + kStreamTokens - 1) / kStreamTokens + active);
 }
 
 Layout make_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k) {
   const int64_t P = T * top_k;
   Layout L;
-  // Size the tile table for the smallest token tile so every configuration fits.
-  L.max_tiles = max_tiles_for(P, E, gemm_tile_tokens(kGemmSmall));
+  L.max_big = max_big_tiles(P);
+  L.max_small = max_small_tiles(P, E);
   size_t off = 0;
   L.ids = off;       off = align_up(off + (size_t)P * 4);
   L.weights = off;   off = align_up(off + (size_t)P * 4);
   L.offsets = off;   off = align_up(off + (size_t)(E + 1) * 4);
   L.sorted = off;    off = align_up(off + (size_t)P * 4);
-  L.num_tiles = off; off = align_up(off + 4);
-  L.tiles = off;     off = align_up(off + (size_t)L.max_tiles * 16);
+  L.counts = off;    off = align_up(off + 8);
+  L.big = off;       off = align_up(off + (size_t)L.max_big * 16);
+  L.small = off;     off = align_up(off + (size_t)L.max_small * 16);
   L.act = off;       off = align_up(off + (size_t)P * (size_t)I * 2);
   L.zw = off;        off = align_up(off + (size_t)P * (size_t)H * 4);
   L.total = off;
@@ -86,21 +90,13 @@ Layout make_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-GemmConfig choose_config(int64_t P, int64_t E, int64_t H, int64_t I) {
-  // The wide loader/compute kernel stages every scale byte of its weight rows
-  // in LDS, which bounds K (= H for gate_up, I for down) at 4096.
-  const bool wide_ok = H <= 4096 && I <= 4096;
+// Full tiles of kWideTokens pairs go to the wide kernel unless the
+// environment asks for the streaming kernel alone (MXFP4MOE_PATH=stream, used
+// to test that kernel on every shape).
+int big_tile_tokens() {
   const char* env = std::getenv("MXFP4MOE_PATH");
-  if (env != nullptr) {
-    if (std::strcmp(env, "small") == 0) return kGemmSmall;
-    if (std::strcmp(env, "mid") == 0) return kGemmMid;
-    if (std::strcmp(env, "wide") == 0) return wide_ok ? kGemmWide : kGemmMid;
-  }
-  const int64_t active = E < P ? E : P;
-  const int64_t per_expert = active > 0 ? P / active : 0;
-  if (per_expert >= 96 && wide_ok) return kGemmWide;
-  if (per_expert >= 16) return kGemmMid;
-  return kGemmSmall;
+  if (env != nullptr && std::strcmp(env, "stream") == 0) return 0;
+  return kWideTokens;
 }
 
 int check_route_shape(int64_t T, int64_t E, int64_t top_k) {
@@ -151,7 +147,7 @@ int moe_mxfp4_route(const float* router_logits, int64_t T, int64_t E, int64_t to
   hipStream_t s = (hipStream_t)stream;
   hipError_t err = launch_route(router_logits, (int)T, (int)E, (int)top_k, topk_ids, topk_weights, s);
   if (err == hipSuccess)
-    err = launch_group(topk_ids, (int)(T * top_k), (int)E, expert_offsets, sorted_pairs, nullptr, nullptr, 32, s);
+    err = launch_group(topk_ids, (int)(T * top_k), (int)E, expert_offsets, sorted_pairs, TileTables{}, s);
   return err == hipSuccess ? MXFP4MOE_OK : MXFP4MOE_ERR_HIP;
 }
 
@@ -164,7 +160,7 @@ int moe_mxfp4_forward(const uint16_t* x, const float* router_logits, const uint8
   int st = check_route_shape(T, E, top_k);
   if (st != MXFP4MOE_OK) return st;
   if (H <= 0 || I <= 0 || (H & 31) != 0 || (I & 31) != 0) return MXFP4MOE_ERR_SHAPE;
-  if (H > (1 << 20) || I > (1 << 20)) return MXFP4MOE_ERR_SHAPE;
+  if (H > MXFP4MOE_MAX_HIDDEN || I > MXFP4MOE_MAX_HIDDEN) return MXFP4MOE_ERR_SHAPE;
   const Layout L = make_layout(T, H, I, E, top_k);
   if (workspace == nullptr) {
     *workspace_bytes = L.total;
@@ -185,26 +181,27 @@ int moe_mxfp4_forward(const uint16_t* x, const float* router_logits, const uint8
   float* weights = reinterpret_cast<float*>(ws + L.weights);
   int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
   int32_t* sorted = reinterpret_cast<int32_t*>(ws + L.sorted);
-  int32_t* num_tiles = reinterpret_cast<int32_t*>(ws + L.num_tiles);
-  int32_t* tiles = reinterpret_cast<int32_t*>(ws + L.tiles);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
   uint16_t* act = reinterpret_cast<uint16_t*>(ws + L.act);
   float* zw = reinterpret_cast<float*>(ws + L.zw);
 
   const int64_t P = T * top_k;
-  const GemmConfig cfg = choose_config(P, E, H, I);
-  const int tile_tokens = gemm_tile_tokens(cfg);
+  TileTables tt;
+  tt.big = reinterpret_cast<int32_t*>(ws + L.big);
+  tt.num_big = counts;
+  tt.small = reinterpret_cast<int32_t*>(ws + L.small);
+  tt.num_small = counts + 1;
+  tt.big_tokens = big_tile_tokens();
+  tt.small_tokens = kStreamTokens;
+  const int max_big = tt.big_tokens > 0 ? L.max_big : 0;
   hipStream_t s = (hipStream_t)stream;
 
   hipError_t err = launch_route(router_logits, (int)T, (int)E, (int)top_k, ids, weights, s);
-  if (err == hipSuccess)
-    err = launch_group(ids, (int)P, (int)E, offsets, sorted, tiles, num_tiles, tile_tokens, s);
+  if (err == hipSuccess) err = launch_group(ids, (int)P, (int)E, offsets, sorted, tt, s);
   GemmArgs g{};
   g.sorted_pairs = sorted;
-  g.tiles = tiles;
-  g.num_tiles = num_tiles;
   g.topk_weights = weights;
   g.top_k = (int)top_k;
-  g.max_tiles = max_tiles_for(P, E, tile_tokens);
   if (err == hipSuccess) {
     g.wblocks = w13_blocks;
     g.wscales = w13_scales;
@@ -213,7 +210,7 @@ int moe_mxfp4_forward(const uint16_t* x, const float* router_logits, const uint8
     g.out = act;
     g.N = (int)(2 * I);
     g.K = (int)H;
-    err = launch_gate_up(g, cfg, s);
+    err = launch_gate_up(g, tt, max_big, L.max_small, s);
   }
   if (err == hipSuccess) {
     g.wblocks = w2_blocks;
@@ -223,7 +220,7 @@ int moe_mxfp4_forward(const uint16_t* x, const float* router_logits, const uint8
     g.out = zw;
     g.N = (int)H;
     g.K = (int)I;
-    err = launch_down(g, cfg, s);
+    err = launch_down(g, tt, max_big, L.max_small, s);
   }
   if (err == hipSuccess) err = launch_combine(zw, y, (int)T, (int)H, (int)top_k, s);
   return err == hipSuccess ? MXFP4MOE_OK : MXFP4MOE_ERR_HIP;

@@ -19,8 +19,7 @@
 // (lane / 32) takes group h: it loads that group's 16 packed bytes of its
 // weight row with one 128-bit load and converts dword s (eight codes) to the
 // eight bf16 it feeds to MFMA step s.  The tokens' bf16 rows of the chunk are
-// staged in LDS (row stride 144 B, conflict-free 128-bit reads) and each lane
-// reads the eight values matching its weight codes.  Any consistent
+// staged in LDS and each lane reads the eight values matching its weight codes.  Any consistent
 // assignment of k to (lane half, step, element) yields the same dot products,
 // and this one needs no reshuffle of the checkpoint layout.  Weights are
 // dequantized exactly (E2M1 x 2^(s-127) is a bf16 value) and MFMA
@@ -34,16 +33,6 @@ using mx::bf16x8;
 using mx::f32x16;
 using mx::f32x4;
 using mx::u32x4;
-
-template <int WN, int WM, int RN, int RM>
-struct Shape {
-  static constexpr int kWaves = WN * WM;
-  static constexpr int kThreads = kWaves * 64;
-  static constexpr int BN = WN * RN * 32;  // weight rows per block
-  static constexpr int BM = WM * RM * 32;  // token columns per block
-  static constexpr int kSlots = BM * 8;    // 16-byte slots of one staged chunk (64 bf16 per token)
-  static constexpr int kSlotsPerThread = (kSlots + kThreads - 1) / kThreads;
-};
 
 // Staged token chunks are [BM][8] slots of 16 bytes with an XOR swizzle of the
 // slot column, so the 128-bit LDS reads of 8 (or 16) consecutive token rows at
@@ -89,50 +78,15 @@ __device__ __forceinline__ bool map_block(int num_tiles, int n_tiles, int& tile,
   return true;
 }
 
-// One 64-wide K chunk of MFMA work for a wave: `ncb` (wave-uniform, in an
-// SGPR) of its RM 32-token blocks hold tokens; each of the four K steps
-// converts the wave's weight codes and issues RN MFMAs per live block.  All
-// LDS reads of the chunk are issued before any conversion or MFMA (the
-// scheduling barrier keeps the compiler from sinking them next to their
-// uses), so the LDS latency is paid once per chunk instead of once per step.
+// One 64-wide K chunk of MFMA work for a wave: for each of the four K steps,
+// RN x RM MFMAs.  All LDS reads of the chunk are issued first (the scheduling
+// barrier keeps the compiler from sinking them next to their uses), and the
+// converts producing step s+1's weight fragments, written to the other half
+// of a double buffer, are interleaved with step s's MFMAs so the matrix core
+// does not wait for a burst of conversions.
 template <int RN, int RM>
-__device__ __forceinline__ void chunk_mma_live(int ncb, f32x16 (&acc)[RN][RM], const u32x4* __restrict__ xb,
-                                               const u32x4 (&w)[RN], const float (&sc)[RN], int m_wave, int lrow,
-                                               int half) {
-  bf16x8 b[4][RM];
-#pragma unroll
-  for (int cb = 0; cb < RM; ++cb) {
-    if (cb < ncb) {
-      const int row = m_wave + cb * 32 + lrow;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) b[s][cb] = __builtin_bit_cast(bf16x8, xb[row * 8 + slot_col(row, half * 4 + s)]);
-    }
-  }
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    bf16x8 a[RN];
-#pragma unroll
-    for (int rb = 0; rb < RN; ++rb) a[rb] = mx::as_bf16x8(mx::fp4x8_to_bf16x8(w[rb][s], sc[rb]));
-#pragma unroll
-    for (int cb = 0; cb < RM; ++cb) {
-      if (cb < ncb) {
-#pragma unroll
-        for (int rb = 0; rb < RN; ++rb)
-          acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[rb], b[s][cb], acc[rb][cb], 0, 0, 0);
-      }
-    }
-  }
-}
-
-// Branch-free chunk for tiles whose RM token blocks all hold tokens.  The
-// converts producing step s+1's weight fragments (into the other half of a
-// double buffer) are interleaved one-for-one with step s's MFMAs, so the
-// matrix core never waits for a burst of conversions.
-template <int RN, int RM>
-__device__ __forceinline__ void chunk_mma_full(f32x16 (&acc)[RN][RM], const u32x4* __restrict__ xb,
-                                               const u32x4 (&w)[RN], const float (&sc)[RN], int lrow, int half) {
-  static_assert(RN * RM >= 4 * RN, "one convert per MFMA needs RM >= 4");
+__device__ __forceinline__ void chunk_mma(f32x16 (&acc)[RN][RM], const u32x4* __restrict__ xb,
+                                          const u32x4 (&w)[RN], const float (&sc)[RN], int lrow, int half) {
   bf16x8 b[4][RM];
 #pragma unroll
   for (int cb = 0; cb < RM; ++cb) {
@@ -144,229 +98,35 @@ __device__ __forceinline__ void chunk_mma_full(f32x16 (&acc)[RN][RM], const u32x
   u32x4 a[2][RN];
 #pragma unroll
   for (int rb = 0; rb < RN; ++rb) a[0][rb] = mx::fp4x8_to_bf16x8(w[rb][0], sc[rb]);
+  auto convert = [&](int s, int i) {  // converts pair i%4 of fragment i/4 for step s
+    const int rb = i / 4, sel = i % 4;
+    const uint32_t packed = w[rb][s];
+    uint32_t v;
+    if (sel == 0) v = mx::fp4x2_to_bf16x2<0>(packed, sc[rb]);
+    else if (sel == 1) v = mx::fp4x2_to_bf16x2<1>(packed, sc[rb]);
+    else if (sel == 2) v = mx::fp4x2_to_bf16x2<2>(packed, sc[rb]);
+    else v = mx::fp4x2_to_bf16x2<3>(packed, sc[rb]);
+    a[s & 1][rb][sel] = v;
+  };
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
 #pragma unroll
     for (int i = 0; i < RN * RM; ++i) {
       const int rb = i % RN, cb = i / RN;
       acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mx::as_bf16x8(a[s & 1][rb]), b[s][cb], acc[rb][cb], 0, 0, 0);
-      if (s + 1 < 4 && i < 4 * RN) {
-        // convert dword (s+1) of weight fragment i/4, element pair i%4
-        const int nrb = i / 4, sel = i % 4;
-        const uint32_t packed = w[nrb][s + 1];
-        uint32_t v;
-        if (sel == 0) v = mx::fp4x2_to_bf16x2<0>(packed, sc[nrb]);
-        else if (sel == 1) v = mx::fp4x2_to_bf16x2<1>(packed, sc[nrb]);
-        else if (sel == 2) v = mx::fp4x2_to_bf16x2<2>(packed, sc[nrb]);
-        else v = mx::fp4x2_to_bf16x2<3>(packed, sc[nrb]);
-        a[(s + 1) & 1][nrb][sel] = v;
-      }
+      if (s + 1 < 4 && i < 4 * RN) convert(s + 1, i);
+    }
+    if (s + 1 < 4) {
+#pragma unroll
+      for (int i = RN * RM; i < 4 * RN; ++i) convert(s + 1, i);
     }
   }
 }
 
-// Epilogue.  Lane holds, for every (rb, cb), token m = m_wave + cb*32 + lrow
-// and features n = n_wave + rb*32 + 8i + 4*half + {0,1,2,3}, i = 0..3.
-// gate_up: add the bias, clamped SwiGLU of (gate, up) = (n, n+1), store a in
-// bf16 at the pair's expert-ordered row.  down: add the bias, multiply by the
-// pair's routing weight, store fp32 at the pair's own row.
-template <int RN, int RM, bool kGateUp>
-__device__ __forceinline__ void store_epilogue(const mxfp4moe::GemmArgs& args, const f32x16 (&acc)[RN][RM], int e,
-                                               int row0, int count, int n_wave, int m_wave, int cb_live, int half,
-                                               int lrow) {
-  const int N = args.N;
-  const uint16_t* bias = args.bias + (size_t)e * N;
-  uint2 bv[RN][4];
-#pragma unroll
-  for (int rb = 0; rb < RN; ++rb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int n = n_wave + rb * 32 + 8 * i + 4 * half;
-      n = n < N ? n : N - 4;
-      bv[rb][i] = *reinterpret_cast<const uint2*>(bias + n);
-    }
-#pragma unroll
-  for (int cb = 0; cb < RM; ++cb) {
-    if (cb >= cb_live) continue;
-    const int m = m_wave + cb * 32 + lrow;
-    if (m >= count) continue;
-    if (kGateUp) {
-      uint32_t* arow = reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(args.out) + (size_t)(row0 + m) * (N >> 1));
-#pragma unroll
-      for (int rb = 0; rb < RN; ++rb) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int n = n_wave + rb * 32 + 8 * i + 4 * half;
-          if (n < N) {
-            const uint2 bb = bv[rb][i];
-            const float b0 = mx::bf16_to_f32(bb.x & 0xffffu), b1 = mx::bf16_to_f32(bb.x >> 16);
-            const float b2 = mx::bf16_to_f32(bb.y & 0xffffu), b3 = mx::bf16_to_f32(bb.y >> 16);
-            const float a0 = swiglu_clamped(acc[rb][cb][4 * i + 0] + b0, acc[rb][cb][4 * i + 1] + b1);
-            const float a1 = swiglu_clamped(acc[rb][cb][4 * i + 2] + b2, acc[rb][cb][4 * i + 3] + b3);
-            arow[n >> 2] = mx::f32_to_bf16_rne(a0) | (mx::f32_to_bf16_rne(a1) << 16);
-          }
-        }
-      }
-    } else {
-      const int p = args.sorted_pairs[row0 + m];
-      const float w = args.topk_weights[p];
-      float* zrow = static_cast<float*>(args.out) + (size_t)p * N;
-#pragma unroll
-      for (int rb = 0; rb < RN; ++rb) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int n = n_wave + rb * 32 + 8 * i + 4 * half;
-          if (n < N) {
-            const uint2 bb = bv[rb][i];
-            f32x4 v;
-            v[0] = w * (acc[rb][cb][4 * i + 0] + mx::bf16_to_f32(bb.x & 0xffffu));
-            v[1] = w * (acc[rb][cb][4 * i + 1] + mx::bf16_to_f32(bb.x >> 16));
-            v[2] = w * (acc[rb][cb][4 * i + 2] + mx::bf16_to_f32(bb.y & 0xffffu));
-            v[3] = w * (acc[rb][cb][4 * i + 3] + mx::bf16_to_f32(bb.y >> 16));
-            *reinterpret_cast<f32x4*>(zrow + n) = v;
-          }
-        }
-      }
-    }
-  }
-}
-
-template <int WN, int WM, int RN, int RM, bool kGateUp>
-__global__ __launch_bounds__(WN * WM * 64, (WN * WM * 64 >= 256 && RN * RM >= 8) ? 2 : 1) void expert_gemm_kernel(
-    mxfp4moe::GemmArgs args) {
-  using S = Shape<WN, WM, RN, RM>;
-  __shared__ __attribute__((aligned(16))) u32x4 xs[2][S::kSlots];
-
-  const int N = args.N, K = args.K;
-  const int n_tiles = (N + S::BN - 1) / S::BN;
-  int tile, ntile;
-  if (!map_block(*args.num_tiles, n_tiles, tile, ntile)) return;  // uniform per block
-  const int4 tl = reinterpret_cast<const int4*>(args.tiles)[tile];
-  const int e = __builtin_amdgcn_readfirstlane(tl.x);
-  const int row0 = __builtin_amdgcn_readfirstlane(tl.y);
-  const int count = __builtin_amdgcn_readfirstlane(tl.z);
-
-  const int kgroups = K >> 5;
-  const int nchunks = (kgroups + 1) >> 1;
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  const int half = lane >> 5;
-  const int lrow = lane & 31;
-  const int wn = wave % WN, wm = wave / WN;
-  const int n_wave = ntile * S::BN + wn * RN * 32;
-  const int m_wave = wm * RM * 32;
-  int cb_live = (count - m_wave + 31) >> 5;  // 32-token blocks of this wave holding tokens
-  cb_live = __builtin_amdgcn_readfirstlane(cb_live < 0 ? 0 : (cb_live > RM ? RM : cb_live));
-
-  // Weight rows of this lane (rows past N re-read row N-1; their outputs are dropped).
-  const uint8_t* wrow[RN];
-  const uint8_t* srow[RN];
-#pragma unroll
-  for (int rb = 0; rb < RN; ++rb) {
-    int n = n_wave + rb * 32 + lrow;
-    n = n < N ? n : N - 1;
-    wrow[rb] = args.wblocks + ((size_t)e * N + n) * (size_t)(K >> 1);
-    srow[rb] = args.wscales + ((size_t)e * N + n) * (size_t)kgroups;
-  }
-
-  // Slots this thread stages: slot p = t + i*threads holds token row p/8,
-  // logical 16-byte column slot_col^-1 of p%8.  Rows past `count` re-read the
-  // tile's first row (their columns are never stored).
-  const uint16_t* xsrc[S::kSlotsPerThread];
-  int xcol[S::kSlotsPerThread];
-#pragma unroll
-  for (int i = 0; i < S::kSlotsPerThread; ++i) {
-    const int p = threadIdx.x + i * S::kThreads;
-    const int r = p >> 3;
-    const int part = slot_col(r, p & 7);  // the swizzle is an involution on the column
-    int rr = r < count ? r : 0;
-    size_t src_row;
-    if (kGateUp)
-      src_row = (size_t)(args.sorted_pairs[row0 + rr] / args.top_k);
-    else
-      src_row = (size_t)(row0 + rr);
-    xsrc[i] = args.act + src_row * (size_t)K + part * 8;
-    xcol[i] = part * 8;
-  }
-
-  u32x4 xstage[S::kSlotsPerThread];
-  auto load_x = [&](int c) {
-#pragma unroll
-    for (int i = 0; i < S::kSlotsPerThread; ++i) {
-      if (S::kSlots % S::kThreads == 0 || threadIdx.x + i * S::kThreads < S::kSlots) {
-        // K tail: the missing half chunk re-reads the first half (its weights are zero)
-        const int koff = (c * 64 + xcol[i] < K) ? c * 64 : c * 64 - 32;
-        xstage[i] = *reinterpret_cast<const u32x4*>(xsrc[i] + koff);
-      }
-    }
-  };
-  auto store_x = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < S::kSlotsPerThread; ++i)
-      if (S::kSlots % S::kThreads == 0 || threadIdx.x + i * S::kThreads < S::kSlots)
-        xs[buf][threadIdx.x + i * S::kThreads] = xstage[i];
-  };
-
-  u32x4 wcur[RN], wnxt[RN];
-  uint32_t scur[RN], snxt[RN];
-  auto load_w = [&](int c, u32x4* w, uint32_t* s) {
-    const int g = 2 * c + half;
-    const int gg = g < kgroups ? g : g - 1;
-#pragma unroll
-    for (int rb = 0; rb < RN; ++rb) {
-      w[rb] = *reinterpret_cast<const u32x4*>(wrow[rb] + (size_t)gg * 16);
-      s[rb] = srow[rb][gg];
-    }
-  };
-
-  f32x16 acc[RN][RM];
-#pragma unroll
-  for (int rb = 0; rb < RN; ++rb)
-#pragma unroll
-    for (int cb = 0; cb < RM; ++cb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[rb][cb][r] = 0.f;
-
-  load_w(0, wcur, scur);
-  load_x(0);
-  store_x(0);
-  __syncthreads();
-
-  for (int c = 0; c < nchunks; ++c) {
-    const int buf = c & 1;
-    const bool more = c + 1 < nchunks;
-    if (more) {
-      load_w(c + 1, wnxt, snxt);
-      load_x(c + 1);
-    }
-    const bool glive = 2 * c + half < kgroups;
-    {
-      u32x4 w[RN];
-      float sc[RN];
-#pragma unroll
-      for (int rb = 0; rb < RN; ++rb) {
-        w[rb] = glive ? wcur[rb] : u32x4{0u, 0u, 0u, 0u};
-        sc[rb] = mx::e8m0_operand(scur[rb]);
-      }
-      chunk_mma_live<RN, RM>(cb_live, acc, xs[buf], w, sc, m_wave, lrow, half);
-    }
-    if (more) {
-      store_x(buf ^ 1);
-#pragma unroll
-      for (int rb = 0; rb < RN; ++rb) {
-        wcur[rb] = wnxt[rb];
-        scur[rb] = snxt[rb];
-      }
-    }
-    __syncthreads();
-  }
-
-  store_epilogue<RN, RM, kGateUp>(args, acc, e, row0, count, n_wave, m_wave, cb_live, half, lrow);
-}
-
-// Wide tiles for prefill-sized expert groups.
+// The expert GEMM kernel.
 //
-// One wave per SIMD, each computing a (32*RN) x (32*RM) tile with its
+// One wave per SIMD in the wide configuration (several per SIMD in the
+// streaming one), each computing a (32*RN) x (32*RM) tile with its
 // accumulators in registers; WN waves stack along the weight rows, so a block
 // covers (32*RN*WN) weight rows x (32*RM) tokens and every staged token chunk
 // feeds WN waves.  Per 64-wide K chunk a block moves BM*128 bytes of tokens
@@ -375,11 +135,99 @@ __global__ __launch_bounds__(WN * WM * 64, (WN * WM * 64 >= 256 && RN * RM >= 8)
 // chunk c from LDS; all loads of a wave have the same age, so they complete in
 // order without draining the ring.  Staged chunks are written to the spare of
 // two LDS stages; one barrier per chunk.  The scale bytes of the block's
-// weight rows are staged once, group-major.
+// weight rows are staged once.  Tiles always hold RM*32 live tokens except the
+// remainder tiles of the streaming configuration (RM = 1), whose dead token
+// columns are computed and dropped.
 constexpr int kWideMaxGroups = 128;  // K <= 4096
 
-template <int WN, int RN, int RM, int kDepth, bool kGateUp>
-__global__ __launch_bounds__(WN * 64, 1) void expert_gemm_wide_kernel(mxfp4moe::GemmArgs args) {
+// Epilogue, staged through an LDS region of RM*32*128 bytes per wave so
+// that every token's outputs leave as full 128-byte rows: the lane layout of
+// the MFMA results (four consecutive features of one token per lane) is
+// written to LDS as [token][features] (16-byte chunks XOR-swizzled by token),
+// then read back along the features and stored with 16-byte stores.
+// gate_up: bias, clamped SwiGLU, bf16 -> a[pair row][I] (16*RN activations,
+// 32*RN bytes, per token per wave).  down: bias, routing weight, fp32 ->
+// zw[pair][H], one 32-feature slab (128 bytes per token) per pass.
+template <int RN, int RM, bool kGateUp>
+__device__ __forceinline__ void store_epilogue(const mxfp4moe::GemmArgs& args, const f32x16 (&acc)[RN][RM], int e,
+                                              int row0, int count, int n_wave, int lane, uint8_t* region) {
+  const int N = args.N;
+  const int half = lane >> 5, lrow = lane & 31;
+  const uint16_t* bias = args.bias + (size_t)e * N;
+  auto chunk_addr = [](int m, int chunk) { return m * 128 + ((chunk ^ (m & 7)) << 4); };
+  if (kGateUp) {
+    // stage a[m][q_local], q_local = 0..16*RN-1 for this wave's 32*RN rows of w13
+#pragma unroll
+    for (int rb = 0; rb < RN; ++rb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        int n = n_wave + rb * 32 + 8 * i + 4 * half;
+        const uint2 bb = *reinterpret_cast<const uint2*>(bias + (n < N ? n : N - 4));
+        const float b0 = mx::bf16_to_f32(bb.x & 0xffffu), b1 = mx::bf16_to_f32(bb.x >> 16);
+        const float b2 = mx::bf16_to_f32(bb.y & 0xffffu), b3 = mx::bf16_to_f32(bb.y >> 16);
+        const int byte = rb * 32 + 8 * i + 4 * half;  // 2 * q_local
+#pragma unroll
+        for (int cb = 0; cb < RM; ++cb) {
+          const int m = cb * 32 + lrow;
+          const float a0 = swiglu_clamped(acc[rb][cb][4 * i + 0] + b0, acc[rb][cb][4 * i + 1] + b1);
+          const float a1 = swiglu_clamped(acc[rb][cb][4 * i + 2] + b2, acc[rb][cb][4 * i + 3] + b3);
+          *reinterpret_cast<uint32_t*>(region + chunk_addr(m, byte >> 4) + (byte & 15)) =
+              mx::f32_to_bf16_rne(a0) | (mx::f32_to_bf16_rne(a1) << 16);
+        }
+      }
+    }
+    const int I = N >> 1;
+    const int q0 = n_wave >> 1;
+    constexpr int kChunks = 2 * RN;  // 16-byte chunks of a per token (RN*16 activations)
+#pragma unroll 4
+    for (int j = 0; j < RM * 32 * kChunks / 64; ++j) {
+      const int idx = j * 64 + lane;
+      const int m = idx / kChunks, chunk = idx % kChunks;
+      const int q = q0 + chunk * 8;
+      if (m < count && q < I) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(region + chunk_addr(m, chunk));
+        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(args.out) + (size_t)(row0 + m) * I + q) = v;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int rb = 0; rb < RN; ++rb) {
+      // stage zw[m][32 features of block rb]
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        int n = n_wave + rb * 32 + 8 * i + 4 * half;
+        const uint2 bb = *reinterpret_cast<const uint2*>(bias + (n < N ? n : N - 4));
+        const float b0 = mx::bf16_to_f32(bb.x & 0xffffu), b1 = mx::bf16_to_f32(bb.x >> 16);
+        const float b2 = mx::bf16_to_f32(bb.y & 0xffffu), b3 = mx::bf16_to_f32(bb.y >> 16);
+#pragma unroll
+        for (int cb = 0; cb < RM; ++cb) {
+          const int m = cb * 32 + lrow;
+          const float w = m < count ? args.topk_weights[args.sorted_pairs[row0 + m]] : 0.f;
+          f32x4 v;
+          v[0] = w * (acc[rb][cb][4 * i + 0] + b0);
+          v[1] = w * (acc[rb][cb][4 * i + 1] + b1);
+          v[2] = w * (acc[rb][cb][4 * i + 2] + b2);
+          v[3] = w * (acc[rb][cb][4 * i + 3] + b3);
+          *reinterpret_cast<f32x4*>(region + chunk_addr(m, 2 * i + half)) = v;
+        }
+      }
+#pragma unroll 4
+      for (int j = 0; j < RM * 32 * 8 / 64; ++j) {
+        const int idx = j * 64 + lane;
+        const int m = idx >> 3, chunk = idx & 7;
+        const int n = n_wave + rb * 32 + chunk * 4;
+        if (m < count && n < N) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(region + chunk_addr(m, chunk));
+          const int p = args.sorted_pairs[row0 + m];
+          *reinterpret_cast<f32x4*>(static_cast<float*>(args.out) + (size_t)p * N + n) = v;
+        }
+      }
+    }
+  }
+}
+
+template <int WN, int RN, int RM, int kDepth, int kMinBlocks, bool kGateUp>
+__global__ __launch_bounds__(WN * 64, kMinBlocks) void expert_gemm_kernel(mxfp4moe::GemmArgs args) {
   constexpr int kThreads = WN * 64;
   constexpr int BN = WN * RN * 32;
   constexpr int BM = RM * 32;
@@ -388,9 +236,10 @@ __global__ __launch_bounds__(WN * 64, 1) void expert_gemm_wide_kernel(mxfp4moe::
   constexpr int kXPer = kXSlots / kThreads;
   constexpr int kWPer = kWSlots / kThreads;
   static_assert(kXSlots % kThreads == 0 && kWSlots % kThreads == 0, "tile / thread mismatch");
+  static_assert(WN == 4 && RN >= RM, "four epilogue regions of RM*32*128 bytes");
   __shared__ __attribute__((aligned(16))) u32x4 xs[2][kXSlots];
   __shared__ __attribute__((aligned(16))) u32x4 wsm[2][kWSlots];
-  __shared__ uint8_t sst[BN * kWideMaxGroups];
+  __shared__ __attribute__((aligned(16))) uint8_t sst[BN * kWideMaxGroups];
 
   const int N = args.N, K = args.K;
   const int n_tiles = (N + BN - 1) / BN;
@@ -409,13 +258,15 @@ __global__ __launch_bounds__(WN * 64, 1) void expert_gemm_wide_kernel(mxfp4moe::
   const int half = lane >> 5;
   const int lrow = lane & 31;
 
-  // scale bytes of the block's rows, group-major: sst[g * BN + row]
-  for (int i = t; i < BN * kgroups; i += kThreads) {
-    const int r = i / kgroups;
-    const int g = i - r * kgroups;
-    int n = ntile * BN + r;
-    n = n < N ? n : N - 1;
-    sst[g * BN + r] = args.wscales[((size_t)e * N + n) * (size_t)kgroups + g];
+  // Scale bytes of the block's rows, row-major as in memory: the block's rows
+  // are one contiguous, 32-byte aligned range (row counts and tile starts are
+  // multiples of 32), copied with 16-byte loads.  Rows past N are not copied
+  // (their outputs are dropped).
+  {
+    const int nv = min(BN, N - ntile * BN);
+    const u32x4* src = reinterpret_cast<const u32x4*>(args.wscales + ((size_t)e * N + ntile * BN) * (size_t)kgroups);
+    u32x4* dst = reinterpret_cast<u32x4*>(sst);
+    for (int i = t; i < (nv * kgroups) >> 4; i += kThreads) dst[i] = src[i];
   }
 
   // token slot p = t + i*threads -> row p/8, logical column slot_col(row, p%8);
@@ -466,10 +317,9 @@ __global__ __launch_bounds__(WN * 64, 1) void expert_gemm_wide_kernel(mxfp4moe::
 
   // compute-side constants
   const int n_wave = ntile * BN + wave * RN * 32;
-  int cb_live = (count + 31) >> 5;
-  cb_live = __builtin_amdgcn_readfirstlane(cb_live > RM ? RM : cb_live);
   const int wslot0 = (wave * RN * 32 + lrow) * 2 + half;
-  const uint8_t* srow = sst + wave * RN * 32 + lrow;
+  const uint8_t* srow = sst + (wave * RN * 32 + lrow) * kgroups;
+  const int rb_stride = 32 * kgroups;
 
   f32x16 acc[RN][RM];
 #pragma unroll
@@ -503,24 +353,29 @@ __global__ __launch_bounds__(WN * 64, 1) void expert_gemm_wide_kernel(mxfp4moe::
 #pragma unroll
         for (int rb = 0; rb < RN; ++rb) {
           w[rb] = wsm[st][wslot0 + rb * 64];
-          sc[rb] = mx::e8m0_operand(srow[gg * BN + rb * 32]);
+          sc[rb] = mx::e8m0_operand(srow[rb * rb_stride + gg]);
           if (!glive) w[rb] = u32x4{0u, 0u, 0u, 0u};
         }
-        chunk_mma_full<RN, RM>(acc, xs[st], w, sc, lrow, half);
+        chunk_mma<RN, RM>(acc, xs[st], w, sc, lrow, half);
       }
       __syncthreads();
     }
   }
-  store_epilogue<RN, RM, kGateUp>(args, acc, e, row0, count, n_wave, 0, cb_live, half, lrow);
+  // every wave has passed the loop's last barrier: the staging buffers are free
+  uint8_t* region = wave == 0 ? reinterpret_cast<uint8_t*>(xs[0])
+                  : wave == 1 ? reinterpret_cast<uint8_t*>(xs[1])
+                  : wave == 2 ? reinterpret_cast<uint8_t*>(wsm[0]) : reinterpret_cast<uint8_t*>(wsm[1]);
+  store_epilogue<RN, RM, kGateUp>(args, acc, e, row0, count, n_wave, lane, region);
 }
 
-template <int WN, int RN, int RM, int kDepth, bool kGateUp>
-hipError_t launch_wide(const mxfp4moe::GemmArgs& a, hipStream_t stream) {
+template <int WN, int RN, int RM, int kDepth, int kMinBlocks, bool kGateUp>
+hipError_t launch_cfg(const mxfp4moe::GemmArgs& a, hipStream_t stream) {
   constexpr int BN = WN * RN * 32;
   const long n_tiles = (a.N + BN - 1) / BN;
   const long blocks = n_tiles * a.max_tiles;
+  if (blocks == 0) return hipSuccess;
   const long grid = (blocks + kXcds - 1) / kXcds * kXcds;
-  expert_gemm_wide_kernel<WN, RN, RM, kDepth, kGateUp><<<(unsigned)grid, WN * 64, 0, stream>>>(a);
+  expert_gemm_kernel<WN, RN, RM, kDepth, kMinBlocks, kGateUp><<<(unsigned)grid, WN * 64, 0, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -547,47 +402,43 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   *reinterpret_cast<uint2*>(y + (size_t)t * H + n) = o;
 }
 
-template <int WN, int WM, int RN, int RM, bool kGateUp>
-hipError_t launch_cfg(const mxfp4moe::GemmArgs& a, hipStream_t stream) {
-  using S = Shape<WN, WM, RN, RM>;
-  const long n_tiles = (a.N + S::BN - 1) / S::BN;
-  const long blocks = n_tiles * a.max_tiles;
-  const long grid = (blocks + kXcds - 1) / kXcds * kXcds;
-  expert_gemm_kernel<WN, WM, RN, RM, kGateUp><<<(unsigned)grid, S::kThreads, 0, stream>>>(a);
-  return hipGetLastError();
-}
-
 }  // namespace
 
 namespace mxfp4moe {
 
-// small: 4 waves x 32 weight rows, 32 tokens; mid: 2x2 waves of 64 rows x 32 tokens;
-// wide: 4 waves of 128 rows x 128 tokens (block 512 x 128), register-ring staging.
-#define MX_SMALL 4, 1, 1, 1
-#define MX_MID 2, 2, 2, 1
-#define MX_WIDE_WN 4
-#define MX_WIDE_RN 4
-#define MX_WIDE_RM 4
-#define MX_WIDE_DEPTH 2
+// wide: 4 waves of 128 weight rows x 128 tokens (block 512 x 128), one wave per SIMD.
+// stream: 4 waves of 32 weight rows x 32 tokens (block 128 x 32), several blocks per CU,
+// a deeper ring so that enough weight bytes are in flight for HBM streaming.
+#define MX_WIDE 4, 4, 4, 2, 1
+#define MX_STREAM 4, 1, 1, 6, 4
+static_assert(kWideTokens == 4 * 32 && kStreamTokens == 1 * 32, "tile sizes");
 
-int gemm_tile_tokens(GemmConfig cfg) {
-  return cfg == kGemmSmall ? Shape<MX_SMALL>::BM : cfg == kGemmMid ? Shape<MX_MID>::BM : (MX_WIDE_RM * 32);
+template <bool kGateUp>
+static hipError_t launch_both(GemmArgs a, const TileTables& tt, int max_big, int max_small, hipStream_t stream) {
+  hipError_t err = hipSuccess;
+  if (tt.big_tokens > 0 && max_big > 0) {
+    a.tiles = tt.big;
+    a.num_tiles = tt.num_big;
+    a.max_tiles = max_big;
+    err = launch_cfg<MX_WIDE, kGateUp>(a, stream);
+  }
+  if (err == hipSuccess && max_small > 0) {
+    a.tiles = tt.small;
+    a.num_tiles = tt.num_small;
+    a.max_tiles = max_small;
+    err = launch_cfg<MX_STREAM, kGateUp>(a, stream);
+  }
+  return err;
 }
 
-hipError_t launch_gate_up(const GemmArgs& a, GemmConfig cfg, hipStream_t stream) {
-  if (a.max_tiles == 0) return hipSuccess;
+hipError_t launch_gate_up(GemmArgs a, const TileTables& tt, int max_big, int max_small, hipStream_t stream) {
   ProfileScope prof(kStageGateUp, stream);
-  if (cfg == kGemmSmall) return launch_cfg<MX_SMALL, true>(a, stream);
-  if (cfg == kGemmMid) return launch_cfg<MX_MID, true>(a, stream);
-  return launch_wide<MX_WIDE_WN, MX_WIDE_RN, MX_WIDE_RM, MX_WIDE_DEPTH, true>(a, stream);
+  return launch_both<true>(a, tt, max_big, max_small, stream);
 }
 
-hipError_t launch_down(const GemmArgs& a, GemmConfig cfg, hipStream_t stream) {
-  if (a.max_tiles == 0) return hipSuccess;
+hipError_t launch_down(GemmArgs a, const TileTables& tt, int max_big, int max_small, hipStream_t stream) {
   ProfileScope prof(kStageDown, stream);
-  if (cfg == kGemmSmall) return launch_cfg<MX_SMALL, false>(a, stream);
-  if (cfg == kGemmMid) return launch_cfg<MX_MID, false>(a, stream);
-  return launch_wide<MX_WIDE_WN, MX_WIDE_RN, MX_WIDE_RM, MX_WIDE_DEPTH, false>(a, stream);
+  return launch_both<false>(a, tt, max_big, max_small, stream);
 }
 
 hipError_t launch_combine(const float* zw, uint16_t* y, int T, int H, int top_k, hipStream_t stream) {

@@ -33,23 +33,30 @@ class ProfileScope {
 
 int device_cu_count();
 
-// Tile configurations of the expert GEMMs.  Both GEMMs of one call use the
-// same token tile (the tile table is shared).
-enum GemmConfig : int {
-  kGemmSmall = 0,  // 32 token columns per tile: decode-sized expert groups
-  kGemmMid = 1,    // 64 token columns per tile
-  kGemmWide = 2,   // 256 token columns per tile: prefill-sized expert groups
+// Token tiles of the expert GEMMs.  Every expert's pairs are cut into full
+// tiles of kWideTokens pairs, computed by the wide kernel, and a remainder
+// cut into tiles of kStreamTokens pairs, computed by the streaming kernel
+// (which is also the whole path for decode-sized batches).
+constexpr int kWideTokens = 128;
+constexpr int kStreamTokens = 32;
+
+struct TileTables {
+  int32_t* big;        // [max_big][4]   = {expert, first sorted row, rows, 0}
+  int32_t* num_big;
+  int32_t* small;      // [max_small][4]
+  int32_t* num_small;
+  int big_tokens;      // 0: no full tiles, everything goes to the small table
+  int small_tokens;
 };
-int gemm_tile_tokens(GemmConfig cfg);
 
 // Routing: one wave per token.
 hipError_t launch_route(const float* logits, int T, int E, int top_k, int32_t* ids, float* weights,
                         hipStream_t stream);
 
 // Grouping: counts, offsets, stable expert-ordered pair list, and (when
-// tiles != nullptr) the GEMM tile table for tiles of `tile_tokens` pairs.
+// tt.big != nullptr) the GEMM tile tables.
 hipError_t launch_group(const int32_t* ids, int P, int E, int32_t* offsets, int32_t* sorted_pairs,
-                        int32_t* tiles, int32_t* num_tiles, int tile_tokens, hipStream_t stream);
+                        const TileTables& tt, hipStream_t stream);
 
 struct GemmArgs {
   const uint8_t* wblocks;   // [E, N, K/2]
@@ -64,8 +71,10 @@ struct GemmArgs {
   int N, K, top_k, max_tiles;
 };
 
-hipError_t launch_gate_up(const GemmArgs& a, GemmConfig cfg, hipStream_t stream);
-hipError_t launch_down(const GemmArgs& a, GemmConfig cfg, hipStream_t stream);
+// Both GEMM stages launch the wide kernel over the full tiles (when there are
+// any) and the streaming kernel over the remainder tiles.
+hipError_t launch_gate_up(GemmArgs a, const TileTables& tt, int max_big, int max_small, hipStream_t stream);
+hipError_t launch_down(GemmArgs a, const TileTables& tt, int max_big, int max_small, hipStream_t stream);
 hipError_t launch_combine(const float* zw, uint16_t* y, int T, int H, int top_k, hipStream_t stream);
 
 hipError_t launch_dequant(const uint8_t* blocks, const uint8_t* scales, uint16_t* out, int64_t N, int64_t K,

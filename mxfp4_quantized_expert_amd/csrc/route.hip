@@ -107,7 +107,9 @@ __device__ int block_exclusive_scan_wave0(const int* vals, int* out, int n, int*
 }
 
 // Single workgroup: histogram of experts, exclusive scan into offsets, a
-// stable scatter of pair ids into expert order, and the GEMM tile table.
+// stable scatter of pair ids into expert order, and the GEMM tile tables:
+// full tiles of big_tokens pairs, then every expert's remainder in tiles of
+// small_tokens pairs.
 // The scatter walks the pairs in chunks of 1024; inside a wave the lanes with
 // the same expert are found by matching the expert id bit by bit with
 // ballots, and the per-wave counts are turned into positions wave by wave, so
@@ -115,8 +117,7 @@ __device__ int block_exclusive_scan_wave0(const int* vals, int* out, int n, int*
 __global__ __launch_bounds__(kGroupThreads) void group_kernel(const int32_t* __restrict__ ids, int P, int E,
                                                               int32_t* __restrict__ offsets,
                                                               int32_t* __restrict__ sorted_pairs,
-                                                              int32_t* __restrict__ tiles,
-                                                              int32_t* __restrict__ num_tiles, int tile_tokens) {
+                                                              mxfp4moe::TileTables tt) {
   extern __shared__ int smem[];
   int* cnt = smem;                 // [E]
   int* base = cnt + E;             // [E]
@@ -133,20 +134,33 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(const int32_t* __r
   for (int e = threadIdx.x; e < E; e += kGroupThreads) offsets[e] = base[e];
   if (threadIdx.x == 0) offsets[E] = P;
 
-  if (tiles != nullptr) {
-    for (int e = threadIdx.x; e < E; e += kGroupThreads) ntile[e] = (cnt[e] + tile_tokens - 1) / tile_tokens;
+  if (tt.big != nullptr) {
+    // full tiles of big_tokens pairs: expert e owns cnt[e] / big_tokens of them
+    const int bt = tt.big_tokens;
+    for (int e = threadIdx.x; e < E; e += kGroupThreads) ntile[e] = bt > 0 ? cnt[e] / bt : 0;
     __syncthreads();
-    const int n_tiles = block_exclusive_scan_wave0(ntile, tile_base, E, &total_slot);
-    if (threadIdx.x == 0) *num_tiles = n_tiles;
+    const int n_big = block_exclusive_scan_wave0(ntile, tile_base, E, &total_slot);
+    if (threadIdx.x == 0) *tt.num_big = n_big;
     for (int e = threadIdx.x; e < E; e += kGroupThreads) {
-      for (int i = 0; i < ntile[e]; ++i) {
-        int4 tl;
-        tl.x = e;
-        tl.y = base[e] + i * tile_tokens;
-        tl.z = min(tile_tokens, cnt[e] - i * tile_tokens);
-        tl.w = 0;
-        reinterpret_cast<int4*>(tiles)[tile_base[e] + i] = tl;
-      }
+      for (int i = 0; i < ntile[e]; ++i)
+        reinterpret_cast<int4*>(tt.big)[tile_base[e] + i] = int4{e, base[e] + i * bt, bt, 0};
+    }
+    __syncthreads();
+    // the remainder of every expert in tiles of small_tokens pairs
+    const int st = tt.small_tokens;
+    for (int e = threadIdx.x; e < E; e += kGroupThreads) {
+      const int rem = bt > 0 ? cnt[e] % bt : cnt[e];
+      ntile[e] = (rem + st - 1) / st;
+    }
+    __syncthreads();
+    const int n_small = block_exclusive_scan_wave0(ntile, tile_base, E, &total_slot);
+    if (threadIdx.x == 0) *tt.num_small = n_small;
+    for (int e = threadIdx.x; e < E; e += kGroupThreads) {
+      const int done = bt > 0 ? cnt[e] / bt * bt : 0;
+      const int rem = cnt[e] - done;
+      for (int i = 0; i < ntile[e]; ++i)
+        reinterpret_cast<int4*>(tt.small)[tile_base[e] + i] =
+            int4{e, base[e] + done + i * st, min(st, rem - i * st), 0};
     }
   }
 
@@ -198,11 +212,10 @@ hipError_t launch_route(const float* logits, int T, int E, int top_k, int32_t* i
 }
 
 hipError_t launch_group(const int32_t* ids, int P, int E, int32_t* offsets, int32_t* sorted_pairs,
-                        int32_t* tiles, int32_t* num_tiles, int tile_tokens, hipStream_t stream) {
+                        const TileTables& tt, hipStream_t stream) {
   const size_t smem = (size_t)(4 + kGroupWaves) * E * sizeof(int);
   ProfileScope prof(kStageGroup, stream);
-  group_kernel<<<1, kGroupThreads, smem, stream>>>(ids, P, E, offsets, sorted_pairs, tiles, num_tiles,
-                                                   tile_tokens);
+  group_kernel<<<1, kGroupThreads, smem, stream>>>(ids, P, E, offsets, sorted_pairs, tt);
   return hipGetLastError();
 }
 

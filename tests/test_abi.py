@@ -80,6 +80,9 @@ def test_forward_argument_checks(lib):
     assert _fwd(lib, E=64, k=33)[0] == -2     # top_k above the maximum
     assert _fwd(lib, H=48)[0] == -2           # not a multiple of 32
     assert _fwd(lib, I=40)[0] == -2
+    assert _fwd(lib, H=4128)[0] == -2         # above the largest supported hidden size
+    assert _fwd(lib, I=4128)[0] == -2
+    assert _fwd(lib, H=4096, I=4096, ws=None, ws_bytes=0)[0] == 0  # size query accepted
     assert _fwd(lib, b13=None)[0] == -1       # biases are required
     assert _fwd(lib, b2=None)[0] == -1
     assert _fwd(lib, x=None)[0] == -1
