@@ -9,7 +9,9 @@ one batch of synthetic tokens whose inputs are already resident in HBM.
 
 Prints one JSON line.  Workloads: 120b_prefill (default: gpt-oss-120b shaped
 layer, T=4096 long prefill with Zipf-skewed routing), 20b_prefill, 20b_decode,
-tiny, and dequant_120b (the standalone dequant of a 120b-shaped w13 bank).
+tiny, dequant_120b (the standalone dequant of a 120b-shaped w13 bank) and copy
+(a plain 1 GiB device copy: the achievable-bandwidth reference that also
+calibrates the HBM byte counters).
 """
 
 from __future__ import annotations
@@ -27,7 +29,7 @@ if ROOT not in sys.path:
 METRIC = "MoE-layer tokens/s; decode HBM GB/s & prefill MFMA TFLOP/s vs MI355X peak"
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
-W13_BYTES_PER_ROW_PER_K = 0.5 + 1.0 / 32.0  # packed nibbles + one E8M0 byte per 32
+PEAK_FP4_TFLOPS = 10100.0    # MI355X dense fp4 MFMA
 
 
 def log(*a):
@@ -42,31 +44,50 @@ def layer_bytes(H, I):
 
 
 def cpu_baseline_moe(layer, spec, budget_s=15.0):
-    """Time the float64 CPU oracle on the first tokens of the same layer."""
+    """Time the float64 CPU oracle, single-threaded, on the first tokens of the same layer."""
     import numpy as np
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_limits
 
     from oracle import mxfp4_moe as O
 
     n = 1
     elapsed = 0.0
-    while True:
-        tokens = np.arange(min(n, spec.T))
-        t0 = time.perf_counter()
-        O.moe_forward(layer, spec.top_k, tokens=tokens)
-        elapsed = time.perf_counter() - t0
-        if elapsed >= budget_s / 3 or n >= spec.T:
-            break
-        n *= 2
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    with threadpool_limits(limits=1):
+        while True:
+            tokens = np.arange(min(n, spec.T))
+            t0 = time.perf_counter()
+            O.moe_forward(layer, spec.top_k, tokens=tokens)
+            elapsed = time.perf_counter() - t0
+            if elapsed >= budget_s / 3 or n >= spec.T:
+                break
+            n *= 2
     return {
         "value": len(tokens) / elapsed,
         "unit": "tokens/s",
-        "cores": int(threads),
+        "cores": 1,
         "kind": "oracle",
-        "sample": f"first {len(tokens)} of {spec.T} tokens of the same layer, float64 numpy oracle, "
-                  f"{elapsed:.1f} s",
+        "sample": f"first {len(tokens)} of {spec.T} tokens of the same layer through the float64 numpy "
+                  f"oracle, one BLAS thread, {elapsed:.1f} s (host has {os.cpu_count()} cores)",
     }
+
+
+def copy_bandwidth(nbytes=1 << 30, reps=10):
+    """Achievable HBM bandwidth of a plain device copy (read + write bytes / time)."""
+    import torch
+
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    stop.record()
+    stop.synchronize()
+    ms = start.elapsed_time(stop) / reps
+    del src, dst
+    return 2 * nbytes / (ms / 1e3) / 1e9, ms
 
 
 def run_moe(args):
@@ -74,21 +95,23 @@ def run_moe(args):
     import torch
 
     from mxfp4_quantized_expert_amd import binding, workloads
-    from oracle import mxfp4_moe as O
 
     spec = workloads.LAYERS[args.workload]
     T, H, I, E, k = spec.T, spec.H, spec.I, spec.E, spec.top_k
+    P = T * k
     log(f"[bench] generating {args.workload}: T={T} H={H} I={I} E={E} k={k}")
     layer = workloads.make_layer(spec)
-    ids, _ = O.route(layer["router_logits"], k)
-    counts = np.bincount(ids.ravel(), minlength=E)
+    dev = binding.layer_to_device(layer, "cuda")
+    # Expert loads from the library's own routing (used for the roofline accounting).
+    _, _, offsets, _ = binding.moe_mxfp4_route(dev["router_logits"], k)
+    counts = np.diff(offsets.cpu().numpy().astype(np.int64))
     n_active = int((counts > 0).sum())
+    full_pairs = int((counts // 128).sum() * 128)
     w13_b, w2_b = layer_bytes(H, I)
     # Weight copies rotate so that repeated steps cannot be served from the
     # 256 MB Infinity Cache when the active weights would fit in it.
     active_bytes = n_active * (w13_b + w2_b)
     copies = 1 if active_bytes > 512e6 else max(2, int(np.ceil(1.2e9 / (E * (w13_b + w2_b)))))
-    dev = binding.layer_to_device(layer, "cuda")
     weight_sets = [dev]
     for _ in range(copies - 1):
         weight_sets.append({kk: (v.clone() if kk.startswith("w") else v) for kk, v in dev.items()})
@@ -106,45 +129,56 @@ def run_moe(args):
         step(i)
     torch.cuda.synchronize()
 
-    binding.profile_begin("gate_up", args.steps)
+    # The dominant kernel: gate_up over full 128-pair tiles when there are any,
+    # else gate_up over the streamed tiles.  Its launches inside the timed
+    # region are bracketed with HIP events on the stream they run on.
+    dominant = "gate_up_wide" if full_pairs > 0 else "gate_up_stream"
+    binding.profile_begin(dominant, args.steps)
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    gate_up_ms = binding.profile_end(args.steps)
+    dom_ms = binding.profile_end(args.steps)
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     value = T / (ms_per_step / 1e3)
-    gu_ms = float(np.mean(gate_up_ms))
+    kms = float(np.mean(dom_ms))
 
-    # Stage breakdown (outside the timed region, diagnostics on stderr).
+    # Stage breakdown (outside the timed region, diagnostics).
     stages = {}
-    for st in ["route", "group", "gate_up", "down", "combine"]:
+    for st in ["route", "group", "gate_up", "gate_up_wide", "gate_up_mid", "gate_up_stream", "down",
+               "down_wide", "down_mid", "down_stream", "combine"]:
         binding.profile_begin(st, 5)
         for i in range(5):
             step(i)
         torch.cuda.synchronize()
-        stages[st] = float(np.mean(binding.profile_end(5)))
+        got = binding.profile_end(5)
+        stages[st] = float(np.mean(got)) if got else 0.0
     log("[bench] stage ms: " + ", ".join(f"{s}={v:.4f}" for s, v in stages.items()))
+    copy_gbs, _ = copy_bandwidth()
 
-    P = T * k
     flops_total = 6.0 * H * I * P
-    gu_flops = 4.0 * H * I * P
-    gu_bytes = n_active * w13_b + P * (2 * H + 2 * I)  # weights of active experts + x rows in + a rows out
-    if P / max(n_active, 1) >= 64:
-        roof = {"bound": "mfma", "achieved": gu_flops / (gu_ms / 1e3) / 1e12, "peak": PEAK_BF16_TFLOPS,
+    if dominant == "gate_up_wide":
+        # 2*H*2I FLOPs per pair, over the pairs of the full tiles
+        work = 4.0 * H * I * full_pairs
+        roof = {"bound": "mfma", "achieved": work / (kms / 1e3) / 1e12, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s"}
+        per_unit = f"33,177,600 FLOPs per pair at H=I=2880 (2*H*2I) x {full_pairs} pairs in full tiles"
     else:
-        roof = {"bound": "hbm", "achieved": gu_bytes / (gu_ms / 1e3) / 1e9, "peak": PEAK_HBM_GBS,
-                "unit": "GB/s"}
+        # packed w13 (blocks, scales, bias) of every active expert + x rows + a rows out
+        work = n_active * w13_b + T * H * 2 + P * I * 2
+        roof = {"bound": "hbm", "achieved": work / (kms / 1e3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+        per_unit = (f"{w13_b} B of packed w13 per active expert x {n_active} + x {T * H * 2} B + a {P * I * 2} B")
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = None
-    roof["kernel"] = "gate_up grouped GEMM (expert_gemm_kernel, gate_up epilogue)"
-    roof["kernel_ms"] = gu_ms
+    roof["kernel"] = f"expert_gemm_kernel, {dominant.replace('_', ' ')} launch"
+    roof["kernel_ms"] = kms
+    roof["algorithmic"] = per_unit
+    layer_tflops = flops_total / (ms_per_step / 1e3) / 1e12
+    alg_bytes = active_bytes + T * H * 2 + T * E * 4 + T * H * 2
     log(f"[bench] {args.workload}: {ms_per_step:.4f} ms/step, {value:.1f} tokens/s, "
-        f"layer {flops_total / (ms_per_step / 1e3) / 1e12:.1f} TFLOP/s, "
-        f"active experts {n_active}, weight bytes {active_bytes / 1e6:.1f} MB -> "
-        f"{active_bytes / (ms_per_step / 1e3) / 1e9:.1f} GB/s; copies {copies}")
+        f"layer {layer_tflops:.1f} TFLOP/s, active experts {n_active}, weight bytes {active_bytes / 1e6:.1f} MB "
+        f"-> {alg_bytes / (ms_per_step / 1e3) / 1e9:.1f} GB/s; copies {copies}; copy kernel {copy_gbs:.0f} GB/s")
 
     out = {
         "metric": METRIC,
@@ -163,12 +197,16 @@ def run_moe(args):
             "workload": f"{args.workload}: MXFP4 MoE expert layer T={T} H={H} I={I} E={E} top_k={k}"
                         + (f", Zipf({spec.zipf_s}) routing skew" if spec.zipf_s else ""),
             "T": T, "H": H, "I": I, "E": E, "top_k": k,
-            "weights": "mxfp4 (e2m1 codes, e8m0 scale per 32)",
-            "accumulate": "fp32",
+            "weights": "mxfp4 (e2m1 codes, e8m0 scale per 32), bf16 MFMA, fp32 accumulate",
             "active_experts": n_active,
+            "pairs_in_full_tiles": full_pairs,
             "weight_copies_rotated": copies,
-            "layer_tflops": flops_total / (ms_per_step / 1e3) / 1e12,
-            "active_weight_gbs": active_bytes / (ms_per_step / 1e3) / 1e9,
+            "layer_tflops": layer_tflops,
+            "layer_frac_bf16_peak": layer_tflops / PEAK_BF16_TFLOPS,
+            "layer_frac_fp4_peak": layer_tflops / PEAK_FP4_TFLOPS,
+            "layer_algorithmic_gbs": alg_bytes / (ms_per_step / 1e3) / 1e9,
+            "layer_frac_hbm_peak": alg_bytes / (ms_per_step / 1e3) / 1e9 / PEAK_HBM_GBS,
+            "hbm_copy_gbs": copy_gbs,
             "stage_ms": stages,
         },
         "roofline": roof,
@@ -176,6 +214,14 @@ def run_moe(args):
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_moe(layer, spec)
     return out
+
+
+def run_copy(args):
+    gbs, ms = copy_bandwidth(reps=args.steps)
+    return {"metric": "device copy GB/s", "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": 2, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "u8", "data": "synthetic",
+            "config": {"workload": "copy of a 1 GiB device buffer (torch copy kernel), read + write bytes"}}
 
 
 def run_dequant(args):
@@ -233,7 +279,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="120b_prefill",
-                    choices=["120b_prefill", "20b_prefill", "20b_decode", "tiny", "dequant_120b"])
+                    choices=["120b_prefill", "20b_prefill", "20b_decode", "tiny", "dequant_120b", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -247,7 +293,12 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
-    res = run_dequant(args) if args.workload == "dequant_120b" else run_moe(args)
+    if args.workload == "dequant_120b":
+        res = run_dequant(args)
+    elif args.workload == "copy":
+        res = run_copy(args)
+    else:
+        res = run_moe(args)
     print(json.dumps(res), flush=True)
 
 

@@ -130,10 +130,11 @@ int moe_mxfp4_route(const float* router_logits, int64_t T, int64_t E, int64_t to
  * Biases are required (a NULL bias is MXFP4MOE_ERR_ARG); there is no mode that
  * applies the routing weight to the input.  Accumulation is fp32; the SwiGLU
  * output is rounded to bf16 before the down GEMM.  T == 0 is a no-op.
- * Each expert's pairs are cut into full tiles of 128 (one GEMM kernel
- * configuration) and a remainder in tiles of 32 (a streaming configuration
- * that is also the whole decode path); MXFP4MOE_PATH=stream in the environment
- * sends every pair through the streaming configuration.
+ * Each expert's pairs are cut into full tiles of 128 pairs and one remainder
+ * tile, each kind with a GEMM kernel of its own (the streaming kernel for
+ * remainders of at most 32 pairs is the whole decode path);
+ * MXFP4MOE_PATH=stream in the environment sends every pair through the
+ * streaming kernel, in tiles of 32.
  */
 int moe_mxfp4_forward(const uint16_t* x, const float* router_logits,
                       const uint8_t* w13_blocks, const uint8_t* w13_scales, const uint16_t* w13_bias,
@@ -148,7 +149,9 @@ const char* mxfp4moe_status_string(int status);
  * Kernel timing hook for benchmarks.  mxfp4moe_profile_begin(stage, max_calls)
  * makes the next max_calls launches of one kernel stage record a pair of HIP
  * events around that launch, on the stream the kernel runs on.  Stages:
- * 1 route, 2 group, 3 gate_up GEMM, 4 down GEMM, 5 combine, 6 dequant.
+ * 1 route, 2 group, 3 gate_up GEMM, 4 down GEMM, 5 combine, 6 dequant,
+ * then single launches of the GEMM stages: 7 / 11 / 8 the full-tile /
+ * mid-remainder / streaming launch of gate_up, 9 / 12 / 10 the same for down.
  * mxfp4moe_profile_end(ms, capacity) synchronises on the recorded events,
  * stores up to `capacity` per-launch durations in milliseconds (host array),
  * releases the events and returns how many were stored (negative on error).

@@ -25,7 +25,9 @@ STATUS = {
     -5: "HIP launch error",
 }
 
-STAGES = {"route": 1, "group": 2, "gate_up": 3, "down": 4, "combine": 5, "dequant": 6}
+STAGES = {"route": 1, "group": 2, "gate_up": 3, "down": 4, "combine": 5, "dequant": 6,
+          "gate_up_wide": 7, "gate_up_stream": 8, "down_wide": 9, "down_stream": 10,
+          "gate_up_mid": 11, "down_mid": 12}
 
 _lib: Optional[ctypes.CDLL] = None
 

@@ -57,30 +57,40 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t ids, weights, offsets, sorted, counts, big, small, act, zw, total;
-  int max_big, max_small;
+  size_t ids, weights, offsets, sorted, counts, big, mid, small, act, zw, total;
+  int max_big, max_mid, max_small;
 };
 
-// Tile table bounds: the full tiles of all experts hold at most P pairs; every
-// expert with pairs adds at most one partial small tile on top of P/32 full ones.
-int max_big_tiles(int64_t P) { return (int)(P / kWideTokens); }
-int max_small_tiles(int64_t P, int64_t E) {
+// Tile table capacities.  An expert gets at most T pairs (a token's k
+// experts are distinct).  Full tiles hold at most P pairs; every expert with
+// pairs has at most one remainder tile, and a mid remainder holds more than
+// kStreamTokens pairs.  Without full tiles the streaming table holds up to
+// P/kStreamTokens full tiles plus one partial tile per expert.
+TileBounds tile_bounds(int64_t T, int64_t P, int64_t E, bool wide) {
   const int64_t active = E < P ? E : P;
-  return (int)((P + kStreamTokens - 1) / kStreamTokens + active);
+  TileBounds b;
+  b.max_big = (wide && T >= kWideTokens) ? (int)(P / kWideTokens) : 0;
+  const int64_t mids = P / (kStreamTokens + 1);
+  b.max_mid = (wide && T > kStreamTokens) ? (int)(active < mids ? active : mids) : 0;
+  b.max_small = wide ? (int)active : (int)(P / kStreamTokens + active);
+  return b;
 }
 
 Layout make_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k) {
   const int64_t P = T * top_k;
   Layout L;
-  L.max_big = max_big_tiles(P);
-  L.max_small = max_small_tiles(P, E);
+  const TileBounds with_wide = tile_bounds(T, P, E, true), stream_only = tile_bounds(T, P, E, false);
+  L.max_big = with_wide.max_big;
+  L.max_mid = with_wide.max_mid;
+  L.max_small = stream_only.max_small;  // the larger of the two
   size_t off = 0;
   L.ids = off;       off = align_up(off + (size_t)P * 4);
   L.weights = off;   off = align_up(off + (size_t)P * 4);
   L.offsets = off;   off = align_up(off + (size_t)(E + 1) * 4);
   L.sorted = off;    off = align_up(off + (size_t)P * 4);
-  L.counts = off;    off = align_up(off + 8);
+  L.counts = off;    off = align_up(off + 12);
   L.big = off;       off = align_up(off + (size_t)L.max_big * 16);
+  L.mid = off;       off = align_up(off + (size_t)L.max_mid * 16);
   L.small = off;     off = align_up(off + (size_t)L.max_small * 16);
   L.act = off;       off = align_up(off + (size_t)P * (size_t)I * 2);
   L.zw = off;        off = align_up(off + (size_t)P * (size_t)H * 4);
@@ -161,6 +171,7 @@ int moe_mxfp4_forward(const uint16_t* x, const float* router_logits, const uint8
   if (st != MXFP4MOE_OK) return st;
   if (H <= 0 || I <= 0 || (H & 31) != 0 || (I & 31) != 0) return MXFP4MOE_ERR_SHAPE;
   if (H > MXFP4MOE_MAX_HIDDEN || I > MXFP4MOE_MAX_HIDDEN) return MXFP4MOE_ERR_SHAPE;
+  static_assert(MXFP4MOE_MAX_HIDDEN == kMaxHidden, "one bound on H and I");
   const Layout L = make_layout(T, H, I, E, top_k);
   if (workspace == nullptr) {
     *workspace_bytes = L.total;
@@ -189,11 +200,12 @@ int moe_mxfp4_forward(const uint16_t* x, const float* router_logits, const uint8
   TileTables tt;
   tt.big = reinterpret_cast<int32_t*>(ws + L.big);
   tt.num_big = counts;
+  tt.mid = reinterpret_cast<int32_t*>(ws + L.mid);
+  tt.num_mid = counts + 1;
   tt.small = reinterpret_cast<int32_t*>(ws + L.small);
-  tt.num_small = counts + 1;
+  tt.num_small = counts + 2;
   tt.big_tokens = big_tile_tokens();
-  tt.small_tokens = kStreamTokens;
-  const int max_big = tt.big_tokens > 0 ? L.max_big : 0;
+  const TileBounds tb = tile_bounds(T, P, E, tt.big_tokens > 0);
   hipStream_t s = (hipStream_t)stream;
 
   hipError_t err = launch_route(router_logits, (int)T, (int)E, (int)top_k, ids, weights, s);
@@ -210,7 +222,7 @@ int moe_mxfp4_forward(const uint16_t* x, const float* router_logits, const uint8
     g.out = act;
     g.N = (int)(2 * I);
     g.K = (int)H;
-    err = launch_gate_up(g, tt, max_big, L.max_small, s);
+    err = launch_gate_up(g, tt, tb, s);
   }
   if (err == hipSuccess) {
     g.wblocks = w2_blocks;
@@ -220,14 +232,14 @@ int moe_mxfp4_forward(const uint16_t* x, const float* router_logits, const uint8
     g.out = zw;
     g.N = (int)H;
     g.K = (int)I;
-    err = launch_down(g, tt, max_big, L.max_small, s);
+    err = launch_down(g, tt, tb, s);
   }
   if (err == hipSuccess) err = launch_combine(zw, y, (int)T, (int)H, (int)top_k, s);
   return err == hipSuccess ? MXFP4MOE_OK : MXFP4MOE_ERR_HIP;
 }
 
 int mxfp4moe_profile_begin(int stage, int max_calls) {
-  if (stage < kStageRoute || stage > kStageDequant || max_calls < 1 || max_calls > 100000)
+  if (stage < kStageRoute || stage > kStageLast || max_calls < 1 || max_calls > 100000)
     return MXFP4MOE_ERR_ARG;
   std::lock_guard<std::mutex> lk(g_prof_mu);
   for (hipEvent_t ev : g_prof_start) (void)hipEventDestroy(ev);

@@ -140,6 +140,20 @@ __device__ __forceinline__ void chunk_mma(f32x16 (&acc)[RN][RM], const u32x4* __
 // columns are computed and dropped.
 constexpr int kWideMaxGroups = 128;  // K <= 4096
 
+// Scale bytes of a block's BN weight rows, row-major as in memory: the rows
+// are one contiguous, 32-byte aligned range (row counts and tile starts are
+// multiples of 32), copied with 16-byte loads.  Rows past N are not copied
+// (their outputs are dropped).
+template <int BN, int kThreads>
+__device__ __forceinline__ void stage_scales(uint8_t* sst, const mxfp4moe::GemmArgs& args, int e, int ntile,
+                                             int kgroups, int t) {
+  const int N = args.N;
+  const int nv = min(BN, N - ntile * BN);
+  const u32x4* src = reinterpret_cast<const u32x4*>(args.wscales + ((size_t)e * N + ntile * BN) * (size_t)kgroups);
+  u32x4* dst = reinterpret_cast<u32x4*>(sst);
+  for (int i = t; i < (nv * kgroups) >> 4; i += kThreads) dst[i] = src[i];
+}
+
 // Epilogue, staged through an LDS region of RM*32*128 bytes per wave so
 // that every token's outputs leave as full 128-byte rows: the lane layout of
 // the MFMA results (four consecutive features of one token per lane) is
@@ -226,17 +240,18 @@ __device__ __forceinline__ void store_epilogue(const mxfp4moe::GemmArgs& args, c
   }
 }
 
-template <int WN, int RN, int RM, int kDepth, int kMinBlocks, bool kGateUp>
-__global__ __launch_bounds__(WN * 64, kMinBlocks) void expert_gemm_kernel(mxfp4moe::GemmArgs args) {
-  constexpr int kThreads = WN * 64;
+template <int WN, int WM, int RN, int RM, int kDepth, int kMinBlocks, bool kGateUp>
+__global__ __launch_bounds__(WN * WM * 64, kMinBlocks) void expert_gemm_kernel(mxfp4moe::GemmArgs args) {
+  constexpr int kThreads = WN * WM * 64;
   constexpr int BN = WN * RN * 32;
-  constexpr int BM = RM * 32;
+  constexpr int BM = WM * RM * 32;
   constexpr int kXSlots = BM * 8;  // 16-byte token slots per chunk
   constexpr int kWSlots = BN * 2;  // 16-byte weight slots per chunk (one 32-code group each)
   constexpr int kXPer = kXSlots / kThreads;
   constexpr int kWPer = kWSlots / kThreads;
   static_assert(kXSlots % kThreads == 0 && kWSlots % kThreads == 0, "tile / thread mismatch");
-  static_assert(WN == 4 && RN >= RM, "four epilogue regions of RM*32*128 bytes");
+  static_assert(WN * WM == 4 && BM * 128 >= RM * 4096 && BN * 32 >= RM * 4096,
+                "four waves, each with an epilogue region of RM*32*128 bytes");
   __shared__ __attribute__((aligned(16))) u32x4 xs[2][kXSlots];
   __shared__ __attribute__((aligned(16))) u32x4 wsm[2][kWSlots];
   __shared__ __attribute__((aligned(16))) uint8_t sst[BN * kWideMaxGroups];
@@ -254,20 +269,12 @@ __global__ __launch_bounds__(WN * 64, kMinBlocks) void expert_gemm_kernel(mxfp4m
   const int niter = (nchunks + kDepth - 1) / kDepth * kDepth;  // padded: every iteration is branch-free
   const int t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wn = wave % WN, wm = wave / WN;  // the wave's weight-row block and token block
   const int lane = t & 63;
   const int half = lane >> 5;
   const int lrow = lane & 31;
 
-  // Scale bytes of the block's rows, row-major as in memory: the block's rows
-  // are one contiguous, 32-byte aligned range (row counts and tile starts are
-  // multiples of 32), copied with 16-byte loads.  Rows past N are not copied
-  // (their outputs are dropped).
-  {
-    const int nv = min(BN, N - ntile * BN);
-    const u32x4* src = reinterpret_cast<const u32x4*>(args.wscales + ((size_t)e * N + ntile * BN) * (size_t)kgroups);
-    u32x4* dst = reinterpret_cast<u32x4*>(sst);
-    for (int i = t; i < (nv * kgroups) >> 4; i += kThreads) dst[i] = src[i];
-  }
+  stage_scales<BN, kThreads>(sst, args, e, ntile, kgroups, t);
 
   // token slot p = t + i*threads -> row p/8, logical column slot_col(row, p%8);
   // rows past `count` re-read the tile's first row (their columns are never stored)
@@ -316,9 +323,11 @@ __global__ __launch_bounds__(WN * 64, kMinBlocks) void expert_gemm_kernel(mxfp4m
   };
 
   // compute-side constants
-  const int n_wave = ntile * BN + wave * RN * 32;
-  const int wslot0 = (wave * RN * 32 + lrow) * 2 + half;
-  const uint8_t* srow = sst + (wave * RN * 32 + lrow) * kgroups;
+  const int n_wave = ntile * BN + wn * RN * 32;
+  const int wslot0 = (wn * RN * 32 + lrow) * 2 + half;
+  const uint8_t* srow = sst + (wn * RN * 32 + lrow) * kgroups;
+  const int m_wave = wm * RM * 32;
+  const bool live = m_wave < count;  // wave-uniform: token blocks past the tile's pairs skip their MFMAs
   const int rb_stride = 32 * kgroups;
 
   f32x16 acc[RN][RM];
@@ -343,7 +352,7 @@ __global__ __launch_bounds__(WN * 64, kMinBlocks) void expert_gemm_kernel(mxfp4m
       // then refill that slot with chunk c+1+kDepth
       commit((u + 1) % kDepth, (c + 1) & 1);
       issue(c + 1 + kDepth, (u + 1) % kDepth);
-      if (c < nchunks) {
+      if (c < nchunks && live) {
         const int st = c & 1;
         const int g = 2 * c + half;
         const bool glive = g < kgroups;
@@ -356,7 +365,7 @@ __global__ __launch_bounds__(WN * 64, kMinBlocks) void expert_gemm_kernel(mxfp4m
           sc[rb] = mx::e8m0_operand(srow[rb * rb_stride + gg]);
           if (!glive) w[rb] = u32x4{0u, 0u, 0u, 0u};
         }
-        chunk_mma<RN, RM>(acc, xs[st], w, sc, lrow, half);
+        chunk_mma<RN, RM>(acc, xs[st] + m_wave * 8, w, sc, lrow, half);
       }
       __syncthreads();
     }
@@ -365,17 +374,200 @@ __global__ __launch_bounds__(WN * 64, kMinBlocks) void expert_gemm_kernel(mxfp4m
   uint8_t* region = wave == 0 ? reinterpret_cast<uint8_t*>(xs[0])
                   : wave == 1 ? reinterpret_cast<uint8_t*>(xs[1])
                   : wave == 2 ? reinterpret_cast<uint8_t*>(wsm[0]) : reinterpret_cast<uint8_t*>(wsm[1]);
-  store_epilogue<RN, RM, kGateUp>(args, acc, e, row0, count, n_wave, lane, region);
+  if (live) store_epilogue<RN, RM, kGateUp>(args, acc, e, row0 + m_wave, count - m_wave, n_wave, lane, region);
 }
 
-template <int WN, int RN, int RM, int kDepth, int kMinBlocks, bool kGateUp>
+template <int WN, int WM, int RN, int RM, int kDepth, int kMinBlocks, bool kGateUp>
 hipError_t launch_cfg(const mxfp4moe::GemmArgs& a, hipStream_t stream) {
   constexpr int BN = WN * RN * 32;
   const long n_tiles = (a.N + BN - 1) / BN;
   const long blocks = n_tiles * a.max_tiles;
   if (blocks == 0) return hipSuccess;
   const long grid = (blocks + kXcds - 1) / kXcds * kXcds;
-  expert_gemm_kernel<WN, RN, RM, kDepth, kMinBlocks, kGateUp><<<(unsigned)grid, WN * 64, 0, stream>>>(a);
+  expert_gemm_kernel<WN, WM, RN, RM, kDepth, kMinBlocks, kGateUp><<<(unsigned)grid, WN * WM * 64, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+// Streaming kernel for tiles of at most kStreamTokens pairs: decode batches
+// and the smallest per-expert remainders of prefill.  It runs on the 16x16x32
+// bf16 MFMA, whose A operand gives lane l row l%16 and the eight K values of
+// quarter q = l/16: so lane (r, q) can take one whole E8M0 group (16 bytes,
+// 32 codes, four MFMA steps) and the four lanes of a row read 64 contiguous
+// bytes of it per load instruction, the pattern that lets HBM stream at full
+// rate (a 32-byte piece per row per instruction does not).  Chunk j holds K
+// [128j, 128j+128): lane (r, q) supplies group 4j+q, and step s uses its codes
+// [8s, 8s+8), i.e. K = 128j + 32q + 8s + i; the B operand (token l%16) holds
+// the same K values of its token.  Sixteen token columns instead of 32 halve
+// the MFMA work of a few-token tile.
+//
+// A block owns 64*RN weight rows of one expert; it copies the tile's token
+// rows and the rows' scale bytes into LDS, then each wave streams its own
+// 16*RN rows from global memory straight into registers, kBatch chunks per
+// batch (every load of a batch issued before its first MFMA; the batches of
+// the several waves per SIMD overlap).  Token columns past the tile's pairs
+// read its first pair (their outputs are dropped).  Even and odd steps
+// accumulate separately.  Outputs: lane (n, q) holds rows 4q..4q+3 of each
+// 16-row block for token n, i.e. two gate/up pairs (gate_up) or four
+// consecutive features (down), stored directly.
+//
+// Dynamic LDS: tokens [kStreamTokens][K] bf16 | scales [64*RN][K/32].
+template <int RN>
+__host__ __device__ constexpr size_t stream_lds_bytes(int K) {
+  return (size_t)mxfp4moe::kStreamTokens * K * 2 + (size_t)64 * RN * (K / 32);
+}
+
+template <int RN, int kBatch, bool kGateUp>
+__global__ __launch_bounds__(256, 4) void expert_stream_kernel(mxfp4moe::GemmArgs args) {
+  constexpr int kThreads = 256;
+  constexpr int BN = 64 * RN;
+  extern __shared__ u32x4 dyn[];
+  uint8_t* const lds = reinterpret_cast<uint8_t*>(dyn);
+
+  const int N = args.N, K = args.K;
+  const int n_tiles = (N + BN - 1) / BN;
+  int tile, ntile;
+  if (!map_block(*args.num_tiles, n_tiles, tile, ntile)) return;  // uniform per block
+  const int4 tl = reinterpret_cast<const int4*>(args.tiles)[tile];
+  const int e = __builtin_amdgcn_readfirstlane(tl.x);
+  const int row0 = __builtin_amdgcn_readfirstlane(tl.y);
+  const int count = __builtin_amdgcn_readfirstlane(tl.z);
+  const int kgroups = K >> 5;
+  const int nchunks = (kgroups + 3) >> 2;
+  const int t = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int lane = t & 63;
+  const int q = lane >> 4;
+  const int lr = lane & 15;
+
+  uint16_t* const xl = reinterpret_cast<uint16_t*>(lds);
+  uint8_t* const sl = lds + (size_t)mxfp4moe::kStreamTokens * K * 2;
+  {
+    // token rows: at most 4 x K/8 <= 2048 pieces of 16 bytes, all loads issued
+    // before the first store
+    static_assert(mxfp4moe::kStreamTokens == 4 && mxfp4moe::kMaxHidden * 4 / 8 <= 8 * kThreads, "copy bounds");
+    size_t xsrc[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int rr = r < count ? r : 0;
+      xsrc[r] = (kGateUp ? (size_t)(args.sorted_pairs[row0 + rr] / args.top_k) : (size_t)(row0 + rr)) * (size_t)K;
+    }
+    const int k16 = K >> 3;
+    const int nx16 = count * k16;
+    u32x4 xv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = min(t + j * kThreads, nx16 - 1);
+      const int r = i / k16, p = i - r * k16;
+      const size_t base = r == 0 ? xsrc[0] : r == 1 ? xsrc[1] : r == 2 ? xsrc[2] : xsrc[3];
+      if (j * kThreads < nx16) xv[j] = reinterpret_cast<const u32x4*>(args.act + base)[p];
+    }
+    stage_scales<BN, kThreads>(sl, args, e, ntile, kgroups, t);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (t + j * kThreads < nx16) reinterpret_cast<u32x4*>(xl)[t + j * kThreads] = xv[j];
+  }
+  __syncthreads();
+
+  const int n_wave = ntile * BN + wave * 16 * RN;
+  if (n_wave >= N) return;  // wave-uniform; no barrier follows
+  f32x4 acc[RN][2];
+#pragma unroll
+  for (int rb = 0; rb < RN; ++rb)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[rb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const uint8_t* wrow[RN];
+  const uint8_t* srow[RN];
+#pragma unroll
+  for (int rb = 0; rb < RN; ++rb) {
+    const int r = min(n_wave + rb * 16 + lr, N - 1);  // rows past N: outputs dropped
+    wrow[rb] = args.wblocks + ((size_t)e * N + r) * (size_t)(K >> 1);
+    srow[rb] = sl + (wave * 16 * RN + rb * 16 + lr) * kgroups;
+  }
+  const uint16_t* xrow = xl + (lr < count ? lr : 0) * K;
+  for (int c0 = 0; c0 < nchunks; c0 += kBatch) {
+    u32x4 w[kBatch][RN];
+    // A group past the last one (K tail, or a padding chunk of the last
+    // batch) reads the last group's weights, scale and token values, which
+    // are finite, and multiplies zero weights.
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int g = min(4 * (c0 + j) + q, kgroups - 1);
+#pragma unroll
+      for (int rb = 0; rb < RN; ++rb) w[j][rb] = *reinterpret_cast<const u32x4*>(wrow[rb] + (size_t)g * 16);
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int g0 = 4 * (c0 + j) + q;
+      const bool glive = g0 < kgroups;
+      const int g = glive ? g0 : kgroups - 1;
+      bf16x8 b[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        b[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xrow + g * 32 + 8 * s));
+#pragma unroll
+      for (int rb = 0; rb < RN; ++rb) {
+        const float sc = mx::e8m0_operand(srow[rb][g]);
+        const u32x4 wj = glive ? w[j][rb] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const bf16x8 a = mx::as_bf16x8(mx::fp4x8_to_bf16x8(wj[s], sc));
+          acc[rb][s & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[s], acc[rb][s & 1], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  if (lr >= count) return;
+  const uint16_t* bias = args.bias + (size_t)e * N;
+#pragma unroll
+  for (int rb = 0; rb < RN; ++rb) {
+    const int n = n_wave + rb * 16 + 4 * q;  // first of this lane's four rows
+    if (n >= N) continue;
+    const uint2 bb = *reinterpret_cast<const uint2*>(bias + n);
+    f32x4 v;
+    v[0] = acc[rb][0][0] + acc[rb][1][0] + mx::bf16_to_f32(bb.x & 0xffffu);
+    v[1] = acc[rb][0][1] + acc[rb][1][1] + mx::bf16_to_f32(bb.x >> 16);
+    v[2] = acc[rb][0][2] + acc[rb][1][2] + mx::bf16_to_f32(bb.y & 0xffffu);
+    v[3] = acc[rb][0][3] + acc[rb][1][3] + mx::bf16_to_f32(bb.y >> 16);
+    if (kGateUp) {
+      const int I = N >> 1;
+      const uint32_t packed = mx::f32_to_bf16_rne(swiglu_clamped(v[0], v[1])) |
+                              (mx::f32_to_bf16_rne(swiglu_clamped(v[2], v[3])) << 16);
+      *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(args.out) + (size_t)(row0 + lr) * I + (n >> 1)) = packed;
+    } else {
+      const int p = args.sorted_pairs[row0 + lr];
+      const float wt = args.topk_weights[p];
+      v[0] *= wt;
+      v[1] *= wt;
+      v[2] *= wt;
+      v[3] *= wt;
+      *reinterpret_cast<f32x4*>(static_cast<float*>(args.out) + (size_t)p * N + n) = v;
+    }
+  }
+}
+
+#ifndef MX_STREAM_RN
+#define MX_STREAM_RN 1
+#endif
+#ifndef MX_STREAM_BATCH
+#define MX_STREAM_BATCH 8
+#endif
+
+template <bool kGateUp>
+hipError_t launch_stream(const mxfp4moe::GemmArgs& a, hipStream_t stream) {
+  constexpr int RN = MX_STREAM_RN;
+  constexpr int kBatch = MX_STREAM_BATCH;
+  constexpr int BN = 64 * RN;
+  const long n_tiles = (a.N + BN - 1) / BN;
+  const long blocks = n_tiles * a.max_tiles;
+  if (blocks == 0) return hipSuccess;
+  const long grid = (blocks + kXcds - 1) / kXcds * kXcds;
+  const size_t lds = stream_lds_bytes<RN>(a.K);
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&expert_stream_kernel<RN, kBatch, kGateUp>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, (int)stream_lds_bytes<RN>(mxfp4moe::kMaxHidden));
+  if (attr != hipSuccess) return attr;
+  expert_stream_kernel<RN, kBatch, kGateUp><<<(unsigned)grid, 256, lds, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -407,38 +599,49 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 namespace mxfp4moe {
 
 // wide: 4 waves of 128 weight rows x 128 tokens (block 512 x 128), one wave per SIMD.
-// stream: 4 waves of 32 weight rows x 32 tokens (block 128 x 32), several blocks per CU,
-// a deeper ring so that enough weight bytes are in flight for HBM streaming.
-#define MX_WIDE 4, 4, 4, 2, 1
-#define MX_STREAM 4, 1, 1, 6, 4
-static_assert(kWideTokens == 4 * 32 && kStreamTokens == 1 * 32, "tile sizes");
+// mid: 4 waves stacked along the tokens, each 128 weight rows x 32 tokens (block
+// 128 x 128), two blocks per CU; waves past the tile's pairs skip their MFMAs.
+// stream: 16x16x32 MFMA, 4 waves of 16*MX_STREAM_RN weight rows x (at most 4)
+// tokens, weights streamed in batches of MX_STREAM_BATCH chunks of 128 K.
+#define MX_WIDE 4, 1, 4, 4, 2, 1
+#define MX_MID 1, 4, 4, 1, 2, 2
+static_assert(kWideTokens == 128 && kStreamTokens == 4, "tile sizes");
 
 template <bool kGateUp>
-static hipError_t launch_both(GemmArgs a, const TileTables& tt, int max_big, int max_small, hipStream_t stream) {
+static hipError_t launch_all(GemmArgs a, const TileTables& tt, const TileBounds& tb, hipStream_t stream) {
   hipError_t err = hipSuccess;
-  if (tt.big_tokens > 0 && max_big > 0) {
+  if (tb.max_big > 0) {
+    ProfileScope prof(kGateUp ? kStageGateUpWide : kStageDownWide, stream);
     a.tiles = tt.big;
     a.num_tiles = tt.num_big;
-    a.max_tiles = max_big;
+    a.max_tiles = tb.max_big;
     err = launch_cfg<MX_WIDE, kGateUp>(a, stream);
   }
-  if (err == hipSuccess && max_small > 0) {
+  if (err == hipSuccess && tb.max_mid > 0) {
+    ProfileScope prof(kGateUp ? kStageGateUpMid : kStageDownMid, stream);
+    a.tiles = tt.mid;
+    a.num_tiles = tt.num_mid;
+    a.max_tiles = tb.max_mid;
+    err = launch_cfg<MX_MID, kGateUp>(a, stream);
+  }
+  if (err == hipSuccess && tb.max_small > 0) {
+    ProfileScope prof(kGateUp ? kStageGateUpStream : kStageDownStream, stream);
     a.tiles = tt.small;
     a.num_tiles = tt.num_small;
-    a.max_tiles = max_small;
-    err = launch_cfg<MX_STREAM, kGateUp>(a, stream);
+    a.max_tiles = tb.max_small;
+    err = launch_stream<kGateUp>(a, stream);
   }
   return err;
 }
 
-hipError_t launch_gate_up(GemmArgs a, const TileTables& tt, int max_big, int max_small, hipStream_t stream) {
+hipError_t launch_gate_up(GemmArgs a, const TileTables& tt, const TileBounds& tb, hipStream_t stream) {
   ProfileScope prof(kStageGateUp, stream);
-  return launch_both<true>(a, tt, max_big, max_small, stream);
+  return launch_all<true>(a, tt, tb, stream);
 }
 
-hipError_t launch_down(GemmArgs a, const TileTables& tt, int max_big, int max_small, hipStream_t stream) {
+hipError_t launch_down(GemmArgs a, const TileTables& tt, const TileBounds& tb, hipStream_t stream) {
   ProfileScope prof(kStageDown, stream);
-  return launch_both<false>(a, tt, max_big, max_small, stream);
+  return launch_all<false>(a, tt, tb, stream);
 }
 
 hipError_t launch_combine(const float* zw, uint16_t* y, int T, int H, int top_k, hipStream_t stream) {

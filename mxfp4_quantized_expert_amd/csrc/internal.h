@@ -15,6 +15,13 @@ enum Stage : int {
   kStageDown = 4,
   kStageCombine = 5,
   kStageDequant = 6,
+  kStageGateUpWide = 7,    // the full-tile launch of gate_up alone
+  kStageGateUpStream = 8,  // the remainder-tile launch of gate_up alone
+  kStageDownWide = 9,
+  kStageDownStream = 10,
+  kStageGateUpMid = 11,    // the mid-size remainder launch of gate_up alone
+  kStageDownMid = 12,
+  kStageLast = kStageDownMid,
 };
 
 // Records a HIP event pair around one launch when the benchmark hook asked for
@@ -34,19 +41,28 @@ class ProfileScope {
 int device_cu_count();
 
 // Token tiles of the expert GEMMs.  Every expert's pairs are cut into full
-// tiles of kWideTokens pairs, computed by the wide kernel, and a remainder
-// cut into tiles of kStreamTokens pairs, computed by the streaming kernel
-// (which is also the whole path for decode-sized batches).
+// tiles of kWideTokens pairs (wide kernel) and one remainder tile: of more
+// than kStreamTokens pairs (mid kernel) or of at most kStreamTokens pairs
+// (streaming kernel, which is also the whole path for decode-sized batches).
+// With big_tokens == 0 every pair goes to the streaming kernel in tiles of
+// kStreamTokens.
 constexpr int kWideTokens = 128;
-constexpr int kStreamTokens = 32;
+constexpr int kStreamTokens = 4;
+constexpr int kMaxHidden = 4096;  // bound on H and I (the GEMMs stage scale rows in LDS)
 
 struct TileTables {
   int32_t* big;        // [max_big][4]   = {expert, first sorted row, rows, 0}
   int32_t* num_big;
+  int32_t* mid;        // [max_mid][4]
+  int32_t* num_mid;
   int32_t* small;      // [max_small][4]
   int32_t* num_small;
-  int big_tokens;      // 0: no full tiles, everything goes to the small table
-  int small_tokens;
+  int big_tokens;      // kWideTokens, or 0
+};
+
+// Capacities of the tile tables (bounds the GEMM grids).
+struct TileBounds {
+  int max_big, max_mid, max_small;
 };
 
 // Routing: one wave per token.
@@ -71,10 +87,10 @@ struct GemmArgs {
   int N, K, top_k, max_tiles;
 };
 
-// Both GEMM stages launch the wide kernel over the full tiles (when there are
-// any) and the streaming kernel over the remainder tiles.
-hipError_t launch_gate_up(GemmArgs a, const TileTables& tt, int max_big, int max_small, hipStream_t stream);
-hipError_t launch_down(GemmArgs a, const TileTables& tt, int max_big, int max_small, hipStream_t stream);
+// Both GEMM stages launch the wide, mid and streaming kernels over their
+// tables (each launch skipped when its table has no capacity).
+hipError_t launch_gate_up(GemmArgs a, const TileTables& tt, const TileBounds& tb, hipStream_t stream);
+hipError_t launch_down(GemmArgs a, const TileTables& tt, const TileBounds& tb, hipStream_t stream);
 hipError_t launch_combine(const float* zw, uint16_t* y, int T, int H, int top_k, hipStream_t stream);
 
 hipError_t launch_dequant(const uint8_t* blocks, const uint8_t* scales, uint16_t* out, int64_t N, int64_t K,

@@ -108,8 +108,8 @@ __device__ int block_exclusive_scan_wave0(const int* vals, int* out, int n, int*
 
 // Single workgroup: histogram of experts, exclusive scan into offsets, a
 // stable scatter of pair ids into expert order, and the GEMM tile tables:
-// full tiles of big_tokens pairs, then every expert's remainder in tiles of
-// small_tokens pairs.
+// full tiles of big_tokens pairs, then every expert's remainder as one mid
+// tile (more than kStreamTokens pairs) or one streaming tile.
 // The scatter walks the pairs in chunks of 1024; inside a wave the lanes with
 // the same expert are found by matching the expert id bit by bit with
 // ballots, and the per-wave counts are turned into positions wave by wave, so
@@ -135,8 +135,9 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(const int32_t* __r
   if (threadIdx.x == 0) offsets[E] = P;
 
   if (tt.big != nullptr) {
-    // full tiles of big_tokens pairs: expert e owns cnt[e] / big_tokens of them
     const int bt = tt.big_tokens;
+    constexpr int st = mxfp4moe::kStreamTokens;
+    // full tiles of bt pairs: expert e owns cnt[e] / bt of them
     for (int e = threadIdx.x; e < E; e += kGroupThreads) ntile[e] = bt > 0 ? cnt[e] / bt : 0;
     __syncthreads();
     const int n_big = block_exclusive_scan_wave0(ntile, tile_base, E, &total_slot);
@@ -146,11 +147,26 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(const int32_t* __r
         reinterpret_cast<int4*>(tt.big)[tile_base[e] + i] = int4{e, base[e] + i * bt, bt, 0};
     }
     __syncthreads();
-    // the remainder of every expert in tiles of small_tokens pairs
-    const int st = tt.small_tokens;
+    // a remainder of more than st pairs: one mid tile
+    for (int e = threadIdx.x; e < E; e += kGroupThreads) {
+      const int rem = bt > 0 ? cnt[e] % bt : 0;
+      ntile[e] = rem > st ? 1 : 0;
+    }
+    __syncthreads();
+    const int n_mid = block_exclusive_scan_wave0(ntile, tile_base, E, &total_slot);
+    if (threadIdx.x == 0) *tt.num_mid = n_mid;
+    for (int e = threadIdx.x; e < E; e += kGroupThreads) {
+      if (ntile[e] > 0) {
+        const int done = cnt[e] / bt * bt;
+        reinterpret_cast<int4*>(tt.mid)[tile_base[e]] = int4{e, base[e] + done, cnt[e] - done, 0};
+      }
+    }
+    __syncthreads();
+    // a remainder of at most st pairs: one streaming tile; without full tiles,
+    // every pair in streaming tiles of st
     for (int e = threadIdx.x; e < E; e += kGroupThreads) {
       const int rem = bt > 0 ? cnt[e] % bt : cnt[e];
-      ntile[e] = (rem + st - 1) / st;
+      ntile[e] = bt > 0 ? (rem > 0 && rem <= st ? 1 : 0) : (rem + st - 1) / st;
     }
     __syncthreads();
     const int n_small = block_exclusive_scan_wave0(ntile, tile_base, E, &total_slot);
