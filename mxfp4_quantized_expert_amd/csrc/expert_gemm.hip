@@ -571,6 +571,217 @@ hipError_t launch_stream(const mxfp4moe::GemmArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Mid-size tiles (kStreamTokens < pairs <= kMidTokens): the per-expert
+// remainders of prefill.  16x16x32 MFMA (A: lane (r, q) takes group 4c+q of
+// row r, step s its codes [8s, 8s+8), so K = 128c + 32q + 8s + i; B: the same
+// K values of token l%16).  A block owns 128 weight rows (four waves of
+// 2 x 16 rows) and up to 64 tokens (four 16-token column blocks).  K runs in
+// panels of kP chunks (128 K each); both operands of a panel are staged in
+// LDS: the block's 128 weight rows as kP*64 contiguous bytes per row (eight
+// lanes per row, 128 bytes per row per load: the pattern HBM streams at full
+// rate) and the tile's token rows as kP*256 bytes each.  The loads of panel
+// p+1 are issued before the MFMAs of panel p and stored after them (single
+// LDS buffer, two barriers per panel); two blocks per CU overlap further.
+// Token columns past the tile's pairs read its first pair (their outputs are
+// dropped).
+//
+// Dynamic LDS: tokens [64][kP*256 + 16] | weights [128][kP*64 + 16] |
+// scales [128][K/32]  (the 16-byte row pads make the 16-lane column reads
+// conflict-free).
+template <int kP>
+__host__ __device__ constexpr size_t mid_lds_bytes(int K) {
+  return (size_t)64 * (kP * 256 + 16) + (size_t)128 * (kP * 64 + 16) + (size_t)128 * (K / 32);
+}
+
+template <int kP, bool kGateUp>
+__global__ __launch_bounds__(256, 2) void expert_mid_kernel(mxfp4moe::GemmArgs args) {
+  constexpr int kThreads = 256;
+  constexpr int BN = 128;
+  constexpr int kXRow = kP * 256 + 16;      // LDS bytes per token row of a panel
+  constexpr int kWRow = kP * 64 + 16;       // LDS bytes per weight row of a panel
+  constexpr int kXPieces = kP * 16;         // 16-byte pieces per token row of a panel
+  constexpr int kWPieces = kP * 4;          // 16-byte pieces per weight row of a panel
+  constexpr int kXPer = 64 * kXPieces / kThreads;
+  constexpr int kWPer = BN * kWPieces / kThreads;
+  static_assert(64 * kXPieces % kThreads == 0 && BN * kWPieces % kThreads == 0, "panel / thread mismatch");
+  extern __shared__ u32x4 dyn[];
+  uint8_t* const lds = reinterpret_cast<uint8_t*>(dyn);
+
+  const int N = args.N, K = args.K;
+  const int n_tiles = (N + BN - 1) / BN;
+  int tile, ntile;
+  if (!map_block(*args.num_tiles, n_tiles, tile, ntile)) return;  // uniform per block
+  const int4 tl = reinterpret_cast<const int4*>(args.tiles)[tile];
+  const int e = __builtin_amdgcn_readfirstlane(tl.x);
+  const int row0 = __builtin_amdgcn_readfirstlane(tl.y);
+  const int count = __builtin_amdgcn_readfirstlane(tl.z);
+  const int kgroups = K >> 5;
+  const int nchunks = (kgroups + 3) >> 2;
+  const int npanels = (nchunks + kP - 1) / kP;
+  const int k16 = K >> 3;   // 16-byte pieces of a token row
+  const int kg16 = K >> 5;  // 16-byte pieces (groups) of a weight row
+  const int t = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int lane = t & 63;
+  const int q = lane >> 4;
+  const int lr = lane & 15;
+
+  uint8_t* const xs = lds;
+  uint8_t* const ws = lds + 64 * kXRow;
+  uint8_t* const sl = ws + BN * kWRow;
+  stage_scales<BN, kThreads>(sl, args, e, ntile, kgroups, t);
+
+  // load slots: token piece i = t + j*256 -> token i / kXPieces; weight piece
+  // i = t + j*256 -> row i / kWPieces (rows past N re-read row N-1)
+  const u32x4* xsrc[kXPer];
+  int xpiece[kXPer], xdst[kXPer];
+#pragma unroll
+  for (int j = 0; j < kXPer; ++j) {
+    const int i = t + j * kThreads;
+    const int r = i / kXPieces;
+    const int rr = r < count ? r : 0;
+    const size_t src_row = kGateUp ? (size_t)(args.sorted_pairs[row0 + rr] / args.top_k) : (size_t)(row0 + rr);
+    xsrc[j] = reinterpret_cast<const u32x4*>(args.act + src_row * (size_t)K);
+    xpiece[j] = i - r * kXPieces;
+    xdst[j] = r * kXRow + xpiece[j] * 16;
+  }
+  const u32x4* wsrc[kWPer];
+  int wpiece[kWPer], wdst[kWPer];
+#pragma unroll
+  for (int j = 0; j < kWPer; ++j) {
+    const int i = t + j * kThreads;
+    const int r = i / kWPieces;
+    const int gr = min(ntile * BN + r, N - 1);
+    wsrc[j] = reinterpret_cast<const u32x4*>(args.wblocks + ((size_t)e * N + gr) * (size_t)(K >> 1));
+    wpiece[j] = i - r * kWPieces;
+    wdst[j] = r * kWRow + wpiece[j] * 16;
+  }
+  u32x4 xv[kXPer], wv[kWPer];
+  // groups / pieces past the end re-read the last one (finite; the weights of
+  // a missing group are zeroed at use)
+  auto issue = [&](int p) {
+#pragma unroll
+    for (int j = 0; j < kWPer; ++j) wv[j] = wsrc[j][min(p * kWPieces + wpiece[j], kg16 - 1)];
+#pragma unroll
+    for (int j = 0; j < kXPer; ++j) xv[j] = xsrc[j][min(p * kXPieces + xpiece[j], k16 - 1)];
+  };
+  auto commit = [&]() {
+#pragma unroll
+    for (int j = 0; j < kWPer; ++j) *reinterpret_cast<u32x4*>(ws + wdst[j]) = wv[j];
+#pragma unroll
+    for (int j = 0; j < kXPer; ++j)
+      if (t + j * kThreads < count * kXPieces) *reinterpret_cast<u32x4*>(xs + xdst[j]) = xv[j];
+  };
+
+  const int n_wave = ntile * BN + wave * 32;
+  const uint8_t* srow[2];
+  int wrd[2];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    srow[rb] = sl + (wave * 32 + rb * 16 + lr) * kgroups;
+    wrd[rb] = (wave * 32 + rb * 16 + lr) * kWRow + 16 * q;
+  }
+  int xrd[4];  // LDS byte offset of this lane's token row for each column block
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+    const int m = cb * 16 + lr;
+    xrd[cb] = (m < count ? m : 0) * kXRow + 64 * q;
+  }
+  f32x4 acc[2][4];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  issue(0);
+  commit();
+  __syncthreads();  // panel 0 and the scale rows staged
+  for (int p = 0; p < npanels; ++p) {
+    issue(min(p + 1, npanels - 1));  // the last iteration re-reads its own panel (unused)
+#pragma unroll
+    for (int jj = 0; jj < kP; ++jj) {
+      const int g0 = 4 * (p * kP + jj) + q;
+      const bool glive = g0 < kgroups;
+      const int g = glive ? g0 : kgroups - 1;
+      u32x4 a[2][4];  // [rb][step] converted A fragments
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const float sc = mx::e8m0_operand(srow[rb][g]);
+        u32x4 wj = *reinterpret_cast<const u32x4*>(ws + wrd[rb] + jj * 64);
+        wj = glive ? wj : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int st = 0; st < 4; ++st) a[rb][st] = mx::fp4x8_to_bf16x8(wj[st], sc);
+      }
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          const bf16x8 b = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xs + xrd[cb] + jj * 256 + 16 * st));
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
+            acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mx::as_bf16x8(a[rb][st]), b, acc[rb][cb], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();  // every wave is done with panel p
+    if (p + 1 < npanels) {  // uniform
+      commit();
+      __syncthreads();  // panel p+1 staged
+    }
+  }
+
+  if (n_wave >= N) return;
+  const uint16_t* bias = args.bias + (size_t)e * N;
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int n = n_wave + rb * 16 + 4 * q;  // first of this lane's four rows
+    if (n >= N) continue;
+    const uint2 bb = *reinterpret_cast<const uint2*>(bias + n);
+    const float b0 = mx::bf16_to_f32(bb.x & 0xffffu), b1 = mx::bf16_to_f32(bb.x >> 16);
+    const float b2 = mx::bf16_to_f32(bb.y & 0xffffu), b3 = mx::bf16_to_f32(bb.y >> 16);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      const int m = cb * 16 + lr;
+      if (m >= count) continue;
+      const f32x4 v = acc[rb][cb];
+      if (kGateUp) {
+        const int I = N >> 1;
+        const uint32_t packed = mx::f32_to_bf16_rne(swiglu_clamped(v[0] + b0, v[1] + b1)) |
+                                (mx::f32_to_bf16_rne(swiglu_clamped(v[2] + b2, v[3] + b3)) << 16);
+        *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(args.out) + (size_t)(row0 + m) * I + (n >> 1)) = packed;
+      } else {
+        const int pr = args.sorted_pairs[row0 + m];
+        const float wt = args.topk_weights[pr];
+        f32x4 o;
+        o[0] = wt * (v[0] + b0);
+        o[1] = wt * (v[1] + b1);
+        o[2] = wt * (v[2] + b2);
+        o[3] = wt * (v[3] + b3);
+        *reinterpret_cast<f32x4*>(static_cast<float*>(args.out) + (size_t)pr * N + n) = o;
+      }
+    }
+  }
+}
+
+#ifndef MX_MID_PANEL
+#define MX_MID_PANEL 2
+#endif
+
+template <bool kGateUp>
+hipError_t launch_mid(const mxfp4moe::GemmArgs& a, hipStream_t stream) {
+  constexpr int kP = MX_MID_PANEL;
+  const long n_tiles = (a.N + 127) / 128;
+  const long blocks = n_tiles * a.max_tiles;
+  if (blocks == 0) return hipSuccess;
+  const long grid = (blocks + kXcds - 1) / kXcds * kXcds;
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&expert_mid_kernel<kP, kGateUp>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, (int)mid_lds_bytes<kP>(mxfp4moe::kMaxHidden));
+  if (attr != hipSuccess) return attr;
+  expert_mid_kernel<kP, kGateUp><<<(unsigned)grid, 256, mid_lds_bytes<kP>(a.K), stream>>>(a);
+  return hipGetLastError();
+}
+
 // y[t, n] = bf16(sum_j zw[t*k + j, n]), j ascending; four features per thread.
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ zw, uint16_t* __restrict__ y,
                                                       int T, int H, int top_k) {
@@ -599,12 +810,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 namespace mxfp4moe {
 
 // wide: 4 waves of 128 weight rows x 128 tokens (block 512 x 128), one wave per SIMD.
-// mid: 4 waves stacked along the tokens, each 128 weight rows x 32 tokens (block
-// 128 x 128), two blocks per CU; waves past the tile's pairs skip their MFMAs.
+// mid: 16x16x32 MFMA, 4 waves of 32 weight rows x (up to) 64 tokens, token
+// panels of MX_MID_PANEL chunks staged in LDS.
 // stream: 16x16x32 MFMA, 4 waves of 16*MX_STREAM_RN weight rows x (at most 4)
 // tokens, weights streamed in batches of MX_STREAM_BATCH chunks of 128 K.
 #define MX_WIDE 4, 1, 4, 4, 2, 1
-#define MX_MID 1, 4, 4, 1, 2, 2
 static_assert(kWideTokens == 128 && kStreamTokens == 4, "tile sizes");
 
 template <bool kGateUp>
@@ -622,7 +832,7 @@ static hipError_t launch_all(GemmArgs a, const TileTables& tt, const TileBounds&
     a.tiles = tt.mid;
     a.num_tiles = tt.num_mid;
     a.max_tiles = tb.max_mid;
-    err = launch_cfg<MX_MID, kGateUp>(a, stream);
+    err = launch_mid<kGateUp>(a, stream);
   }
   if (err == hipSuccess && tb.max_small > 0) {
     ProfileScope prof(kGateUp ? kStageGateUpStream : kStageDownStream, stream);

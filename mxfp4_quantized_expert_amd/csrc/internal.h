@@ -41,13 +41,15 @@ class ProfileScope {
 int device_cu_count();
 
 // Token tiles of the expert GEMMs.  Every expert's pairs are cut into full
-// tiles of kWideTokens pairs (wide kernel) and one remainder tile: of more
-// than kStreamTokens pairs (mid kernel) or of at most kStreamTokens pairs
-// (streaming kernel, which is also the whole path for decode-sized batches).
+// tiles of kWideTokens pairs (wide kernel) and a remainder: of more than
+// kStreamTokens pairs, cut into mid tiles of at most kMidTokens pairs (mid
+// kernel), or of at most kStreamTokens pairs, one streaming tile (streaming
+// kernel, which is also the whole path for decode-sized batches).
 // With big_tokens == 0 every pair goes to the streaming kernel in tiles of
 // kStreamTokens.
 constexpr int kWideTokens = 128;
 constexpr int kStreamTokens = 4;
+constexpr int kMidTokens = 64;
 constexpr int kMaxHidden = 4096;  // bound on H and I (the GEMMs stage scale rows in LDS)
 
 struct TileTables {

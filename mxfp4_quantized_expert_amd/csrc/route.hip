@@ -108,8 +108,8 @@ __device__ int block_exclusive_scan_wave0(const int* vals, int* out, int n, int*
 
 // Single workgroup: histogram of experts, exclusive scan into offsets, a
 // stable scatter of pair ids into expert order, and the GEMM tile tables:
-// full tiles of big_tokens pairs, then every expert's remainder as one mid
-// tile (more than kStreamTokens pairs) or one streaming tile.
+// full tiles of big_tokens pairs, then every expert's remainder as mid tiles
+// (more than kStreamTokens pairs) or one streaming tile.
 // The scatter walks the pairs in chunks of 1024; inside a wave the lanes with
 // the same expert are found by matching the expert id bit by bit with
 // ballots, and the per-wave counts are turned into positions wave by wave, so
@@ -147,19 +147,20 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(const int32_t* __r
         reinterpret_cast<int4*>(tt.big)[tile_base[e] + i] = int4{e, base[e] + i * bt, bt, 0};
     }
     __syncthreads();
-    // a remainder of more than st pairs: one mid tile
+    // a remainder of more than st pairs: mid tiles of at most mt pairs
+    constexpr int mt = mxfp4moe::kMidTokens;
     for (int e = threadIdx.x; e < E; e += kGroupThreads) {
       const int rem = bt > 0 ? cnt[e] % bt : 0;
-      ntile[e] = rem > st ? 1 : 0;
+      ntile[e] = rem > st ? (rem + mt - 1) / mt : 0;
     }
     __syncthreads();
     const int n_mid = block_exclusive_scan_wave0(ntile, tile_base, E, &total_slot);
     if (threadIdx.x == 0) *tt.num_mid = n_mid;
     for (int e = threadIdx.x; e < E; e += kGroupThreads) {
-      if (ntile[e] > 0) {
-        const int done = cnt[e] / bt * bt;
-        reinterpret_cast<int4*>(tt.mid)[tile_base[e]] = int4{e, base[e] + done, cnt[e] - done, 0};
-      }
+      const int done = bt > 0 ? cnt[e] / bt * bt : 0;
+      const int rem = cnt[e] - done;
+      for (int i = 0; i < ntile[e]; ++i)
+        reinterpret_cast<int4*>(tt.mid)[tile_base[e] + i] = int4{e, base[e] + done + i * mt, min(mt, rem - i * mt), 0};
     }
     __syncthreads();
     // a remainder of at most st pairs: one streaming tile; without full tiles,
