@@ -124,7 +124,7 @@ def run_moe(args):
     _, _, offsets, _ = binding.moe_mxfp4_route(dev["router_logits"], k)
     counts = np.diff(offsets.cpu().numpy().astype(np.int64))
     n_active = int((counts > 0).sum())
-    full_pairs = int((counts // 128).sum() * 128)
+    full_pairs = int(counts[counts >= 128].sum())  # pairs of the experts computed in 128-pair tiles
     w13_b, w2_b = layer_bytes(H, I)
     # Weight copies rotate so that repeated steps cannot be served from the
     # 256 MB Infinity Cache when the active weights would fit in it.
@@ -183,7 +183,7 @@ def run_moe(args):
         work = 4.0 * H * I * full_pairs
         roof = {"bound": "mfma", "achieved": work / (kms / 1e3) / 1e12, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s"}
-        per_unit = f"33,177,600 FLOPs per pair at H=I=2880 (2*H*2I) x {full_pairs} pairs in full tiles"
+        per_unit = f"33,177,600 FLOPs per pair at H=I=2880 (2*H*2I) x {full_pairs} pairs in 128-pair tiles"
     else:
         # packed w13 (blocks, scales, bias) of every active expert + x rows + a rows out
         work = n_active * w13_b + T * H * 2 + P * I * 2

@@ -62,16 +62,17 @@ struct Layout {
 };
 
 // Tile table capacities.  An expert gets at most T pairs (a token's k
-// experts are distinct).  Full tiles hold at most P pairs; every expert with
-// pairs has at most one streaming or two mid remainder tiles.  Without full tiles the streaming table holds up to
-// P/kStreamTokens full tiles plus one partial tile per expert.
+// experts are distinct).  An expert with at least kWideTokens pairs makes
+// ceil(c / kWideTokens) wide tiles (at most P / kWideTokens full ones plus one
+// partial per such expert); one with kStreamTokens < c < kWideTokens pairs at
+// most two mid tiles; one with fewer, one streaming tile.  Without wide tiles
+// every pair goes to streaming tiles of kStreamTokens.
 TileBounds tile_bounds(int64_t T, int64_t P, int64_t E, bool wide) {
   const int64_t active = E < P ? E : P;
+  const int64_t fulls = P / kWideTokens;
   TileBounds b;
-  b.max_big = (wide && T >= kWideTokens) ? (int)(P / kWideTokens) : 0;
-  // a remainder below kWideTokens makes at most two mid tiles, the first of
-  // more than kStreamTokens pairs
-  static_assert(2 * kMidTokens >= kWideTokens, "two mid tiles cover a remainder");
+  b.max_big = (wide && T >= kWideTokens) ? (int)(fulls + (active < fulls ? active : fulls)) : 0;
+  static_assert(2 * kMidTokens >= kWideTokens, "two mid tiles cover an expert below kWideTokens");
   const int64_t mids = 2 * (P / (kStreamTokens + 1));
   b.max_mid = (wide && T > kStreamTokens) ? (int)(2 * active < mids ? 2 * active : mids) : 0;
   b.max_small = wide ? (int)active : (int)(P / kStreamTokens + active);

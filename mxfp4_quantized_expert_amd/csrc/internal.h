@@ -40,11 +40,12 @@ class ProfileScope {
 
 int device_cu_count();
 
-// Token tiles of the expert GEMMs.  Every expert's pairs are cut into full
-// tiles of kWideTokens pairs (wide kernel) and a remainder: of more than
-// kStreamTokens pairs, cut into mid tiles of at most kMidTokens pairs (mid
-// kernel), or of at most kStreamTokens pairs, one streaming tile (streaming
-// kernel, which is also the whole path for decode-sized batches).
+// Token tiles of the expert GEMMs.  An expert with at least kWideTokens pairs
+// is cut into tiles of kWideTokens pairs, the last one partial (wide kernel);
+// one with more than kStreamTokens pairs into mid tiles of at most
+// kMidTokens pairs (mid kernel); one with at most kStreamTokens pairs makes a
+// single streaming tile (streaming kernel, which is also the whole path for
+// decode-sized batches).  Every expert's weights are streamed by one kernel.
 // With big_tokens == 0 every pair goes to the streaming kernel in tiles of
 // kStreamTokens.
 constexpr int kWideTokens = 128;

@@ -107,9 +107,9 @@ __device__ int block_exclusive_scan_wave0(const int* vals, int* out, int n, int*
 }
 
 // Single workgroup: histogram of experts, exclusive scan into offsets, a
-// stable scatter of pair ids into expert order, and the GEMM tile tables:
-// full tiles of big_tokens pairs, then every expert's remainder as mid tiles
-// (more than kStreamTokens pairs) or one streaming tile.
+// stable scatter of pair ids into expert order, and the GEMM tile tables: an
+// expert with at least big_tokens pairs goes to wide tiles, one with more than
+// kStreamTokens pairs to mid tiles, the rest to one streaming tile.
 // The scatter walks the pairs in chunks of 1024; inside a wave the lanes with
 // the same expert are found by matching the expert id bit by bit with
 // ballots, and the per-wave counts are turned into positions wave by wave, so
@@ -137,47 +137,44 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(const int32_t* __r
   if (tt.big != nullptr) {
     const int bt = tt.big_tokens;
     constexpr int st = mxfp4moe::kStreamTokens;
-    // full tiles of bt pairs: expert e owns cnt[e] / bt of them
-    for (int e = threadIdx.x; e < E; e += kGroupThreads) ntile[e] = bt > 0 ? cnt[e] / bt : 0;
+    // an expert with at least bt pairs: all its pairs in tiles of bt (the
+    // last one partial), so its weights are streamed by one kernel only
+    for (int e = threadIdx.x; e < E; e += kGroupThreads)
+      ntile[e] = (bt > 0 && cnt[e] >= bt) ? (cnt[e] + bt - 1) / bt : 0;
     __syncthreads();
     const int n_big = block_exclusive_scan_wave0(ntile, tile_base, E, &total_slot);
     if (threadIdx.x == 0) *tt.num_big = n_big;
     for (int e = threadIdx.x; e < E; e += kGroupThreads) {
       for (int i = 0; i < ntile[e]; ++i)
-        reinterpret_cast<int4*>(tt.big)[tile_base[e] + i] = int4{e, base[e] + i * bt, bt, 0};
+        reinterpret_cast<int4*>(tt.big)[tile_base[e] + i] = int4{e, base[e] + i * bt, min(bt, cnt[e] - i * bt), 0};
     }
     __syncthreads();
-    // a remainder of more than st pairs: mid tiles of at most mt pairs
+    // fewer than bt pairs, more than st: mid tiles of at most mt pairs
     constexpr int mt = mxfp4moe::kMidTokens;
     for (int e = threadIdx.x; e < E; e += kGroupThreads) {
-      const int rem = bt > 0 ? cnt[e] % bt : 0;
-      ntile[e] = rem > st ? (rem + mt - 1) / mt : 0;
+      const int c = cnt[e];
+      ntile[e] = (bt > 0 && c > st && c < bt) ? (c + mt - 1) / mt : 0;
     }
     __syncthreads();
     const int n_mid = block_exclusive_scan_wave0(ntile, tile_base, E, &total_slot);
     if (threadIdx.x == 0) *tt.num_mid = n_mid;
     for (int e = threadIdx.x; e < E; e += kGroupThreads) {
-      const int done = bt > 0 ? cnt[e] / bt * bt : 0;
-      const int rem = cnt[e] - done;
       for (int i = 0; i < ntile[e]; ++i)
-        reinterpret_cast<int4*>(tt.mid)[tile_base[e] + i] = int4{e, base[e] + done + i * mt, min(mt, rem - i * mt), 0};
+        reinterpret_cast<int4*>(tt.mid)[tile_base[e] + i] = int4{e, base[e] + i * mt, min(mt, cnt[e] - i * mt), 0};
     }
     __syncthreads();
-    // a remainder of at most st pairs: one streaming tile; without full tiles,
+    // at most st pairs: one streaming tile; without full tiles (bt == 0),
     // every pair in streaming tiles of st
     for (int e = threadIdx.x; e < E; e += kGroupThreads) {
-      const int rem = bt > 0 ? cnt[e] % bt : cnt[e];
-      ntile[e] = bt > 0 ? (rem > 0 && rem <= st ? 1 : 0) : (rem + st - 1) / st;
+      const int c = cnt[e];
+      ntile[e] = bt > 0 ? (c > 0 && c <= st ? 1 : 0) : (c + st - 1) / st;
     }
     __syncthreads();
     const int n_small = block_exclusive_scan_wave0(ntile, tile_base, E, &total_slot);
     if (threadIdx.x == 0) *tt.num_small = n_small;
     for (int e = threadIdx.x; e < E; e += kGroupThreads) {
-      const int done = bt > 0 ? cnt[e] / bt * bt : 0;
-      const int rem = cnt[e] - done;
       for (int i = 0; i < ntile[e]; ++i)
-        reinterpret_cast<int4*>(tt.small)[tile_base[e] + i] =
-            int4{e, base[e] + done + i * st, min(st, rem - i * st), 0};
+        reinterpret_cast<int4*>(tt.small)[tile_base[e] + i] = int4{e, base[e] + i * st, min(st, cnt[e] - i * st), 0};
     }
   }
 
