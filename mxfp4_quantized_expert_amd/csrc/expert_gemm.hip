@@ -656,21 +656,23 @@ __global__ __launch_bounds__(256, 2) void expert_mid_kernel(mxfp4moe::GemmArgs a
     wpiece[j] = i - r * kWPieces;
     wdst[j] = r * kWRow + wpiece[j] * 16;
   }
-  u32x4 xv[kXPer], wv[kWPer];
-  // groups / pieces past the end re-read the last one (finite; the weights of
-  // a missing group are zeroed at use)
-  auto issue = [&](int p) {
+  // Two register slots hold the next two panels in flight.  Groups / pieces
+  // past the end re-read the last one (finite; the weights of a missing group
+  // are zeroed at use); panels past the last re-read the last panel.
+  u32x4 xv[2][kXPer], wv[2][kWPer];
+  auto issue = [&](int p, int sl2) {
+    p = min(p, npanels - 1);
 #pragma unroll
-    for (int j = 0; j < kWPer; ++j) wv[j] = wsrc[j][min(p * kWPieces + wpiece[j], kg16 - 1)];
+    for (int j = 0; j < kWPer; ++j) wv[sl2][j] = wsrc[j][min(p * kWPieces + wpiece[j], kg16 - 1)];
 #pragma unroll
-    for (int j = 0; j < kXPer; ++j) xv[j] = xsrc[j][min(p * kXPieces + xpiece[j], k16 - 1)];
+    for (int j = 0; j < kXPer; ++j) xv[sl2][j] = xsrc[j][min(p * kXPieces + xpiece[j], k16 - 1)];
   };
-  auto commit = [&]() {
+  auto commit = [&](int sl2) {
 #pragma unroll
-    for (int j = 0; j < kWPer; ++j) *reinterpret_cast<u32x4*>(ws + wdst[j]) = wv[j];
+    for (int j = 0; j < kWPer; ++j) *reinterpret_cast<u32x4*>(ws + wdst[j]) = wv[sl2][j];
 #pragma unroll
     for (int j = 0; j < kXPer; ++j)
-      if (t + j * kThreads < count * kXPieces) *reinterpret_cast<u32x4*>(xs + xdst[j]) = xv[j];
+      if (t + j * kThreads < count * kXPieces) *reinterpret_cast<u32x4*>(xs + xdst[j]) = xv[sl2][j];
   };
 
   const int n_wave = ntile * BN + wave * 32;
@@ -681,6 +683,7 @@ __global__ __launch_bounds__(256, 2) void expert_mid_kernel(mxfp4moe::GemmArgs a
     srow[rb] = sl + (wave * 32 + rb * 16 + lr) * kgroups;
     wrd[rb] = (wave * 32 + rb * 16 + lr) * kWRow + 16 * q;
   }
+  const int ncb = (count + 15) >> 4;  // live 16-token column blocks
   int xrd[4];  // LDS byte offset of this lane's token row for each column block
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb) {
@@ -693,11 +696,15 @@ __global__ __launch_bounds__(256, 2) void expert_mid_kernel(mxfp4moe::GemmArgs a
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  issue(0);
-  commit();
+  issue(0, 0);
+  issue(1, 1);
+  commit(0);
   __syncthreads();  // panel 0 and the scale rows staged
-  for (int p = 0; p < npanels; ++p) {
-    issue(min(p + 1, npanels - 1));  // the last iteration re-reads its own panel (unused)
+  issue(2, 0);
+  // iteration p: panel p is in LDS, slot (p+1)&1 holds panel p+1 and slot p&1
+  // panel p+2; after the MFMAs, panel p+1 goes to LDS and its slot is refilled
+  // with panel p+3.  Unrolled by two so the slots are static.
+  auto compute = [&](int p) {
 #pragma unroll
     for (int jj = 0; jj < kP; ++jj) {
       const int g0 = 4 * (p * kP + jj) + q;
@@ -714,20 +721,32 @@ __global__ __launch_bounds__(256, 2) void expert_mid_kernel(mxfp4moe::GemmArgs a
       }
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
+        if (cb < ncb) {  // wave-uniform: column blocks past the tile's pairs are skipped
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          const bf16x8 b = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xs + xrd[cb] + jj * 256 + 16 * st));
+          for (int st = 0; st < 4; ++st) {
+            const bf16x8 b =
+                __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xs + xrd[cb] + jj * 256 + 16 * st));
 #pragma unroll
-          for (int rb = 0; rb < 2; ++rb)
-            acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mx::as_bf16x8(a[rb][st]), b, acc[rb][cb], 0, 0, 0);
+            for (int rb = 0; rb < 2; ++rb)
+              acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mx::as_bf16x8(a[rb][st]), b, acc[rb][cb], 0, 0, 0);
+          }
         }
       }
     }
+  };
+  for (int p = 0; p < npanels; p += 2) {
+    compute(p);
     __syncthreads();  // every wave is done with panel p
-    if (p + 1 < npanels) {  // uniform
-      commit();
-      __syncthreads();  // panel p+1 staged
-    }
+    if (p + 1 >= npanels) break;  // uniform
+    commit(1);
+    __syncthreads();  // panel p+1 staged
+    issue(p + 3, 1);
+    compute(p + 1);
+    __syncthreads();
+    if (p + 2 >= npanels) break;
+    commit(0);
+    __syncthreads();  // panel p+2 staged
+    issue(p + 4, 0);
   }
 
   if (n_wave >= N) return;
