@@ -49,7 +49,9 @@ __device__ __forceinline__ float swiglu_clamped(float gate, float up) {
   // up clamped on both sides, +1 after the clamp.
   const float g = fminf(gate, 7.0f);
   const float u = fminf(fmaxf(up, -7.0f), 7.0f);
-  return g * (1.0f / (1.0f + __expf(-1.702f * g))) * (u + 1.0f);
+  // sigmoid through the hardware reciprocal (about 1 ulp; the result is
+  // rounded to bf16)
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-1.702f * g)) * (u + 1.0f);
 }
 
 // Block -> (tile, weight-row tile).  Blocks are dealt to the 8 XCDs round
@@ -185,8 +187,7 @@ __device__ __forceinline__ void store_epilogue(const mxfp4moe::GemmArgs& args, c
           const int m = cb * 32 + lrow;
           const float a0 = swiglu_clamped(acc[rb][cb][4 * i + 0] + b0, acc[rb][cb][4 * i + 1] + b1);
           const float a1 = swiglu_clamped(acc[rb][cb][4 * i + 2] + b2, acc[rb][cb][4 * i + 3] + b3);
-          *reinterpret_cast<uint32_t*>(region + chunk_addr(m, byte >> 4) + (byte & 15)) =
-              mx::f32_to_bf16_rne(a0) | (mx::f32_to_bf16_rne(a1) << 16);
+          *reinterpret_cast<uint32_t*>(region + chunk_addr(m, byte >> 4) + (byte & 15)) = mx::pack_bf16x2_rne(a0, a1);
         }
       }
     }
@@ -531,8 +532,7 @@ __global__ __launch_bounds__(256, 4) void expert_stream_kernel(mxfp4moe::GemmArg
     v[3] = acc[rb][0][3] + acc[rb][1][3] + mx::bf16_to_f32(bb.y >> 16);
     if (kGateUp) {
       const int I = N >> 1;
-      const uint32_t packed = mx::f32_to_bf16_rne(swiglu_clamped(v[0], v[1])) |
-                              (mx::f32_to_bf16_rne(swiglu_clamped(v[2], v[3])) << 16);
+      const uint32_t packed = mx::pack_bf16x2_rne(swiglu_clamped(v[0], v[1]), swiglu_clamped(v[2], v[3]));
       *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(args.out) + (size_t)(row0 + lr) * I + (n >> 1)) = packed;
     } else {
       const int p = args.sorted_pairs[row0 + lr];
@@ -765,8 +765,7 @@ __global__ __launch_bounds__(256, 2) void expert_mid_kernel(mxfp4moe::GemmArgs a
       const f32x4 v = acc[rb][cb];
       if (kGateUp) {
         const int I = N >> 1;
-        const uint32_t packed = mx::f32_to_bf16_rne(swiglu_clamped(v[0] + b0, v[1] + b1)) |
-                                (mx::f32_to_bf16_rne(swiglu_clamped(v[2] + b2, v[3] + b3)) << 16);
+        const uint32_t packed = mx::pack_bf16x2_rne(swiglu_clamped(v[0] + b0, v[1] + b1), swiglu_clamped(v[2] + b2, v[3] + b3));
         *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(args.out) + (size_t)(row0 + m) * I + (n >> 1)) = packed;
       } else {
         const int pr = args.sorted_pairs[row0 + m];
@@ -819,8 +818,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     s[3] += v[3];
   }
   uint2 o;
-  o.x = mx::f32_to_bf16_rne(s[0]) | (mx::f32_to_bf16_rne(s[1]) << 16);
-  o.y = mx::f32_to_bf16_rne(s[2]) | (mx::f32_to_bf16_rne(s[3]) << 16);
+  o.x = mx::pack_bf16x2_rne(s[0], s[1]);
+  o.y = mx::pack_bf16x2_rne(s[2], s[3]);
   *reinterpret_cast<uint2*>(y + (size_t)t * H + n) = o;
 }
 

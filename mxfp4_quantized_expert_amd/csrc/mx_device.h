@@ -42,11 +42,13 @@ __device__ __forceinline__ u32x4 fp4x8_to_bf16x8(uint32_t packed, float scale) {
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // float -> bf16 bits, round to nearest, ties to even; NaN -> 0x7FC0.
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+// Two floats -> two bf16 (round to nearest even) packed low/high, with the
+// gfx950 conversion instruction (one v_cvt_pk_bf16_f32).
+typedef __attribute__((ext_vector_type(2))) float f32x2v;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2v;
+__device__ __forceinline__ uint32_t pack_bf16x2_rne(float lo, float hi) {
+  const f32x2v v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v));
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
