@@ -211,8 +211,13 @@ int moe_mxfp4_forward(const uint16_t* x, const float* router_logits, const uint8
   const TileBounds tb = tile_bounds(T, P, E, tt.big_tokens > 0);
   hipStream_t s = (hipStream_t)stream;
 
-  hipError_t err = launch_route(router_logits, (int)T, (int)E, (int)top_k, ids, weights, s);
-  if (err == hipSuccess) err = launch_group(ids, (int)P, (int)E, offsets, sorted, tt, s);
+  hipError_t err;
+  if (T <= kFusedRouteTokens) {
+    err = launch_route_group(router_logits, (int)T, (int)E, (int)top_k, ids, weights, offsets, sorted, tt, s);
+  } else {
+    err = launch_route(router_logits, (int)T, (int)E, (int)top_k, ids, weights, s);
+    if (err == hipSuccess) err = launch_group(ids, (int)P, (int)E, offsets, sorted, tt, s);
+  }
   GemmArgs g{};
   g.sorted_pairs = sorted;
   g.topk_weights = weights;

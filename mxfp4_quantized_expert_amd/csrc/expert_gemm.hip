@@ -418,7 +418,7 @@ __host__ __device__ constexpr size_t stream_lds_bytes(int K) {
 }
 
 template <int RN, int kBatch, bool kGateUp>
-__global__ __launch_bounds__(256, 4) void expert_stream_kernel(mxfp4moe::GemmArgs args) {
+__global__ __launch_bounds__(256, 5) void expert_stream_kernel(mxfp4moe::GemmArgs args) {
   constexpr int kThreads = 256;
   constexpr int BN = 64 * RN;
   extern __shared__ u32x4 dyn[];
@@ -439,6 +439,29 @@ __global__ __launch_bounds__(256, 4) void expert_stream_kernel(mxfp4moe::GemmArg
   const int lane = t & 63;
   const int q = lane >> 4;
   const int lr = lane & 15;
+
+  const int n_wave = ntile * BN + wave * 16 * RN;
+  const uint8_t* wrow[RN];
+#pragma unroll
+  for (int rb = 0; rb < RN; ++rb) {
+    const int r = min(n_wave + rb * 16 + lr, N - 1);  // rows past N: outputs dropped
+    wrow[rb] = args.wblocks + ((size_t)e * N + r) * (size_t)(K >> 1);
+  }
+  // A group past the last one (K tail, or a padding chunk of the last batch)
+  // reads the last group's weights, scale and token values, which are finite,
+  // and multiplies zero weights.
+  auto load_batch = [&](int c0, u32x4 (&w)[kBatch][RN]) {
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int g = min(4 * (c0 + j) + q, kgroups - 1);
+#pragma unroll
+      for (int rb = 0; rb < RN; ++rb) w[j][rb] = *reinterpret_cast<const u32x4*>(wrow[rb] + (size_t)g * 16);
+    }
+  };
+  // The first batch's weight loads go out before the staging below, so the
+  // two round trips to memory overlap.
+  u32x4 w_first[kBatch][RN];
+  load_batch(0, w_first);
 
   uint16_t* const xl = reinterpret_cast<uint16_t*>(lds);
   uint8_t* const sl = lds + (size_t)mxfp4moe::kStreamTokens * K * 2;
@@ -469,33 +492,17 @@ __global__ __launch_bounds__(256, 4) void expert_stream_kernel(mxfp4moe::GemmArg
   }
   __syncthreads();
 
-  const int n_wave = ntile * BN + wave * 16 * RN;
   if (n_wave >= N) return;  // wave-uniform; no barrier follows
   f32x4 acc[RN][2];
 #pragma unroll
   for (int rb = 0; rb < RN; ++rb)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[rb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const uint8_t* wrow[RN];
   const uint8_t* srow[RN];
 #pragma unroll
-  for (int rb = 0; rb < RN; ++rb) {
-    const int r = min(n_wave + rb * 16 + lr, N - 1);  // rows past N: outputs dropped
-    wrow[rb] = args.wblocks + ((size_t)e * N + r) * (size_t)(K >> 1);
-    srow[rb] = sl + (wave * 16 * RN + rb * 16 + lr) * kgroups;
-  }
+  for (int rb = 0; rb < RN; ++rb) srow[rb] = sl + (wave * 16 * RN + rb * 16 + lr) * kgroups;
   const uint16_t* xrow = xl + (lr < count ? lr : 0) * K;
-  for (int c0 = 0; c0 < nchunks; c0 += kBatch) {
-    u32x4 w[kBatch][RN];
-    // A group past the last one (K tail, or a padding chunk of the last
-    // batch) reads the last group's weights, scale and token values, which
-    // are finite, and multiplies zero weights.
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      const int g = min(4 * (c0 + j) + q, kgroups - 1);
-#pragma unroll
-      for (int rb = 0; rb < RN; ++rb) w[j][rb] = *reinterpret_cast<const u32x4*>(wrow[rb] + (size_t)g * 16);
-    }
+  auto compute_batch = [&](int c0, const u32x4 (&w)[kBatch][RN]) {
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
       const int g0 = 4 * (c0 + j) + q;
@@ -516,6 +523,12 @@ __global__ __launch_bounds__(256, 4) void expert_stream_kernel(mxfp4moe::GemmArg
         }
       }
     }
+  };
+  compute_batch(0, w_first);
+  for (int c0 = kBatch; c0 < nchunks; c0 += kBatch) {
+    u32x4 w[kBatch][RN];
+    load_batch(c0, w);
+    compute_batch(c0, w);
   }
 
   if (lr >= count) return;
@@ -550,7 +563,7 @@ __global__ __launch_bounds__(256, 4) void expert_stream_kernel(mxfp4moe::GemmArg
 #define MX_STREAM_RN 1
 #endif
 #ifndef MX_STREAM_BATCH
-#define MX_STREAM_BATCH 8
+#define MX_STREAM_BATCH 6
 #endif
 
 template <bool kGateUp>

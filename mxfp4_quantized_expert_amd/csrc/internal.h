@@ -77,6 +77,12 @@ hipError_t launch_route(const float* logits, int T, int E, int top_k, int32_t* i
 hipError_t launch_group(const int32_t* ids, int P, int E, int32_t* offsets, int32_t* sorted_pairs,
                         const TileTables& tt, hipStream_t stream);
 
+// Routing and grouping in one single-block launch, for batches of at most
+// kFusedRouteTokens tokens (one wave routes each token).
+constexpr int kFusedRouteTokens = 64;
+hipError_t launch_route_group(const float* logits, int T, int E, int top_k, int32_t* ids, float* weights,
+                              int32_t* offsets, int32_t* sorted_pairs, const TileTables& tt, hipStream_t stream);
+
 struct GemmArgs {
   const uint8_t* wblocks;   // [E, N, K/2]
   const uint8_t* wscales;   // [E, N, K/32]

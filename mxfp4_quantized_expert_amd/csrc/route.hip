@@ -13,16 +13,13 @@ namespace {
 constexpr int kRouteThreads = 256;  // four tokens per block, one wave each
 constexpr int kPerLane = MXFP4MOE_MAX_EXPERTS / 64;
 
-// One wave per token.  Lane l holds logits l, l+64, ...; k rounds of a
+// Token t, by one wave.  Lane l holds logits l, l+64, ...; k rounds of a
 // wave-wide argmax (ties to the lower expert index) pick the experts in
 // descending order; lane j keeps the j-th pick.  The softmax runs over the
 // picks relative to the largest one.
-__global__ __launch_bounds__(kRouteThreads) void route_kernel(const float* __restrict__ logits, int T, int E,
-                                                              int top_k, int32_t* __restrict__ ids,
-                                                              float* __restrict__ weights) {
+__device__ void route_token(const float* __restrict__ logits, int t, int E, int top_k, int32_t* __restrict__ ids,
+                            float* __restrict__ weights) {
   const int lane = mx::lane_id();
-  const int t = blockIdx.x * (kRouteThreads / 64) + (threadIdx.x >> 6);
-  if (t >= T) return;  // uniform per wave
   const float* row = logits + (size_t)t * E;
   float v[kPerLane];
   uint32_t avail = 0;
@@ -79,6 +76,14 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const float* __res
   }
 }
 
+__global__ __launch_bounds__(kRouteThreads) void route_kernel(const float* __restrict__ logits, int T, int E,
+                                                              int top_k, int32_t* __restrict__ ids,
+                                                              float* __restrict__ weights) {
+  const int t = blockIdx.x * (kRouteThreads / 64) + (threadIdx.x >> 6);
+  if (t >= T) return;  // uniform per wave
+  route_token(logits, t, E, top_k, ids, weights);
+}
+
 constexpr int kGroupThreads = 1024;
 constexpr int kGroupWaves = kGroupThreads / 64;
 
@@ -114,7 +119,13 @@ __device__ int block_exclusive_scan_wave0(const int* vals, int* out, int n, int*
 // the same expert are found by matching the expert id bit by bit with
 // ballots, and the per-wave counts are turned into positions wave by wave, so
 // pairs keep ascending id order inside every expert.
-__global__ __launch_bounds__(kGroupThreads) void group_kernel(const int32_t* __restrict__ ids, int P, int E,
+// With logits != nullptr the block first routes the T tokens itself (one
+// wave per token), saving a launch for small batches.  All waves of a
+// workgroup run on one CU and share its L1, so the barrier after the routing
+// is enough for the block to read the ids it wrote.
+__global__ __launch_bounds__(kGroupThreads) void group_kernel(const float* __restrict__ logits, int T, int top_k,
+                                                              float* __restrict__ weights,
+                                                              int32_t* __restrict__ ids, int P, int E,
                                                               int32_t* __restrict__ offsets,
                                                               int32_t* __restrict__ sorted_pairs,
                                                               mxfp4moe::TileTables tt) {
@@ -126,6 +137,10 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(const int32_t* __r
   int* wave_cnt = ntile + E;       // [kGroupWaves][E]
   __shared__ int total_slot;
 
+  if (logits != nullptr) {
+    for (int t = threadIdx.x >> 6; t < T; t += kGroupWaves) route_token(logits, t, E, top_k, ids, weights);
+    __syncthreads();
+  }
   for (int e = threadIdx.x; e < E; e += kGroupThreads) cnt[e] = 0;
   __syncthreads();
   for (int p = threadIdx.x; p < P; p += kGroupThreads) atomicAdd(&cnt[ids[p]], 1);
@@ -229,7 +244,17 @@ hipError_t launch_group(const int32_t* ids, int P, int E, int32_t* offsets, int3
                         const TileTables& tt, hipStream_t stream) {
   const size_t smem = (size_t)(4 + kGroupWaves) * E * sizeof(int);
   ProfileScope prof(kStageGroup, stream);
-  group_kernel<<<1, kGroupThreads, smem, stream>>>(ids, P, E, offsets, sorted_pairs, tt);
+  group_kernel<<<1, kGroupThreads, smem, stream>>>(nullptr, 0, 1, nullptr, const_cast<int32_t*>(ids), P, E,
+                                                   offsets, sorted_pairs, tt);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_group(const float* logits, int T, int E, int top_k, int32_t* ids, float* weights,
+                              int32_t* offsets, int32_t* sorted_pairs, const TileTables& tt, hipStream_t stream) {
+  const size_t smem = (size_t)(4 + kGroupWaves) * E * sizeof(int);
+  ProfileScope prof(kStageGroup, stream);
+  group_kernel<<<1, kGroupThreads, smem, stream>>>(logits, T, top_k, weights, ids, T * top_k, E, offsets,
+                                                   sorted_pairs, tt);
   return hipGetLastError();
 }
 
