@@ -99,12 +99,13 @@ def test_120b_long_prefill_sampled(gpu):
 
 @pytest.mark.parametrize("T,H,I,E,k", [(5, 96, 160, 7, 3), (1, 64, 32, 3, 3), (37, 224, 96, 9, 2),
                                        (300, 128, 64, 5, 1), (3, 32, 32, 1, 1), (600, 96, 160, 3, 2),
-                                       (700, 4096, 64, 2, 1)])
+                                       (700, 4096, 64, 2, 1), (9, 32, 64, 512, 32)])
 @pytest.mark.parametrize("path", [None, "stream"])
 def test_ragged_shapes(gpu, T, H, I, E, k, path):
     # K tails (H/32 or I/32 odd), partial weight-row tiles, partial token tiles,
     # top_k = E, a single expert, experts with several full 128-pair tiles plus
-    # a remainder, the largest supported hidden size.  path None: full tiles in
+    # a remainder, the largest supported hidden size, the most experts and the
+    # largest top_k.  path None: full tiles in
     # the wide configuration, remainders streamed; "stream": everything streamed.
     spec = W.LAYERS["tiny"].with_(T=T, H=H, I=I, E=E, top_k=k)
     L = W.make_layer(spec, seed=T + H)
@@ -137,3 +138,25 @@ def test_bias_after_scale_identity(gpu):
     ref = O.moe_forward(L, spec.top_k)
     y = _forward(gpu, L, spec.top_k)
     assert_layer_parity(y, ref, "bias-after-scale")
+
+
+@pytest.mark.parametrize("path", [None, "stream"])
+def test_tile_boundaries(gpu, path):
+    # Expert loads on every side of the tile limits: 128 (one full wide tile),
+    # 127 / 129 / 259 (mid tiles, wide tiles with a partial last one), 4 / 5
+    # (largest streaming tile, smallest mid tile), 64 / 65 (one or two mid
+    # tiles), 1 and 0.  k = 1 with one dominant logit per token forces them.
+    counts = [128, 127, 129, 4, 5, 64, 65, 1, 0, 259]
+    E = len(counts)
+    T = sum(counts)
+    spec = W.LAYERS["tiny"].with_(T=T, H=64, I=96, E=E, top_k=1)
+    L = W.make_layer(spec, seed=11)
+    rng = np.random.default_rng(12)
+    owner = rng.permutation(np.repeat(np.arange(E), counts))
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    logits[np.arange(T), owner] += 20.0
+    L["router_logits"] = logits
+    ids, _ = O.route(logits, 1)
+    assert np.array_equal(np.bincount(ids.ravel(), minlength=E), counts)
+    y = _forward(gpu, L, 1, path)
+    assert_layer_parity(y, O.moe_forward(L, 1), f"tile boundaries/{path}")
