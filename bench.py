@@ -9,7 +9,9 @@ one batch of synthetic tokens whose inputs are already resident in HBM.
 
 Prints one JSON line.  Workloads: 120b_prefill (default: gpt-oss-120b shaped
 layer, T=4096 long prefill with Zipf-skewed routing), 20b_prefill, 20b_decode,
-tiny, dequant_120b (the standalone dequant of a 120b-shaped w13 bank) and copy
+tiny, dequant_120b (the standalone dequant of a 120b-shaped w13 bank),
+dequant_host_120b (the same bank dequantized on copy from page-locked host
+memory) and copy
 (a plain 1 GiB device copy: the achievable-bandwidth reference that also
 calibrates the HBM byte counters).
 """
@@ -236,6 +238,52 @@ def run_moe(args):
     return out
 
 
+def run_dequant_host(args):
+    """Dequant-on-copy of a 120b-shaped w13 bank held in page-locked host memory."""
+    import numpy as np
+    import torch
+
+    from mxfp4_quantized_expert_amd import binding, workloads
+
+    bank = workloads.DEQUANT_BANK_120B[0]
+    blocks, scales = workloads.make_bank(bank)
+    hb = torch.from_numpy(blocks).pin_memory()
+    hs = torch.from_numpy(scales).pin_memory()
+    out = torch.empty(blocks.shape[:-1] + (bank.K,), dtype=torch.bfloat16, device="cuda")
+    N = bank.E * bank.N
+    staging = torch.empty((binding.offload_staging_bytes(N, bank.K),), dtype=torch.uint8, device="cuda")
+    for _ in range(args.warmup):
+        binding.mxfp4_dequantize_from_host(hb, hs, out=out, staging=staging)
+    torch.cuda.synchronize()
+    n_chunks = -(-N // max(1, (16 << 20) // (bank.K // 2 + bank.K // 32)))
+    binding.profile_begin("dequant", args.steps * n_chunks)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        binding.mxfp4_dequantize_from_host(hb, hs, out=out, staging=staging)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kms = binding.profile_end(args.steps * n_chunks)
+    ms = (t1 - t0) * 1e3 / args.steps
+    host_bytes = blocks.nbytes + scales.nbytes
+    chunk_rows = N // n_chunks
+    kernel_bytes = chunk_rows * (bank.K // 2 + bank.K // 32 + bank.K * 2)
+    kmean = float(np.mean(kms))
+    return {
+        "metric": "mxfp4 dequant-on-copy from host memory, host GB/s",
+        "value": host_bytes / (ms / 1e3) / 1e9,
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "u8->bf16", "data": "synthetic",
+        "config": {"workload": f"dequant-on-copy of a gpt-oss-120b shaped w13 bank {list(blocks.shape)} from "
+                               f"page-locked host memory, {n_chunks} chunks through two staging slots",
+                   "output_gbs": out.numel() * 2 / (ms / 1e3) / 1e9},
+        "roofline": {"bound": "hbm", "achieved": kernel_bytes / (kmean / 1e3) / 1e9, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": kernel_bytes / (kmean / 1e3) / 1e9 / PEAK_HBM_GBS, "traffic": None,
+                     "kernel": "mxfp4_dequant_kernel (one chunk)", "kernel_ms": kmean},
+    }
+
+
 def run_copy(args):
     gbs, ms = copy_bandwidth(reps=args.steps)
     return {"metric": "device copy GB/s", "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -299,7 +347,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="120b_prefill",
-                    choices=["120b_prefill", "20b_prefill", "20b_decode", "tiny", "dequant_120b", "copy"])
+                    choices=["120b_prefill", "20b_prefill", "20b_decode", "tiny", "dequant_120b",
+                             "dequant_host_120b", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -315,6 +364,8 @@ def main():
     torch.cuda.set_device(0)
     if args.workload == "dequant_120b":
         res = run_dequant(args)
+    elif args.workload == "dequant_host_120b":
+        res = run_dequant_host(args)
     elif args.workload == "copy":
         res = run_copy(args)
     else:

@@ -67,6 +67,36 @@ int mxfp4_dequantize(const uint8_t* blocks, const uint8_t* scales, uint16_t* out
                      int64_t N, int64_t K, void* stream);
 
 /*
+ * mxfp4_dequantize_from_host - dequant-on-copy of packed rows held in host
+ * memory: copy to the device and expand to bf16 on arrival.
+ *
+ * Defined by "feat(gpt-oss): expert offloading Phase 2 - MXFP4 dequant-on-copy
+ * execution" (MoE-Infinity PR #152), Changes: offloaded packed experts are
+ * copied to the device and dequantized to bf16 there; and "feat(gpt-oss):
+ * expert offloading Phase 3" (MoE-Infinity PR #153), description: the six
+ * packed components per layer are what is offloaded.
+ *
+ *   host_blocks [N, K/2]  uint8 in host memory; page-locked memory (e.g.
+ *                         hipHostMalloc) lets the copies run asynchronously
+ *   host_scales [N, K/32] uint8 in host memory
+ *   out_bf16    [N, K]    bf16 bits, device memory, 16-byte aligned
+ *   staging     device scratch of at least *staging_bytes bytes, 256-byte
+ *               aligned; with staging == NULL the call only stores the size it
+ *               needs (two slots of about 16 MiB of packed rows) and returns
+ *               MXFP4MOE_OK.
+ * Same values as mxfp4_dequantize.  The rows move in chunks: the copy of
+ * chunk i+1 runs on a copy stream the library creates once per device
+ * (default priority) while chunk i is dequantized on `stream`.  The call
+ * returns after enqueueing; the output and the host buffers' use are complete
+ * when `stream` is.  The host buffers must stay valid and unmodified until
+ * then.  Calls are serialised inside the process (they share the copy
+ * stream); two calls must not share one staging buffer unless ordered on one
+ * stream.  N == 0 is a no-op.
+ */
+int mxfp4_dequantize_from_host(const uint8_t* host_blocks, const uint8_t* host_scales, uint16_t* out_bf16,
+                               int64_t N, int64_t K, void* staging, size_t* staging_bytes, void* stream);
+
+/*
  * moe_mxfp4_route - the routing data the MXFP4 experts consume: top-k
  * selection, softmax over the k selected logits, and the tokens grouped by
  * expert.

@@ -52,6 +52,8 @@ def load() -> ctypes.CDLL:
     lib = ctypes.CDLL(LIB_PATH)
     lib.mxfp4_dequantize.argtypes = [_vp, _vp, _vp, _i64, _i64, _vp]
     lib.mxfp4_dequantize.restype = ctypes.c_int
+    lib.mxfp4_dequantize_from_host.argtypes = [_vp, _vp, _vp, _i64, _i64, _vp, ctypes.POINTER(ctypes.c_size_t), _vp]
+    lib.mxfp4_dequantize_from_host.restype = ctypes.c_int
     lib.moe_mxfp4_route.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp]
     lib.moe_mxfp4_route.restype = ctypes.c_int
     lib.moe_mxfp4_forward.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -111,6 +113,45 @@ def mxfp4_dequantize(blocks: torch.Tensor, scales: torch.Tensor, out: Optional[t
         N *= d
     st = lib.mxfp4_dequantize(blocks.data_ptr(), scales.data_ptr(), out.data_ptr(), N, K, _stream(stream))
     _raise("mxfp4_dequantize", st)
+    return out
+
+
+def offload_staging_bytes(N: int, K: int) -> int:
+    """Device staging mxfp4_dequantize_from_host needs for N rows of K elements."""
+    n = ctypes.c_size_t(0)
+    st = load().mxfp4_dequantize_from_host(None, None, None, N, K, None, ctypes.byref(n), None)
+    _raise("mxfp4_dequantize_from_host(staging query)", st)
+    return int(n.value)
+
+
+def mxfp4_dequantize_from_host(blocks: torch.Tensor, scales: torch.Tensor, out: Optional[torch.Tensor] = None,
+                               staging: Optional[torch.Tensor] = None, device="cuda",
+                               stream=None) -> torch.Tensor:
+    """Host blocks [..., N, K/2] + host scales [..., N, K/32] (uint8, CPU; pinned memory copies
+    asynchronously) -> device bf16 [..., N, K], copied in chunks and dequantized on arrival."""
+    lib = load()
+    half_k = blocks.shape[-1]
+    K = 2 * half_k
+    lead = tuple(blocks.shape[:-1])
+    for t, name, shape in ((blocks, "blocks", None), (scales, "scales", lead + (K // 32,))):
+        if t.dtype != torch.uint8 or t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous uint8 host tensor")
+        if shape is not None and tuple(t.shape) != shape:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
+    N = 1
+    for d in lead:
+        N *= d
+    if out is None:
+        out = torch.empty(lead + (K,), dtype=torch.bfloat16, device=device)
+    _check(out, "out", torch.bfloat16, lead + (K,))
+    need = offload_staging_bytes(N, K)
+    if staging is None:
+        staging = torch.empty((max(need, 1),), dtype=torch.uint8, device=out.device)
+    _check(staging, "staging", torch.uint8)
+    n = ctypes.c_size_t(staging.numel())
+    st = lib.mxfp4_dequantize_from_host(blocks.data_ptr(), scales.data_ptr(), out.data_ptr(), N, K,
+                                        staging.data_ptr(), ctypes.byref(n), _stream(stream))
+    _raise("mxfp4_dequantize_from_host", st)
     return out
 
 

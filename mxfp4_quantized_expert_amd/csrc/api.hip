@@ -149,6 +149,25 @@ int mxfp4_dequantize(const uint8_t* blocks, const uint8_t* scales, uint16_t* out
   return err == hipSuccess ? MXFP4MOE_OK : MXFP4MOE_ERR_HIP;
 }
 
+int mxfp4_dequantize_from_host(const uint8_t* host_blocks, const uint8_t* host_scales, uint16_t* out_bf16,
+                               int64_t N, int64_t K, void* staging, size_t* staging_bytes, void* stream) {
+  if (staging_bytes == nullptr) return MXFP4MOE_ERR_ARG;
+  if (N < 0 || K <= 0 || (K & 31) != 0) return MXFP4MOE_ERR_SHAPE;
+  if (N > 0 && K > ((int64_t)1 << 62) / N) return MXFP4MOE_ERR_SHAPE;
+  const size_t need = offload_staging_bytes(N, K);
+  if (staging == nullptr) {
+    *staging_bytes = need;
+    return MXFP4MOE_OK;
+  }
+  if (N == 0) return MXFP4MOE_OK;
+  if (host_blocks == nullptr || host_scales == nullptr || out_bf16 == nullptr) return MXFP4MOE_ERR_ARG;
+  if (*staging_bytes < need) return MXFP4MOE_ERR_WORKSPACE;
+  if (((uintptr_t)staging & (kAlign - 1)) != 0 || !aligned16(out_bf16)) return MXFP4MOE_ERR_ALIGN;
+  hipError_t err = launch_dequant_from_host(host_blocks, host_scales, out_bf16, N, K,
+                                            static_cast<uint8_t*>(staging), (hipStream_t)stream);
+  return err == hipSuccess ? MXFP4MOE_OK : MXFP4MOE_ERR_HIP;
+}
+
 int moe_mxfp4_route(const float* router_logits, int64_t T, int64_t E, int64_t top_k, int32_t* topk_ids,
                     float* topk_weights, int32_t* expert_offsets, int32_t* sorted_pairs, void* stream) {
   int st = check_route_shape(T, E, top_k);

@@ -105,4 +105,10 @@ hipError_t launch_combine(const float* zw, uint16_t* y, int T, int H, int top_k,
 hipError_t launch_dequant(const uint8_t* blocks, const uint8_t* scales, uint16_t* out, int64_t N, int64_t K,
                           hipStream_t stream);
 
+// Dequant-on-copy from host memory through two device staging slots.
+int64_t offload_chunk_rows(int64_t K);
+size_t offload_staging_bytes(int64_t N, int64_t K);
+hipError_t launch_dequant_from_host(const uint8_t* host_blocks, const uint8_t* host_scales, uint16_t* out,
+                                    int64_t N, int64_t K, uint8_t* staging, hipStream_t stream);
+
 }  // namespace mxfp4moe

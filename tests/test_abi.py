@@ -55,6 +55,25 @@ def test_dequant_argument_checks(lib):
     assert f(None, None, None, 0, 32, None) == 0  # empty: no-op
 
 
+def test_dequant_from_host_argument_checks(lib):
+    f = lib.mxfp4_dequantize_from_host
+    n = ctypes.c_size_t(0)
+    assert f(None, None, None, 737280, 2880, None, ctypes.byref(n), None) == 0  # size query
+    assert 2 * 15 * 2**20 <= n.value <= 2 * 17 * 2**20  # two slots of about 16 MiB of packed rows
+    assert f(None, None, None, 3, 64, None, ctypes.byref(n), None) == 0 and n.value >= 2 * 3 * (32 + 2)
+    big = ctypes.c_size_t(1 << 40)
+    assert f(A, A, A, 10, 48, A, ctypes.byref(big), None) == -2   # K not a multiple of 32
+    assert f(A, A, A, -1, 32, A, ctypes.byref(big), None) == -2
+    assert f(A, A, A, 10, 32, A, None, None) == -1                # no size argument
+    assert f(None, A, A, 10, 32, A, ctypes.byref(big), None) == -1
+    assert f(A, A, None, 10, 32, A, ctypes.byref(big), None) == -1
+    small = ctypes.c_size_t(16)
+    assert f(A, A, A, 10, 32, A, ctypes.byref(small), None) == -3
+    assert f(A, A, A, 10, 32, A + 16, ctypes.byref(big), None) == -4   # staging not 256-byte aligned
+    assert f(A, A, A + 8, 10, 32, A, ctypes.byref(big), None) == -4    # output not 16-byte aligned
+    assert f(None, None, None, 0, 32, A, ctypes.byref(big), None) == 0  # empty: no-op
+
+
 def _fwd(lib, T=4, H=64, I=64, E=4, k=2, ws=A, ws_bytes=1 << 30, x=A, lg=A, b13=A, b2=A, y=A,
          wb=A):
     n = ctypes.c_size_t(ws_bytes)
