@@ -172,6 +172,26 @@ int moe_mxfp4_forward(const uint16_t* x, const float* router_logits,
                       uint16_t* y, int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k,
                       void* workspace, size_t* workspace_bytes, void* stream);
 
+/*
+ * moe_mxfp4_forward_ex - moe_mxfp4_forward with layout flags.
+ *
+ *   flags = 0                       w13 gate/up rows interleaved (row 2i gate i,
+ *                                   row 2i+1 up i; bias likewise), as above
+ *   flags = MXFP4MOE_GATE_UP_SPLIT  w13 rows [0, I) are gate, [I, 2I) are up
+ *                                   (blocks, scales and bias alike)
+ * The split layout is the uninterleaved spelling of the same clamped SwiGLU
+ * ("feat(gguf): serve gpt-oss gguf checkpoints on gpt_oss", FreeToken PR #838,
+ * "What it does": swigluoai with interleaved=False).  Results are identical
+ * to the interleaved call on the correspondingly permuted rows.  Any other
+ * flag bit is MXFP4MOE_ERR_ARG.
+ */
+#define MXFP4MOE_GATE_UP_SPLIT 1u
+int moe_mxfp4_forward_ex(const uint16_t* x, const float* router_logits,
+                         const uint8_t* w13_blocks, const uint8_t* w13_scales, const uint16_t* w13_bias,
+                         const uint8_t* w2_blocks, const uint8_t* w2_scales, const uint16_t* w2_bias,
+                         uint16_t* y, int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k,
+                         uint32_t flags, void* workspace, size_t* workspace_bytes, void* stream);
+
 /* Short English text for a status code (static storage). */
 const char* mxfp4moe_status_string(int status);
 

@@ -60,6 +60,10 @@ def load() -> ctypes.CDLL:
                                       _i64, _i64, _i64, _i64, _i64, _vp,
                                       ctypes.POINTER(ctypes.c_size_t), _vp]
     lib.moe_mxfp4_forward.restype = ctypes.c_int
+    lib.moe_mxfp4_forward_ex.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                         _i64, _i64, _i64, _i64, _i64, ctypes.c_uint32, _vp,
+                                         ctypes.POINTER(ctypes.c_size_t), _vp]
+    lib.moe_mxfp4_forward_ex.restype = ctypes.c_int
     lib.mxfp4moe_status_string.argtypes = [ctypes.c_int]
     lib.mxfp4moe_status_string.restype = ctypes.c_char_p
     lib.mxfp4moe_profile_begin.argtypes = [ctypes.c_int, ctypes.c_int]
@@ -186,8 +190,10 @@ def moe_mxfp4_forward(x: torch.Tensor, router_logits: torch.Tensor,
                       w13_blocks: torch.Tensor, w13_scales: torch.Tensor, w13_bias: torch.Tensor,
                       w2_blocks: torch.Tensor, w2_scales: torch.Tensor, w2_bias: torch.Tensor,
                       top_k: int, out: Optional[torch.Tensor] = None,
-                      workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """One MXFP4 MoE expert layer; returns y [T, H] bfloat16."""
+                      workspace: Optional[torch.Tensor] = None, stream=None,
+                      gate_up_split: bool = False) -> torch.Tensor:
+    """One MXFP4 MoE expert layer; returns y [T, H] bfloat16.  gate_up_split: w13 rows are
+    [I gate rows; I up rows] instead of interleaved."""
     lib = load()
     T, H = x.shape
     E = router_logits.shape[1]
@@ -208,11 +214,11 @@ def moe_mxfp4_forward(x: torch.Tensor, router_logits: torch.Tensor,
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
     _check(workspace, "workspace", torch.uint8)
     n = ctypes.c_size_t(workspace.numel())
-    st = lib.moe_mxfp4_forward(x.data_ptr(), router_logits.data_ptr(),
-                               w13_blocks.data_ptr(), w13_scales.data_ptr(), w13_bias.data_ptr(),
-                               w2_blocks.data_ptr(), w2_scales.data_ptr(), w2_bias.data_ptr(),
-                               out.data_ptr(), T, H, I, E, top_k, workspace.data_ptr(),
-                               ctypes.byref(n), _stream(stream))
+    st = lib.moe_mxfp4_forward_ex(x.data_ptr(), router_logits.data_ptr(),
+                                  w13_blocks.data_ptr(), w13_scales.data_ptr(), w13_bias.data_ptr(),
+                                  w2_blocks.data_ptr(), w2_scales.data_ptr(), w2_bias.data_ptr(),
+                                  out.data_ptr(), T, H, I, E, top_k, 1 if gate_up_split else 0,
+                                  workspace.data_ptr(), ctypes.byref(n), _stream(stream))
     _raise("moe_mxfp4_forward", st)
     return out
 

@@ -188,6 +188,16 @@ int moe_mxfp4_forward(const uint16_t* x, const float* router_logits, const uint8
                       const uint8_t* w2_scales, const uint16_t* w2_bias, uint16_t* y, int64_t T, int64_t H,
                       int64_t I, int64_t E, int64_t top_k, void* workspace, size_t* workspace_bytes,
                       void* stream) {
+  return moe_mxfp4_forward_ex(x, router_logits, w13_blocks, w13_scales, w13_bias, w2_blocks, w2_scales, w2_bias, y,
+                              T, H, I, E, top_k, 0u, workspace, workspace_bytes, stream);
+}
+
+int moe_mxfp4_forward_ex(const uint16_t* x, const float* router_logits, const uint8_t* w13_blocks,
+                         const uint8_t* w13_scales, const uint16_t* w13_bias, const uint8_t* w2_blocks,
+                         const uint8_t* w2_scales, const uint16_t* w2_bias, uint16_t* y, int64_t T, int64_t H,
+                         int64_t I, int64_t E, int64_t top_k, uint32_t flags, void* workspace,
+                         size_t* workspace_bytes, void* stream) {
+  if ((flags & ~(uint32_t)MXFP4MOE_GATE_UP_SPLIT) != 0) return MXFP4MOE_ERR_ARG;
   if (workspace_bytes == nullptr) return MXFP4MOE_ERR_ARG;
   int st = check_route_shape(T, E, top_k);
   if (st != MXFP4MOE_OK) return st;
@@ -242,6 +252,7 @@ int moe_mxfp4_forward(const uint16_t* x, const float* router_logits, const uint8
   g.topk_weights = weights;
   g.top_k = (int)top_k;
   if (err == hipSuccess) {
+    g.split_gate_up = (flags & MXFP4MOE_GATE_UP_SPLIT) ? 1 : 0;
     g.wblocks = w13_blocks;
     g.wscales = w13_scales;
     g.bias = w13_bias;
@@ -259,6 +270,7 @@ int moe_mxfp4_forward(const uint16_t* x, const float* router_logits, const uint8
     g.out = zw;
     g.N = (int)H;
     g.K = (int)I;
+    g.split_gate_up = 0;
     err = launch_down(g, tt, tb, s);
   }
   if (err == hipSuccess) err = launch_combine(zw, y, (int)T, (int)H, (int)top_k, s);

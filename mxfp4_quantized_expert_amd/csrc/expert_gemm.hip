@@ -54,6 +54,36 @@ __device__ __forceinline__ float swiglu_clamped(float gate, float up) {
   return g * __builtin_amdgcn_rcpf(1.0f + __expf(-1.702f * g)) * (u + 1.0f);
 }
 
+// gate/up row layout of w13.  Logical row 2i is gate i and 2i+1 is up i (the
+// order every kernel computes in).  Interleaved checkpoints store them so;
+// split ones ("feat(gguf): serve gpt-oss gguf checkpoints on gpt_oss",
+// FreeToken PR #838, "What it does": swigluoai is the uninterleaved spelling
+// of the same activation) store the I gate rows first, then the I up rows.
+__device__ __forceinline__ int w13_row(int r, int N, bool split) {
+  return split ? ((r & 1) ? (N >> 1) + (r >> 1) : (r >> 1)) : r;
+}
+// LDS row of block-local logical row rl after stage_scales (split: the block's
+// gate rows, then its up rows).
+__device__ __forceinline__ int staged_row(int rl, int nv, bool split) {
+  return split ? ((rl & 1) ? (nv >> 1) + (rl >> 1) : (rl >> 1)) : rl;
+}
+// Biases of logical rows n..n+3 (n a multiple of 4, below N).
+__device__ __forceinline__ f32x4 load_bias4(const uint16_t* bias, int n, int N, bool split) {
+  uint32_t lo, hi;
+  if (split) {  // gate n/2, up n/2, gate n/2+1, up n/2+1
+    const uint32_t g = *reinterpret_cast<const uint32_t*>(bias + (n >> 1));
+    const uint32_t u = *reinterpret_cast<const uint32_t*>(bias + (N >> 1) + (n >> 1));
+    lo = (g & 0xffffu) | (u << 16);
+    hi = (g >> 16) | (u & 0xffff0000u);
+  } else {
+    const uint2 b = *reinterpret_cast<const uint2*>(bias + n);
+    lo = b.x;
+    hi = b.y;
+  }
+  return f32x4{mx::bf16_to_f32(lo & 0xffffu), mx::bf16_to_f32(lo >> 16), mx::bf16_to_f32(hi & 0xffffu),
+               mx::bf16_to_f32(hi >> 16)};
+}
+
 // Block -> (tile, weight-row tile).  Blocks are dealt to the 8 XCDs round
 // robin (block b runs on XCD b % 8), so the id is first remapped so that each
 // XCD owns a contiguous range of the work, then walked in groups of kGroup
@@ -148,12 +178,21 @@ constexpr int kWideMaxGroups = 128;  // K <= 4096
 // (their outputs are dropped).
 template <int BN, int kThreads>
 __device__ __forceinline__ void stage_scales(uint8_t* sst, const mxfp4moe::GemmArgs& args, int e, int ntile,
-                                             int kgroups, int t) {
+                                             int kgroups, int t, bool split = false) {
   const int N = args.N;
   const int nv = min(BN, N - ntile * BN);
-  const u32x4* src = reinterpret_cast<const u32x4*>(args.wscales + ((size_t)e * N + ntile * BN) * (size_t)kgroups);
   u32x4* dst = reinterpret_cast<u32x4*>(sst);
-  for (int i = t; i < (nv * kgroups) >> 4; i += kThreads) dst[i] = src[i];
+  if (!split) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(args.wscales + ((size_t)e * N + ntile * BN) * (size_t)kgroups);
+    for (int i = t; i < (nv * kgroups) >> 4; i += kThreads) dst[i] = src[i];
+  } else {
+    // the block's gate rows, then its up rows (each range contiguous, 16-byte aligned)
+    const int h = ((nv >> 1) * kgroups) >> 4;
+    const u32x4* g = reinterpret_cast<const u32x4*>(args.wscales + ((size_t)e * N + (ntile * BN >> 1)) * (size_t)kgroups);
+    const u32x4* u =
+        reinterpret_cast<const u32x4*>(args.wscales + ((size_t)e * N + (N >> 1) + (ntile * BN >> 1)) * (size_t)kgroups);
+    for (int i = t; i < 2 * h; i += kThreads) dst[i] = i < h ? g[i] : u[i - h];
+  }
 }
 
 // Epilogue, staged through an LDS region of RM*32*128 bytes per wave so
@@ -178,9 +217,8 @@ __device__ __forceinline__ void store_epilogue(const mxfp4moe::GemmArgs& args, c
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         int n = n_wave + rb * 32 + 8 * i + 4 * half;
-        const uint2 bb = *reinterpret_cast<const uint2*>(bias + (n < N ? n : N - 4));
-        const float b0 = mx::bf16_to_f32(bb.x & 0xffffu), b1 = mx::bf16_to_f32(bb.x >> 16);
-        const float b2 = mx::bf16_to_f32(bb.y & 0xffffu), b3 = mx::bf16_to_f32(bb.y >> 16);
+        const f32x4 bv = load_bias4(bias, n < N ? n : N - 4, N, args.split_gate_up != 0);
+        const float b0 = bv[0], b1 = bv[1], b2 = bv[2], b3 = bv[3];
         const int byte = rb * 32 + 8 * i + 4 * half;  // 2 * q_local
 #pragma unroll
         for (int cb = 0; cb < RM; ++cb) {
@@ -275,7 +313,8 @@ __global__ __launch_bounds__(WN * WM * 64, kMinBlocks) void expert_gemm_kernel(m
   const int half = lane >> 5;
   const int lrow = lane & 31;
 
-  stage_scales<BN, kThreads>(sst, args, e, ntile, kgroups, t);
+  const bool split = kGateUp && args.split_gate_up;  // uniform
+  stage_scales<BN, kThreads>(sst, args, e, ntile, kgroups, t, split);
 
   // token slot p = t + i*threads -> row p/8, logical column slot_col(row, p%8);
   // rows past `count` re-read the tile's first row (their columns are never stored)
@@ -296,7 +335,7 @@ __global__ __launch_bounds__(WN * WM * 64, kMinBlocks) void expert_gemm_kernel(m
 #pragma unroll
   for (int j = 0; j < kWPer; ++j) {
     int wr = ntile * BN + ((t + j * kThreads) >> 1);
-    wr = wr < N ? wr : N - 1;
+    wr = w13_row(wr < N ? wr : N - 1, N, split);
     wsrc[j] = args.wblocks + ((size_t)e * N + wr) * (size_t)(K >> 1);
   }
   const int wh = t & 1;
@@ -326,10 +365,10 @@ __global__ __launch_bounds__(WN * WM * 64, kMinBlocks) void expert_gemm_kernel(m
   // compute-side constants
   const int n_wave = ntile * BN + wn * RN * 32;
   const int wslot0 = (wn * RN * 32 + lrow) * 2 + half;
-  const uint8_t* srow = sst + (wn * RN * 32 + lrow) * kgroups;
+  const uint8_t* srow = sst + staged_row(wn * RN * 32 + lrow, min(BN, N - ntile * BN), split) * kgroups;
   const int m_wave = wm * RM * 32;
   const bool live = m_wave < count;  // wave-uniform: token blocks past the tile's pairs skip their MFMAs
-  const int rb_stride = 32 * kgroups;
+  const int rb_stride = (split ? 16 : 32) * kgroups;  // staged_row(x + 32) = staged_row(x) + 16 when split
 
   f32x16 acc[RN][RM];
 #pragma unroll
@@ -440,11 +479,12 @@ __global__ __launch_bounds__(256, 5) void expert_stream_kernel(mxfp4moe::GemmArg
   const int q = lane >> 4;
   const int lr = lane & 15;
 
+  const bool split = kGateUp && args.split_gate_up;  // uniform
   const int n_wave = ntile * BN + wave * 16 * RN;
   const uint8_t* wrow[RN];
 #pragma unroll
   for (int rb = 0; rb < RN; ++rb) {
-    const int r = min(n_wave + rb * 16 + lr, N - 1);  // rows past N: outputs dropped
+    const int r = w13_row(min(n_wave + rb * 16 + lr, N - 1), N, split);  // rows past N: outputs dropped
     wrow[rb] = args.wblocks + ((size_t)e * N + r) * (size_t)(K >> 1);
   }
   // A group past the last one (K tail, or a padding chunk of the last batch)
@@ -485,7 +525,7 @@ __global__ __launch_bounds__(256, 5) void expert_stream_kernel(mxfp4moe::GemmArg
       const size_t base = r == 0 ? xsrc[0] : r == 1 ? xsrc[1] : r == 2 ? xsrc[2] : xsrc[3];
       if (j * kThreads < nx16) xv[j] = reinterpret_cast<const u32x4*>(args.act + base)[p];
     }
-    stage_scales<BN, kThreads>(sl, args, e, ntile, kgroups, t);
+    stage_scales<BN, kThreads>(sl, args, e, ntile, kgroups, t, split);
 #pragma unroll
     for (int j = 0; j < 8; ++j)
       if (t + j * kThreads < nx16) reinterpret_cast<u32x4*>(xl)[t + j * kThreads] = xv[j];
@@ -500,7 +540,8 @@ __global__ __launch_bounds__(256, 5) void expert_stream_kernel(mxfp4moe::GemmArg
     for (int j = 0; j < 2; ++j) acc[rb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   const uint8_t* srow[RN];
 #pragma unroll
-  for (int rb = 0; rb < RN; ++rb) srow[rb] = sl + (wave * 16 * RN + rb * 16 + lr) * kgroups;
+  for (int rb = 0; rb < RN; ++rb)
+    srow[rb] = sl + staged_row(wave * 16 * RN + rb * 16 + lr, min(BN, N - ntile * BN), split) * kgroups;
   const uint16_t* xrow = xl + (lr < count ? lr : 0) * K;
   auto compute_batch = [&](int c0, const u32x4 (&w)[kBatch][RN]) {
 #pragma unroll
@@ -537,12 +578,12 @@ __global__ __launch_bounds__(256, 5) void expert_stream_kernel(mxfp4moe::GemmArg
   for (int rb = 0; rb < RN; ++rb) {
     const int n = n_wave + rb * 16 + 4 * q;  // first of this lane's four rows
     if (n >= N) continue;
-    const uint2 bb = *reinterpret_cast<const uint2*>(bias + n);
+    const f32x4 bv = load_bias4(bias, n, N, split);
     f32x4 v;
-    v[0] = acc[rb][0][0] + acc[rb][1][0] + mx::bf16_to_f32(bb.x & 0xffffu);
-    v[1] = acc[rb][0][1] + acc[rb][1][1] + mx::bf16_to_f32(bb.x >> 16);
-    v[2] = acc[rb][0][2] + acc[rb][1][2] + mx::bf16_to_f32(bb.y & 0xffffu);
-    v[3] = acc[rb][0][3] + acc[rb][1][3] + mx::bf16_to_f32(bb.y >> 16);
+    v[0] = acc[rb][0][0] + acc[rb][1][0] + bv[0];
+    v[1] = acc[rb][0][1] + acc[rb][1][1] + bv[1];
+    v[2] = acc[rb][0][2] + acc[rb][1][2] + bv[2];
+    v[3] = acc[rb][0][3] + acc[rb][1][3] + bv[3];
     if (kGateUp) {
       const int I = N >> 1;
       const uint32_t packed = mx::pack_bf16x2_rne(swiglu_clamped(v[0], v[1]), swiglu_clamped(v[2], v[3]));
@@ -642,7 +683,8 @@ __global__ __launch_bounds__(256, 2) void expert_mid_kernel(mxfp4moe::GemmArgs a
   uint8_t* const xs = lds;
   uint8_t* const ws = lds + 64 * kXRow;
   uint8_t* const sl = ws + BN * kWRow;
-  stage_scales<BN, kThreads>(sl, args, e, ntile, kgroups, t);
+  const bool split = kGateUp && args.split_gate_up;  // uniform
+  stage_scales<BN, kThreads>(sl, args, e, ntile, kgroups, t, split);
 
   // load slots: token piece i = t + j*256 -> token i / kXPieces; weight piece
   // i = t + j*256 -> row i / kWPieces (rows past N re-read row N-1)
@@ -664,7 +706,7 @@ __global__ __launch_bounds__(256, 2) void expert_mid_kernel(mxfp4moe::GemmArgs a
   for (int j = 0; j < kWPer; ++j) {
     const int i = t + j * kThreads;
     const int r = i / kWPieces;
-    const int gr = min(ntile * BN + r, N - 1);
+    const int gr = w13_row(min(ntile * BN + r, N - 1), N, split);
     wsrc[j] = reinterpret_cast<const u32x4*>(args.wblocks + ((size_t)e * N + gr) * (size_t)(K >> 1));
     wpiece[j] = i - r * kWPieces;
     wdst[j] = r * kWRow + wpiece[j] * 16;
@@ -693,7 +735,7 @@ __global__ __launch_bounds__(256, 2) void expert_mid_kernel(mxfp4moe::GemmArgs a
   int wrd[2];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
-    srow[rb] = sl + (wave * 32 + rb * 16 + lr) * kgroups;
+    srow[rb] = sl + staged_row(wave * 32 + rb * 16 + lr, min(BN, N - ntile * BN), split) * kgroups;
     wrd[rb] = (wave * 32 + rb * 16 + lr) * kWRow + 16 * q;
   }
   const int ncb = (count + 15) >> 4;  // live 16-token column blocks
@@ -768,9 +810,8 @@ __global__ __launch_bounds__(256, 2) void expert_mid_kernel(mxfp4moe::GemmArgs a
   for (int rb = 0; rb < 2; ++rb) {
     const int n = n_wave + rb * 16 + 4 * q;  // first of this lane's four rows
     if (n >= N) continue;
-    const uint2 bb = *reinterpret_cast<const uint2*>(bias + n);
-    const float b0 = mx::bf16_to_f32(bb.x & 0xffffu), b1 = mx::bf16_to_f32(bb.x >> 16);
-    const float b2 = mx::bf16_to_f32(bb.y & 0xffffu), b3 = mx::bf16_to_f32(bb.y >> 16);
+    const f32x4 bv = load_bias4(bias, n, N, split);
+    const float b0 = bv[0], b1 = bv[1], b2 = bv[2], b3 = bv[3];
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
       const int m = cb * 16 + lr;

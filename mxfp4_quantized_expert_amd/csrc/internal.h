@@ -94,6 +94,7 @@ struct GemmArgs {
   const float* topk_weights;  // [P] (down only)
   void* out;                // gate_up: a [P, N/2] bf16 in expert order; down: zw [P, N] f32 by pair id
   int N, K, top_k, max_tiles;
+  int split_gate_up;        // gate_up only: w13 rows stored [I gate rows; I up rows] instead of interleaved
 };
 
 // Both GEMM stages launch the wide, mid and streaming kernels over their

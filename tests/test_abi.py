@@ -115,6 +115,13 @@ def test_forward_argument_checks(lib):
     del n
 
 
+def test_forward_ex_rejects_unknown_flags(lib):
+    n = ctypes.c_size_t(0)
+    f = lib.moe_mxfp4_forward_ex
+    assert f(A, A, A, A, A, A, A, A, A, 4, 64, 64, 4, 2, 2, None, ctypes.byref(n), None) == -1
+    assert f(A, A, A, A, A, A, A, A, A, 4, 64, 64, 4, 2, 1, None, ctypes.byref(n), None) == 0 and n.value > 0
+
+
 def test_route_argument_checks(lib):
     f = lib.moe_mxfp4_route
     assert f(A, 4, 0, 1, A, A, A, A, None) == -2

@@ -160,3 +160,40 @@ def test_tile_boundaries(gpu, path):
     assert np.array_equal(np.bincount(ids.ravel(), minlength=E), counts)
     y = _forward(gpu, L, 1, path)
     assert_layer_parity(y, O.moe_forward(L, 1), f"tile boundaries/{path}")
+
+
+def _split_rows(a: np.ndarray) -> np.ndarray:
+    """Interleaved w13 rows (2i gate i, 2i+1 up i) -> [I gate rows; I up rows] along axis 1."""
+    return np.concatenate([a[:, 0::2], a[:, 1::2]], axis=1)
+
+
+@pytest.mark.parametrize("case", ["boundaries", "20b_decode"])
+def test_split_gate_up_layout(gpu, case):
+    # The uninterleaved (swigluoai) layout of the same weights must give the
+    # same output, bit for bit, through every kernel (wide, mid and streaming
+    # tiles, partial weight-row tiles), and match the oracle.
+    if case == "boundaries":
+        counts = [128, 127, 129, 4, 5, 64, 65, 1, 0, 259]
+        E = len(counts)
+        T = sum(counts)
+        spec = W.LAYERS["20b_live"].with_(T=T, H=64, I=96, E=E, top_k=1)
+        L = W.make_layer(spec, seed=21)
+        rng = np.random.default_rng(22)
+        owner = rng.permutation(np.repeat(np.arange(E), counts))
+        logits = rng.standard_normal((T, E)).astype(np.float32)
+        logits[np.arange(T), owner] += 20.0
+        L["router_logits"] = logits
+        k = 1
+    else:
+        spec = W.LAYERS["20b_live"]
+        L = W.make_layer(spec)
+        k = spec.top_k
+    Ls = dict(L, w13_blocks=_split_rows(L["w13_blocks"]), w13_scales=_split_rows(L["w13_scales"]),
+              w13_bias=_split_rows(L["w13_bias"]))
+    y = _forward(gpu, L, k)
+    d = gpu.layer_to_device(Ls)
+    ys = gpu.moe_mxfp4_forward(d["x"], d["router_logits"], d["w13_blocks"], d["w13_scales"], d["w13_bias"],
+                               d["w2_blocks"], d["w2_scales"], d["w2_bias"], k, gate_up_split=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_u16(y), bits_u16(ys))
+    assert_layer_parity(ys, O.moe_forward(L, k), f"split layout/{case}")
