@@ -33,6 +33,7 @@ __all__ = [
     "DequantBankSpec",
     "DEQUANT_BANK_120B",
     "make_layer",
+    "make_nvfp4_layer",
     "make_routing_inputs",
     "make_bank",
     "to_bf16_bits",
@@ -142,6 +143,31 @@ def make_layer(spec: LayerSpec, seed: Optional[int] = None) -> Dict[str, np.ndar
     out["w13_bias"] = to_bf16_bits(rng.standard_normal((E, 2 * I), dtype=np.float32) * np.float32(spec.bias_std))
     out["w2_blocks"] = _uniform_bytes(rng, (E, H, I // 2))
     out["w2_scales"] = _scale_bytes(rng, (E, H, I // 32), spec.scale_lo, spec.scale_hi)
+    out["w2_bias"] = to_bf16_bits(rng.standard_normal((E, H), dtype=np.float32) * np.float32(spec.bias_std))
+    return out
+
+
+def make_nvfp4_layer(spec: LayerSpec, seed: Optional[int] = None, scale_lo: int = 0x30,
+                     scale_hi: int = 0x48) -> Dict[str, np.ndarray]:
+    """An NVFP4 expert layer of the same shapes: blocks [E,N,K/2] uint8, E4M3
+    block scales [E,N,K/16] uint8 drawn uniform in [scale_lo, scale_hi] (positive
+    values 0.5 .. 4 by default), second-level scales w13_scale2 / w2_scale2 [E]
+    float32 drawn uniform in [1/16, 1/4], biases bf16 N(0, bias_std).  Draw
+    order: x, logits, (Zipf permutation), w13 blocks, w13 scales, w13 scale2,
+    w13 bias, w2 blocks, w2 scales, w2 scale2, w2 bias."""
+    rng = np.random.default_rng(spec.seed if seed is None else seed)
+    H, I, E = spec.H, spec.I, spec.E
+    if H % 32 or I % 32:
+        raise ValueError("H and I must be multiples of 32")
+    out: Dict[str, np.ndarray] = {}
+    out["x"], out["router_logits"] = _draw_x_logits(rng, spec)
+    out["w13_blocks"] = _uniform_bytes(rng, (E, 2 * I, H // 2))
+    out["w13_scales"] = _scale_bytes(rng, (E, 2 * I, H // 16), scale_lo, scale_hi)
+    out["w13_scale2"] = rng.uniform(1 / 16, 1 / 4, size=E).astype(np.float32)
+    out["w13_bias"] = to_bf16_bits(rng.standard_normal((E, 2 * I), dtype=np.float32) * np.float32(spec.bias_std))
+    out["w2_blocks"] = _uniform_bytes(rng, (E, H, I // 2))
+    out["w2_scales"] = _scale_bytes(rng, (E, H, I // 16), scale_lo, scale_hi)
+    out["w2_scale2"] = rng.uniform(1 / 16, 1 / 4, size=E).astype(np.float32)
     out["w2_bias"] = to_bf16_bits(rng.standard_normal((E, H), dtype=np.float32) * np.float32(spec.bias_std))
     return out
 

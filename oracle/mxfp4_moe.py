@@ -20,6 +20,8 @@ passage of the pages it cites (page title, then section):
 * "Restore GPT-OSS's router-masked expert-parallel plan" (transformers PR
   #49431), description: MXFP4 experts consume routing data (top-k ids and
   weights) and group their tokens themselves.
+* FreeToken PR #838, review item 3, for the NVFP4 variant: the second-level
+  weight_scale_2 multiplies the expert output before its bias.
 * "Add native GPT-OSS MXFP4 QMoE export" (mobius PR #719): Summary (blocks
   [E, N, K/32, 16], one E8M0 scale byte per 16-byte block) and Validation
   (scale bytes 0x00..0xfe are valid, 0xff is not).
@@ -181,6 +183,84 @@ def mxfp4_dequantize(blocks: np.ndarray, scales: np.ndarray) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# NVFP4 experts ("feat(gguf): serve gpt-oss gguf checkpoints on gpt_oss",
+# FreeToken PR #838, review item 3: NVFP4 experts carry a second-level
+# weight_scale_2 that multiplies the expert output before the bias,
+# sum_k w*(s*y + b)).  Element format, as publicly described for NVFP4: E2M1
+# codes in blocks of 16 with one FP8 E4M3 scale byte each, times one float32
+# second-level scale per expert and projection.
+# --------------------------------------------------------------------------
+
+NV_GROUP = 16
+
+
+def e4m3_value(b) -> np.ndarray:
+    """FP8 E4M3 (OCP, no infinities): 1 sign, 4 exponent bits (bias 7), 3
+    mantissa bits; exponent field 0 is subnormal (m * 2^-9); S.1111.111 is NaN."""
+    b = np.asarray(b, dtype=np.int64)
+    sign = np.where((b >> 7) & 1, -1.0, 1.0)
+    e = (b >> 3) & 0xF
+    m = b & 0x7
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.ldexp(1.0, e - 7))
+    return np.where((b & 0x7F) == 0x7F, np.nan, sign * mag)
+
+
+def nvfp4_dequantize_f64(blocks: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Exact value of every element before the second-level scale:
+    E2M1(code) * E4M3(scale of its 16-element block).
+
+    blocks [..., N, K/2] uint8, scales [..., N, K/16] uint8 -> [..., N, K] float64.
+    """
+    codes = unpack_codes(blocks)
+    K = codes.shape[-1]
+    if scales.shape[-1] * NV_GROUP != K:
+        raise ValueError("scales must have K/16 entries per row")
+    return E2M1_VALUES[codes] * np.repeat(e4m3_value(scales), NV_GROUP, axis=-1)
+
+
+def expert_ffn_nvfp4(xrows: np.ndarray, w13_blocks, w13_scales, w13_scale2, w13_bias_bits,
+                     w2_blocks, w2_scales, w2_scale2, w2_bias_bits) -> np.ndarray:
+    """One NVFP4 expert: h = s2_13 * (x W13^T) + b13, a = clamped SwiGLU,
+    z = s2_2 * (a W2^T) + b2.  Each second-level scale multiplies its GEMM
+    result before that GEMM's bias is added."""
+    W13 = nvfp4_dequantize_f64(w13_blocks, w13_scales)
+    h = float(w13_scale2) * (xrows @ W13.T) + bf16_decode(w13_bias_bits)[None, :]
+    a = swiglu_clamped(h[:, 0::2], h[:, 1::2])
+    W2 = nvfp4_dequantize_f64(w2_blocks, w2_scales)
+    return float(w2_scale2) * (a @ W2.T) + bf16_decode(w2_bias_bits)[None, :]
+
+
+def moe_forward_nvfp4(layer: Dict[str, np.ndarray], top_k: int,
+                      tokens: Optional[Sequence[int]] = None) -> np.ndarray:
+    """Routed NVFP4 layer: y_t = sum_j w_tj * z_{e_tj}(x_t) with z as in
+    expert_ffn_nvfp4 (the routing weight multiplies s*y + b)."""
+    x = bf16_decode(layer["x"])
+    logits = np.asarray(layer["router_logits"])
+    if tokens is not None:
+        tokens = np.asarray(tokens, dtype=np.int64)
+        x = x[tokens]
+        logits = logits[tokens]
+    T, H = x.shape
+    E = logits.shape[1]
+    ids, w = route(logits, top_k)
+    counts, offsets, perm = group_by_expert(ids, E)
+    z = np.zeros((T * top_k, H), dtype=np.float64)
+    for e in range(E):
+        if counts[e] == 0:
+            continue
+        pairs = perm[offsets[e]:offsets[e + 1]]
+        z[pairs] = expert_ffn_nvfp4(
+            x[pairs // top_k],
+            layer["w13_blocks"][e], layer["w13_scales"][e], layer["w13_scale2"][e], layer["w13_bias"][e],
+            layer["w2_blocks"][e], layer["w2_scales"][e], layer["w2_scale2"][e], layer["w2_bias"][e])
+    z = z.reshape(T, top_k, H)
+    y = np.zeros((T, H), dtype=np.float64)
+    for j in range(top_k):
+        y += w[:, j:j + 1] * z[:, j, :]
+    return y
+
+
+# --------------------------------------------------------------------------
 # Routing (top-k, softmax over the selected logits) and grouping by expert
 # --------------------------------------------------------------------------
 
@@ -323,5 +403,6 @@ __all__ = [
     "dequantize_f64", "mxfp4_dequantize", "route", "group_by_expert",
     "swiglu_clamped", "expert_ffn", "moe_forward", "moe_forward_dense",
     "parity_errors", "flops_per_pair",
+    "NV_GROUP", "e4m3_value", "nvfp4_dequantize_f64", "expert_ffn_nvfp4", "moe_forward_nvfp4",
 ]
 

@@ -370,3 +370,83 @@ def test_planted_defects_fail_parity(defect, case):
     assert O.parity_errors(_variant_forward(L, spec.top_k, "none"), ref)[0] <= 1e-12
     rel, _ = O.parity_errors(_variant_forward(L, spec.top_k, defect), ref)
     assert rel > 1e-2, (defect, rel)
+
+
+# ---------------------------------------------------------------- NVFP4 variant
+
+def test_e4m3_matches_torch_float8():
+    # FP8 E4M3 (OCP, finite-only): an independent decoder is torch's float8_e4m3fn.
+    import torch
+
+    b = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(b).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    got = O.e4m3_value(b)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+    assert O.e4m3_value(0x7E) == 448.0 and O.e4m3_value(0x38) == 1.0 and O.e4m3_value(0x01) == 2.0 ** -9
+
+
+def test_nvfp4_block_axis_and_nibble_order():
+    # one row of 64 elements: codes 2 (1.0) everywhere except element 17 (high
+    # nibble of byte 8) = code 7 (6.0); four 16-element blocks with scales 1, 2, 4, 0.5
+    blocks = np.full((1, 32), 0x22, np.uint8)
+    blocks[0, 8] = 0x72
+    scales = np.array([[0x38, 0x40, 0x48, 0x30]], np.uint8)
+    got = O.nvfp4_dequantize_f64(blocks, scales)[0]
+    want = np.repeat([1.0, 2.0, 4.0, 0.5], 16)
+    want[17] = 6.0 * 2.0
+    assert np.array_equal(got, want)
+
+
+def _nvfp4_small_layer(T=5, H=64, I=32, E=3, k=2, seed=3, bias_std=0.5, scale_lo=0x30, scale_hi=0x48):
+    spec = W.LAYERS["20b_live"].with_(T=T, H=H, I=I, E=E, top_k=k, bias_std=bias_std)
+    return W.make_nvfp4_layer(spec, seed=seed, scale_lo=scale_lo, scale_hi=scale_hi), k
+
+
+def test_nvfp4_expert_against_scalar_loops():
+    L, k = _nvfp4_small_layer()
+    e, t = 1, 2
+    x = O.bf16_decode(L["x"][t])
+    codes13 = O.unpack_codes(L["w13_blocks"][e])
+    codes2 = O.unpack_codes(L["w2_blocks"][e])
+    H = x.shape[0]
+    I = codes2.shape[1]
+    s13 = float(L["w13_scale2"][e])
+    s2 = float(L["w2_scale2"][e])
+    h = []
+    for r in range(2 * I):
+        acc = 0.0
+        for kk in range(H):
+            acc += x[kk] * O.E2M1_VALUES[codes13[r, kk]] * float(O.e4m3_value(L["w13_scales"][e][r, kk // 16]))
+        h.append(s13 * acc + float(O.bf16_decode(L["w13_bias"][e][r])))
+    a = [float(O.swiglu_clamped(h[2 * i], h[2 * i + 1])) for i in range(I)]
+    z = []
+    for n in range(H):
+        acc = 0.0
+        for i in range(I):
+            acc += a[i] * O.E2M1_VALUES[codes2[n, i]] * float(O.e4m3_value(L["w2_scales"][e][n, i // 16]))
+        z.append(s2 * acc + float(O.bf16_decode(L["w2_bias"][e][n])))
+    got = O.expert_ffn_nvfp4(x[None, :], L["w13_blocks"][e], L["w13_scales"][e], L["w13_scale2"][e],
+                             L["w13_bias"][e], L["w2_blocks"][e], L["w2_scales"][e], L["w2_scale2"][e],
+                             L["w2_bias"][e])[0]
+    assert np.allclose(got, z, rtol=1e-12, atol=1e-12)
+
+
+def test_nvfp4_bias_after_second_level_scale():
+    # z(s2 = c) = c * z(s2 = 1, b2 = 0) + b2 exactly for a power-of-two c; folding
+    # the scale into the routing weight ahead of the bias (sum w*s*(y + b)) must
+    # miss the parity bar by far.
+    # small block scales and large biases: the bias is a large part of z
+    L, k = _nvfp4_small_layer(T=8, H=128, I=64, E=4, k=2, seed=9, bias_std=2.0, scale_lo=0x18, scale_hi=0x20)
+    c = 0.125
+    L["w2_scale2"][:] = c
+    ref = O.moe_forward_nvfp4(L, k)
+    L1 = dict(L, w2_scale2=np.ones_like(L["w2_scale2"]), w2_bias=np.zeros_like(L["w2_bias"]))
+    y1 = O.moe_forward_nvfp4(L1, k)
+    ids, w = O.route(L["router_logits"], k)
+    b2 = O.bf16_decode(L["w2_bias"])
+    ident = c * y1 + sum(w[:, j:j + 1] * b2[ids[:, j]] for j in range(k))
+    assert np.allclose(ident, ref, rtol=1e-13, atol=1e-13)
+    folded = c * (y1 + sum(w[:, j:j + 1] * b2[ids[:, j]] for j in range(k)))  # sum w*s*(y + b)
+    assert O.parity_errors(folded, ref)[0] > 10 * 1e-2
