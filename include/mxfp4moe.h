@@ -192,6 +192,32 @@ int moe_mxfp4_forward_ex(const uint16_t* x, const float* router_logits,
                          uint16_t* y, int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k,
                          uint32_t flags, void* workspace, size_t* workspace_bytes, void* stream);
 
+/*
+ * moe_nvfp4_forward - the same expert layer over NVFP4 experts.
+ *
+ * "feat(gguf): serve gpt-oss gguf checkpoints on gpt_oss" (FreeToken PR #838),
+ * review item 3: NVFP4 experts carry a second-level scale (weight_scale_2)
+ * that multiplies the expert's GEMM output before the bias is added, so the
+ * layer is y_t = sum_j w_tj * (s2 * (a W2^T) + b2), never sum_j w_tj * s2 * (y + b2);
+ * the gate_up GEMM likewise: h = s2_13 * (x W13^T) + b13.  Element format (the
+ * public NVFP4 description; the pages name only the format and its second-
+ * level scale): E2M1 codes, two per byte, low nibble first, in blocks of 16
+ * elements with one FP8 E4M3 scale byte each.
+ *
+ *   w13_blocks [E, 2I, H/2] uint8, w13_scales [E, 2I, H/16] uint8 (E4M3),
+ *   w13_scale2 [E] float32, w2_blocks [E, H, I/2], w2_scales [E, H, I/16],
+ *   w2_scale2 [E] float32; everything else as moe_mxfp4_forward (gate/up rows
+ *   interleaved), and the same workspace query.
+ * Every pair runs in mid-size or streaming tiles.  A NULL second-level scale
+ * with a workspace is MXFP4MOE_ERR_ARG.
+ */
+int moe_nvfp4_forward(const uint16_t* x, const float* router_logits,
+                      const uint8_t* w13_blocks, const uint8_t* w13_scales, const float* w13_scale2,
+                      const uint16_t* w13_bias, const uint8_t* w2_blocks, const uint8_t* w2_scales,
+                      const float* w2_scale2, const uint16_t* w2_bias, uint16_t* y, int64_t T, int64_t H,
+                      int64_t I, int64_t E, int64_t top_k, void* workspace, size_t* workspace_bytes,
+                      void* stream);
+
 /* Short English text for a status code (static storage). */
 const char* mxfp4moe_status_string(int status);
 

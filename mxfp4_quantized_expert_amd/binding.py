@@ -64,6 +64,9 @@ def load() -> ctypes.CDLL:
                                          _i64, _i64, _i64, _i64, _i64, ctypes.c_uint32, _vp,
                                          ctypes.POINTER(ctypes.c_size_t), _vp]
     lib.moe_mxfp4_forward_ex.restype = ctypes.c_int
+    lib.moe_nvfp4_forward.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                      _i64, _i64, _i64, _i64, _i64, _vp, ctypes.POINTER(ctypes.c_size_t), _vp]
+    lib.moe_nvfp4_forward.restype = ctypes.c_int
     lib.mxfp4moe_status_string.argtypes = [ctypes.c_int]
     lib.mxfp4moe_status_string.restype = ctypes.c_char_p
     lib.mxfp4moe_profile_begin.argtypes = [ctypes.c_int, ctypes.c_int]
@@ -223,6 +226,45 @@ def moe_mxfp4_forward(x: torch.Tensor, router_logits: torch.Tensor,
     return out
 
 
+def moe_nvfp4_forward(x: torch.Tensor, router_logits: torch.Tensor,
+                      w13_blocks: torch.Tensor, w13_scales: torch.Tensor, w13_scale2: torch.Tensor,
+                      w13_bias: torch.Tensor, w2_blocks: torch.Tensor, w2_scales: torch.Tensor,
+                      w2_scale2: torch.Tensor, w2_bias: torch.Tensor, top_k: int,
+                      out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                      stream=None) -> torch.Tensor:
+    """One NVFP4 MoE expert layer (E4M3 block scales per 16, float32 second-level
+    scales [E]); returns y [T, H] bfloat16."""
+    lib = load()
+    T, H = x.shape
+    E = router_logits.shape[1]
+    I = w2_blocks.shape[-1] * 2
+    _check(x, "x", torch.bfloat16, (T, H))
+    _check(router_logits, "router_logits", torch.float32, (T, E))
+    _check(w13_blocks, "w13_blocks", torch.uint8, (E, 2 * I, H // 2))
+    _check(w13_scales, "w13_scales", torch.uint8, (E, 2 * I, H // 16))
+    _check(w13_scale2, "w13_scale2", torch.float32, (E,))
+    _check(w13_bias, "w13_bias", torch.bfloat16, (E, 2 * I))
+    _check(w2_blocks, "w2_blocks", torch.uint8, (E, H, I // 2))
+    _check(w2_scales, "w2_scales", torch.uint8, (E, H, I // 16))
+    _check(w2_scale2, "w2_scale2", torch.float32, (E,))
+    _check(w2_bias, "w2_bias", torch.bfloat16, (E, H))
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    _check(out, "out", torch.bfloat16, (T, H))
+    need = workspace_bytes(T, H, I, E, top_k)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
+    _check(workspace, "workspace", torch.uint8)
+    n = ctypes.c_size_t(workspace.numel())
+    st = lib.moe_nvfp4_forward(x.data_ptr(), router_logits.data_ptr(), w13_blocks.data_ptr(),
+                               w13_scales.data_ptr(), w13_scale2.data_ptr(), w13_bias.data_ptr(),
+                               w2_blocks.data_ptr(), w2_scales.data_ptr(), w2_scale2.data_ptr(),
+                               w2_bias.data_ptr(), out.data_ptr(), T, H, I, E, top_k, workspace.data_ptr(),
+                               ctypes.byref(n), _stream(stream))
+    _raise("moe_nvfp4_forward", st)
+    return out
+
+
 def profile_begin(stage: str, max_calls: int) -> None:
     """Record HIP events around the next ``max_calls`` launches of one kernel stage."""
     st = load().mxfp4moe_profile_begin(STAGES[stage], max_calls)
@@ -248,7 +290,7 @@ def layer_to_device(layer, device="cuda"):
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
         return torch.from_numpy(a).to(device)
 
-    return {
+    out = {
         "x": dev(layer["x"], torch.bfloat16),
         "router_logits": dev(layer["router_logits"], torch.float32),
         "w13_blocks": dev(layer["w13_blocks"], torch.uint8),
@@ -258,3 +300,7 @@ def layer_to_device(layer, device="cuda"):
         "w2_scales": dev(layer["w2_scales"], torch.uint8),
         "w2_bias": dev(layer["w2_bias"], torch.bfloat16),
     }
+    for k in ("w13_scale2", "w2_scale2"):  # NVFP4 layers
+        if k in layer:
+            out[k] = dev(np.asarray(layer[k], dtype=np.float32), torch.float32)
+    return out

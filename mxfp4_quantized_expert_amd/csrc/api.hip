@@ -65,27 +65,36 @@ struct Layout {
 // experts are distinct).  An expert with at least kWideTokens pairs makes
 // ceil(c / kWideTokens) wide tiles (at most P / kWideTokens full ones plus one
 // partial per such expert); one with kStreamTokens < c < kWideTokens pairs at
-// most two mid tiles; one with fewer, one streaming tile.  Without wide tiles
-// every pair goes to streaming tiles of kStreamTokens.
-TileBounds tile_bounds(int64_t T, int64_t P, int64_t E, bool wide) {
+// most two mid tiles; one with fewer, one streaming tile.  With no wide tiles
+// (NVFP4) an expert with more than kStreamTokens pairs makes ceil(c /
+// kMidTokens) mid tiles.  With streaming tiles only, every pair goes to tiles
+// of kStreamTokens.
+enum TileMode { kTilesWide, kTilesNoWide, kTilesStreamOnly };
+TileBounds tile_bounds(int64_t T, int64_t P, int64_t E, TileMode mode) {
   const int64_t active = E < P ? E : P;
   const int64_t fulls = P / kWideTokens;
   TileBounds b;
-  b.max_big = (wide && T >= kWideTokens) ? (int)(fulls + (active < fulls ? active : fulls)) : 0;
+  b.max_big = (mode == kTilesWide && T >= kWideTokens) ? (int)(fulls + (active < fulls ? active : fulls)) : 0;
   static_assert(2 * kMidTokens >= kWideTokens, "two mid tiles cover an expert below kWideTokens");
   const int64_t mids = 2 * (P / (kStreamTokens + 1));
-  b.max_mid = (wide && T > kStreamTokens) ? (int)(2 * active < mids ? 2 * active : mids) : 0;
-  b.max_small = wide ? (int)active : (int)(P / kStreamTokens + active);
+  if (mode == kTilesWide)
+    b.max_mid = T > kStreamTokens ? (int)(2 * active < mids ? 2 * active : mids) : 0;
+  else if (mode == kTilesNoWide)
+    b.max_mid = T > kStreamTokens ? (int)(P / kMidTokens + active) : 0;
+  else
+    b.max_mid = 0;
+  b.max_small = mode == kTilesStreamOnly ? (int)(P / kStreamTokens + active) : (int)active;
   return b;
 }
 
 Layout make_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k) {
   const int64_t P = T * top_k;
   Layout L;
-  const TileBounds with_wide = tile_bounds(T, P, E, true), stream_only = tile_bounds(T, P, E, false);
-  L.max_big = with_wide.max_big;
-  L.max_mid = with_wide.max_mid;
-  L.max_small = stream_only.max_small;  // the larger of the two
+  const TileBounds wide = tile_bounds(T, P, E, kTilesWide), no_wide = tile_bounds(T, P, E, kTilesNoWide),
+                   stream_only = tile_bounds(T, P, E, kTilesStreamOnly);
+  L.max_big = wide.max_big;
+  L.max_mid = wide.max_mid > no_wide.max_mid ? wide.max_mid : no_wide.max_mid;
+  L.max_small = stream_only.max_small;  // the largest of the three
   size_t off = 0;
   L.ids = off;       off = align_up(off + (size_t)P * 4);
   L.weights = off;   off = align_up(off + (size_t)P * 4);
@@ -123,6 +132,103 @@ int check_route_shape(int64_t T, int64_t E, int64_t top_k) {
 }  // namespace mxfp4moe
 
 using namespace mxfp4moe;
+
+namespace {
+
+const float kNvQuery = 0.f;  // stands in for the NVFP4 scale pointers of a size query
+
+// The layer.  scale2_13 / scale2_2 != nullptr selects NVFP4 weights (E4M3
+// block scales per 16 elements, one second-level scale per expert and
+// projection, multiplied before the bias).
+int forward_impl(const uint16_t* x, const float* router_logits, const uint8_t* w13_blocks, const uint8_t* w13_scales,
+                 const float* scale2_13, const uint16_t* w13_bias, const uint8_t* w2_blocks,
+                 const uint8_t* w2_scales, const float* scale2_2, const uint16_t* w2_bias, uint16_t* y, int64_t T,
+                 int64_t H, int64_t I, int64_t E, int64_t top_k, uint32_t flags, void* workspace,
+                 size_t* workspace_bytes, void* stream) {
+  const bool nv = scale2_13 != nullptr;
+  if (workspace_bytes == nullptr) return MXFP4MOE_ERR_ARG;
+  int st = check_route_shape(T, E, top_k);
+  if (st != MXFP4MOE_OK) return st;
+  if (H <= 0 || I <= 0 || (H & 31) != 0 || (I & 31) != 0) return MXFP4MOE_ERR_SHAPE;
+  if (H > MXFP4MOE_MAX_HIDDEN || I > MXFP4MOE_MAX_HIDDEN) return MXFP4MOE_ERR_SHAPE;
+  static_assert(MXFP4MOE_MAX_HIDDEN == kMaxHidden, "one bound on H and I");
+  const Layout L = make_layout(T, H, I, E, top_k);
+  if (workspace == nullptr) {
+    *workspace_bytes = L.total;
+    return MXFP4MOE_OK;
+  }
+  if (w13_blocks == nullptr || w13_scales == nullptr || w13_bias == nullptr || w2_blocks == nullptr ||
+      w2_scales == nullptr || w2_bias == nullptr)
+    return MXFP4MOE_ERR_ARG;
+  if (T > 0 && (x == nullptr || router_logits == nullptr || y == nullptr)) return MXFP4MOE_ERR_ARG;
+  if (*workspace_bytes < L.total) return MXFP4MOE_ERR_WORKSPACE;
+  if (((uintptr_t)workspace & (kAlign - 1)) != 0) return MXFP4MOE_ERR_ALIGN;
+  if (!aligned16(w13_blocks) || !aligned16(w2_blocks)) return MXFP4MOE_ERR_ALIGN;
+  if (T > 0 && (!aligned16(x) || !aligned16(y))) return MXFP4MOE_ERR_ALIGN;
+  if (T == 0) return MXFP4MOE_OK;
+
+  char* ws = static_cast<char*>(workspace);
+  int32_t* ids = reinterpret_cast<int32_t*>(ws + L.ids);
+  float* weights = reinterpret_cast<float*>(ws + L.weights);
+  int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+  int32_t* sorted = reinterpret_cast<int32_t*>(ws + L.sorted);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
+  uint16_t* act = reinterpret_cast<uint16_t*>(ws + L.act);
+  float* zw = reinterpret_cast<float*>(ws + L.zw);
+
+  const int64_t P = T * top_k;
+  TileTables tt;
+  tt.big = reinterpret_cast<int32_t*>(ws + L.big);
+  tt.num_big = counts;
+  tt.mid = reinterpret_cast<int32_t*>(ws + L.mid);
+  tt.num_mid = counts + 1;
+  tt.small = reinterpret_cast<int32_t*>(ws + L.small);
+  tt.num_small = counts + 2;
+  tt.big_tokens = nv ? 0 : big_tile_tokens();
+  tt.no_wide = nv ? 1 : 0;
+  const TileBounds tb = tile_bounds(T, P, E, nv ? kTilesNoWide : tt.big_tokens > 0 ? kTilesWide : kTilesStreamOnly);
+  hipStream_t s = (hipStream_t)stream;
+
+  hipError_t err;
+  if (T <= kFusedRouteTokens) {
+    err = launch_route_group(router_logits, (int)T, (int)E, (int)top_k, ids, weights, offsets, sorted, tt, s);
+  } else {
+    err = launch_route(router_logits, (int)T, (int)E, (int)top_k, ids, weights, s);
+    if (err == hipSuccess) err = launch_group(ids, (int)P, (int)E, offsets, sorted, tt, s);
+  }
+  GemmArgs g{};
+  g.sorted_pairs = sorted;
+  g.topk_weights = weights;
+  g.top_k = (int)top_k;
+  if (err == hipSuccess) {
+    g.split_gate_up = (flags & MXFP4MOE_GATE_UP_SPLIT) ? 1 : 0;
+    g.scale2 = nv ? scale2_13 : nullptr;
+    g.wblocks = w13_blocks;
+    g.wscales = w13_scales;
+    g.bias = w13_bias;
+    g.act = x;
+    g.out = act;
+    g.N = (int)(2 * I);
+    g.K = (int)H;
+    err = launch_gate_up(g, tt, tb, s);
+  }
+  if (err == hipSuccess) {
+    g.wblocks = w2_blocks;
+    g.wscales = w2_scales;
+    g.bias = w2_bias;
+    g.act = act;
+    g.out = zw;
+    g.N = (int)H;
+    g.K = (int)I;
+    g.split_gate_up = 0;
+    g.scale2 = nv ? scale2_2 : nullptr;
+    err = launch_down(g, tt, tb, s);
+  }
+  if (err == hipSuccess) err = launch_combine(zw, y, (int)T, (int)H, (int)top_k, s);
+  return err == hipSuccess ? MXFP4MOE_OK : MXFP4MOE_ERR_HIP;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -198,83 +304,19 @@ int moe_mxfp4_forward_ex(const uint16_t* x, const float* router_logits, const ui
                          int64_t I, int64_t E, int64_t top_k, uint32_t flags, void* workspace,
                          size_t* workspace_bytes, void* stream) {
   if ((flags & ~(uint32_t)MXFP4MOE_GATE_UP_SPLIT) != 0) return MXFP4MOE_ERR_ARG;
-  if (workspace_bytes == nullptr) return MXFP4MOE_ERR_ARG;
-  int st = check_route_shape(T, E, top_k);
-  if (st != MXFP4MOE_OK) return st;
-  if (H <= 0 || I <= 0 || (H & 31) != 0 || (I & 31) != 0) return MXFP4MOE_ERR_SHAPE;
-  if (H > MXFP4MOE_MAX_HIDDEN || I > MXFP4MOE_MAX_HIDDEN) return MXFP4MOE_ERR_SHAPE;
-  static_assert(MXFP4MOE_MAX_HIDDEN == kMaxHidden, "one bound on H and I");
-  const Layout L = make_layout(T, H, I, E, top_k);
-  if (workspace == nullptr) {
-    *workspace_bytes = L.total;
-    return MXFP4MOE_OK;
-  }
-  if (w13_blocks == nullptr || w13_scales == nullptr || w13_bias == nullptr || w2_blocks == nullptr ||
-      w2_scales == nullptr || w2_bias == nullptr)
-    return MXFP4MOE_ERR_ARG;
-  if (T > 0 && (x == nullptr || router_logits == nullptr || y == nullptr)) return MXFP4MOE_ERR_ARG;
-  if (*workspace_bytes < L.total) return MXFP4MOE_ERR_WORKSPACE;
-  if (((uintptr_t)workspace & (kAlign - 1)) != 0) return MXFP4MOE_ERR_ALIGN;
-  if (!aligned16(w13_blocks) || !aligned16(w2_blocks)) return MXFP4MOE_ERR_ALIGN;
-  if (T > 0 && (!aligned16(x) || !aligned16(y))) return MXFP4MOE_ERR_ALIGN;
-  if (T == 0) return MXFP4MOE_OK;
+  return forward_impl(x, router_logits, w13_blocks, w13_scales, nullptr, w13_bias, w2_blocks, w2_scales, nullptr,
+                      w2_bias, y, T, H, I, E, top_k, flags, workspace, workspace_bytes, stream);
+}
 
-  char* ws = static_cast<char*>(workspace);
-  int32_t* ids = reinterpret_cast<int32_t*>(ws + L.ids);
-  float* weights = reinterpret_cast<float*>(ws + L.weights);
-  int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
-  int32_t* sorted = reinterpret_cast<int32_t*>(ws + L.sorted);
-  int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
-  uint16_t* act = reinterpret_cast<uint16_t*>(ws + L.act);
-  float* zw = reinterpret_cast<float*>(ws + L.zw);
-
-  const int64_t P = T * top_k;
-  TileTables tt;
-  tt.big = reinterpret_cast<int32_t*>(ws + L.big);
-  tt.num_big = counts;
-  tt.mid = reinterpret_cast<int32_t*>(ws + L.mid);
-  tt.num_mid = counts + 1;
-  tt.small = reinterpret_cast<int32_t*>(ws + L.small);
-  tt.num_small = counts + 2;
-  tt.big_tokens = big_tile_tokens();
-  const TileBounds tb = tile_bounds(T, P, E, tt.big_tokens > 0);
-  hipStream_t s = (hipStream_t)stream;
-
-  hipError_t err;
-  if (T <= kFusedRouteTokens) {
-    err = launch_route_group(router_logits, (int)T, (int)E, (int)top_k, ids, weights, offsets, sorted, tt, s);
-  } else {
-    err = launch_route(router_logits, (int)T, (int)E, (int)top_k, ids, weights, s);
-    if (err == hipSuccess) err = launch_group(ids, (int)P, (int)E, offsets, sorted, tt, s);
-  }
-  GemmArgs g{};
-  g.sorted_pairs = sorted;
-  g.topk_weights = weights;
-  g.top_k = (int)top_k;
-  if (err == hipSuccess) {
-    g.split_gate_up = (flags & MXFP4MOE_GATE_UP_SPLIT) ? 1 : 0;
-    g.wblocks = w13_blocks;
-    g.wscales = w13_scales;
-    g.bias = w13_bias;
-    g.act = x;
-    g.out = act;
-    g.N = (int)(2 * I);
-    g.K = (int)H;
-    err = launch_gate_up(g, tt, tb, s);
-  }
-  if (err == hipSuccess) {
-    g.wblocks = w2_blocks;
-    g.wscales = w2_scales;
-    g.bias = w2_bias;
-    g.act = act;
-    g.out = zw;
-    g.N = (int)H;
-    g.K = (int)I;
-    g.split_gate_up = 0;
-    err = launch_down(g, tt, tb, s);
-  }
-  if (err == hipSuccess) err = launch_combine(zw, y, (int)T, (int)H, (int)top_k, s);
-  return err == hipSuccess ? MXFP4MOE_OK : MXFP4MOE_ERR_HIP;
+int moe_nvfp4_forward(const uint16_t* x, const float* router_logits, const uint8_t* w13_blocks,
+                      const uint8_t* w13_scales, const float* w13_scale2, const uint16_t* w13_bias,
+                      const uint8_t* w2_blocks, const uint8_t* w2_scales, const float* w2_scale2,
+                      const uint16_t* w2_bias, uint16_t* y, int64_t T, int64_t H, int64_t I, int64_t E,
+                      int64_t top_k, void* workspace, size_t* workspace_bytes, void* stream) {
+  if (workspace != nullptr && (w13_scale2 == nullptr || w2_scale2 == nullptr)) return MXFP4MOE_ERR_ARG;
+  return forward_impl(x, router_logits, w13_blocks, w13_scales, w13_scale2 ? w13_scale2 : &kNvQuery, w13_bias,
+                      w2_blocks, w2_scales, w2_scale2 ? w2_scale2 : &kNvQuery, w2_bias, y, T, H, I, E, top_k, 0u,
+                      workspace, workspace_bytes, stream);
 }
 
 int mxfp4moe_profile_begin(int stage, int max_calls) {

@@ -84,6 +84,28 @@ __device__ __forceinline__ f32x4 load_bias4(const uint16_t* bias, int n, int N, 
                mx::bf16_to_f32(hi >> 16)};
 }
 
+// Scale operands of the 32 codes a lane converts at once (one 16-byte piece).
+// MXFP4: one E8M0 byte for all 32.  NVFP4: two E4M3 block scales, the first
+// for the codes of steps 0 and 1, the second for steps 2 and 3; the result is
+// exact in bf16 (a code has at most 2 significant bits, an E4M3 value 4).
+template <bool kNv>
+struct GroupScale {
+  float lo, hi;
+  __device__ __forceinline__ GroupScale(const uint8_t* srow, int g) {
+    if (kNv) {
+      lo = mx::e4m3_operand(srow[2 * g]);
+      hi = mx::e4m3_operand(srow[2 * g + 1]);
+    } else {
+      lo = hi = mx::e8m0_operand(srow[g]);
+    }
+  }
+  __device__ __forceinline__ float step(int s) const { return s < 2 ? lo : hi; }
+  // eight codes of step s as bf16
+  __device__ __forceinline__ u32x4 convert(uint32_t packed, int s) const {
+    return kNv ? mx::fp4x8_to_bf16x8_any_scale(packed, step(s)) : mx::fp4x8_to_bf16x8(packed, step(s));
+  }
+};
+
 // Block -> (tile, weight-row tile).  Blocks are dealt to the 8 XCDs round
 // robin (block b runs on XCD b % 8), so the id is first remapped so that each
 // XCD owns a contiguous range of the work, then walked in groups of kGroup
@@ -179,6 +201,7 @@ constexpr int kWideMaxGroups = 128;  // K <= 4096
 template <int BN, int kThreads>
 __device__ __forceinline__ void stage_scales(uint8_t* sst, const mxfp4moe::GemmArgs& args, int e, int ntile,
                                              int kgroups, int t, bool split = false) {
+  // kgroups: scale bytes per weight row (K/32 for MXFP4, K/16 for NVFP4)
   const int N = args.N;
   const int nv = min(BN, N - ntile * BN);
   u32x4* dst = reinterpret_cast<u32x4*>(sst);
@@ -451,12 +474,13 @@ hipError_t launch_cfg(const mxfp4moe::GemmArgs& a, hipStream_t stream) {
 // consecutive features (down), stored directly.
 //
 // Dynamic LDS: tokens [kStreamTokens][K] bf16 | scales [64*RN][K/32].
-template <int RN>
+template <int RN, bool kNv = false>
 __host__ __device__ constexpr size_t stream_lds_bytes(int K) {
+  if (kNv) return (size_t)mxfp4moe::kStreamTokens * K * 2 + (size_t)64 * RN * (K / 16);
   return (size_t)mxfp4moe::kStreamTokens * K * 2 + (size_t)64 * RN * (K / 32);
 }
 
-template <int RN, int kBatch, bool kGateUp>
+template <int RN, int kBatch, bool kGateUp, bool kNv>
 __global__ __launch_bounds__(256, 5) void expert_stream_kernel(mxfp4moe::GemmArgs args) {
   constexpr int kThreads = 256;
   constexpr int BN = 64 * RN;
@@ -525,7 +549,7 @@ __global__ __launch_bounds__(256, 5) void expert_stream_kernel(mxfp4moe::GemmArg
       const size_t base = r == 0 ? xsrc[0] : r == 1 ? xsrc[1] : r == 2 ? xsrc[2] : xsrc[3];
       if (j * kThreads < nx16) xv[j] = reinterpret_cast<const u32x4*>(args.act + base)[p];
     }
-    stage_scales<BN, kThreads>(sl, args, e, ntile, kgroups, t, split);
+    stage_scales<BN, kThreads>(sl, args, e, ntile, kNv ? 2 * kgroups : kgroups, t, split);
 #pragma unroll
     for (int j = 0; j < 8; ++j)
       if (t + j * kThreads < nx16) reinterpret_cast<u32x4*>(xl)[t + j * kThreads] = xv[j];
@@ -541,7 +565,8 @@ __global__ __launch_bounds__(256, 5) void expert_stream_kernel(mxfp4moe::GemmArg
   const uint8_t* srow[RN];
 #pragma unroll
   for (int rb = 0; rb < RN; ++rb)
-    srow[rb] = sl + staged_row(wave * 16 * RN + rb * 16 + lr, min(BN, N - ntile * BN), split) * kgroups;
+    srow[rb] = sl + staged_row(wave * 16 * RN + rb * 16 + lr, min(BN, N - ntile * BN), split) * (kNv ? 2 : 1) *
+                        kgroups;
   const uint16_t* xrow = xl + (lr < count ? lr : 0) * K;
   auto compute_batch = [&](int c0, const u32x4 (&w)[kBatch][RN]) {
 #pragma unroll
@@ -555,11 +580,11 @@ __global__ __launch_bounds__(256, 5) void expert_stream_kernel(mxfp4moe::GemmArg
         b[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xrow + g * 32 + 8 * s));
 #pragma unroll
       for (int rb = 0; rb < RN; ++rb) {
-        const float sc = mx::e8m0_operand(srow[rb][g]);
+        const GroupScale<kNv> sc(srow[rb], g);
         const u32x4 wj = glive ? w[j][rb] : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          const bf16x8 a = mx::as_bf16x8(mx::fp4x8_to_bf16x8(wj[s], sc));
+          const bf16x8 a = mx::as_bf16x8(sc.convert(wj[s], s));
           acc[rb][s & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[s], acc[rb][s & 1], 0, 0, 0);
         }
       }
@@ -579,11 +604,12 @@ __global__ __launch_bounds__(256, 5) void expert_stream_kernel(mxfp4moe::GemmArg
     const int n = n_wave + rb * 16 + 4 * q;  // first of this lane's four rows
     if (n >= N) continue;
     const f32x4 bv = load_bias4(bias, n, N, split);
+    const float s2 = kNv ? args.scale2[e] : 1.0f;  // second-level scale, before the bias
     f32x4 v;
-    v[0] = acc[rb][0][0] + acc[rb][1][0] + bv[0];
-    v[1] = acc[rb][0][1] + acc[rb][1][1] + bv[1];
-    v[2] = acc[rb][0][2] + acc[rb][1][2] + bv[2];
-    v[3] = acc[rb][0][3] + acc[rb][1][3] + bv[3];
+    v[0] = s2 * (acc[rb][0][0] + acc[rb][1][0]) + bv[0];
+    v[1] = s2 * (acc[rb][0][1] + acc[rb][1][1]) + bv[1];
+    v[2] = s2 * (acc[rb][0][2] + acc[rb][1][2]) + bv[2];
+    v[3] = s2 * (acc[rb][0][3] + acc[rb][1][3]) + bv[3];
     if (kGateUp) {
       const int I = N >> 1;
       const uint32_t packed = mx::pack_bf16x2_rne(swiglu_clamped(v[0], v[1]), swiglu_clamped(v[2], v[3]));
@@ -607,7 +633,7 @@ __global__ __launch_bounds__(256, 5) void expert_stream_kernel(mxfp4moe::GemmArg
 #define MX_STREAM_BATCH 6
 #endif
 
-template <bool kGateUp>
+template <bool kGateUp, bool kNv>
 hipError_t launch_stream(const mxfp4moe::GemmArgs& a, hipStream_t stream) {
   constexpr int RN = MX_STREAM_RN;
   constexpr int kBatch = MX_STREAM_BATCH;
@@ -616,12 +642,12 @@ hipError_t launch_stream(const mxfp4moe::GemmArgs& a, hipStream_t stream) {
   const long blocks = n_tiles * a.max_tiles;
   if (blocks == 0) return hipSuccess;
   const long grid = (blocks + kXcds - 1) / kXcds * kXcds;
-  const size_t lds = stream_lds_bytes<RN>(a.K);
+  const size_t lds = stream_lds_bytes<RN, kNv>(a.K);
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&expert_stream_kernel<RN, kBatch, kGateUp>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, (int)stream_lds_bytes<RN>(mxfp4moe::kMaxHidden));
+      reinterpret_cast<const void*>(&expert_stream_kernel<RN, kBatch, kGateUp, kNv>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, (int)stream_lds_bytes<RN, kNv>(mxfp4moe::kMaxHidden));
   if (attr != hipSuccess) return attr;
-  expert_stream_kernel<RN, kBatch, kGateUp><<<(unsigned)grid, 256, lds, stream>>>(a);
+  expert_stream_kernel<RN, kBatch, kGateUp, kNv><<<(unsigned)grid, 256, lds, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -642,12 +668,12 @@ hipError_t launch_stream(const mxfp4moe::GemmArgs& a, hipStream_t stream) {
 // Dynamic LDS: tokens [64][kP*256 + 16] | weights [128][kP*64 + 16] |
 // scales [128][K/32]  (the 16-byte row pads make the 16-lane column reads
 // conflict-free).
-template <int kP>
+template <int kP, bool kNv = false>
 __host__ __device__ constexpr size_t mid_lds_bytes(int K) {
-  return (size_t)64 * (kP * 256 + 16) + (size_t)128 * (kP * 64 + 16) + (size_t)128 * (K / 32);
+  return (size_t)64 * (kP * 256 + 16) + (size_t)128 * (kP * 64 + 16) + (size_t)128 * (K / (kNv ? 16 : 32));
 }
 
-template <int kP, bool kGateUp>
+template <int kP, bool kGateUp, bool kNv>
 __global__ __launch_bounds__(256, 2) void expert_mid_kernel(mxfp4moe::GemmArgs args) {
   constexpr int kThreads = 256;
   constexpr int BN = 128;
@@ -684,7 +710,7 @@ __global__ __launch_bounds__(256, 2) void expert_mid_kernel(mxfp4moe::GemmArgs a
   uint8_t* const ws = lds + 64 * kXRow;
   uint8_t* const sl = ws + BN * kWRow;
   const bool split = kGateUp && args.split_gate_up;  // uniform
-  stage_scales<BN, kThreads>(sl, args, e, ntile, kgroups, t, split);
+  stage_scales<BN, kThreads>(sl, args, e, ntile, kNv ? 2 * kgroups : kgroups, t, split);
 
   // load slots: token piece i = t + j*256 -> token i / kXPieces; weight piece
   // i = t + j*256 -> row i / kWPieces (rows past N re-read row N-1)
@@ -735,7 +761,7 @@ __global__ __launch_bounds__(256, 2) void expert_mid_kernel(mxfp4moe::GemmArgs a
   int wrd[2];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
-    srow[rb] = sl + staged_row(wave * 32 + rb * 16 + lr, min(BN, N - ntile * BN), split) * kgroups;
+    srow[rb] = sl + staged_row(wave * 32 + rb * 16 + lr, min(BN, N - ntile * BN), split) * (kNv ? 2 : 1) * kgroups;
     wrd[rb] = (wave * 32 + rb * 16 + lr) * kWRow + 16 * q;
   }
   const int ncb = (count + 15) >> 4;  // live 16-token column blocks
@@ -768,11 +794,11 @@ __global__ __launch_bounds__(256, 2) void expert_mid_kernel(mxfp4moe::GemmArgs a
       u32x4 a[2][4];  // [rb][step] converted A fragments
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
-        const float sc = mx::e8m0_operand(srow[rb][g]);
+        const GroupScale<kNv> sc(srow[rb], g);
         u32x4 wj = *reinterpret_cast<const u32x4*>(ws + wrd[rb] + jj * 64);
         wj = glive ? wj : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int st = 0; st < 4; ++st) a[rb][st] = mx::fp4x8_to_bf16x8(wj[st], sc);
+        for (int st = 0; st < 4; ++st) a[rb][st] = sc.convert(wj[st], st);
       }
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
@@ -816,7 +842,8 @@ __global__ __launch_bounds__(256, 2) void expert_mid_kernel(mxfp4moe::GemmArgs a
     for (int cb = 0; cb < 4; ++cb) {
       const int m = cb * 16 + lr;
       if (m >= count) continue;
-      const f32x4 v = acc[rb][cb];
+      const float s2 = kNv ? args.scale2[e] : 1.0f;  // second-level scale, before the bias
+      const f32x4 v = f32x4{s2 * acc[rb][cb][0], s2 * acc[rb][cb][1], s2 * acc[rb][cb][2], s2 * acc[rb][cb][3]};
       if (kGateUp) {
         const int I = N >> 1;
         const uint32_t packed = mx::pack_bf16x2_rne(swiglu_clamped(v[0] + b0, v[1] + b1), swiglu_clamped(v[2] + b2, v[3] + b3));
@@ -839,7 +866,7 @@ __global__ __launch_bounds__(256, 2) void expert_mid_kernel(mxfp4moe::GemmArgs a
 #define MX_MID_PANEL 2
 #endif
 
-template <bool kGateUp>
+template <bool kGateUp, bool kNv>
 hipError_t launch_mid(const mxfp4moe::GemmArgs& a, hipStream_t stream) {
   constexpr int kP = MX_MID_PANEL;
   const long n_tiles = (a.N + 127) / 128;
@@ -847,10 +874,10 @@ hipError_t launch_mid(const mxfp4moe::GemmArgs& a, hipStream_t stream) {
   if (blocks == 0) return hipSuccess;
   const long grid = (blocks + kXcds - 1) / kXcds * kXcds;
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&expert_mid_kernel<kP, kGateUp>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, (int)mid_lds_bytes<kP>(mxfp4moe::kMaxHidden));
+      reinterpret_cast<const void*>(&expert_mid_kernel<kP, kGateUp, kNv>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, (int)mid_lds_bytes<kP, kNv>(mxfp4moe::kMaxHidden));
   if (attr != hipSuccess) return attr;
-  expert_mid_kernel<kP, kGateUp><<<(unsigned)grid, 256, mid_lds_bytes<kP>(a.K), stream>>>(a);
+  expert_mid_kernel<kP, kGateUp, kNv><<<(unsigned)grid, 256, mid_lds_bytes<kP, kNv>(a.K), stream>>>(a);
   return hipGetLastError();
 }
 
@@ -892,6 +919,7 @@ static_assert(kWideTokens == 128 && kStreamTokens == 4, "tile sizes");
 template <bool kGateUp>
 static hipError_t launch_all(GemmArgs a, const TileTables& tt, const TileBounds& tb, hipStream_t stream) {
   hipError_t err = hipSuccess;
+  if (tb.max_big > 0 && a.scale2 != nullptr) return hipErrorInvalidValue;  // NVFP4 runs mid / streaming tiles only
   if (tb.max_big > 0) {
     ProfileScope prof(kGateUp ? kStageGateUpWide : kStageDownWide, stream);
     a.tiles = tt.big;
@@ -904,14 +932,14 @@ static hipError_t launch_all(GemmArgs a, const TileTables& tt, const TileBounds&
     a.tiles = tt.mid;
     a.num_tiles = tt.num_mid;
     a.max_tiles = tb.max_mid;
-    err = launch_mid<kGateUp>(a, stream);
+    err = a.scale2 != nullptr ? launch_mid<kGateUp, true>(a, stream) : launch_mid<kGateUp, false>(a, stream);
   }
   if (err == hipSuccess && tb.max_small > 0) {
     ProfileScope prof(kGateUp ? kStageGateUpStream : kStageDownStream, stream);
     a.tiles = tt.small;
     a.num_tiles = tt.num_small;
     a.max_tiles = tb.max_small;
-    err = launch_stream<kGateUp>(a, stream);
+    err = a.scale2 != nullptr ? launch_stream<kGateUp, true>(a, stream) : launch_stream<kGateUp, false>(a, stream);
   }
   return err;
 }

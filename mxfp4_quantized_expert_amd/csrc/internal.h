@@ -60,7 +60,8 @@ struct TileTables {
   int32_t* num_mid;
   int32_t* small;      // [max_small][4]
   int32_t* num_small;
-  int big_tokens;      // kWideTokens, or 0
+  int big_tokens;      // kWideTokens, or 0 (then: every pair in streaming tiles unless no_wide)
+  int no_wide;         // no wide tiles: more than kStreamTokens pairs -> mid tiles, whatever the count
 };
 
 // Capacities of the tile tables (bounds the GEMM grids).
@@ -95,6 +96,7 @@ struct GemmArgs {
   void* out;                // gate_up: a [P, N/2] bf16 in expert order; down: zw [P, N] f32 by pair id
   int N, K, top_k, max_tiles;
   int split_gate_up;        // gate_up only: w13 rows stored [I gate rows; I up rows] instead of interleaved
+  const float* scale2;      // NVFP4: [E] second-level scale per expert (scales are E4M3 per 16), else nullptr
 };
 
 // Both GEMM stages launch the wide, mid and streaming kernels over their

@@ -155,7 +155,7 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(const float* __res
     // an expert with at least bt pairs: all its pairs in tiles of bt (the
     // last one partial), so its weights are streamed by one kernel only
     for (int e = threadIdx.x; e < E; e += kGroupThreads)
-      ntile[e] = (bt > 0 && cnt[e] >= bt) ? (cnt[e] + bt - 1) / bt : 0;
+      ntile[e] = (bt > 0 && !tt.no_wide && cnt[e] >= bt) ? (cnt[e] + bt - 1) / bt : 0;
     __syncthreads();
     const int n_big = block_exclusive_scan_wave0(ntile, tile_base, E, &total_slot);
     if (threadIdx.x == 0) *tt.num_big = n_big;
@@ -166,9 +166,10 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(const float* __res
     __syncthreads();
     // fewer than bt pairs, more than st: mid tiles of at most mt pairs
     constexpr int mt = mxfp4moe::kMidTokens;
+    const bool mid_on = bt > 0 || tt.no_wide;  // else everything in streaming tiles
     for (int e = threadIdx.x; e < E; e += kGroupThreads) {
       const int c = cnt[e];
-      ntile[e] = (bt > 0 && c > st && c < bt) ? (c + mt - 1) / mt : 0;
+      ntile[e] = (mid_on && c > st && (tt.no_wide || c < bt)) ? (c + mt - 1) / mt : 0;
     }
     __syncthreads();
     const int n_mid = block_exclusive_scan_wave0(ntile, tile_base, E, &total_slot);
@@ -182,7 +183,7 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(const float* __res
     // every pair in streaming tiles of st
     for (int e = threadIdx.x; e < E; e += kGroupThreads) {
       const int c = cnt[e];
-      ntile[e] = bt > 0 ? (c > 0 && c <= st ? 1 : 0) : (c + st - 1) / st;
+      ntile[e] = mid_on ? (c > 0 && c <= st ? 1 : 0) : (c + st - 1) / st;
     }
     __syncthreads();
     const int n_small = block_exclusive_scan_wave0(ntile, tile_base, E, &total_slot);

@@ -122,6 +122,17 @@ def test_forward_ex_rejects_unknown_flags(lib):
     assert f(A, A, A, A, A, A, A, A, A, 4, 64, 64, 4, 2, 1, None, ctypes.byref(n), None) == 0 and n.value > 0
 
 
+def test_nvfp4_forward_argument_checks(lib):
+    f = lib.moe_nvfp4_forward
+    n = ctypes.c_size_t(0)
+    assert f(None, None, None, None, None, None, None, None, None, None, None, 4, 64, 64, 4, 2, None,
+             ctypes.byref(n), None) == 0 and n.value > 0  # size query
+    big = ctypes.c_size_t(1 << 30)
+    assert f(A, A, A, A, None, A, A, A, A, A, A, 4, 64, 64, 4, 2, A, ctypes.byref(big), None) == -1  # no scale2
+    assert f(A, A, A, A, A, A, A, A, None, A, A, 4, 64, 64, 4, 2, A, ctypes.byref(big), None) == -1
+    assert f(A, A, A, A, A, A, A, A, A, A, A, 4, 48, 64, 4, 2, A, ctypes.byref(big), None) == -2
+
+
 def test_route_argument_checks(lib):
     f = lib.moe_mxfp4_route
     assert f(A, 4, 0, 1, A, A, A, A, None) == -2
