@@ -38,10 +38,13 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def layer_bytes(H, I):
-    """Packed bytes of one expert: (gate_up blocks+scales+bias, down blocks+scales+bias)."""
-    w13 = 2 * I * (H // 2) + 2 * I * (H // 32) + 2 * I * 2
-    w2 = H * (I // 2) + H * (I // 32) + H * 2
+def layer_bytes(H, I, nvfp4=False):
+    """Packed bytes of one expert: (gate_up blocks+scales+bias, down blocks+scales+bias).
+    MXFP4: one scale byte per 32 elements; NVFP4: one per 16 plus a float32 second-level scale."""
+    g = 16 if nvfp4 else 32
+    extra = 4 if nvfp4 else 0
+    w13 = 2 * I * (H // 2) + 2 * I * (H // g) + 2 * I * 2 + extra
+    w2 = H * (I // 2) + H * (I // g) + H * 2 + extra
     return w13, w2
 
 
@@ -63,7 +66,7 @@ def measured_traffic(workload, kernel_tag):
     return None if ent is None else float(ent["bytes"])
 
 
-def cpu_baseline_moe(layer, spec, budget_s=15.0):
+def cpu_baseline_moe(layer, spec, nvfp4=False, budget_s=15.0):
     """Time the float64 CPU oracle, single-threaded, on the first tokens of the same layer."""
     import numpy as np
     from threadpoolctl import threadpool_limits
@@ -76,7 +79,7 @@ def cpu_baseline_moe(layer, spec, budget_s=15.0):
         while True:
             tokens = np.arange(min(n, spec.T))
             t0 = time.perf_counter()
-            O.moe_forward(layer, spec.top_k, tokens=tokens)
+            (O.moe_forward_nvfp4 if nvfp4 else O.moe_forward)(layer, spec.top_k, tokens=tokens)
             elapsed = time.perf_counter() - t0
             if elapsed >= budget_s / 3 or n >= spec.T:
                 break
@@ -116,18 +119,19 @@ def run_moe(args):
 
     from mxfp4_quantized_expert_amd import binding, workloads
 
-    spec = workloads.LAYERS[args.workload]
+    nvfp4 = args.workload.startswith("nvfp4_")
+    spec = workloads.LAYERS[args.workload[len("nvfp4_"):] if nvfp4 else args.workload]
     T, H, I, E, k = spec.T, spec.H, spec.I, spec.E, spec.top_k
     P = T * k
     log(f"[bench] generating {args.workload}: T={T} H={H} I={I} E={E} k={k}")
-    layer = workloads.make_layer(spec)
+    layer = workloads.make_nvfp4_layer(spec) if nvfp4 else workloads.make_layer(spec)
     dev = binding.layer_to_device(layer, "cuda")
     # Expert loads from the library's own routing (used for the roofline accounting).
     _, _, offsets, _ = binding.moe_mxfp4_route(dev["router_logits"], k)
     counts = np.diff(offsets.cpu().numpy().astype(np.int64))
     n_active = int((counts > 0).sum())
-    full_pairs = int(counts[counts >= 128].sum())  # pairs of the experts computed in 128-pair tiles
-    w13_b, w2_b = layer_bytes(H, I)
+    full_pairs = 0 if nvfp4 else int(counts[counts >= 128].sum())  # pairs of the experts in 128-pair tiles
+    w13_b, w2_b = layer_bytes(H, I, nvfp4)
     # Weight copies rotate so that repeated steps cannot be served from the
     # 256 MB Infinity Cache when the active weights would fit in it.
     active_bytes = n_active * (w13_b + w2_b)
@@ -141,9 +145,14 @@ def run_moe(args):
 
     def step(i):
         d = weight_sets[i % copies]
-        binding.moe_mxfp4_forward(dev["x"], dev["router_logits"], d["w13_blocks"], d["w13_scales"],
-                                  d["w13_bias"], d["w2_blocks"], d["w2_scales"], d["w2_bias"], k,
-                                  out=y, workspace=ws)
+        if nvfp4:
+            binding.moe_nvfp4_forward(dev["x"], dev["router_logits"], d["w13_blocks"], d["w13_scales"],
+                                      d["w13_scale2"], d["w13_bias"], d["w2_blocks"], d["w2_scales"],
+                                      d["w2_scale2"], d["w2_bias"], k, out=y, workspace=ws)
+        else:
+            binding.moe_mxfp4_forward(dev["x"], dev["router_logits"], d["w13_blocks"], d["w13_scales"],
+                                      d["w13_bias"], d["w2_blocks"], d["w2_scales"], d["w2_bias"], k,
+                                      out=y, workspace=ws)
 
     for i in range(args.warmup):
         step(i)
@@ -165,7 +174,7 @@ def run_moe(args):
     # The dominant kernel: gate_up over full 128-pair tiles when there are any,
     # else gate_up over the streamed tiles.  Its launches inside the timed
     # region are bracketed with HIP events on the stream they run on.
-    dominant = "gate_up_wide" if full_pairs > 0 else "gate_up_stream"
+    dominant = "gate_up_wide" if full_pairs > 0 else "gate_up_stream" if T <= 4 else "gate_up_mid"
     binding.profile_begin(dominant, args.steps)
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -180,17 +189,32 @@ def run_moe(args):
     copy_gbs, _ = copy_bandwidth()
 
     flops_total = 6.0 * H * I * P
-    if dominant == "gate_up_wide":
-        # 2*H*2I FLOPs per pair, over the pairs of the full tiles
-        work = 4.0 * H * I * full_pairs
+    # Pairs of the experts that go to mid tiles (more than 4 pairs, below the
+    # wide threshold; NVFP4 layers use mid tiles for every such expert).
+    mid_pairs = int(counts[(counts > 4) & ((counts < 128) | nvfp4)].sum())
+    mid_experts = int(((counts > 4) & ((counts < 128) | nvfp4)).sum())
+    # The mid launch is priced against whichever roof is lower for its work:
+    # its experts' packed w13 once from HBM, or 2*H*2I MFMA FLOPs per pair.
+    mid_mfma = (dominant == "gate_up_mid" and
+                4.0 * H * I * mid_pairs / (PEAK_BF16_TFLOPS * 1e12) > mid_experts * w13_b / (PEAK_HBM_GBS * 1e9))
+    if dominant == "gate_up_wide" or mid_mfma:
+        # 2*H*2I FLOPs per pair, over the pairs of the tiles of that launch
+        tile_pairs = full_pairs if dominant == "gate_up_wide" else mid_pairs
+        work = 4.0 * H * I * tile_pairs
         roof = {"bound": "mfma", "achieved": work / (kms / 1e3) / 1e12, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s"}
-        per_unit = f"33,177,600 FLOPs per pair at H=I=2880 (2*H*2I) x {full_pairs} pairs in 128-pair tiles"
+        per_unit = (f"{4 * H * I:,} FLOPs per pair (2*H*2I) x {tile_pairs} pairs in "
+                    + ("128-pair tiles" if dominant == "gate_up_wide" else "mid tiles of at most 64 pairs"))
     else:
         # packed w13 (blocks, scales, bias) of every active expert + x rows + a rows out
-        work = n_active * w13_b + T * H * 2 + P * I * 2
+        # (the streaming or the mid launch carries every expert of a small batch)
+        if dominant == "gate_up_mid":
+            n_exp, rows_in, rows_out = mid_experts, mid_pairs * H * 2, mid_pairs * I * 2
+        else:
+            n_exp, rows_in, rows_out = n_active, T * H * 2, P * I * 2
+        work = n_exp * w13_b + rows_in + rows_out
         roof = {"bound": "hbm", "achieved": work / (kms / 1e3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
-        per_unit = (f"{w13_b} B of packed w13 per active expert x {n_active} + x {T * H * 2} B + a {P * I * 2} B")
+        per_unit = (f"{w13_b} B of packed w13 per expert x {n_exp} + x {rows_in} B + a {rows_out} B")
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = measured_traffic(args.workload, dominant)
     roof["kernel"] = f"expert_gemm_kernel, {dominant.replace('_', ' ')} launch"
@@ -219,7 +243,8 @@ def run_moe(args):
             "workload": f"{args.workload}: MXFP4 MoE expert layer T={T} H={H} I={I} E={E} top_k={k}"
                         + (f", Zipf({spec.zipf_s}) routing skew" if spec.zipf_s else ""),
             "T": T, "H": H, "I": I, "E": E, "top_k": k,
-            "weights": "mxfp4 (e2m1 codes, e8m0 scale per 32), bf16 MFMA, fp32 accumulate",
+            "weights": ("nvfp4 (e2m1 codes, e4m3 scale per 16, fp32 second-level scale)" if nvfp4 else
+                        "mxfp4 (e2m1 codes, e8m0 scale per 32)") + ", bf16 MFMA, fp32 accumulate",
             "active_experts": n_active,
             "pairs_in_full_tiles": full_pairs,
             "weight_copies_rotated": copies,
@@ -234,7 +259,7 @@ def run_moe(args):
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline_moe(layer, spec)
+        out["cpu_baseline"] = cpu_baseline_moe(layer, spec, nvfp4)
     return out
 
 
@@ -347,8 +372,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="120b_prefill",
-                    choices=["120b_prefill", "20b_prefill", "20b_decode", "tiny", "dequant_120b",
-                             "dequant_host_120b", "copy"])
+                    choices=["120b_prefill", "20b_prefill", "20b_decode", "tiny", "nvfp4_20b_decode",
+                             "nvfp4_20b_prefill", "nvfp4_120b_prefill", "dequant_120b", "dequant_host_120b", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:

@@ -160,11 +160,12 @@ int moe_mxfp4_route(const float* router_logits, int64_t T, int64_t E, int64_t to
  * Biases are required (a NULL bias is MXFP4MOE_ERR_ARG); there is no mode that
  * applies the routing weight to the input.  Accumulation is fp32; the SwiGLU
  * output is rounded to bf16 before the down GEMM.  T == 0 is a no-op.
- * Each expert's pairs are cut into full tiles of 128 pairs and one remainder
- * tile, each kind with a GEMM kernel of its own (the streaming kernel for
- * remainders of at most 32 pairs is the whole decode path);
+ * An expert with at least 128 pairs is cut into tiles of 128 (the last one
+ * partial), one with 5..127 pairs into tiles of at most 64, one with at most
+ * 4 pairs makes one streaming tile; each kind has a GEMM kernel of its own
+ * (with T <= 4 every expert has one streaming tile: the decode path).
  * MXFP4MOE_PATH=stream in the environment sends every pair through the
- * streaming kernel, in tiles of 32.
+ * streaming kernels, in tiles of 4.
  */
 int moe_mxfp4_forward(const uint16_t* x, const float* router_logits,
                       const uint8_t* w13_blocks, const uint8_t* w13_scales, const uint16_t* w13_bias,
