@@ -35,6 +35,7 @@ __all__ = [
     "make_layer",
     "make_nvfp4_layer",
     "make_routing_inputs",
+    "make_router",
     "make_bank",
     "to_bf16_bits",
 ]
@@ -145,6 +146,25 @@ def make_layer(spec: LayerSpec, seed: Optional[int] = None) -> Dict[str, np.ndar
     out["w2_scales"] = _scale_bytes(rng, (E, H, I // 32), spec.scale_lo, spec.scale_hi)
     out["w2_bias"] = to_bf16_bits(rng.standard_normal((E, H), dtype=np.float32) * np.float32(spec.bias_std))
     return out
+
+
+def make_router(spec: LayerSpec, seed: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """Router weights for the layer of ``spec``: router_w [E, H] and router_b [E]
+    as bf16 bits, from a stream of their own (seed sequence [seed, 1]), so that
+    adding a router leaves every other tensor of the layer unchanged.
+
+    W_r is N(0, logit_std^2 / H), which gives logits of about logit_std on
+    x ~ N(0, x_std^2) rows of std 1; the bias is the Zipf(s) log-offset
+    -s*ln(rank) over a seeded rank permutation for skewed layers, else
+    N(0, (logit_std / 4)^2)."""
+    rng = np.random.default_rng([spec.seed if seed is None else seed, 1])
+    w = rng.standard_normal((spec.E, spec.H), dtype=np.float32) * np.float32(spec.logit_std / np.sqrt(spec.H))
+    if spec.zipf_s is not None:
+        rank = rng.permutation(spec.E).astype(np.float64) + 1.0
+        b = (-spec.zipf_s * np.log(rank)).astype(np.float32)
+    else:
+        b = rng.standard_normal(spec.E, dtype=np.float32) * np.float32(spec.logit_std / 4)
+    return {"router_w": to_bf16_bits(w), "router_b": to_bf16_bits(b)}
 
 
 def make_nvfp4_layer(spec: LayerSpec, seed: Optional[int] = None, scale_lo: int = 0x30,

@@ -22,6 +22,9 @@ passage of the pages it cites (page title, then section):
   weights) and group their tokens themselves.
 * FreeToken PR #838, review item 3, for the NVFP4 variant: the second-level
   weight_scale_2 multiplies the expert output before its bias.
+* FreeToken PR #838, the cleanups (the router is mlp.router) and "What it
+  does" (the router bias is loaded, the router input's bias is required), for
+  the router projection: logits = x W_r^T + b_r ahead of the top-k.
 * "Add native GPT-OSS MXFP4 QMoE export" (mobius PR #719): Summary (blocks
   [E, N, K/32, 16], one E8M0 scale byte per 16-byte block) and Validation
   (scale bytes 0x00..0xfe are valid, 0xff is not).
@@ -292,6 +295,34 @@ def group_by_expert(ids: np.ndarray, E: int):
 
 
 # --------------------------------------------------------------------------
+# Router projection ("feat(gguf): serve gpt-oss gguf checkpoints on gpt_oss",
+# FreeToken PR #838: the cleanups name the router mlp.router, and "What it
+# does" loads the router bias with the dense weights and lists the router
+# input's bias among the tensors a file must carry).  The router is a linear
+# layer with a bias over the hidden state; its output is the logits that
+# route() consumes.
+# --------------------------------------------------------------------------
+
+def router_logits(x_bits: np.ndarray, w_bits: np.ndarray, b_bits: np.ndarray) -> np.ndarray:
+    """logits[t, e] = sum_h x[t, h] * W_r[e, h] + b_r[e], in float64.
+
+    x [T, H], W_r [E, H] and b_r [E] are bf16 bit patterns.
+    """
+    x = bf16_decode(x_bits)
+    w = bf16_decode(w_bits)
+    b = bf16_decode(b_bits)
+    return x @ w.T + b[None, :]
+
+
+def moe_forward_router(layer: Dict[str, np.ndarray], top_k: int,
+                       tokens: Optional[Sequence[int]] = None) -> np.ndarray:
+    """moe_forward with the logits produced by the router projection of the
+    layer's own x (layer["router_w"], layer["router_b"])."""
+    logits = router_logits(layer["x"], layer["router_w"], layer["router_b"])
+    return moe_forward(dict(layer, router_logits=logits), top_k, tokens=tokens)
+
+
+# --------------------------------------------------------------------------
 # Clamped SwiGLU (gpt-oss), FreeToken PR #838 "What it does"
 # --------------------------------------------------------------------------
 
@@ -404,5 +435,6 @@ __all__ = [
     "swiglu_clamped", "expert_ffn", "moe_forward", "moe_forward_dense",
     "parity_errors", "flops_per_pair",
     "NV_GROUP", "e4m3_value", "nvfp4_dequantize_f64", "expert_ffn_nvfp4", "moe_forward_nvfp4",
+    "router_logits", "moe_forward_router",
 ]
 

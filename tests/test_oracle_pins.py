@@ -450,3 +450,54 @@ def test_nvfp4_bias_after_second_level_scale():
     assert np.allclose(ident, ref, rtol=1e-13, atol=1e-13)
     folded = c * (y1 + sum(w[:, j:j + 1] * b2[ids[:, j]] for j in range(k)))  # sum w*s*(y + b)
     assert O.parity_errors(folded, ref)[0] > 10 * 1e-2
+
+
+# ---------------------------------------------------------------- router projection
+
+def _router_case(T, H, E, seed):
+    rng = np.random.default_rng(seed)
+    x = W.to_bf16_bits(rng.standard_normal((T, H), dtype=np.float32))
+    w = W.to_bf16_bits(rng.standard_normal((E, H), dtype=np.float32) / np.float32(np.sqrt(H)))
+    b = W.to_bf16_bits(rng.standard_normal(E, dtype=np.float32))
+    return x, w, b
+
+
+def test_router_logits_against_torch_linear():
+    # A linear layer with a bias: torch.nn.functional.linear in float64.
+    x, w, b = _router_case(37, 96, 12, 1)
+    ref = torch.nn.functional.linear(torch.from_numpy(O.bf16_decode(x)), torch.from_numpy(O.bf16_decode(w)),
+                                     torch.from_numpy(O.bf16_decode(b))).numpy()
+    np.testing.assert_allclose(O.router_logits(x, w, b), ref, rtol=1e-12, atol=1e-12)
+
+
+def test_router_logits_one_hot_rows_pick_weight_columns():
+    # Square case (E == H) so that a transposed W_r would pass a shape check:
+    # x = e_h gives logits = W_r[:, h] + b_r.
+    H = E = 16
+    _, w, b = _router_case(1, H, E, 2)
+    one = W.to_bf16_bits(np.eye(H, dtype=np.float32))
+    got = O.router_logits(one, w, b)
+    wd, bd = O.bf16_decode(w), O.bf16_decode(b)
+    for h in range(H):
+        assert np.array_equal(got[h], wd[:, h] + bd)
+
+
+def test_router_logits_zero_weights_give_bias_on_every_token():
+    x, w, b = _router_case(5, 64, 7, 3)
+    w0 = np.zeros_like(w)
+    got = O.router_logits(x, w0, b)
+    assert np.array_equal(got, np.broadcast_to(O.bf16_decode(b), (5, 7)))
+
+
+def test_moe_forward_router_dominant_bias_is_one_expert():
+    # A router bias of +64 on expert 2 sends every token there first; with
+    # top_k = 1 the layer is that expert's FFN with weight 1 (closed form).
+    spec = W.LAYERS["tiny"].with_(T=8, E=4, top_k=1)
+    L = dict(W.make_layer(spec), **W.make_router(spec))
+    bias = O.bf16_decode(L["router_b"]).astype(np.float32)
+    bias[2] = 64.0
+    L["router_b"] = W.to_bf16_bits(bias)
+    y = O.moe_forward_router(L, 1)
+    z = O.expert_ffn(O.bf16_decode(L["x"]), L["w13_blocks"][2], L["w13_scales"][2], L["w13_bias"][2],
+                     L["w2_blocks"][2], L["w2_scales"][2], L["w2_bias"][2])
+    np.testing.assert_allclose(y, z, rtol=0, atol=1e-12)
