@@ -66,7 +66,7 @@ def measured_traffic(workload, kernel_tag):
     return None if ent is None else float(ent["bytes"])
 
 
-def cpu_baseline_moe(layer, spec, nvfp4=False, budget_s=15.0):
+def cpu_baseline_moe(layer, spec, nvfp4=False, router=False, budget_s=15.0):
     """Time the float64 CPU oracle, single-threaded, on the first tokens of the same layer."""
     import numpy as np
     from threadpoolctl import threadpool_limits
@@ -79,7 +79,8 @@ def cpu_baseline_moe(layer, spec, nvfp4=False, budget_s=15.0):
         while True:
             tokens = np.arange(min(n, spec.T))
             t0 = time.perf_counter()
-            (O.moe_forward_nvfp4 if nvfp4 else O.moe_forward)(layer, spec.top_k, tokens=tokens)
+            fwd = O.moe_forward_nvfp4 if nvfp4 else O.moe_forward_router if router else O.moe_forward
+            fwd(layer, spec.top_k, tokens=tokens)
             elapsed = time.perf_counter() - t0
             if elapsed >= budget_s / 3 or n >= spec.T:
                 break
@@ -120,13 +121,19 @@ def run_moe(args):
     from mxfp4_quantized_expert_amd import binding, workloads
 
     nvfp4 = args.workload.startswith("nvfp4_")
-    spec = workloads.LAYERS[args.workload[len("nvfp4_"):] if nvfp4 else args.workload]
+    router = args.workload.startswith("router_")
+    base = args.workload[len("nvfp4_"):] if nvfp4 else args.workload[len("router_"):] if router else args.workload
+    spec = workloads.LAYERS[base]
     T, H, I, E, k = spec.T, spec.H, spec.I, spec.E, spec.top_k
     P = T * k
     log(f"[bench] generating {args.workload}: T={T} H={H} I={I} E={E} k={k}")
     layer = workloads.make_nvfp4_layer(spec) if nvfp4 else workloads.make_layer(spec)
+    if router:  # logits from the router projection of x (the skew rides the router bias)
+        layer.update(workloads.make_router(spec))
     dev = binding.layer_to_device(layer, "cuda")
     # Expert loads from the library's own routing (used for the roofline accounting).
+    if router:
+        dev["router_logits"] = binding.moe_mxfp4_router(dev["x"], dev["router_w"], dev["router_b"], k)[0]
     _, _, offsets, _ = binding.moe_mxfp4_route(dev["router_logits"], k)
     counts = np.diff(offsets.cpu().numpy().astype(np.int64))
     n_active = int((counts > 0).sum())
@@ -145,7 +152,11 @@ def run_moe(args):
 
     def step(i):
         d = weight_sets[i % copies]
-        if nvfp4:
+        if router:
+            binding.moe_mxfp4_forward_router(dev["x"], dev["router_w"], dev["router_b"], d["w13_blocks"],
+                                             d["w13_scales"], d["w13_bias"], d["w2_blocks"], d["w2_scales"],
+                                             d["w2_bias"], k, out=y, workspace=ws)
+        elif nvfp4:
             binding.moe_nvfp4_forward(dev["x"], dev["router_logits"], d["w13_blocks"], d["w13_scales"],
                                       d["w13_scale2"], d["w13_bias"], d["w2_blocks"], d["w2_scales"],
                                       d["w2_scale2"], d["w2_bias"], k, out=y, workspace=ws)
@@ -240,7 +251,8 @@ def run_moe(args):
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": f"{args.workload}: MXFP4 MoE expert layer T={T} H={H} I={I} E={E} top_k={k}"
+            "workload": f"{args.workload}: {'NVFP4' if nvfp4 else 'MXFP4'} MoE expert layer T={T} H={H} I={I} E={E} "
+                        f"top_k={k}" + (", router projection fused ahead of the top-k" if router else "")
                         + (f", Zipf({spec.zipf_s}) routing skew" if spec.zipf_s else ""),
             "T": T, "H": H, "I": I, "E": E, "top_k": k,
             "weights": ("nvfp4 (e2m1 codes, e4m3 scale per 16, fp32 second-level scale)" if nvfp4 else
@@ -259,7 +271,7 @@ def run_moe(args):
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline_moe(layer, spec, nvfp4)
+        out["cpu_baseline"] = cpu_baseline_moe(layer, spec, nvfp4, router)
     return out
 
 
@@ -373,7 +385,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="120b_prefill",
                     choices=["120b_prefill", "20b_prefill", "20b_decode", "tiny", "nvfp4_20b_decode",
-                             "nvfp4_20b_prefill", "nvfp4_120b_prefill", "dequant_120b", "dequant_host_120b", "copy"])
+                             "nvfp4_20b_prefill", "nvfp4_120b_prefill", "router_20b_decode", "router_120b_prefill",
+                             "dequant_120b", "dequant_host_120b", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:

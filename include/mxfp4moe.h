@@ -194,6 +194,43 @@ int moe_mxfp4_forward_ex(const uint16_t* x, const float* router_logits,
                          uint32_t flags, void* workspace, size_t* workspace_bytes, void* stream);
 
 /*
+ * moe_mxfp4_router - the router projection fused ahead of the top-k:
+ *
+ *   logits[t, e] = sum_h x[t, h] * router_w[e, h] + router_b[e]   (fp32 accumulation)
+ *   (topk_ids, topk_weights) = top-k of logits[t], softmax over the k selected
+ *
+ * "feat(gguf): serve gpt-oss gguf checkpoints on gpt_oss" (FreeToken PR
+ * #838): the cleanups name the router mlp.router (a linear layer), and
+ * "What it does" loads the router bias and requires the router input's bias.
+ * One launch: each 16-token tile computes its logits on the MFMA into LDS,
+ * writes them out, and routes from LDS (same order and ties as
+ * moe_mxfp4_route).
+ *
+ *   x            [T, H] bf16, 16-byte aligned
+ *   router_w     [E, H] bf16, 16-byte aligned
+ *   router_b     [E] bf16 (required)
+ *   logits       [T, E] float32 out
+ *   topk_ids     [T, top_k] int32 out;  topk_weights [T, top_k] float32 out
+ *   H a multiple of 32; E, top_k as moe_mxfp4_route.  T == 0 is a no-op.
+ */
+int moe_mxfp4_router(const uint16_t* x, const uint16_t* router_w, const uint16_t* router_b, int64_t T,
+                     int64_t H, int64_t E, int64_t top_k, float* logits, int32_t* topk_ids,
+                     float* topk_weights, void* stream);
+
+/*
+ * moe_mxfp4_forward_router - moe_mxfp4_forward_ex with the logits computed
+ * by the router projection of x (as moe_mxfp4_router) instead of passed in.
+ * router_w [E, H] bf16 (16-byte aligned) and router_b [E] bf16 are required
+ * when T > 0 and a workspace is given; flags as moe_mxfp4_forward_ex; the
+ * workspace query and every other argument as moe_mxfp4_forward.
+ */
+int moe_mxfp4_forward_router(const uint16_t* x, const uint16_t* router_w, const uint16_t* router_b,
+                             const uint8_t* w13_blocks, const uint8_t* w13_scales, const uint16_t* w13_bias,
+                             const uint8_t* w2_blocks, const uint8_t* w2_scales, const uint16_t* w2_bias,
+                             uint16_t* y, int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k,
+                             uint32_t flags, void* workspace, size_t* workspace_bytes, void* stream);
+
+/*
  * moe_nvfp4_forward - the same expert layer over NVFP4 experts.
  *
  * "feat(gguf): serve gpt-oss gguf checkpoints on gpt_oss" (FreeToken PR #838),

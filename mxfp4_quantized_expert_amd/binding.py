@@ -67,6 +67,12 @@ def load() -> ctypes.CDLL:
     lib.moe_nvfp4_forward.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                       _i64, _i64, _i64, _i64, _i64, _vp, ctypes.POINTER(ctypes.c_size_t), _vp]
     lib.moe_nvfp4_forward.restype = ctypes.c_int
+    lib.moe_mxfp4_router.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp]
+    lib.moe_mxfp4_router.restype = ctypes.c_int
+    lib.moe_mxfp4_forward_router.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                             _i64, _i64, _i64, _i64, _i64, ctypes.c_uint32, _vp,
+                                             ctypes.POINTER(ctypes.c_size_t), _vp]
+    lib.moe_mxfp4_forward_router.restype = ctypes.c_int
     lib.mxfp4moe_status_string.argtypes = [ctypes.c_int]
     lib.mxfp4moe_status_string.restype = ctypes.c_char_p
     lib.mxfp4moe_profile_begin.argtypes = [ctypes.c_int, ctypes.c_int]
@@ -179,6 +185,25 @@ def moe_mxfp4_route(router_logits: torch.Tensor, top_k: int, stream=None):
     return ids, w, offsets, pairs
 
 
+def moe_mxfp4_router(x: torch.Tensor, router_w: torch.Tensor, router_b: torch.Tensor, top_k: int, stream=None):
+    """Router projection fused ahead of the top-k.  Returns (logits [T,E] float32,
+    topk_ids [T,k] int32, topk_weights [T,k] float32)."""
+    lib = load()
+    T, H = x.shape
+    E = router_w.shape[0]
+    _check(x, "x", torch.bfloat16, (T, H))
+    _check(router_w, "router_w", torch.bfloat16, (E, H))
+    _check(router_b, "router_b", torch.bfloat16, (E,))
+    dev = x.device
+    logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+    ids = torch.empty((T, top_k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, top_k), dtype=torch.float32, device=dev)
+    st = lib.moe_mxfp4_router(x.data_ptr(), router_w.data_ptr(), router_b.data_ptr(), T, H, E, top_k,
+                              logits.data_ptr(), ids.data_ptr(), w.data_ptr(), _stream(stream))
+    _raise("moe_mxfp4_router", st)
+    return logits, ids, w
+
+
 def workspace_bytes(T: int, H: int, I: int, E: int, top_k: int) -> int:
     """Device workspace moe_mxfp4_forward needs for these sizes."""
     lib = load()
@@ -223,6 +248,44 @@ def moe_mxfp4_forward(x: torch.Tensor, router_logits: torch.Tensor,
                                   out.data_ptr(), T, H, I, E, top_k, 1 if gate_up_split else 0,
                                   workspace.data_ptr(), ctypes.byref(n), _stream(stream))
     _raise("moe_mxfp4_forward", st)
+    return out
+
+
+def moe_mxfp4_forward_router(x: torch.Tensor, router_w: torch.Tensor, router_b: torch.Tensor,
+                             w13_blocks: torch.Tensor, w13_scales: torch.Tensor, w13_bias: torch.Tensor,
+                             w2_blocks: torch.Tensor, w2_scales: torch.Tensor, w2_bias: torch.Tensor,
+                             top_k: int, out: Optional[torch.Tensor] = None,
+                             workspace: Optional[torch.Tensor] = None, stream=None,
+                             gate_up_split: bool = False) -> torch.Tensor:
+    """One MXFP4 MoE expert layer whose logits come from the router projection
+    x W_r^T + b_r (router_w [E,H], router_b [E] bfloat16); returns y [T, H] bfloat16."""
+    lib = load()
+    T, H = x.shape
+    E = router_w.shape[0]
+    I = w2_blocks.shape[-1] * 2
+    _check(x, "x", torch.bfloat16, (T, H))
+    _check(router_w, "router_w", torch.bfloat16, (E, H))
+    _check(router_b, "router_b", torch.bfloat16, (E,))
+    _check(w13_blocks, "w13_blocks", torch.uint8, (E, 2 * I, H // 2))
+    _check(w13_scales, "w13_scales", torch.uint8, (E, 2 * I, H // 32))
+    _check(w13_bias, "w13_bias", torch.bfloat16, (E, 2 * I))
+    _check(w2_blocks, "w2_blocks", torch.uint8, (E, H, I // 2))
+    _check(w2_scales, "w2_scales", torch.uint8, (E, H, I // 32))
+    _check(w2_bias, "w2_bias", torch.bfloat16, (E, H))
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    _check(out, "out", torch.bfloat16, (T, H))
+    need = workspace_bytes(T, H, I, E, top_k)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
+    _check(workspace, "workspace", torch.uint8)
+    n = ctypes.c_size_t(workspace.numel())
+    st = lib.moe_mxfp4_forward_router(x.data_ptr(), router_w.data_ptr(), router_b.data_ptr(),
+                                      w13_blocks.data_ptr(), w13_scales.data_ptr(), w13_bias.data_ptr(),
+                                      w2_blocks.data_ptr(), w2_scales.data_ptr(), w2_bias.data_ptr(),
+                                      out.data_ptr(), T, H, I, E, top_k, 1 if gate_up_split else 0,
+                                      workspace.data_ptr(), ctypes.byref(n), _stream(stream))
+    _raise("moe_mxfp4_forward_router", st)
     return out
 
 
@@ -303,4 +366,7 @@ def layer_to_device(layer, device="cuda"):
     for k in ("w13_scale2", "w2_scale2"):  # NVFP4 layers
         if k in layer:
             out[k] = dev(np.asarray(layer[k], dtype=np.float32), torch.float32)
+    for k in ("router_w", "router_b"):  # layers with a router projection
+        if k in layer:
+            out[k] = dev(layer[k], torch.bfloat16)
     return out

@@ -57,7 +57,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t ids, weights, offsets, sorted, counts, big, mid, small, act, zw, total;
+  size_t ids, weights, offsets, sorted, counts, big, mid, small, act, zw, logits, total;
   int max_big, max_mid, max_small;
 };
 
@@ -106,6 +106,7 @@ Layout make_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k) {
   L.small = off;     off = align_up(off + (size_t)L.max_small * 16);
   L.act = off;       off = align_up(off + (size_t)P * (size_t)I * 2);
   L.zw = off;        off = align_up(off + (size_t)P * (size_t)H * 4);
+  L.logits = off;    off = align_up(off + (size_t)T * (size_t)E * 4);  // router projection output
   L.total = off;
   return L;
 }
@@ -139,8 +140,10 @@ const float kNvQuery = 0.f;  // stands in for the NVFP4 scale pointers of a size
 
 // The layer.  scale2_13 / scale2_2 != nullptr selects NVFP4 weights (E4M3
 // block scales per 16 elements, one second-level scale per expert and
-// projection, multiplied before the bias).
-int forward_impl(const uint16_t* x, const float* router_logits, const uint8_t* w13_blocks, const uint8_t* w13_scales,
+// projection, multiplied before the bias).  router_w != nullptr replaces the
+// logits by the router projection of x (router_logits is then unused).
+int forward_impl(const uint16_t* x, const float* router_logits, const uint16_t* router_w, const uint16_t* router_b,
+                 const uint8_t* w13_blocks, const uint8_t* w13_scales,
                  const float* scale2_13, const uint16_t* w13_bias, const uint8_t* w2_blocks,
                  const uint8_t* w2_scales, const float* scale2_2, const uint16_t* w2_bias, uint16_t* y, int64_t T,
                  int64_t H, int64_t I, int64_t E, int64_t top_k, uint32_t flags, void* workspace,
@@ -160,7 +163,10 @@ int forward_impl(const uint16_t* x, const float* router_logits, const uint8_t* w
   if (w13_blocks == nullptr || w13_scales == nullptr || w13_bias == nullptr || w2_blocks == nullptr ||
       w2_scales == nullptr || w2_bias == nullptr)
     return MXFP4MOE_ERR_ARG;
-  if (T > 0 && (x == nullptr || router_logits == nullptr || y == nullptr)) return MXFP4MOE_ERR_ARG;
+  if (T > 0 && (x == nullptr || y == nullptr)) return MXFP4MOE_ERR_ARG;
+  if (T > 0 && router_w == nullptr && router_logits == nullptr) return MXFP4MOE_ERR_ARG;
+  if (T > 0 && router_w != nullptr && router_b == nullptr) return MXFP4MOE_ERR_ARG;
+  if (T > 0 && router_w != nullptr && !aligned16(router_w)) return MXFP4MOE_ERR_ALIGN;
   if (*workspace_bytes < L.total) return MXFP4MOE_ERR_WORKSPACE;
   if (((uintptr_t)workspace & (kAlign - 1)) != 0) return MXFP4MOE_ERR_ALIGN;
   if (!aligned16(w13_blocks) || !aligned16(w2_blocks)) return MXFP4MOE_ERR_ALIGN;
@@ -190,7 +196,11 @@ int forward_impl(const uint16_t* x, const float* router_logits, const uint8_t* w
   hipStream_t s = (hipStream_t)stream;
 
   hipError_t err;
-  if (T <= kFusedRouteTokens) {
+  if (router_w != nullptr) {
+    err = launch_route_proj(x, router_w, router_b, (int)T, (int)H, (int)E, (int)top_k,
+                            reinterpret_cast<float*>(ws + L.logits), ids, weights, s);
+    if (err == hipSuccess) err = launch_group(ids, (int)P, (int)E, offsets, sorted, tt, s);
+  } else if (T <= kFusedRouteTokens) {
     err = launch_route_group(router_logits, (int)T, (int)E, (int)top_k, ids, weights, offsets, sorted, tt, s);
   } else {
     err = launch_route(router_logits, (int)T, (int)E, (int)top_k, ids, weights, s);
@@ -304,8 +314,8 @@ int moe_mxfp4_forward_ex(const uint16_t* x, const float* router_logits, const ui
                          int64_t I, int64_t E, int64_t top_k, uint32_t flags, void* workspace,
                          size_t* workspace_bytes, void* stream) {
   if ((flags & ~(uint32_t)MXFP4MOE_GATE_UP_SPLIT) != 0) return MXFP4MOE_ERR_ARG;
-  return forward_impl(x, router_logits, w13_blocks, w13_scales, nullptr, w13_bias, w2_blocks, w2_scales, nullptr,
-                      w2_bias, y, T, H, I, E, top_k, flags, workspace, workspace_bytes, stream);
+  return forward_impl(x, router_logits, nullptr, nullptr, w13_blocks, w13_scales, nullptr, w13_bias, w2_blocks,
+                      w2_scales, nullptr, w2_bias, y, T, H, I, E, top_k, flags, workspace, workspace_bytes, stream);
 }
 
 int moe_nvfp4_forward(const uint16_t* x, const float* router_logits, const uint8_t* w13_blocks,
@@ -314,9 +324,38 @@ int moe_nvfp4_forward(const uint16_t* x, const float* router_logits, const uint8
                       const uint16_t* w2_bias, uint16_t* y, int64_t T, int64_t H, int64_t I, int64_t E,
                       int64_t top_k, void* workspace, size_t* workspace_bytes, void* stream) {
   if (workspace != nullptr && (w13_scale2 == nullptr || w2_scale2 == nullptr)) return MXFP4MOE_ERR_ARG;
-  return forward_impl(x, router_logits, w13_blocks, w13_scales, w13_scale2 ? w13_scale2 : &kNvQuery, w13_bias,
+  return forward_impl(x, router_logits, nullptr, nullptr, w13_blocks, w13_scales, w13_scale2 ? w13_scale2 : &kNvQuery,
+                      w13_bias,
                       w2_blocks, w2_scales, w2_scale2 ? w2_scale2 : &kNvQuery, w2_bias, y, T, H, I, E, top_k, 0u,
                       workspace, workspace_bytes, stream);
+}
+
+int moe_mxfp4_router(const uint16_t* x, const uint16_t* router_w, const uint16_t* router_b, int64_t T, int64_t H,
+                     int64_t E, int64_t top_k, float* logits, int32_t* topk_ids, float* topk_weights, void* stream) {
+  int st = check_route_shape(T, E, top_k);
+  if (st != MXFP4MOE_OK) return st;
+  if (H <= 0 || (H & 31) != 0) return MXFP4MOE_ERR_SHAPE;
+  if (T == 0) return MXFP4MOE_OK;
+  if (x == nullptr || router_w == nullptr || router_b == nullptr || logits == nullptr || topk_ids == nullptr ||
+      topk_weights == nullptr)
+    return MXFP4MOE_ERR_ARG;
+  if (!aligned16(x) || !aligned16(router_w)) return MXFP4MOE_ERR_ALIGN;
+  hipError_t err = launch_route_proj(x, router_w, router_b, (int)T, (int)H, (int)E, (int)top_k, logits, topk_ids,
+                                     topk_weights, (hipStream_t)stream);
+  return err == hipSuccess ? MXFP4MOE_OK : MXFP4MOE_ERR_HIP;
+}
+
+int moe_mxfp4_forward_router(const uint16_t* x, const uint16_t* router_w, const uint16_t* router_b,
+                             const uint8_t* w13_blocks, const uint8_t* w13_scales, const uint16_t* w13_bias,
+                             const uint8_t* w2_blocks, const uint8_t* w2_scales, const uint16_t* w2_bias, uint16_t* y,
+                             int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k, uint32_t flags,
+                             void* workspace, size_t* workspace_bytes, void* stream) {
+  if ((flags & ~(uint32_t)MXFP4MOE_GATE_UP_SPLIT) != 0) return MXFP4MOE_ERR_ARG;
+  if (workspace != nullptr && T > 0 && router_w == nullptr) return MXFP4MOE_ERR_ARG;
+  static const uint16_t kRouterQuery = 0;  // stands in for the router pointers of a size query
+  return forward_impl(x, nullptr, router_w ? router_w : &kRouterQuery, router_b, w13_blocks, w13_scales, nullptr,
+                      w13_bias, w2_blocks, w2_scales, nullptr, w2_bias, y, T, H, I, E, top_k, flags, workspace,
+                      workspace_bytes, stream);
 }
 
 int mxfp4moe_profile_begin(int stage, int max_calls) {

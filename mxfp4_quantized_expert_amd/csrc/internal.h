@@ -73,6 +73,11 @@ struct TileBounds {
 hipError_t launch_route(const float* logits, int T, int E, int top_k, int32_t* ids, float* weights,
                         hipStream_t stream);
 
+// Router projection and routing in one launch: logits = x W_r^T + b_r (fp32,
+// written to `logits`), then the top-k and softmax as launch_route.
+hipError_t launch_route_proj(const uint16_t* x, const uint16_t* router_w, const uint16_t* router_b, int T, int H,
+                             int E, int top_k, float* logits, int32_t* ids, float* weights, hipStream_t stream);
+
 // Grouping: counts, offsets, stable expert-ordered pair list, and (when
 // tt.big != nullptr) the GEMM tile tables.
 hipError_t launch_group(const int32_t* ids, int P, int E, int32_t* offsets, int32_t* sorted_pairs,

@@ -17,10 +17,9 @@ constexpr int kPerLane = MXFP4MOE_MAX_EXPERTS / 64;
 // wave-wide argmax (ties to the lower expert index) pick the experts in
 // descending order; lane j keeps the j-th pick.  The softmax runs over the
 // picks relative to the largest one.
-__device__ void route_token(const float* __restrict__ logits, int t, int E, int top_k, int32_t* __restrict__ ids,
-                            float* __restrict__ weights) {
+__device__ void route_row(const float* row, int t, int E, int top_k, int32_t* __restrict__ ids,
+                          float* __restrict__ weights) {
   const int lane = mx::lane_id();
-  const float* row = logits + (size_t)t * E;
   float v[kPerLane];
   uint32_t avail = 0;
 #pragma unroll
@@ -74,6 +73,97 @@ __device__ void route_token(const float* __restrict__ logits, int t, int E, int 
     ids[(size_t)t * top_k + lane] = my_e;
     weights[(size_t)t * top_k + lane] = ex / sum;
   }
+}
+
+__device__ __forceinline__ void route_token(const float* __restrict__ logits, int t, int E, int top_k,
+                                            int32_t* __restrict__ ids, float* __restrict__ weights) {
+  route_row(logits + (size_t)t * E, t, E, top_k, ids, weights);
+}
+
+// Router projection fused ahead of the top-k ("feat(gguf): serve gpt-oss gguf
+// checkpoints on gpt_oss", FreeToken PR #838: the router is mlp.router, a
+// linear layer whose bias is a required tensor):
+//   logits[t, e] = sum_h x[t, h] W_r[e, h] + b_r[e]
+// for a tile of 16 tokens on the 16x16x32 bf16 MFMA (A: 16 router rows, B:
+// the 16 tokens; bf16 products are exact, accumulation is fp32).  Wave w
+// takes K quarter w % 4 of the 16-expert blocks w / 4, w / 4 + 4, ... and
+// parks its partial sums in LDS; after a barrier the quarters are added in
+// order (so the logits do not depend on scheduling), the bias last, and
+// written out; then one wave per token routes from the LDS row as
+// route_kernel does.
+constexpr int kProjTokens = 16;
+constexpr int kProjThreads = 1024;
+constexpr int kProjWaves = kProjThreads / 64;
+constexpr int kProjParts = 4;  // K parts
+constexpr int kProjBatch = 8;  // K steps of 32 whose loads are issued together
+
+__global__ __launch_bounds__(kProjThreads) void route_proj_kernel(const uint16_t* __restrict__ x,
+                                                                   const uint16_t* __restrict__ w,
+                                                                   const uint16_t* __restrict__ b, int T, int H,
+                                                                   int E, int top_k, float* __restrict__ logits,
+                                                                   int32_t* __restrict__ ids,
+                                                                   float* __restrict__ weights) {
+  extern __shared__ float part[];  // [nq][kProjTokens][E] partial sums, then [kProjTokens][E] logits in part 0
+  const int t0 = blockIdx.x * kProjTokens;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int q = lane >> 4;
+  const int lr = lane & 15;
+  const int nk = H >> 5;                    // K steps of 32
+  const int neb = (E + 15) >> 4;
+  constexpr int nq = kProjParts;
+  const int kq = wave % nq;
+  const int k_begin = nk * kq / nq, k_end = nk * (kq + 1) / nq;
+  const uint16_t* xrow = x + (size_t)min(t0 + lr, T - 1) * H + 8 * q;  // B: token lr, K values 8q..8q+7
+  // the bias of the logits this thread adds up after the barrier
+  constexpr int kPerThread = kProjTokens * MXFP4MOE_MAX_EXPERTS / kProjThreads;
+  float bias[kPerThread];
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) {
+    const int i = threadIdx.x + j * kProjThreads;
+    bias[j] = i < kProjTokens * E ? mx::bf16_to_f32(b[i % E]) : 0.f;
+  }
+  for (int eb = wave / nq; eb < neb; eb += kProjWaves / nq) {
+    const uint16_t* wrow = w + (size_t)min(eb * 16 + lr, E - 1) * H + 8 * q;  // A: router row lr of the block
+    mx::f32x4 acc[2] = {mx::f32x4{0.f, 0.f, 0.f, 0.f}, mx::f32x4{0.f, 0.f, 0.f, 0.f}};
+    for (int k0 = k_begin; k0 < k_end; k0 += kProjBatch) {
+      mx::u32x4 av[kProjBatch], bv[kProjBatch];
+#pragma unroll
+      for (int j = 0; j < kProjBatch; ++j) {
+        const int kk = min(k0 + j, k_end - 1);  // steps past the quarter re-read its last one (zeroed below)
+        av[j] = *reinterpret_cast<const mx::u32x4*>(wrow + (size_t)kk * 32);
+        bv[j] = *reinterpret_cast<const mx::u32x4*>(xrow + (size_t)kk * 32);
+      }
+#pragma unroll
+      for (int j = 0; j < kProjBatch; ++j) {
+        const mx::u32x4 a = k0 + j < k_end ? av[j] : mx::u32x4{0u, 0u, 0u, 0u};
+        acc[j & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mx::as_bf16x8(a), mx::as_bf16x8(bv[j]), acc[j & 1], 0, 0, 0);
+      }
+    }
+    // lane (lr, q) holds experts eb*16 + 4q + i of token lr
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = eb * 16 + 4 * q + i;
+      if (e < E) part[((size_t)kq * kProjTokens + lr) * E + e] = acc[0][i] + acc[1][i];
+    }
+  }
+  __syncthreads();
+  const size_t slab = (size_t)kProjTokens * E;
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) {
+    const int i = threadIdx.x + j * kProjThreads;
+    if (i < kProjTokens * E) {
+      float v = part[i];
+      for (int pq = 1; pq < nq; ++pq) v += part[pq * slab + i];
+      v += bias[j];
+      part[i] = v;
+      const int t = t0 + i / E;
+      if (t < T) logits[(size_t)t * E + i % E] = v;
+    }
+  }
+  __syncthreads();
+  for (int tt = wave; tt < kProjTokens; tt += kProjThreads / 64)
+    if (t0 + tt < T) route_row(part + (size_t)tt * E, t0 + tt, E, top_k, ids, weights);
 }
 
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(const float* __restrict__ logits, int T, int E,
@@ -238,6 +328,20 @@ hipError_t launch_route(const float* logits, int T, int E, int top_k, int32_t* i
   const unsigned grid = (unsigned)((T + per_block - 1) / per_block);
   ProfileScope prof(kStageRoute, stream);
   route_kernel<<<grid, kRouteThreads, 0, stream>>>(logits, T, E, top_k, ids, weights);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_proj(const uint16_t* x, const uint16_t* router_w, const uint16_t* router_b, int T, int H,
+                             int E, int top_k, float* logits, int32_t* ids, float* weights, hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  const size_t lds = (size_t)kProjParts * kProjTokens * E * sizeof(float);
+  static const hipError_t attr =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&route_proj_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)((size_t)kProjParts * kProjTokens * MXFP4MOE_MAX_EXPERTS * sizeof(float)));
+  if (attr != hipSuccess) return attr;
+  ProfileScope prof(kStageRoute, stream);
+  route_proj_kernel<<<(unsigned)((T + kProjTokens - 1) / kProjTokens), kProjThreads, lds, stream>>>(
+      x, router_w, router_b, T, H, E, top_k, logits, ids, weights);
   return hipGetLastError();
 }
 

@@ -139,3 +139,30 @@ def test_route_argument_checks(lib):
     assert f(A, 4, 8, 9, A, A, A, A, None) == -2
     assert f(A, 4, 8, 2, A, A, None, A, None) == -1
     assert f(None, 4, 8, 2, A, A, A, A, None) == -1
+
+
+def test_router_argument_checks(lib):
+    f = lib.moe_mxfp4_router
+    assert f(A, A, A, 4, 64, 0, 1, A, A, A, None) == -2      # no experts
+    assert f(A, A, A, 4, 64, 8, 9, A, A, A, None) == -2      # top_k > E
+    assert f(A, A, A, 4, 48, 8, 2, A, A, A, None) == -2      # H not a multiple of 32
+    assert f(A, A, None, 4, 64, 8, 2, A, A, A, None) == -1   # the router bias is required
+    assert f(A, None, A, 4, 64, 8, 2, A, A, A, None) == -1
+    assert f(A, A, A, 4, 64, 8, 2, None, A, A, None) == -1   # logits out
+    assert f(A + 2, A, A, 4, 64, 8, 2, A, A, A, None) == -4
+    assert f(A, A + 4, A, 4, 64, 8, 2, A, A, A, None) == -4
+    assert f(None, None, None, 0, 64, 8, 2, None, None, None, None) == 0  # empty batch
+
+
+def test_forward_router_argument_checks(lib):
+    f = lib.moe_mxfp4_forward_router
+    n = ctypes.c_size_t(0)
+    assert f(*([None] * 10), 4, 64, 64, 4, 2, 0, None, ctypes.byref(n), None) == 0
+    assert n.value == binding.workspace_bytes(4, 64, 64, 4, 2)  # same workspace as the logits entry
+    big = ctypes.c_size_t(1 << 30)
+    w = [A] * 6
+    assert f(A, None, A, *w, A, 4, 64, 64, 4, 2, 0, A, ctypes.byref(big), None) == -1  # no router weights
+    assert f(A, A, None, *w, A, 4, 64, 64, 4, 2, 0, A, ctypes.byref(big), None) == -1  # no router bias
+    assert f(A, A, A, *w, A, 4, 64, 64, 4, 2, 2, A, ctypes.byref(big), None) == -1     # unknown flag
+    assert f(A, A + 2, A, *w, A, 4, 64, 64, 4, 2, 0, A, ctypes.byref(big), None) == -4  # misaligned router
+    assert f(A, A, A, *w, A, 4, 48, 64, 4, 2, 0, A, ctypes.byref(big), None) == -2
