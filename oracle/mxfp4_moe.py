@@ -391,6 +391,114 @@ def moe_forward(layer: Dict[str, np.ndarray], top_k: int,
     return y
 
 
+# --------------------------------------------------------------------------
+# Block-scaled FP8 activations for the opt-in FP4 scaled-MFMA path.  This is
+# an approximation of this implementation's own (the pages fix fp32
+# accumulation of exact bf16 products only); it is defined here so that the
+# GPU's quantized codes can be checked exactly.  Encodings from the OCP
+# Microscaling Formats v1.0 specification: MXFP8 E4M3 elements in blocks of
+# 32 along K sharing one E8M0 scale.  Reading: the shared exponent is
+# floor(log2(max|v|)) - 7, one below the specification's emax-based choice,
+# so that no element of a block needs clamping (scaled magnitudes stay below
+# 256 <= 448); an all-zero block takes scale byte 127.  "split" activations
+# add a second MXFP8 tensor that quantizes the residual v - hi the same way.
+# --------------------------------------------------------------------------
+
+def e4m3_encode_rne(v) -> np.ndarray:
+    """float64 -> FP8 E4M3 code, round to nearest, ties to even.  |v| <= 448."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    if np.any(a > 448.0):
+        raise ValueError("E4M3 magnitude above 448")
+    _, ex = np.frexp(np.where(a > 0, a, 1.0))   # a = m * 2^ex, m in [0.5, 1)
+    e = np.maximum(ex - 1, -6)                   # binade; below 2^-6 the subnormal quantum 2^-9
+    q = np.ldexp(1.0, e - 3)                     # three mantissa bits
+    r = np.round(a / q) * q                      # numpy rounds halves to even
+    _, ex2 = np.frexp(np.where(r > 0, r, 1.0))
+    e2 = ex2 - 1
+    normal = r >= 2.0 ** -6
+    expf = np.where(normal, e2 + 7, 0)
+    mant = np.where(normal, np.round(r / np.ldexp(1.0, e2) * 8 - 8), np.round(r / 2.0 ** -9))
+    code = (np.signbit(v).astype(np.int64) << 7) | (expf.astype(np.int64) << 3) | mant.astype(np.int64)
+    return code.astype(np.uint8)
+
+
+def mxfp8_quantize(v: np.ndarray):
+    """[..., K] float64 -> (E4M3 codes [..., K] uint8, E8M0 scale bytes [..., K/32] uint8)."""
+    v = np.asarray(v, dtype=np.float64)
+    K = v.shape[-1]
+    if K % GROUP:
+        raise ValueError("K must be a multiple of 32")
+    blk = v.reshape(v.shape[:-1] + (K // GROUP, GROUP))
+    amax = np.abs(blk).max(axis=-1)
+    _, ex = np.frexp(np.where(amax > 0, amax, 1.0))
+    X = np.where(amax > 0, ex - 1 - 7, 0)
+    sbyte = np.clip(X + 127, 0, 254)
+    scaled = blk / np.ldexp(1.0, (sbyte - 127).astype(np.int64))[..., None]
+    codes = e4m3_encode_rne(scaled).reshape(v.shape)
+    return codes, sbyte.astype(np.uint8)
+
+
+def mxfp8_dequantize(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    vals = e4m3_value(codes)
+    return vals * np.repeat(np.ldexp(1.0, scales.astype(np.int64) - 127), GROUP, axis=-1)
+
+
+def mxfp8_activations(v: np.ndarray, mode: str) -> np.ndarray:
+    """The value the FP4 scaled-MFMA path multiplies in place of v: one MXFP8
+    tensor ("single") or an MXFP8 tensor plus the MXFP8 tensor of its
+    residual ("split")."""
+    hi_c, hi_s = mxfp8_quantize(v)
+    hi = mxfp8_dequantize(hi_c, hi_s)
+    if mode == "single":
+        return hi
+    if mode != "split":
+        raise ValueError(mode)
+    lo_c, lo_s = mxfp8_quantize(np.asarray(v, dtype=np.float64) - hi)
+    return hi + mxfp8_dequantize(lo_c, lo_s)
+
+
+def expert_ffn_fp8act(xrows: np.ndarray, w13_blocks, w13_scales, w13_bias_bits,
+                      w2_blocks, w2_scales, w2_bias_bits, mode: str) -> np.ndarray:
+    """expert_ffn with block-scaled FP8 activations feeding both GEMMs: x
+    quantized as above; the SwiGLU output rounded to bf16 (the path's
+    intermediate), then quantized the same way."""
+    W13 = dequantize_f64(w13_blocks, w13_scales)
+    h = mxfp8_activations(xrows, mode) @ W13.T + bf16_decode(w13_bias_bits)[None, :]
+    a = bf16_decode(bf16_encode_rne(swiglu_clamped(h[:, 0::2], h[:, 1::2])))
+    W2 = dequantize_f64(w2_blocks, w2_scales)
+    return mxfp8_activations(a, mode) @ W2.T + bf16_decode(w2_bias_bits)[None, :]
+
+
+def moe_forward_fp8act(layer: Dict[str, np.ndarray], top_k: int, quantized: np.ndarray, mode: str,
+                       tokens: Optional[Sequence[int]] = None) -> np.ndarray:
+    """moe_forward where the experts with quantized[e] run expert_ffn_fp8act
+    (the FP4 scaled-MFMA path applies to whole experts) and the rest expert_ffn."""
+    x = bf16_decode(layer["x"])
+    logits = np.asarray(layer["router_logits"])
+    if tokens is not None:
+        tokens = np.asarray(tokens, dtype=np.int64)
+        x = x[tokens]
+        logits = logits[tokens]
+    T, H = x.shape
+    E = logits.shape[1]
+    ids, w = route(logits, top_k)
+    counts, offsets, perm = group_by_expert(ids, E)
+    z = np.zeros((T * top_k, H), dtype=np.float64)
+    for e in range(E):
+        if counts[e] == 0:
+            continue
+        pairs = perm[offsets[e]:offsets[e + 1]]
+        args = (x[pairs // top_k], layer["w13_blocks"][e], layer["w13_scales"][e], layer["w13_bias"][e],
+                layer["w2_blocks"][e], layer["w2_scales"][e], layer["w2_bias"][e])
+        z[pairs] = expert_ffn_fp8act(*args, mode) if quantized[e] else expert_ffn(*args)
+    z = z.reshape(T, top_k, H)
+    y = np.zeros((T, H), dtype=np.float64)
+    for j in range(top_k):
+        y += w[:, j:j + 1] * z[:, j, :]
+    return y
+
+
 def moe_forward_dense(layer: Dict[str, np.ndarray], top_k: int) -> np.ndarray:
     """Brute force for tiny layers: every expert on every token, then a dense
     routing matrix R[T, E] (softmax weight at the selected experts, 0 elsewhere)
@@ -436,5 +544,7 @@ __all__ = [
     "parity_errors", "flops_per_pair",
     "NV_GROUP", "e4m3_value", "nvfp4_dequantize_f64", "expert_ffn_nvfp4", "moe_forward_nvfp4",
     "router_logits", "moe_forward_router",
+    "e4m3_encode_rne", "mxfp8_quantize", "mxfp8_dequantize", "mxfp8_activations", "expert_ffn_fp8act",
+    "moe_forward_fp8act",
 ]
 

@@ -501,3 +501,52 @@ def test_moe_forward_router_dominant_bias_is_one_expert():
     z = O.expert_ffn(O.bf16_decode(L["x"]), L["w13_blocks"][2], L["w13_scales"][2], L["w13_bias"][2],
                      L["w2_blocks"][2], L["w2_scales"][2], L["w2_bias"][2])
     np.testing.assert_allclose(y, z, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- MXFP8 activations (FP4 scaled-MFMA path)
+
+def test_e4m3_encode_round_trips_every_code():
+    codes = np.arange(256, dtype=np.uint8)
+    codes = codes[(codes & 0x7F) != 0x7F]  # not NaN
+    assert np.array_equal(O.e4m3_encode_rne(O.e4m3_value(codes)), codes)
+
+
+def test_e4m3_encode_matches_torch_incl_ties():
+    rng = np.random.default_rng(3)
+    v = np.concatenate([rng.uniform(-448, 448, 20000), rng.uniform(-2 ** -5, 2 ** -5, 20000)])
+    # every midpoint between adjacent positive codes: ties go to the even code
+    pos = O.e4m3_value(np.arange(0, 0x7E, dtype=np.uint8))
+    mids = (pos[:-1] + pos[1:]) / 2
+    v = np.concatenate([v, mids, -mids])
+    ref = torch.from_numpy(v.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.e4m3_encode_rne(v), ref)
+    got = O.e4m3_encode_rne(mids)
+    assert np.all(got % 2 == 0)  # even mantissa at every tie
+
+
+def test_mxfp8_scale_rule():
+    # max|block| = 1 -> shared exponent -7 (byte 120); 3 -> -6 (121); zeros -> 127
+    v = np.zeros((3, 32))
+    v[0, 5] = 1.0
+    v[1, :] = np.linspace(-3.0, 3.0, 32)
+    codes, scales = O.mxfp8_quantize(v)
+    assert list(scales) == [120, 121, 127]
+    assert np.all(codes[2] == 0)
+    scaled = O.e4m3_value(codes[:2])
+    assert np.abs(scaled).max(axis=1).tolist() == [128.0, 192.0]  # 1 * 2^7, 3 * 2^6
+
+
+def test_mxfp8_split_error_bound_and_exact_cases():
+    rng = np.random.default_rng(4)
+    v = O.bf16_decode(W.to_bf16_bits(rng.standard_normal((64, 256)).astype(np.float32)))
+    q = O.mxfp8_activations(v, "split")
+    amax = np.repeat(np.abs(v.reshape(64, 8, 32)).max(axis=-1), 32, axis=-1)
+    assert np.all(np.abs(v - q) <= 2.0 ** -8 * amax)
+    # values with at most four significant bits inside a block's range need no residual
+    codes = rng.integers(0x30, 0x50, size=(4, 64)).astype(np.uint8)
+    w = O.e4m3_value(codes) * 2.0 ** -3
+    assert np.array_equal(O.mxfp8_activations(w, "split"), w)
+    assert np.array_equal(O.mxfp8_activations(w, "single"), w)
+    # a single MXFP8 tensor is coarser than the split
+    e1 = np.abs(v - O.mxfp8_activations(v, "single")).max()
+    assert e1 > 4 * np.abs(v - q).max()
