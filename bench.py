@@ -32,6 +32,7 @@ METRIC = "MoE-layer tokens/s; decode HBM GB/s & prefill MFMA TFLOP/s vs MI355X p
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 PEAK_FP4_TFLOPS = 10100.0    # MI355X dense fp4 MFMA
+PEAK_FP8_TFLOPS = 5000.0     # MI355X dense fp8 MFMA
 
 
 def log(*a):
@@ -147,7 +148,10 @@ def run_moe(args):
     for _ in range(copies - 1):
         weight_sets.append({kk: (v.clone() if kk.startswith("w") else v) for kk, v in dev.items()})
     torch.cuda.synchronize()
-    ws = torch.empty((binding.workspace_bytes(T, H, I, E, k),), dtype=torch.uint8, device="cuda")
+    if args.act != "bf16" and (nvfp4 or router):
+        raise SystemExit("--act applies to the MXFP4 workloads with logits input")
+    ws = torch.empty((binding.workspace_bytes(T, H, I, E, k, binding.ACT_FLAGS[args.act]),), dtype=torch.uint8,
+                     device="cuda")
     y = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
 
     def step(i):
@@ -163,7 +167,7 @@ def run_moe(args):
         else:
             binding.moe_mxfp4_forward(dev["x"], dev["router_logits"], d["w13_blocks"], d["w13_scales"],
                                       d["w13_bias"], d["w2_blocks"], d["w2_scales"], d["w2_bias"], k,
-                                      out=y, workspace=ws)
+                                      out=y, workspace=ws, act=args.act)
 
     for i in range(args.warmup):
         step(i)
@@ -172,7 +176,7 @@ def run_moe(args):
     # Stage breakdown (untimed diagnostics, run before the timed region so that
     # the timed steps also start with the GPU at its steady clock).
     stages = {}
-    for st in ["route", "group", "gate_up", "gate_up_wide", "gate_up_mid", "gate_up_stream", "down",
+    for st in ["route", "group", "act_quant", "gate_up", "gate_up_wide", "gate_up_mid", "gate_up_stream", "down",
                "down_wide", "down_mid", "down_stream", "combine"]:
         binding.profile_begin(st, 5)
         for i in range(5):
@@ -212,8 +216,9 @@ def run_moe(args):
         # 2*H*2I FLOPs per pair, over the pairs of the tiles of that launch
         tile_pairs = full_pairs if dominant == "gate_up_wide" else mid_pairs
         work = 4.0 * H * I * tile_pairs
-        roof = {"bound": "mfma", "achieved": work / (kms / 1e3) / 1e12, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s"}
+        # the FP4 scaled-MFMA path runs at the FP8 rate (fp4 x fp8 operands)
+        peak = PEAK_FP8_TFLOPS if args.act != "bf16" and dominant == "gate_up_wide" else PEAK_BF16_TFLOPS
+        roof = {"bound": "mfma", "achieved": work / (kms / 1e3) / 1e12, "peak": peak, "unit": "TFLOP/s"}
         per_unit = (f"{4 * H * I:,} FLOPs per pair (2*H*2I) x {tile_pairs} pairs in "
                     + ("128-pair tiles" if dominant == "gate_up_wide" else "mid tiles of at most 64 pairs"))
     else:
@@ -248,7 +253,7 @@ def run_moe(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if args.act == "bf16" else "fp4 x fp8 (full tiles), bf16 (remainder tiles)",
         "data": "synthetic",
         "config": {
             "workload": f"{args.workload}: {'NVFP4' if nvfp4 else 'MXFP4'} MoE expert layer T={T} H={H} I={I} E={E} "
@@ -257,6 +262,11 @@ def run_moe(args):
             "T": T, "H": H, "I": I, "E": E, "top_k": k,
             "weights": ("nvfp4 (e2m1 codes, e4m3 scale per 16, fp32 second-level scale)" if nvfp4 else
                         "mxfp4 (e2m1 codes, e8m0 scale per 32)") + ", bf16 MFMA, fp32 accumulate",
+            "activations": {"bf16": "bf16 (exact products)",
+                            "mxfp8_split": "experts with >= 128 pairs: MXFP8 + residual MXFP8 on the FP4 x FP8 "
+                                           "block-scaled MFMA (opt-in; ~1.7e-3 from the exact layer)",
+                            "mxfp8": "experts with >= 128 pairs: one MXFP8 tensor on the FP4 x FP8 block-scaled "
+                                     "MFMA (opt-in; up to ~21 % from the exact layer)"}[args.act],
             "active_experts": n_active,
             "pairs_in_full_tiles": full_pairs,
             "weight_copies_rotated": copies,
@@ -388,6 +398,9 @@ def main():
                              "nvfp4_20b_prefill", "nvfp4_120b_prefill", "router_20b_decode", "router_120b_prefill",
                              "dequant_120b", "dequant_host_120b", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--act", default="bf16", choices=["bf16", "mxfp8_split", "mxfp8"],
+                    help="activations of the full 128-pair tiles: exact bf16 (default) or the opt-in "
+                         "FP4 scaled-MFMA path over MXFP8 activations")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})",

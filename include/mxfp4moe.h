@@ -183,15 +183,51 @@ int moe_mxfp4_forward(const uint16_t* x, const float* router_logits,
  * The split layout is the uninterleaved spelling of the same clamped SwiGLU
  * ("feat(gguf): serve gpt-oss gguf checkpoints on gpt_oss", FreeToken PR #838,
  * "What it does": swigluoai with interleaved=False).  Results are identical
- * to the interleaved call on the correspondingly permuted rows.  Any other
- * flag bit is MXFP4MOE_ERR_ARG.
+ * to the interleaved call on the correspondingly permuted rows.
+ *
+ *   flags |= MXFP4MOE_ACT_MXFP8_SPLIT  (opt-in approximation) experts with at
+ *           least 128 pairs run both GEMMs on the gfx950 block-scaled MFMA
+ *           (v_mfma_scale_f32_32x32x64_f8f6f4): packed E2M1 weights with their
+ *           E8M0 scales times activations quantized to MXFP8 (E4M3 in blocks
+ *           of 32, one E8M0 scale per block, shared exponent
+ *           floor(log2 max) - 7, round to nearest even) plus the MXFP8
+ *           quantization of the residual; about 1e-3 normwise from the
+ *           exact layer on the test layers.  The SwiGLU output is rounded to
+ *           bf16, then quantized the same way.
+ *   flags |= MXFP4MOE_ACT_MXFP8        the same with a single MXFP8 tensor
+ *           (half the MFMAs; 4 to 20 % normwise from the exact layer on the
+ *           test layers, outside the 1e-2 bar: for measurement only).
+ * Experts with fewer pairs keep the exact bf16 path.  The two ACT flags are
+ * exclusive (SPLIT wins); the workspace query must pass the same flags (the
+ * quantized activations live in the workspace).  Not available for NVFP4.
+ * Any other flag bit is MXFP4MOE_ERR_ARG.
  */
 #define MXFP4MOE_GATE_UP_SPLIT 1u
+#define MXFP4MOE_ACT_MXFP8 2u
+#define MXFP4MOE_ACT_MXFP8_SPLIT 4u
 int moe_mxfp4_forward_ex(const uint16_t* x, const float* router_logits,
                          const uint8_t* w13_blocks, const uint8_t* w13_scales, const uint16_t* w13_bias,
                          const uint8_t* w2_blocks, const uint8_t* w2_scales, const uint16_t* w2_bias,
                          uint16_t* y, int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k,
                          uint32_t flags, void* workspace, size_t* workspace_bytes, void* stream);
+
+/*
+ * moe_mxfp8_quantize - the activation quantizer of the MXFP4MOE_ACT_* paths,
+ * exposed for tests and callers that keep activations in this form.
+ *
+ *   src     [rows, K] bf16, 16-byte aligned; K a multiple of 32
+ *   codes   [rows, 128 * ceil(K/64)] uint8 out, 16-byte aligned: per 64-wide K
+ *           chunk c, the 64 E4M3 codes of K [64c, 64c+64), then the 64 codes
+ *           of the residual (zeros unless split)
+ *   scales  [rows, 4 * ceil(K/64)] uint8 out, 4-byte aligned: per chunk the
+ *           E8M0 bytes of groups 2c, 2c+1, then the residual's (127 unless split)
+ * A chunk past K (K % 64 == 32) holds zero codes and scale 127.  Encodings
+ * (OCP Microscaling Formats v1.0): E4M3 elements in blocks of 32 sharing one
+ * E8M0 scale; the shared exponent is floor(log2(max|v|)) - 7 (127 for an
+ * all-zero block) and elements round to nearest, ties to even.
+ */
+int moe_mxfp8_quantize(const uint16_t* src, int64_t rows, int64_t K, int split, uint8_t* codes,
+                       uint8_t* scales, void* stream);
 
 /*
  * moe_mxfp4_router - the router projection fused ahead of the top-k:
@@ -265,7 +301,8 @@ const char* mxfp4moe_status_string(int status);
  * events around that launch, on the stream the kernel runs on.  Stages:
  * 1 route, 2 group, 3 gate_up GEMM, 4 down GEMM, 5 combine, 6 dequant,
  * then single launches of the GEMM stages: 7 / 11 / 8 the full-tile /
- * mid-remainder / streaming launch of gate_up, 9 / 12 / 10 the same for down.
+ * mid-remainder / streaming launch of gate_up, 9 / 12 / 10 the same for down,
+ * 13 the MXFP8 activation quantizer of the ACT flags.
  * mxfp4moe_profile_end(ms, capacity) synchronises on the recorded events,
  * stores up to `capacity` per-launch durations in milliseconds (host array),
  * releases the events and returns how many were stored (negative on error).

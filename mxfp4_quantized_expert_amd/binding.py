@@ -27,7 +27,7 @@ STATUS = {
 
 STAGES = {"route": 1, "group": 2, "gate_up": 3, "down": 4, "combine": 5, "dequant": 6,
           "gate_up_wide": 7, "gate_up_stream": 8, "down_wide": 9, "down_stream": 10,
-          "gate_up_mid": 11, "down_mid": 12}
+          "gate_up_mid": 11, "down_mid": 12, "act_quant": 13}
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -73,6 +73,8 @@ def load() -> ctypes.CDLL:
                                              _i64, _i64, _i64, _i64, _i64, ctypes.c_uint32, _vp,
                                              ctypes.POINTER(ctypes.c_size_t), _vp]
     lib.moe_mxfp4_forward_router.restype = ctypes.c_int
+    lib.moe_mxfp8_quantize.argtypes = [_vp, _i64, _i64, ctypes.c_int, _vp, _vp, _vp]
+    lib.moe_mxfp8_quantize.restype = ctypes.c_int
     lib.mxfp4moe_status_string.argtypes = [ctypes.c_int]
     lib.mxfp4moe_status_string.restype = ctypes.c_char_p
     lib.mxfp4moe_profile_begin.argtypes = [ctypes.c_int, ctypes.c_int]
@@ -185,6 +187,21 @@ def moe_mxfp4_route(router_logits: torch.Tensor, top_k: int, stream=None):
     return ids, w, offsets, pairs
 
 
+def moe_mxfp8_quantize(src: torch.Tensor, split: bool = True, stream=None):
+    """bf16 [rows, K] -> (codes [rows, 128*ceil(K/64)] uint8, scales [rows, 4*ceil(K/64)] uint8)
+    in the chunk-interleaved layout of the FP4 scaled-MFMA path."""
+    lib = load()
+    rows, K = src.shape
+    _check(src, "src", torch.bfloat16)
+    nc = (K + 63) // 64
+    codes = torch.empty((rows, 128 * nc), dtype=torch.uint8, device=src.device)
+    scales = torch.empty((rows, 4 * nc), dtype=torch.uint8, device=src.device)
+    st = lib.moe_mxfp8_quantize(src.data_ptr(), rows, K, 1 if split else 0, codes.data_ptr(), scales.data_ptr(),
+                                _stream(stream))
+    _raise("moe_mxfp8_quantize", st)
+    return codes, scales
+
+
 def moe_mxfp4_router(x: torch.Tensor, router_w: torch.Tensor, router_b: torch.Tensor, top_k: int, stream=None):
     """Router projection fused ahead of the top-k.  Returns (logits [T,E] float32,
     topk_ids [T,k] int32, topk_weights [T,k] float32)."""
@@ -204,12 +221,15 @@ def moe_mxfp4_router(x: torch.Tensor, router_w: torch.Tensor, router_b: torch.Te
     return logits, ids, w
 
 
-def workspace_bytes(T: int, H: int, I: int, E: int, top_k: int) -> int:
-    """Device workspace moe_mxfp4_forward needs for these sizes."""
+ACT_FLAGS = {"bf16": 0, "mxfp8": 2, "mxfp8_split": 4}
+
+
+def workspace_bytes(T: int, H: int, I: int, E: int, top_k: int, flags: int = 0) -> int:
+    """Device workspace moe_mxfp4_forward needs for these sizes (and layout/activation flags)."""
     lib = load()
     n = ctypes.c_size_t(0)
-    st = lib.moe_mxfp4_forward(None, None, None, None, None, None, None, None, None,
-                               T, H, I, E, top_k, None, ctypes.byref(n), None)
+    st = lib.moe_mxfp4_forward_ex(None, None, None, None, None, None, None, None, None,
+                                  T, H, I, E, top_k, flags, None, ctypes.byref(n), None)
     _raise("moe_mxfp4_forward(workspace query)", st)
     return int(n.value)
 
@@ -219,9 +239,11 @@ def moe_mxfp4_forward(x: torch.Tensor, router_logits: torch.Tensor,
                       w2_blocks: torch.Tensor, w2_scales: torch.Tensor, w2_bias: torch.Tensor,
                       top_k: int, out: Optional[torch.Tensor] = None,
                       workspace: Optional[torch.Tensor] = None, stream=None,
-                      gate_up_split: bool = False) -> torch.Tensor:
+                      gate_up_split: bool = False, act: str = "bf16") -> torch.Tensor:
     """One MXFP4 MoE expert layer; returns y [T, H] bfloat16.  gate_up_split: w13 rows are
-    [I gate rows; I up rows] instead of interleaved."""
+    [I gate rows; I up rows] instead of interleaved.  act: "bf16" (exact), or the opt-in
+    FP4 scaled-MFMA path for experts with at least 128 pairs over MXFP8 activations,
+    "mxfp8_split" (high part + residual) or "mxfp8" (one tensor)."""
     lib = load()
     T, H = x.shape
     E = router_logits.shape[1]
@@ -237,7 +259,8 @@ def moe_mxfp4_forward(x: torch.Tensor, router_logits: torch.Tensor,
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
     _check(out, "out", torch.bfloat16, (T, H))
-    need = workspace_bytes(T, H, I, E, top_k)
+    flags = (1 if gate_up_split else 0) | ACT_FLAGS[act]
+    need = workspace_bytes(T, H, I, E, top_k, flags)
     if workspace is None:
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
     _check(workspace, "workspace", torch.uint8)
@@ -245,7 +268,7 @@ def moe_mxfp4_forward(x: torch.Tensor, router_logits: torch.Tensor,
     st = lib.moe_mxfp4_forward_ex(x.data_ptr(), router_logits.data_ptr(),
                                   w13_blocks.data_ptr(), w13_scales.data_ptr(), w13_bias.data_ptr(),
                                   w2_blocks.data_ptr(), w2_scales.data_ptr(), w2_bias.data_ptr(),
-                                  out.data_ptr(), T, H, I, E, top_k, 1 if gate_up_split else 0,
+                                  out.data_ptr(), T, H, I, E, top_k, flags,
                                   workspace.data_ptr(), ctypes.byref(n), _stream(stream))
     _raise("moe_mxfp4_forward", st)
     return out

@@ -57,7 +57,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t ids, weights, offsets, sorted, counts, big, mid, small, act, zw, logits, total;
+  size_t ids, weights, offsets, sorted, counts, big, mid, small, act, zw, logits, xq, xqs, aq, aqs, total;
   int max_big, max_mid, max_small;
 };
 
@@ -87,7 +87,7 @@ TileBounds tile_bounds(int64_t T, int64_t P, int64_t E, TileMode mode) {
   return b;
 }
 
-Layout make_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k) {
+Layout make_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k, bool fp8_act = false) {
   const int64_t P = T * top_k;
   Layout L;
   const TileBounds wide = tile_bounds(T, P, E, kTilesWide), no_wide = tile_bounds(T, P, E, kTilesNoWide),
@@ -107,6 +107,12 @@ Layout make_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k) {
   L.act = off;       off = align_up(off + (size_t)P * (size_t)I * 2);
   L.zw = off;        off = align_up(off + (size_t)P * (size_t)H * 4);
   L.logits = off;    off = align_up(off + (size_t)T * (size_t)E * 4);  // router projection output
+  // MXFP8 activations of the FP4 scaled-MFMA path (only with its flag)
+  const size_t nx = fp8_act ? (size_t)T : 0, na = fp8_act ? (size_t)P : 0;
+  L.xq = off;        off = align_up(off + nx * act_quant_row_bytes((int)H));
+  L.xqs = off;       off = align_up(off + nx * act_quant_scale_row_bytes((int)H));
+  L.aq = off;        off = align_up(off + na * act_quant_row_bytes((int)I));
+  L.aqs = off;       off = align_up(off + na * act_quant_scale_row_bytes((int)I));
   L.total = off;
   return L;
 }
@@ -137,6 +143,7 @@ using namespace mxfp4moe;
 namespace {
 
 const float kNvQuery = 0.f;  // stands in for the NVFP4 scale pointers of a size query
+constexpr uint32_t kForwardFlags = MXFP4MOE_GATE_UP_SPLIT | MXFP4MOE_ACT_MXFP8 | MXFP4MOE_ACT_MXFP8_SPLIT;
 
 // The layer.  scale2_13 / scale2_2 != nullptr selects NVFP4 weights (E4M3
 // block scales per 16 elements, one second-level scale per expert and
@@ -155,7 +162,11 @@ int forward_impl(const uint16_t* x, const float* router_logits, const uint16_t* 
   if (H <= 0 || I <= 0 || (H & 31) != 0 || (I & 31) != 0) return MXFP4MOE_ERR_SHAPE;
   if (H > MXFP4MOE_MAX_HIDDEN || I > MXFP4MOE_MAX_HIDDEN) return MXFP4MOE_ERR_SHAPE;
   static_assert(MXFP4MOE_MAX_HIDDEN == kMaxHidden, "one bound on H and I");
-  const Layout L = make_layout(T, H, I, E, top_k);
+  const int act_mode = (flags & MXFP4MOE_ACT_MXFP8_SPLIT) ? kActMxfp8Split
+                       : (flags & MXFP4MOE_ACT_MXFP8)     ? kActMxfp8
+                                                          : kActBf16;
+  if (act_mode != kActBf16 && nv) return MXFP4MOE_ERR_ARG;  // NVFP4 weights have no FP4 scaled-MFMA path here
+  const Layout L = make_layout(T, H, I, E, top_k, act_mode != kActBf16);
   if (workspace == nullptr) {
     *workspace_bytes = L.total;
     return MXFP4MOE_OK;
@@ -220,7 +231,14 @@ int forward_impl(const uint16_t* x, const float* router_logits, const uint16_t* 
     g.out = act;
     g.N = (int)(2 * I);
     g.K = (int)H;
-    err = launch_gate_up(g, tt, tb, s);
+    if (act_mode != kActBf16 && tb.max_big > 0) {
+      g.act_mode = act_mode;
+      g.act_codes = reinterpret_cast<const uint8_t*>(ws + L.xq);
+      g.act_scales = reinterpret_cast<const uint8_t*>(ws + L.xqs);
+      err = launch_act_quant(x, (int)T, (int)H, act_mode == kActMxfp8Split, reinterpret_cast<uint8_t*>(ws + L.xq),
+                             reinterpret_cast<uint8_t*>(ws + L.xqs), s);
+    }
+    if (err == hipSuccess) err = launch_gate_up(g, tt, tb, s);
   }
   if (err == hipSuccess) {
     g.wblocks = w2_blocks;
@@ -230,9 +248,15 @@ int forward_impl(const uint16_t* x, const float* router_logits, const uint16_t* 
     g.out = zw;
     g.N = (int)H;
     g.K = (int)I;
+    if (g.act_mode != kActBf16) {
+      g.act_codes = reinterpret_cast<const uint8_t*>(ws + L.aq);
+      g.act_scales = reinterpret_cast<const uint8_t*>(ws + L.aqs);
+      err = launch_act_quant(act, (int)P, (int)I, act_mode == kActMxfp8Split, reinterpret_cast<uint8_t*>(ws + L.aq),
+                             reinterpret_cast<uint8_t*>(ws + L.aqs), s);
+    }
     g.split_gate_up = 0;
     g.scale2 = nv ? scale2_2 : nullptr;
-    err = launch_down(g, tt, tb, s);
+    if (err == hipSuccess) err = launch_down(g, tt, tb, s);
   }
   if (err == hipSuccess) err = launch_combine(zw, y, (int)T, (int)H, (int)top_k, s);
   return err == hipSuccess ? MXFP4MOE_OK : MXFP4MOE_ERR_HIP;
@@ -313,7 +337,7 @@ int moe_mxfp4_forward_ex(const uint16_t* x, const float* router_logits, const ui
                          const uint8_t* w2_scales, const uint16_t* w2_bias, uint16_t* y, int64_t T, int64_t H,
                          int64_t I, int64_t E, int64_t top_k, uint32_t flags, void* workspace,
                          size_t* workspace_bytes, void* stream) {
-  if ((flags & ~(uint32_t)MXFP4MOE_GATE_UP_SPLIT) != 0) return MXFP4MOE_ERR_ARG;
+  if ((flags & ~kForwardFlags) != 0) return MXFP4MOE_ERR_ARG;
   return forward_impl(x, router_logits, nullptr, nullptr, w13_blocks, w13_scales, nullptr, w13_bias, w2_blocks,
                       w2_scales, nullptr, w2_bias, y, T, H, I, E, top_k, flags, workspace, workspace_bytes, stream);
 }
@@ -328,6 +352,17 @@ int moe_nvfp4_forward(const uint16_t* x, const float* router_logits, const uint8
                       w13_bias,
                       w2_blocks, w2_scales, w2_scale2 ? w2_scale2 : &kNvQuery, w2_bias, y, T, H, I, E, top_k, 0u,
                       workspace, workspace_bytes, stream);
+}
+
+int moe_mxfp8_quantize(const uint16_t* src, int64_t rows, int64_t K, int split, uint8_t* codes, uint8_t* scales,
+                       void* stream) {
+  if (rows < 0 || K <= 0 || (K & 31) != 0 || K > ((int64_t)1 << 30) || rows > ((int64_t)1 << 40) / K)
+    return MXFP4MOE_ERR_SHAPE;
+  if (rows == 0) return MXFP4MOE_OK;
+  if (src == nullptr || codes == nullptr || scales == nullptr) return MXFP4MOE_ERR_ARG;
+  if (!aligned16(src) || !aligned16(codes) || ((uintptr_t)scales & 3u) != 0) return MXFP4MOE_ERR_ALIGN;
+  hipError_t err = launch_act_quant(src, (int)rows, (int)K, split != 0, codes, scales, (hipStream_t)stream);
+  return err == hipSuccess ? MXFP4MOE_OK : MXFP4MOE_ERR_HIP;
 }
 
 int moe_mxfp4_router(const uint16_t* x, const uint16_t* router_w, const uint16_t* router_b, int64_t T, int64_t H,
@@ -350,7 +385,7 @@ int moe_mxfp4_forward_router(const uint16_t* x, const uint16_t* router_w, const 
                              const uint8_t* w2_blocks, const uint8_t* w2_scales, const uint16_t* w2_bias, uint16_t* y,
                              int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k, uint32_t flags,
                              void* workspace, size_t* workspace_bytes, void* stream) {
-  if ((flags & ~(uint32_t)MXFP4MOE_GATE_UP_SPLIT) != 0) return MXFP4MOE_ERR_ARG;
+  if ((flags & ~kForwardFlags) != 0) return MXFP4MOE_ERR_ARG;
   if (workspace != nullptr && T > 0 && router_w == nullptr) return MXFP4MOE_ERR_ARG;
   static const uint16_t kRouterQuery = 0;  // stands in for the router pointers of a size query
   return forward_impl(x, nullptr, router_w ? router_w : &kRouterQuery, router_b, w13_blocks, w13_scales, nullptr,

@@ -451,6 +451,188 @@ hipError_t launch_cfg(const mxfp4moe::GemmArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// FP4 scaled-MFMA variant of the wide kernel (opt-in): the same 512-row x
+// 128-token tiles, staging and epilogue, with v_mfma_scale_f32_32x32x64_f8f6f4
+// multiplying the packed E2M1 weights, scaled by their E8M0 bytes, with the
+// tokens as MXFP8 E4M3 codes scaled by their own block bytes (the
+// quantizer's chunk-interleaved rows; kSplit adds a second MFMA for the
+// residual codes).  No weight is converted: the checkpoint's 16-byte group is
+// the A operand.  Operand layouts of the 32x32x64 instruction (measured on
+// gfx950): A lane (r, h) holds row r, K [32h, 32h + 32) of the chunk as 32
+// nibbles, low nibble first, with its scale byte; B lane (n, h) holds token
+// n, K [16h, 16h + 16) in bytes 0..15 and K [32 + 16h, 48 + 16h) in bytes
+// 16..31, with the scale of group h; D as the bf16 32x32 MFMA.
+template <bool kGateUp, bool kSplit>
+__global__ __launch_bounds__(256, 1) void expert_fp4_kernel(mxfp4moe::GemmArgs args) {
+  constexpr int WN = 4, RN = 4, RM = 4, kDepth = 2;
+  constexpr int kThreads = 256;
+  constexpr int BN = WN * RN * 32;
+  constexpr int BM = RM * 32;
+  constexpr int kXSlots = BM * 8;  // 16-byte token slots per chunk (64 high + 64 residual codes per token)
+  constexpr int kWSlots = BN * 2;  // 16-byte weight slots per chunk
+  constexpr int kXPer = kXSlots / kThreads;
+  constexpr int kWPer = kWSlots / kThreads;
+  static_assert(BM * 128 >= RM * 4096 && BN * 32 >= RM * 4096, "epilogue regions");
+  __shared__ __attribute__((aligned(16))) u32x4 xs[2][kXSlots];
+  __shared__ __attribute__((aligned(16))) u32x4 wsm[2][kWSlots];
+  __shared__ uint32_t xsc[2][BM];
+  __shared__ __attribute__((aligned(16))) uint8_t sst[BN * kWideMaxGroups];
+
+  const int N = args.N, K = args.K;
+  const int n_tiles = (N + BN - 1) / BN;
+  int tile, ntile;
+  if (!map_block(*args.num_tiles, n_tiles, tile, ntile)) return;  // uniform per block
+  const int4 tl = reinterpret_cast<const int4*>(args.tiles)[tile];
+  const int e = __builtin_amdgcn_readfirstlane(tl.x);
+  const int row0 = __builtin_amdgcn_readfirstlane(tl.y);
+  const int count = __builtin_amdgcn_readfirstlane(tl.z);
+  const int kgroups = K >> 5;
+  const int nchunks = (kgroups + 1) >> 1;
+  const int niter = (nchunks + kDepth - 1) / kDepth * kDepth;
+  const int t = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int lane = t & 63;
+  const int half = lane >> 5;
+  const int lrow = lane & 31;
+
+  const bool split = kGateUp && args.split_gate_up;  // uniform
+  stage_scales<BN, kThreads>(sst, args, e, ntile, kgroups, t, split);
+
+  // token slot p = t + i*threads -> row p/8, logical column slot_col(row, p%8);
+  // rows past `count` re-read the tile's first row (their columns are never stored)
+  const size_t qrow = (size_t)128 * nchunks;  // code bytes per quantized row
+  const uint8_t* const q = reinterpret_cast<const uint8_t*>(args.act);
+  const uint8_t* xsrc[kXPer];
+#pragma unroll
+  for (int i = 0; i < kXPer; ++i) {
+    const int p = t + i * kThreads;
+    const int r = p >> 3;
+    const int rr = r < count ? r : 0;
+    const size_t src_row = kGateUp ? (size_t)(args.sorted_pairs[row0 + rr] / args.top_k) : (size_t)(row0 + rr);
+    xsrc[i] = q + src_row * qrow + slot_col(r, p & 7) * 16;
+  }
+  // the 4 scale bytes of token (t % BM) per chunk
+  const int st_tok = t & (BM - 1);
+  const int st_rr = st_tok < count ? st_tok : 0;
+  const uint32_t* ssrc = reinterpret_cast<const uint32_t*>(args.act_scales) +
+                         (kGateUp ? (size_t)(args.sorted_pairs[row0 + st_rr] / args.top_k) : (size_t)(row0 + st_rr)) *
+                             nchunks;
+  const uint8_t* wsrc[kWPer];
+#pragma unroll
+  for (int j = 0; j < kWPer; ++j) {
+    int wr = ntile * BN + ((t + j * kThreads) >> 1);
+    wr = w13_row(wr < N ? wr : N - 1, N, split);
+    wsrc[j] = args.wblocks + ((size_t)e * N + wr) * (size_t)(K >> 1);
+  }
+  const int wh = t & 1;
+
+  u32x4 xr[kDepth][kXPer];
+  u32x4 wr[kDepth][kWPer];
+  uint32_t sr[kDepth];
+  auto issue = [&](int c, int d) {
+    c = c < nchunks ? c : nchunks - 1;  // padding iterations re-read the last chunk
+#pragma unroll
+    for (int i = 0; i < kXPer; ++i) xr[d][i] = *reinterpret_cast<const u32x4*>(xsrc[i] + (size_t)c * 128);
+    sr[d] = ssrc[c];
+    int g = 2 * c + wh;
+    g = g < kgroups ? g : g - 1;
+#pragma unroll
+    for (int j = 0; j < kWPer; ++j) wr[d][j] = *reinterpret_cast<const u32x4*>(wsrc[j] + (size_t)g * 16);
+  };
+  auto commit = [&](int d, int stg) {
+#pragma unroll
+    for (int i = 0; i < kXPer; ++i) xs[stg][t + i * kThreads] = xr[d][i];
+#pragma unroll
+    for (int j = 0; j < kWPer; ++j) wsm[stg][t + j * kThreads] = wr[d][j];
+    if (t < BM) xsc[stg][t] = sr[d];
+  };
+
+  const int n_wave = ntile * BN + wave * RN * 32;
+  const int wslot0 = (wave * RN * 32 + lrow) * 2 + half;
+  const uint8_t* srow = sst + staged_row(wave * RN * 32 + lrow, min(BN, N - ntile * BN), split) * kgroups;
+  const int rb_stride = (split ? 16 : 32) * kgroups;
+
+  f32x16 acc[RN][RM];
+#pragma unroll
+  for (int rb = 0; rb < RN; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < RM; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[rb][cb][r] = 0.f;
+
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d) issue(d, d);
+  commit(0, 0);
+  issue(kDepth, 0);
+  __syncthreads();
+
+  for (int c0 = 0; c0 < niter; c0 += kDepth) {
+#pragma unroll
+    for (int u = 0; u < kDepth; ++u) {
+      const int c = c0 + u;
+      commit((u + 1) % kDepth, (c + 1) & 1);
+      issue(c + 1 + kDepth, (u + 1) % kDepth);
+      if (c < nchunks) {
+        const int stg = c & 1;
+        const int g = 2 * c + half;
+        const bool glive = g < kgroups;
+        const int gg = glive ? g : g - 1;
+        mx::i32x8 a[RN];
+        int sa[RN];
+#pragma unroll
+        for (int rb = 0; rb < RN; ++rb) {
+          const u32x4 w = glive ? wsm[stg][wslot0 + rb * 64] : u32x4{0u, 0u, 0u, 0u};
+          a[rb] = mx::i32x8{(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
+          sa[rb] = srow[rb * rb_stride + gg];
+        }
+#pragma unroll
+        for (int cb = 0; cb < RM; ++cb) {
+          const int row = cb * 32 + lrow;
+          const u32x4* xb = xs[stg] + row * 8;
+          const u32x4 h0 = xb[slot_col(row, half)], h1 = xb[slot_col(row, 2 + half)];
+          const uint32_t sw = xsc[stg][row];
+          const mx::i32x8 bh = {(int)h0[0], (int)h0[1], (int)h0[2], (int)h0[3],
+                                (int)h1[0], (int)h1[1], (int)h1[2], (int)h1[3]};
+          const int sbh = (int)((sw >> (8 * half)) & 255u);
+#pragma unroll
+          for (int rb = 0; rb < RN; ++rb)
+            acc[rb][cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[rb], bh, acc[rb][cb], 4, 0, 0, sa[rb], 0,
+                                                                          sbh);
+          if (kSplit) {
+            const u32x4 l0 = xb[slot_col(row, 4 + half)], l1 = xb[slot_col(row, 6 + half)];
+            const mx::i32x8 bl = {(int)l0[0], (int)l0[1], (int)l0[2], (int)l0[3],
+                                  (int)l1[0], (int)l1[1], (int)l1[2], (int)l1[3]};
+            const int sbl = (int)((sw >> (16 + 8 * half)) & 255u);
+#pragma unroll
+            for (int rb = 0; rb < RN; ++rb)
+              acc[rb][cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[rb], bl, acc[rb][cb], 4, 0, 0, sa[rb],
+                                                                            0, sbl);
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  uint8_t* region = wave == 0 ? reinterpret_cast<uint8_t*>(xs[0])
+                  : wave == 1 ? reinterpret_cast<uint8_t*>(xs[1])
+                  : wave == 2 ? reinterpret_cast<uint8_t*>(wsm[0]) : reinterpret_cast<uint8_t*>(wsm[1]);
+  store_epilogue<RN, RM, kGateUp>(args, acc, e, row0, count, n_wave, lane, region);
+}
+
+template <bool kGateUp>
+hipError_t launch_fp4(const mxfp4moe::GemmArgs& a, bool split_act, hipStream_t stream) {
+  constexpr int BN = 512;
+  const long n_tiles = (a.N + BN - 1) / BN;
+  const long blocks = n_tiles * a.max_tiles;
+  if (blocks == 0) return hipSuccess;
+  const long grid = (blocks + kXcds - 1) / kXcds * kXcds;
+  if (split_act)
+    expert_fp4_kernel<kGateUp, true><<<(unsigned)grid, 256, 0, stream>>>(a);
+  else
+    expert_fp4_kernel<kGateUp, false><<<(unsigned)grid, 256, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
 // Streaming kernel for tiles of at most kStreamTokens pairs: decode batches
 // and the smallest per-expert remainders of prefill.  It runs on the 16x16x32
 // bf16 MFMA, whose A operand gives lane l row l%16 and the eight K values of
@@ -922,10 +1104,16 @@ static hipError_t launch_all(GemmArgs a, const TileTables& tt, const TileBounds&
   if (tb.max_big > 0 && a.scale2 != nullptr) return hipErrorInvalidValue;  // NVFP4 runs mid / streaming tiles only
   if (tb.max_big > 0) {
     ProfileScope prof(kGateUp ? kStageGateUpWide : kStageDownWide, stream);
-    a.tiles = tt.big;
-    a.num_tiles = tt.num_big;
-    a.max_tiles = tb.max_big;
-    err = launch_cfg<MX_WIDE, kGateUp>(a, stream);
+    GemmArgs w = a;
+    w.tiles = tt.big;
+    w.num_tiles = tt.num_big;
+    w.max_tiles = tb.max_big;
+    if (a.act_mode != kActBf16) {  // full tiles on the FP4 scaled MFMA over MXFP8 activations
+      w.act = reinterpret_cast<const uint16_t*>(a.act_codes);
+      err = launch_fp4<kGateUp>(w, a.act_mode == kActMxfp8Split, stream);
+    } else {
+      err = launch_cfg<MX_WIDE, kGateUp>(w, stream);
+    }
   }
   if (err == hipSuccess && tb.max_mid > 0) {
     ProfileScope prof(kGateUp ? kStageGateUpMid : kStageDownMid, stream);

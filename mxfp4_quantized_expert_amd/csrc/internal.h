@@ -21,7 +21,8 @@ enum Stage : int {
   kStageDownStream = 10,
   kStageGateUpMid = 11,    // the mid-size remainder launch of gate_up alone
   kStageDownMid = 12,
-  kStageLast = kStageDownMid,
+  kStageActQuant = 13,     // the MXFP8 activation quantizer of the FP4 scaled-MFMA path
+  kStageLast = kStageActQuant,
 };
 
 // Records a HIP event pair around one launch when the benchmark hook asked for
@@ -102,13 +103,27 @@ struct GemmArgs {
   int N, K, top_k, max_tiles;
   int split_gate_up;        // gate_up only: w13 rows stored [I gate rows; I up rows] instead of interleaved
   const float* scale2;      // NVFP4: [E] second-level scale per expert (scales are E4M3 per 16), else nullptr
+  // FP4 scaled-MFMA path for the full tiles (opt-in): the activations of
+  // `act` quantized to MXFP8 by launch_act_quant (codes and scale words).
+  int act_mode;             // kActBf16, kActMxfp8 or kActMxfp8Split
+  const uint8_t* act_codes;
+  const uint8_t* act_scales;
 };
+enum ActMode : int { kActBf16 = 0, kActMxfp8 = 1, kActMxfp8Split = 2 };
 
 // Both GEMM stages launch the wide, mid and streaming kernels over their
 // tables (each launch skipped when its table has no capacity).
 hipError_t launch_gate_up(GemmArgs a, const TileTables& tt, const TileBounds& tb, hipStream_t stream);
 hipError_t launch_down(GemmArgs a, const TileTables& tt, const TileBounds& tb, hipStream_t stream);
 hipError_t launch_combine(const float* zw, uint16_t* y, int T, int H, int top_k, hipStream_t stream);
+
+// MXFP8 activations (single or split) in the FP4 GEMM's chunk-interleaved
+// layout: per row act_quant_row_bytes(K) code bytes and
+// act_quant_scale_row_bytes(K) scale bytes.
+size_t act_quant_row_bytes(int K);
+size_t act_quant_scale_row_bytes(int K);
+hipError_t launch_act_quant(const uint16_t* src, int rows, int K, bool split, uint8_t* codes, uint8_t* scales,
+                            hipStream_t stream);
 
 hipError_t launch_dequant(const uint8_t* blocks, const uint8_t* scales, uint16_t* out, int64_t N, int64_t K,
                           hipStream_t stream);

@@ -13,6 +13,7 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
 
 // E8M0 scale byte as the float operand of the gfx950 scaled converts.  The
 // converts take only the exponent field of this operand, so s << 23 encodes

@@ -118,8 +118,15 @@ def test_forward_argument_checks(lib):
 def test_forward_ex_rejects_unknown_flags(lib):
     n = ctypes.c_size_t(0)
     f = lib.moe_mxfp4_forward_ex
-    assert f(A, A, A, A, A, A, A, A, A, 4, 64, 64, 4, 2, 2, None, ctypes.byref(n), None) == -1
+    assert f(A, A, A, A, A, A, A, A, A, 4, 64, 64, 4, 2, 8, None, ctypes.byref(n), None) == -1
     assert f(A, A, A, A, A, A, A, A, A, 4, 64, 64, 4, 2, 1, None, ctypes.byref(n), None) == 0 and n.value > 0
+    base = n.value
+    # the MXFP8 activation flags need room for the quantized activations
+    for flags in (2, 4, 6, 7):
+        assert f(None, None, None, None, None, None, None, None, None, 4096, 2880, 2880, 128, 4, flags, None,
+                 ctypes.byref(n), None) == 0
+        assert n.value >= binding.workspace_bytes(4096, 2880, 2880, 128, 4) + 4096 * 5760 + 16384 * 5760
+    del base
 
 
 def test_nvfp4_forward_argument_checks(lib):
@@ -163,6 +170,17 @@ def test_forward_router_argument_checks(lib):
     w = [A] * 6
     assert f(A, None, A, *w, A, 4, 64, 64, 4, 2, 0, A, ctypes.byref(big), None) == -1  # no router weights
     assert f(A, A, None, *w, A, 4, 64, 64, 4, 2, 0, A, ctypes.byref(big), None) == -1  # no router bias
-    assert f(A, A, A, *w, A, 4, 64, 64, 4, 2, 2, A, ctypes.byref(big), None) == -1     # unknown flag
+    assert f(A, A, A, *w, A, 4, 64, 64, 4, 2, 8, A, ctypes.byref(big), None) == -1     # unknown flag
     assert f(A, A + 2, A, *w, A, 4, 64, 64, 4, 2, 0, A, ctypes.byref(big), None) == -4  # misaligned router
     assert f(A, A, A, *w, A, 4, 48, 64, 4, 2, 0, A, ctypes.byref(big), None) == -2
+
+
+def test_mxfp8_quantize_argument_checks(lib):
+    f = lib.moe_mxfp8_quantize
+    assert f(A, 4, 48, 1, A, A, None) == -2      # K not a multiple of 32
+    assert f(A, -1, 64, 1, A, A, None) == -2
+    assert f(None, 4, 64, 1, A, A, None) == -1
+    assert f(A, 4, 64, 1, None, A, None) == -1
+    assert f(A + 2, 4, 64, 1, A, A, None) == -4
+    assert f(A, 4, 64, 1, A, A + 2, None) == -4  # scale rows are read as 4-byte words
+    assert f(None, 0, 64, 1, None, None, None) == 0
