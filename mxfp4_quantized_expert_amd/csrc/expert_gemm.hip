@@ -312,11 +312,14 @@ __global__ __launch_bounds__(WN * WM * 64, kMinBlocks) void expert_gemm_kernel(m
   constexpr int kXPer = kXSlots / kThreads;
   constexpr int kWPer = kWSlots / kThreads;
   static_assert(kXSlots % kThreads == 0 && kWSlots % kThreads == 0, "tile / thread mismatch");
-  static_assert(WN * WM == 4 && BM * 128 >= RM * 4096 && BN * 32 >= RM * 4096,
-                "four waves, each with an epilogue region of RM*32*128 bytes");
-  __shared__ __attribute__((aligned(16))) u32x4 xs[2][kXSlots];
-  __shared__ __attribute__((aligned(16))) u32x4 wsm[2][kWSlots];
-  __shared__ __attribute__((aligned(16))) uint8_t sst[BN * kWideMaxGroups];
+  // One LDS arena: two token stages, two weight stages, the scale rows; after
+  // the loop every wave takes an epilogue region of RM*32*128 bytes of it.
+  constexpr int kArena = 2 * kXSlots * 16 + 2 * kWSlots * 16 + BN * kWideMaxGroups;
+  static_assert(WN * WM * RM * 32 * 128 <= kArena, "epilogue regions fit in the arena");
+  __shared__ __attribute__((aligned(16))) u32x4 arena[kArena / 16];
+  u32x4 (*const xs)[kXSlots] = reinterpret_cast<u32x4 (*)[kXSlots]>(arena);
+  u32x4 (*const wsm)[kWSlots] = reinterpret_cast<u32x4 (*)[kWSlots]>(arena + 2 * kXSlots);
+  uint8_t* const sst = reinterpret_cast<uint8_t*>(arena + 2 * kXSlots + 2 * kWSlots);
 
   const int N = args.N, K = args.K;
   const int n_tiles = (N + BN - 1) / BN;
@@ -434,9 +437,7 @@ __global__ __launch_bounds__(WN * WM * 64, kMinBlocks) void expert_gemm_kernel(m
     }
   }
   // every wave has passed the loop's last barrier: the staging buffers are free
-  uint8_t* region = wave == 0 ? reinterpret_cast<uint8_t*>(xs[0])
-                  : wave == 1 ? reinterpret_cast<uint8_t*>(xs[1])
-                  : wave == 2 ? reinterpret_cast<uint8_t*>(wsm[0]) : reinterpret_cast<uint8_t*>(wsm[1]);
+  uint8_t* region = reinterpret_cast<uint8_t*>(arena) + wave * (RM * 32 * 128);
   if (live) store_epilogue<RN, RM, kGateUp>(args, acc, e, row0 + m_wave, count - m_wave, n_wave, lane, region);
 }
 
@@ -1095,7 +1096,9 @@ namespace mxfp4moe {
 // panels of MX_MID_PANEL chunks staged in LDS.
 // stream: 16x16x32 MFMA, 4 waves of 16*MX_STREAM_RN weight rows x (at most 4)
 // tokens, weights streamed in batches of MX_STREAM_BATCH chunks of 128 K.
+#ifndef MX_WIDE
 #define MX_WIDE 4, 1, 4, 4, 2, 1
+#endif
 static_assert(kWideTokens == 128 && kStreamTokens == 4, "tile sizes");
 
 template <bool kGateUp>
