@@ -18,7 +18,7 @@ constexpr int kPerLane = MXFP4MOE_MAX_EXPERTS / 64;
 // descending order; lane j keeps the j-th pick.  The softmax runs over the
 // picks relative to the largest one.
 __device__ void route_row(const float* row, int t, int E, int top_k, int32_t* __restrict__ ids,
-                          float* __restrict__ weights) {
+                          float* __restrict__ weights, int32_t* ids_copy = nullptr) {
   const int lane = mx::lane_id();
   float v[kPerLane];
   uint32_t avail = 0;
@@ -72,6 +72,7 @@ __device__ void route_row(const float* row, int t, int E, int top_k, int32_t* __
   if (lane < top_k) {
     ids[(size_t)t * top_k + lane] = my_e;
     weights[(size_t)t * top_k + lane] = ex / sum;
+    if (ids_copy != nullptr) ids_copy[t * top_k + lane] = my_e;
   }
 }
 
@@ -174,8 +175,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const float* __res
   route_token(logits, t, E, top_k, ids, weights);
 }
 
-constexpr int kGroupThreads = 1024;
-constexpr int kGroupWaves = kGroupThreads / 64;
+constexpr int kGroupThreadsMax = 1024;
 
 // Exclusive prefix sum of vals[0..n) into out[0..n) by wave 0; returns the
 // total to every thread of the block (after the trailing barrier).
@@ -205,35 +205,40 @@ __device__ int block_exclusive_scan_wave0(const int* vals, int* out, int n, int*
 // stable scatter of pair ids into expert order, and the GEMM tile tables: an
 // expert with at least big_tokens pairs goes to wide tiles, one with more than
 // kStreamTokens pairs to mid tiles, the rest to one streaming tile.
-// The scatter walks the pairs in chunks of 1024; inside a wave the lanes with
+// The scatter walks the pairs in chunks of the block size; inside a wave the lanes with
 // the same expert are found by matching the expert id bit by bit with
 // ballots, and the per-wave counts are turned into positions wave by wave, so
 // pairs keep ascending id order inside every expert.
 // With logits != nullptr the block first routes the T tokens itself (one
-// wave per token), saving a launch for small batches.  All waves of a
-// workgroup run on one CU and share its L1, so the barrier after the routing
-// is enough for the block to read the ids it wrote.
+// wave per token), saving a launch for small batches, and keeps the routed
+// ids in LDS for the histogram and the scatter.
+template <int kGroupThreads>
 __global__ __launch_bounds__(kGroupThreads) void group_kernel(const float* __restrict__ logits, int T, int top_k,
                                                               float* __restrict__ weights,
                                                               int32_t* __restrict__ ids, int P, int E,
                                                               int32_t* __restrict__ offsets,
                                                               int32_t* __restrict__ sorted_pairs,
                                                               mxfp4moe::TileTables tt) {
+  constexpr int kGroupWaves = kGroupThreads / 64;
   extern __shared__ int smem[];
   int* cnt = smem;                 // [E]
   int* base = cnt + E;             // [E]
   int* tile_base = base + E;       // [E]
   int* ntile = tile_base + E;      // [E]
   int* wave_cnt = ntile + E;       // [kGroupWaves][E]
+  int* idl = wave_cnt + kGroupWaves * E;  // [P] the routed ids (fused routing only)
   __shared__ int total_slot;
 
+  const int32_t* idsrc = ids;
   if (logits != nullptr) {
-    for (int t = threadIdx.x >> 6; t < T; t += kGroupWaves) route_token(logits, t, E, top_k, ids, weights);
+    for (int t = threadIdx.x >> 6; t < T; t += kGroupWaves)
+      route_row(logits + (size_t)t * E, t, E, top_k, ids, weights, idl);
+    idsrc = idl;  // the block reads the ids it routed from LDS
     __syncthreads();
   }
   for (int e = threadIdx.x; e < E; e += kGroupThreads) cnt[e] = 0;
   __syncthreads();
-  for (int p = threadIdx.x; p < P; p += kGroupThreads) atomicAdd(&cnt[ids[p]], 1);
+  for (int p = threadIdx.x; p < P; p += kGroupThreads) atomicAdd(&cnt[idsrc[p]], 1);
   __syncthreads();
   block_exclusive_scan_wave0(cnt, base, E, &total_slot);
   for (int e = threadIdx.x; e < E; e += kGroupThreads) offsets[e] = base[e];
@@ -292,7 +297,7 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(const float* __res
     __syncthreads();
     const int p = c0 + threadIdx.x;
     const bool valid = p < P;
-    const int e = valid ? ids[p] : 0;
+    const int e = valid ? idsrc[p] : 0;
     uint64_t match = __ballot(valid);
     for (int b = 0; b < nbits; ++b) {
       const bool bit = (e >> b) & 1;
@@ -347,19 +352,27 @@ hipError_t launch_route_proj(const uint16_t* x, const uint16_t* router_w, const 
 
 hipError_t launch_group(const int32_t* ids, int P, int E, int32_t* offsets, int32_t* sorted_pairs,
                         const TileTables& tt, hipStream_t stream) {
-  const size_t smem = (size_t)(4 + kGroupWaves) * E * sizeof(int);
+  constexpr int kThreads = kGroupThreadsMax;
+  const size_t smem = (size_t)(4 + kThreads / 64) * E * sizeof(int);
   ProfileScope prof(kStageGroup, stream);
-  group_kernel<<<1, kGroupThreads, smem, stream>>>(nullptr, 0, 1, nullptr, const_cast<int32_t*>(ids), P, E,
+  group_kernel<kThreads><<<1, kThreads, smem, stream>>>(nullptr, 0, 1, nullptr, const_cast<int32_t*>(ids), P, E,
                                                    offsets, sorted_pairs, tt);
   return hipGetLastError();
 }
 
 hipError_t launch_route_group(const float* logits, int T, int E, int top_k, int32_t* ids, float* weights,
                               int32_t* offsets, int32_t* sorted_pairs, const TileTables& tt, hipStream_t stream) {
-  const size_t smem = (size_t)(4 + kGroupWaves) * E * sizeof(int);
+  // small batches: four waves (cheaper barriers and scans); the routed ids stay in LDS
+  const int P = T * top_k;
   ProfileScope prof(kStageGroup, stream);
-  group_kernel<<<1, kGroupThreads, smem, stream>>>(logits, T, top_k, weights, ids, T * top_k, E, offsets,
-                                                   sorted_pairs, tt);
+  if (P <= 256) {
+    const size_t smem = (size_t)(4 + 4) * E * sizeof(int) + (size_t)P * sizeof(int);
+    group_kernel<256><<<1, 256, smem, stream>>>(logits, T, top_k, weights, ids, P, E, offsets, sorted_pairs, tt);
+  } else {
+    const size_t smem = (size_t)(4 + kGroupThreadsMax / 64) * E * sizeof(int) + (size_t)P * sizeof(int);
+    group_kernel<kGroupThreadsMax><<<1, kGroupThreadsMax, smem, stream>>>(logits, T, top_k, weights, ids, P, E,
+                                                                          offsets, sorted_pairs, tt);
+  }
   return hipGetLastError();
 }
 
