@@ -104,7 +104,7 @@ def test_layer_against_oracle(gpu, act, case):
 
 def test_tile_boundaries_split(gpu):
     # experts on both sides of the 128-pair threshold in one batch
-    counts = [128, 127, 129, 4, 5, 64, 65, 1, 0, 259]
+    counts = [128, 127, 129, 4, 5, 16, 17, 32, 33, 64, 65, 1, 0, 259]
     E = len(counts)
     T = sum(counts)
     spec = W.LAYERS["20b_live"].with_(T=T, H=64, I=96, E=E, top_k=1)

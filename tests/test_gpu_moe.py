@@ -144,9 +144,10 @@ def test_bias_after_scale_identity(gpu):
 def test_tile_boundaries(gpu, path):
     # Expert loads on every side of the tile limits: 128 (one full wide tile),
     # 127 / 129 / 259 (mid tiles, wide tiles with a partial last one), 4 / 5
-    # (largest streaming tile, smallest mid tile), 64 / 65 (one or two mid
+    # (largest streaming tile, smallest mid tile), 16 / 17 / 32 / 33 (one or
+    # several 16-token column blocks of a mid tile), 64 / 65 (one or two mid
     # tiles), 1 and 0.  k = 1 with one dominant logit per token forces them.
-    counts = [128, 127, 129, 4, 5, 64, 65, 1, 0, 259]
+    counts = [128, 127, 129, 4, 5, 16, 17, 32, 33, 64, 65, 1, 0, 259]
     E = len(counts)
     T = sum(counts)
     spec = W.LAYERS["tiny"].with_(T=T, H=64, I=96, E=E, top_k=1)
@@ -173,7 +174,7 @@ def test_split_gate_up_layout(gpu, case):
     # same output, bit for bit, through every kernel (wide, mid and streaming
     # tiles, partial weight-row tiles), and match the oracle.
     if case == "boundaries":
-        counts = [128, 127, 129, 4, 5, 64, 65, 1, 0, 259]
+        counts = [128, 127, 129, 4, 5, 16, 17, 32, 33, 64, 65, 1, 0, 259]
         E = len(counts)
         T = sum(counts)
         spec = W.LAYERS["20b_live"].with_(T=T, H=64, I=96, E=E, top_k=1)
