@@ -656,17 +656,25 @@ hipError_t launch_fp4(const mxfp4moe::GemmArgs& a, bool split_act, hipStream_t s
 // 16-row block for token n, i.e. two gate/up pairs (gate_up) or four
 // consecutive features (down), stored directly.
 //
-// Dynamic LDS: tokens [kStreamTokens][K] bf16 | scales [64*RN][K/32].
-template <int RN, bool kNv = false>
+// With kKSplit = 2 the two waves of a row group take the two halves of K
+// (the first half rounded up to whole batches) and the second wave's sums
+// reach the first through LDS after a barrier, added in that fixed order:
+// twice the blocks for a launch with few weight rows (the down GEMM of a
+// decode batch), and half the serial batches per wave.
+//
+// Dynamic LDS: tokens [kStreamTokens][K] bf16 | scales [BN][K/32] |
+// (kKSplit = 2) the second halves' sums [BN/16 row groups][RN][64 lanes] f32x4.
+template <int RN, bool kNv = false, int kKSplit = 1>
 __host__ __device__ constexpr size_t stream_lds_bytes(int K) {
-  if (kNv) return (size_t)mxfp4moe::kStreamTokens * K * 2 + (size_t)64 * RN * (K / 16);
-  return (size_t)mxfp4moe::kStreamTokens * K * 2 + (size_t)64 * RN * (K / 32);
+  return (size_t)mxfp4moe::kStreamTokens * K * 2 + (size_t)(64 / kKSplit) * RN * (K / (kNv ? 16 : 32)) +
+         (kKSplit == 2 ? (size_t)2 * RN * 64 * 16 : 0);
 }
 
-template <int RN, int kBatch, bool kGateUp, bool kNv>
+template <int RN, int kBatch, bool kGateUp, bool kNv, int kKSplit = 1>
 __global__ __launch_bounds__(256, 5) void expert_stream_kernel(mxfp4moe::GemmArgs args) {
   constexpr int kThreads = 256;
-  constexpr int BN = 64 * RN;
+  constexpr int BN = 64 * RN / kKSplit;
+  static_assert(kKSplit == 1 || kKSplit == 2, "one or two K parts");
   extern __shared__ u32x4 dyn[];
   uint8_t* const lds = reinterpret_cast<uint8_t*>(dyn);
 
@@ -685,22 +693,28 @@ __global__ __launch_bounds__(256, 5) void expert_stream_kernel(mxfp4moe::GemmArg
   const int lane = t & 63;
   const int q = lane >> 4;
   const int lr = lane & 15;
+  const int rgrp = wave / kKSplit, kpart = wave % kKSplit;  // row group, K part
+  // this wave's chunks [c_begin, c_end)
+  const int half = min(nchunks, ((nchunks + 1) / 2 + kBatch - 1) / kBatch * kBatch);
+  const int c_begin = kKSplit == 1 || kpart == 0 ? 0 : half;
+  const int c_end = kKSplit == 1 || kpart == 1 ? nchunks : half;
+  const bool has_work = c_begin < c_end;  // wave-uniform
 
   const bool split = kGateUp && args.split_gate_up;  // uniform
-  const int n_wave = ntile * BN + wave * 16 * RN;
+  const int n_wave = ntile * BN + rgrp * 16 * RN;
   const uint8_t* wrow[RN];
 #pragma unroll
   for (int rb = 0; rb < RN; ++rb) {
     const int r = w13_row(min(n_wave + rb * 16 + lr, N - 1), N, split);  // rows past N: outputs dropped
     wrow[rb] = args.wblocks + ((size_t)e * N + r) * (size_t)(K >> 1);
   }
-  // A group past the last one (K tail, or a padding chunk of the last batch)
-  // reads the last group's weights, scale and token values, which are finite,
-  // and multiplies zero weights.
+  // A group past the wave's last one (K tail, or a padding chunk of its last
+  // batch) re-reads its last chunk's group, whose weights, scale and token
+  // values are finite, and multiplies zero weights.
   auto load_batch = [&](int c0, u32x4 (&w)[kBatch][RN]) {
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
-      const int g = min(4 * (c0 + j) + q, kgroups - 1);
+      const int g = min(4 * min(c0 + j, c_end - 1) + q, kgroups - 1);
 #pragma unroll
       for (int rb = 0; rb < RN; ++rb) w[j][rb] = *reinterpret_cast<const u32x4*>(wrow[rb] + (size_t)g * 16);
     }
@@ -708,7 +722,7 @@ __global__ __launch_bounds__(256, 5) void expert_stream_kernel(mxfp4moe::GemmArg
   // The first batch's weight loads go out before the staging below, so the
   // two round trips to memory overlap.
   u32x4 w_first[kBatch][RN];
-  load_batch(0, w_first);
+  if (has_work) load_batch(c_begin, w_first);
 
   uint16_t* const xl = reinterpret_cast<uint16_t*>(lds);
   uint8_t* const sl = lds + (size_t)mxfp4moe::kStreamTokens * K * 2;
@@ -739,7 +753,8 @@ __global__ __launch_bounds__(256, 5) void expert_stream_kernel(mxfp4moe::GemmArg
   }
   __syncthreads();
 
-  if (n_wave >= N) return;  // wave-uniform; no barrier follows
+  const bool wave_live = n_wave < N && has_work;  // wave-uniform
+  if (kKSplit == 1 && !wave_live) return;          // no barrier follows
   f32x4 acc[RN][2];
 #pragma unroll
   for (int rb = 0; rb < RN; ++rb)
@@ -748,15 +763,15 @@ __global__ __launch_bounds__(256, 5) void expert_stream_kernel(mxfp4moe::GemmArg
   const uint8_t* srow[RN];
 #pragma unroll
   for (int rb = 0; rb < RN; ++rb)
-    srow[rb] = sl + staged_row(wave * 16 * RN + rb * 16 + lr, min(BN, N - ntile * BN), split) * (kNv ? 2 : 1) *
+    srow[rb] = sl + staged_row(rgrp * 16 * RN + rb * 16 + lr, min(BN, N - ntile * BN), split) * (kNv ? 2 : 1) *
                         kgroups;
   const uint16_t* xrow = xl + (lr < count ? lr : 0) * K;
   auto compute_batch = [&](int c0, const u32x4 (&w)[kBatch][RN]) {
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
       const int g0 = 4 * (c0 + j) + q;
-      const bool glive = g0 < kgroups;
-      const int g = glive ? g0 : kgroups - 1;
+      const bool glive = c0 + j < c_end && g0 < kgroups;
+      const int g = min(4 * min(c0 + j, c_end - 1) + q, kgroups - 1);
       bf16x8 b[4];
 #pragma unroll
       for (int s = 0; s < 4; ++s)
@@ -773,11 +788,28 @@ __global__ __launch_bounds__(256, 5) void expert_stream_kernel(mxfp4moe::GemmArg
       }
     }
   };
-  compute_batch(0, w_first);
-  for (int c0 = kBatch; c0 < nchunks; c0 += kBatch) {
-    u32x4 w[kBatch][RN];
-    load_batch(c0, w);
-    compute_batch(c0, w);
+  if (wave_live) {
+    compute_batch(c_begin, w_first);
+    for (int c0 = c_begin + kBatch; c0 < c_end; c0 += kBatch) {
+      u32x4 w[kBatch][RN];
+      load_batch(c0, w);
+      compute_batch(c0, w);
+    }
+  }
+#pragma unroll
+  for (int rb = 0; rb < RN; ++rb) acc[rb][0] = acc[rb][0] + acc[rb][1];  // (even + odd steps) of this K part
+  if (kKSplit == 2) {
+    f32x4* red = reinterpret_cast<f32x4*>(sl + (size_t)BN * (kNv ? 2 : 1) * kgroups);
+    if (kpart == 1) {
+#pragma unroll
+      for (int rb = 0; rb < RN; ++rb) red[(rgrp * RN + rb) * 64 + lane] = acc[rb][0];
+    }
+    __syncthreads();
+    if (kpart == 1 || n_wave >= N) return;
+#pragma unroll
+    for (int rb = 0; rb < RN; ++rb) {
+      acc[rb][0] = acc[rb][0] + red[(rgrp * RN + rb) * 64 + lane];  // first half, then second half
+    }
   }
 
   if (lr >= count) return;
@@ -789,10 +821,10 @@ __global__ __launch_bounds__(256, 5) void expert_stream_kernel(mxfp4moe::GemmArg
     const f32x4 bv = load_bias4(bias, n, N, split);
     const float s2 = kNv ? args.scale2[e] : 1.0f;  // second-level scale, before the bias
     f32x4 v;
-    v[0] = s2 * (acc[rb][0][0] + acc[rb][1][0]) + bv[0];
-    v[1] = s2 * (acc[rb][0][1] + acc[rb][1][1]) + bv[1];
-    v[2] = s2 * (acc[rb][0][2] + acc[rb][1][2]) + bv[2];
-    v[3] = s2 * (acc[rb][0][3] + acc[rb][1][3]) + bv[3];
+    v[0] = s2 * acc[rb][0][0] + bv[0];
+    v[1] = s2 * acc[rb][0][1] + bv[1];
+    v[2] = s2 * acc[rb][0][2] + bv[2];
+    v[3] = s2 * acc[rb][0][3] + bv[3];
     if (kGateUp) {
       const int I = N >> 1;
       const uint32_t packed = mx::pack_bf16x2_rne(swiglu_clamped(v[0], v[1]), swiglu_clamped(v[2], v[3]));
@@ -816,21 +848,29 @@ __global__ __launch_bounds__(256, 5) void expert_stream_kernel(mxfp4moe::GemmArg
 #define MX_STREAM_BATCH 6
 #endif
 
+#ifndef MX_STREAM_KSPLIT_UP
+#define MX_STREAM_KSPLIT_UP 1
+#endif
+#ifndef MX_STREAM_KSPLIT_DOWN
+#define MX_STREAM_KSPLIT_DOWN 2
+#endif
+
 template <bool kGateUp, bool kNv>
 hipError_t launch_stream(const mxfp4moe::GemmArgs& a, hipStream_t stream) {
   constexpr int RN = MX_STREAM_RN;
   constexpr int kBatch = MX_STREAM_BATCH;
-  constexpr int BN = 64 * RN;
+  constexpr int kKSplit = kGateUp ? MX_STREAM_KSPLIT_UP : MX_STREAM_KSPLIT_DOWN;
+  constexpr int BN = 64 * RN / kKSplit;
   const long n_tiles = (a.N + BN - 1) / BN;
   const long blocks = n_tiles * a.max_tiles;
   if (blocks == 0) return hipSuccess;
   const long grid = (blocks + kXcds - 1) / kXcds * kXcds;
-  const size_t lds = stream_lds_bytes<RN, kNv>(a.K);
+  const size_t lds = stream_lds_bytes<RN, kNv, kKSplit>(a.K);
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&expert_stream_kernel<RN, kBatch, kGateUp, kNv>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, (int)stream_lds_bytes<RN, kNv>(mxfp4moe::kMaxHidden));
+      reinterpret_cast<const void*>(&expert_stream_kernel<RN, kBatch, kGateUp, kNv, kKSplit>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, (int)stream_lds_bytes<RN, kNv, kKSplit>(mxfp4moe::kMaxHidden));
   if (attr != hipSuccess) return attr;
-  expert_stream_kernel<RN, kBatch, kGateUp, kNv><<<(unsigned)grid, 256, lds, stream>>>(a);
+  expert_stream_kernel<RN, kBatch, kGateUp, kNv, kKSplit><<<(unsigned)grid, 256, lds, stream>>>(a);
   return hipGetLastError();
 }
 
