@@ -190,13 +190,44 @@ def run_moe(args):
     # else gate_up over the streamed tiles.  Its launches inside the timed
     # region are bracketed with HIP events on the stream they run on.
     dominant = "gate_up_wide" if full_pairs > 0 else "gate_up_stream" if T <= 4 else "gate_up_mid"
-    binding.profile_begin(dominant, args.steps)
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    dom_ms = binding.profile_end(args.steps)
+    if args.graph:
+        # One captured step per weight set, replayed in the timed region; the
+        # dominant launch is timed on eager steps just before (its events
+        # cannot be recorded inside replays).
+        binding.profile_begin(dominant, args.steps)
+        for i in range(args.steps):
+            step(i)
+        torch.cuda.synchronize()
+        dom_ms = binding.profile_end(args.steps)
+        graphs = []
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for c in range(copies):
+                step(c)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        for c in range(copies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(c)
+            graphs.append(g)
+        for i in range(args.warmup):
+            graphs[i % copies].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            graphs[i % copies].replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    else:
+        binding.profile_begin(dominant, args.steps)
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(i)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        dom_ms = binding.profile_end(args.steps)
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     value = T / (ms_per_step / 1e3)
     kms = float(np.mean(dom_ms))
@@ -273,6 +304,7 @@ def run_moe(args):
             "active_experts": n_active,
             "pairs_in_full_tiles": full_pairs,
             "weight_copies_rotated": copies,
+            "hip_graph": bool(args.graph),
             "layer_tflops": layer_tflops,
             "layer_frac_bf16_peak": layer_tflops / PEAK_BF16_TFLOPS,
             "layer_frac_fp4_peak": layer_tflops / PEAK_FP4_TFLOPS,
@@ -401,6 +433,8 @@ def main():
                              "nvfp4_20b_prefill", "nvfp4_120b_prefill", "router_20b_decode", "router_120b_prefill",
                              "dequant_120b", "dequant_host_120b", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of a HIP graph of one layer call instead of eager calls")
     ap.add_argument("--act", default="bf16", choices=["bf16", "mxfp8_split", "mxfp8"],
                     help="activations of the full 128-pair tiles: exact bf16 (default) or the opt-in "
                          "FP4 scaled-MFMA path over MXFP8 activations")
