@@ -93,4 +93,79 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
 
+// Cross-lane steps on the DPP datapath (GFX9 control encodings): a lane
+// reads another lane's register inside one VALU instruction, without a trip
+// through the LDS permute unit.  A wave is four rows of 16 lanes.  Every
+// helper below expects all 64 lanes of the wave to be active.
+constexpr int kDppQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppRowRor4 = 0x124, kDppRowRor8 = 0x128;
+
+// The value of the lane the control selects; 0 where a row shift reaches
+// past the start of the row.
+template <int kCtrl>
+__device__ __forceinline__ int dpp_i32(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, kCtrl, 0xf, 0xf, true);
+}
+
+template <int kCtrl>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t x) {
+  const uint32_t lo = (uint32_t)dpp_i32<kCtrl>((int)(uint32_t)x);
+  const uint32_t hi = (uint32_t)dpp_i32<kCtrl>((int)(uint32_t)(x >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t x, int lane) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, lane);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), lane);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Inclusive prefix sum over the 16 lanes of each row.
+__device__ __forceinline__ int row_inclusive_sum(int x) {
+  x += dpp_i32<kDppRowShr1>(x);
+  x += dpp_i32<kDppRowShr2>(x);
+  x += dpp_i32<kDppRowShr4>(x);
+  x += dpp_i32<kDppRowShr8>(x);
+  return x;
+}
+
+// Inclusive prefix sum over the wave: row scans, then the earlier rows'
+// totals added from scalar reads of lanes 15, 31 and 47.
+__device__ __forceinline__ int wave_inclusive_sum(int x) {
+  x = row_inclusive_sum(x);
+  const int r0 = __builtin_amdgcn_readlane(x, 15);
+  const int r1 = __builtin_amdgcn_readlane(x, 31);
+  const int r2 = __builtin_amdgcn_readlane(x, 47);
+  const int row = lane_id() >> 4;
+  return x + (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
+}
+
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// Largest key of the wave, returned to every lane: butterfly inside each row
+// (every lane then holds its row's largest), then the four rows' values.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
+  k = max_u64(k, dpp_u64<kDppQuadXor1>(k));
+  k = max_u64(k, dpp_u64<kDppQuadXor2>(k));
+  k = max_u64(k, dpp_u64<kDppRowRor4>(k));
+  k = max_u64(k, dpp_u64<kDppRowRor8>(k));
+  return max_u64(max_u64(readlane_u64(k, 0), readlane_u64(k, 16)), max_u64(readlane_u64(k, 32), readlane_u64(k, 48)));
+}
+
+// Sum over the wave in a fixed order (the same bits on every call with the
+// same inputs), returned to every lane.
+__device__ __forceinline__ float wave_sum_f32(float x) {
+  x += __int_as_float(dpp_i32<kDppQuadXor1>(__float_as_int(x)));
+  x += __int_as_float(dpp_i32<kDppQuadXor2>(__float_as_int(x)));
+  x += __int_as_float(dpp_i32<kDppRowRor4>(__float_as_int(x)));
+  x += __int_as_float(dpp_i32<kDppRowRor8>(__float_as_int(x)));
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
 }  // namespace mx

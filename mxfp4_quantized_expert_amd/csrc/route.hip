@@ -13,62 +13,56 @@ namespace {
 constexpr int kRouteThreads = 256;  // four tokens per block, one wave each
 constexpr int kPerLane = MXFP4MOE_MAX_EXPERTS / 64;
 
-// Token t, by one wave.  Lane l holds logits l, l+64, ...; k rounds of a
-// wave-wide argmax (ties to the lower expert index) pick the experts in
-// descending order; lane j keeps the j-th pick.  The softmax runs over the
-// picks relative to the largest one.
+// Selection key of logit v of expert e: larger keys for larger logits and,
+// between equal logits, for the lower expert index.  The float bits are
+// mapped to an unsigned order (sign flipped for non-negative values, all
+// bits for negative ones); -0 takes the key of +0 since the two compare
+// equal.  Every real key exceeds 0, the key of an empty slot.
+__device__ __forceinline__ uint64_t route_key(float v, int e) {
+  uint32_t b = __float_as_uint(v);
+  if ((b << 1) == 0u) b = 0u;
+  b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((uint64_t)b << 32) | (uint32_t)~(uint32_t)e;
+}
+__device__ __forceinline__ float key_logit(uint64_t k) {
+  const uint32_t u = (uint32_t)(k >> 32);
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
+}
+__device__ __forceinline__ int key_expert(uint64_t k) { return (int)~(uint32_t)k; }
+
+// Token t, by one wave (all 64 lanes active).  Lane l holds the keys of
+// experts l, l+64, ...; k rounds of a wave-wide key maximum pick the experts
+// by descending logit (ties to the lower expert index); lane j keeps the
+// j-th pick.  The softmax runs over the picks relative to the largest one.
 __device__ void route_row(const float* row, int t, int E, int top_k, int32_t* __restrict__ ids,
                           float* __restrict__ weights, int32_t* ids_copy = nullptr) {
   const int lane = mx::lane_id();
-  float v[kPerLane];
-  uint32_t avail = 0;
+  uint64_t key[kPerLane];
 #pragma unroll
   for (int i = 0; i < kPerLane; ++i) {
     const int e = lane + 64 * i;
-    v[i] = 0.f;
-    if (e < E) {
-      v[i] = row[e];
-      avail |= 1u << i;
-    }
+    key[i] = e < E ? route_key(row[e], e) : 0ull;
   }
   float my_v = 0.f, v0 = 0.f;
   int my_e = 0;
   for (int j = 0; j < top_k; ++j) {
-    bool have = false;
-    float bv = 0.f;
-    int be = 0;
+    uint64_t best = 0;
 #pragma unroll
-    for (int i = 0; i < kPerLane; ++i) {
-      if ((avail >> i) & 1u) {
-        if (!have || v[i] > bv) {  // strict: the lower index wins ties inside a lane
-          bv = v[i];
-          be = lane + 64 * i;
-          have = true;
-        }
-      }
-    }
+    for (int i = 0; i < kPerLane; ++i) best = mx::max_u64(best, key[i]);
+    best = mx::wave_max_u64(best);
+    const int be = key_expert(best);
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off, 64);
-      const int oe = __shfl_xor(be, off, 64);
-      const int oh = __shfl_xor((int)have, off, 64);
-      if (oh && (!have || ov > bv || (ov == bv && oe < be))) {
-        bv = ov;
-        be = oe;
-        have = true;
-      }
-    }
-    if ((be & 63) == lane) avail &= ~(1u << (be >> 6));
+    for (int i = 0; i < kPerLane; ++i)
+      if (lane + 64 * i == be) key[i] = 0ull;
+    const float bv = key_logit(best);
     if (lane == j) {
       my_v = bv;
       my_e = be;
     }
     if (j == 0) v0 = bv;
   }
-  float ex = lane < top_k ? expf(my_v - v0) : 0.f;
-  float sum = ex;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
+  const float ex = lane < top_k ? expf(my_v - v0) : 0.f;
+  const float sum = mx::wave_sum_f32(ex);
   if (lane < top_k) {
     ids[(size_t)t * top_k + lane] = my_e;
     weights[(size_t)t * top_k + lane] = ex / sum;
@@ -177,41 +171,36 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const float* __res
 
 constexpr int kGroupThreadsMax = 1024;
 
-// Exclusive prefix sum of vals[0..n) into out[0..n) by wave 0; returns the
-// total to every thread of the block (after the trailing barrier).
-__device__ int block_exclusive_scan_wave0(const int* vals, int* out, int n, int* total_slot) {
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
-    int carry = 0;
-    for (int c0 = 0; c0 < n; c0 += 64) {
-      const int e = c0 + lane;
-      const int x = e < n ? vals[e] : 0;
-      int incl = x;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += y;
-      }
-      if (e < n) out[e] = carry + incl - x;
-      carry += __shfl(incl, 63, 64);
-    }
-    if (lane == 0) *total_slot = carry;
+// Mask of the valid lanes of the wave whose expert id equals this lane's,
+// matched bit by bit (nbits bits cover every id) with ballots.
+__device__ __forceinline__ uint64_t same_expert_lanes(int e, bool valid, int nbits) {
+  uint64_t match = __ballot(valid);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t ones = __ballot(valid && bit);
+    match &= bit ? ones : ~ones;
   }
-  __syncthreads();
-  return *total_slot;
+  return match;
 }
 
-// Single workgroup: histogram of experts, exclusive scan into offsets, a
-// stable scatter of pair ids into expert order, and the GEMM tile tables: an
-// expert with at least big_tokens pairs goes to wide tiles, one with more than
-// kStreamTokens pairs to mid tiles, the rest to one streaming tile.
-// The scatter walks the pairs in chunks of the block size; inside a wave the lanes with
-// the same expert are found by matching the expert id bit by bit with
-// ballots, and the per-wave counts are turned into positions wave by wave, so
-// pairs keep ascending id order inside every expert.
-// With logits != nullptr the block first routes the T tokens itself (one
-// wave per token), saving a launch for small batches, and keeps the routed
-// ids in LDS for the histogram and the scatter.
+// Histogram of experts, exclusive scan into offsets, a stable scatter of pair
+// ids into expert order, and the GEMM tile tables: an expert with at least
+// big_tokens pairs goes to wide tiles, one with more than kStreamTokens pairs
+// to mid tiles, the rest to one streaming tile.
+// The pairs are cut into chunks of the block size and each block scatters an
+// equal run of consecutive chunks (one chunk per block when the grid has one
+// block per chunk).  Every block histograms all P ids, counting separately
+// those before its first chunk, so it knows where its pairs start inside
+// each expert without a second launch or scratch memory.  Inside a chunk the
+// lanes of a wave with the same expert are found by matching the expert id
+// bit by bit with ballots, and the per-wave counts are turned into positions
+// wave by wave, so pairs keep ascending id order inside every expert.
+// Wave 0 scans the counts (and, in block 0, the tile counts of the three
+// kinds) in one pass of DPP prefix sums; block 0 writes the offsets and the
+// tile tables.
+// With logits != nullptr (one block only) the block first routes the T
+// tokens itself (one wave per token), saving a launch for small batches, and
+// keeps the routed ids in LDS for the histogram and the scatter.
 template <int kGroupThreads>
 __global__ __launch_bounds__(kGroupThreads) void group_kernel(const float* __restrict__ logits, int T, int top_k,
                                                               float* __restrict__ weights,
@@ -220,14 +209,14 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(const float* __res
                                                               int32_t* __restrict__ sorted_pairs,
                                                               mxfp4moe::TileTables tt) {
   constexpr int kGroupWaves = kGroupThreads / 64;
+  constexpr int kRep = kGroupWaves / 2;  // histogram copies per expert
+  static_assert(kGroupWaves == 4 || kGroupWaves == 16, "block of 4 or 16 waves");
   extern __shared__ int smem[];
-  int* cnt = smem;                 // [E]
-  int* base = cnt + E;             // [E]
-  int* tile_base = base + E;       // [E]
-  int* ntile = tile_base + E;      // [E]
-  int* wave_cnt = ntile + E;       // [kGroupWaves][E]
+  int* cnt = smem;                 // [E] pairs per expert
+  int* base = cnt + E;             // [E] sorted row of this block's next pair of each expert
+  int* before = base + E;          // [E] pairs of each expert before this block's chunks
+  int* wave_cnt = before + E;      // [E][kGroupWaves]; the histogram copies use it first
   int* idl = wave_cnt + kGroupWaves * E;  // [P] the routed ids (fused routing only)
-  __shared__ int total_slot;
 
   const int32_t* idsrc = ids;
   if (logits != nullptr) {
@@ -236,88 +225,146 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(const float* __res
     idsrc = idl;  // the block reads the ids it routed from LDS
     __syncthreads();
   }
-  for (int e = threadIdx.x; e < E; e += kGroupThreads) cnt[e] = 0;
-  __syncthreads();
-  for (int p = threadIdx.x; p < P; p += kGroupThreads) atomicAdd(&cnt[idsrc[p]], 1);
-  __syncthreads();
-  block_exclusive_scan_wave0(cnt, base, E, &total_slot);
-  for (int e = threadIdx.x; e < E; e += kGroupThreads) offsets[e] = base[e];
-  if (threadIdx.x == 0) offsets[E] = P;
-
-  if (tt.big != nullptr) {
-    const int bt = tt.big_tokens;
-    constexpr int st = mxfp4moe::kStreamTokens;
-    // an expert with at least bt pairs: all its pairs in tiles of bt (the
-    // last one partial), so its weights are streamed by one kernel only
-    for (int e = threadIdx.x; e < E; e += kGroupThreads)
-      ntile[e] = (bt > 0 && !tt.no_wide && cnt[e] >= bt) ? (cnt[e] + bt - 1) / bt : 0;
-    __syncthreads();
-    const int n_big = block_exclusive_scan_wave0(ntile, tile_base, E, &total_slot);
-    if (threadIdx.x == 0) *tt.num_big = n_big;
-    for (int e = threadIdx.x; e < E; e += kGroupThreads) {
-      for (int i = 0; i < ntile[e]; ++i)
-        reinterpret_cast<int4*>(tt.big)[tile_base[e] + i] = int4{e, base[e] + i * bt, min(bt, cnt[e] - i * bt), 0};
-    }
-    __syncthreads();
-    // fewer than bt pairs, more than st: mid tiles of at most mt pairs
-    constexpr int mt = mxfp4moe::kMidTokens;
-    const bool mid_on = bt > 0 || tt.no_wide;  // else everything in streaming tiles
-    for (int e = threadIdx.x; e < E; e += kGroupThreads) {
-      const int c = cnt[e];
-      ntile[e] = (mid_on && c > st && (tt.no_wide || c < bt)) ? (c + mt - 1) / mt : 0;
-    }
-    __syncthreads();
-    const int n_mid = block_exclusive_scan_wave0(ntile, tile_base, E, &total_slot);
-    if (threadIdx.x == 0) *tt.num_mid = n_mid;
-    for (int e = threadIdx.x; e < E; e += kGroupThreads) {
-      for (int i = 0; i < ntile[e]; ++i)
-        reinterpret_cast<int4*>(tt.mid)[tile_base[e] + i] = int4{e, base[e] + i * mt, min(mt, cnt[e] - i * mt), 0};
-    }
-    __syncthreads();
-    // at most st pairs: one streaming tile; without full tiles (bt == 0),
-    // every pair in streaming tiles of st
-    for (int e = threadIdx.x; e < E; e += kGroupThreads) {
-      const int c = cnt[e];
-      ntile[e] = mid_on ? (c > 0 && c <= st ? 1 : 0) : (c + st - 1) / st;
-    }
-    __syncthreads();
-    const int n_small = block_exclusive_scan_wave0(ntile, tile_base, E, &total_slot);
-    if (threadIdx.x == 0) *tt.num_small = n_small;
-    for (int e = threadIdx.x; e < E; e += kGroupThreads) {
-      for (int i = 0; i < ntile[e]; ++i)
-        reinterpret_cast<int4*>(tt.small)[tile_base[e] + i] = int4{e, base[e] + i * st, min(st, cnt[e] - i * st), 0};
-    }
-  }
-
+  const int nchunks = (P + kGroupThreads - 1) / kGroupThreads;
+  const int per_block = (nchunks + (int)gridDim.x - 1) / (int)gridDim.x;
+  const int p_begin = min(P, (int)blockIdx.x * per_block * kGroupThreads);
+  const int p_end = min(P, p_begin + per_block * kGroupThreads);
+  const int lane = mx::lane_id();
   const int wave = threadIdx.x >> 6;
   int nbits = 1;
   while ((1 << nbits) < E) ++nbits;
-  for (int c0 = 0; c0 < P; c0 += kGroupThreads) {
+
+  // Histogram in kRep copies per expert, lane l adding to copy l % kRep, so
+  // fewer lanes of one LDS atomic meet on one address (routing skew puts a
+  // popular expert in many lanes); pairs before p_begin in one set of copies,
+  // the rest in another.
+  int* hist_before = wave_cnt;           // [E][kRep]
+  int* hist_rest = wave_cnt + kRep * E;  // [E][kRep]
+  for (int i = threadIdx.x; i < 2 * kRep * E; i += kGroupThreads) wave_cnt[i] = 0;
+  __syncthreads();
+  {
+    constexpr int kHistBatch = 8;  // ids in flight per thread before their atomics
+    const int copy = lane % kRep;
+    for (int p0 = threadIdx.x; p0 < P; p0 += kHistBatch * kGroupThreads) {
+      int ev[kHistBatch];
+#pragma unroll
+      for (int j = 0; j < kHistBatch; ++j) {
+        const int p = p0 + j * kGroupThreads;
+        ev[j] = p < P ? idsrc[p] : -1;
+      }
+#pragma unroll
+      for (int j = 0; j < kHistBatch; ++j) {
+        if (ev[j] >= 0) {
+          int* h = p0 + j * kGroupThreads < p_begin ? hist_before : hist_rest;
+          atomicAdd(&h[ev[j] * kRep + copy], 1);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kGroupThreads) {
+    int sb = 0, sr = 0;
+#pragma unroll
+    for (int r = 0; r < kRep; ++r) {
+      sb += hist_before[e * kRep + r];
+      sr += hist_rest[e * kRep + r];
+    }
+    before[e] = sb;
+    cnt[e] = sb + sr;
+  }
+  __syncthreads();
+
+  if (wave == 0) {
+    const bool tables = tt.big != nullptr && blockIdx.x == 0;
+    const int bt = tables ? tt.big_tokens : 0;
+    const bool wide_on = bt > 0 && !tt.no_wide;
+    const bool mid_on = bt > 0 || tt.no_wide;  // else everything in streaming tiles
+    constexpr int st = mxfp4moe::kStreamTokens;
+    constexpr int mt = mxfp4moe::kMidTokens;
+    int carry = 0, tb = 0, tm = 0, ts = 0;
+    for (int e0 = 0; e0 < E; e0 += 64) {
+      const int e = e0 + lane;
+      const int c = e < E ? cnt[e] : 0;
+      const int ic = mx::wave_inclusive_sum(c);
+      const int start = carry + ic - c;  // expert e's first sorted row
+      if (e < E) {
+        base[e] = start + before[e];
+        if (blockIdx.x == 0) offsets[e] = start;
+      }
+      carry += __builtin_amdgcn_readlane(ic, 63);
+      if (tables) {
+        // an expert with at least bt pairs: all its pairs in tiles of bt (the
+        // last one partial), so its weights are streamed by one kernel only;
+        // fewer than bt, more than st: mid tiles of at most mt pairs; at most
+        // st: one streaming tile; without full tiles (bt == 0) every pair in
+        // streaming tiles of st
+        const int nb = (wide_on && c >= bt) ? (c + bt - 1) / bt : 0;
+        const int nm = (mid_on && c > st && (tt.no_wide || c < bt)) ? (c + mt - 1) / mt : 0;
+        const int ns = mid_on ? (c > 0 && c <= st ? 1 : 0) : (c + st - 1) / st;
+        const int ib = mx::wave_inclusive_sum(nb);
+        const int im = mx::wave_inclusive_sum(nm);
+        const int is = mx::wave_inclusive_sum(ns);
+        int4* big = reinterpret_cast<int4*>(tt.big) + tb + ib - nb;
+        for (int i = 0; i < nb; ++i) big[i] = int4{e, start + i * bt, min(bt, c - i * bt), 0};
+        int4* mid = reinterpret_cast<int4*>(tt.mid) + tm + im - nm;
+        for (int i = 0; i < nm; ++i) mid[i] = int4{e, start + i * mt, min(mt, c - i * mt), 0};
+        int4* small = reinterpret_cast<int4*>(tt.small) + ts + is - ns;
+        for (int i = 0; i < ns; ++i) small[i] = int4{e, start + i * st, min(st, c - i * st), 0};
+        tb += __builtin_amdgcn_readlane(ib, 63);
+        tm += __builtin_amdgcn_readlane(im, 63);
+        ts += __builtin_amdgcn_readlane(is, 63);
+      }
+    }
+    if (lane == 0 && blockIdx.x == 0) {
+      offsets[E] = P;
+      if (tables) {
+        *tt.num_big = tb;
+        *tt.num_mid = tm;
+        *tt.num_small = ts;
+      }
+    }
+  }
+  __syncthreads();
+
+  for (int c0 = p_begin; c0 < p_end; c0 += kGroupThreads) {
     for (int i = threadIdx.x; i < kGroupWaves * E; i += kGroupThreads) wave_cnt[i] = 0;
     __syncthreads();
     const int p = c0 + threadIdx.x;
-    const bool valid = p < P;
+    const bool valid = p < p_end;
     const int e = valid ? idsrc[p] : 0;
-    uint64_t match = __ballot(valid);
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = (e >> b) & 1;
-      const uint64_t ones = __ballot(valid && bit);
-      match &= bit ? ones : ~ones;
-    }
+    const uint64_t match = same_expert_lanes(e, valid, nbits);
     const int rank = mx::lanes_below(match);
-    if (valid && rank == 0) wave_cnt[wave * E + e] = __popcll(match);
+    if (valid && rank == 0) wave_cnt[e * kGroupWaves + wave] = __popcll(match);
     __syncthreads();
-    for (int ee = threadIdx.x; ee < E; ee += kGroupThreads) {
-      int run = base[ee];
-      for (int w = 0; w < kGroupWaves; ++w) {
-        const int c = wave_cnt[w * E + ee];
-        wave_cnt[w * E + ee] = run;
-        run += c;
+    // each expert's per-wave counts -> the waves' first sorted rows
+    if constexpr (kGroupWaves == 16) {
+      // one DPP row per expert: an in-row prefix sum over the 16 waves; the
+      // row's last lane advances the expert's base for the next chunk (the
+      // row's reads of base[] come first in the wave's LDS order)
+      const int n = kGroupWaves * E;
+      for (int i0 = 0; i0 < n; i0 += kGroupThreads) {  // uniform trip count: all lanes run the DPP steps
+        const int i = i0 + (int)threadIdx.x;
+        const int c = i < n ? wave_cnt[i] : 0;
+        const int incl = mx::row_inclusive_sum(c);
+        if (i < n) {
+          const int b = base[i >> 4];
+          wave_cnt[i] = b + incl - c;
+          if ((i & 15) == 15) base[i >> 4] = b + incl;
+        }
       }
-      base[ee] = run;
+    } else {
+      for (int ee = threadIdx.x; ee < E; ee += kGroupThreads) {
+        int run = base[ee];
+        for (int w = 0; w < kGroupWaves; ++w) {
+          const int c = wave_cnt[ee * kGroupWaves + w];
+          wave_cnt[ee * kGroupWaves + w] = run;
+          run += c;
+        }
+        base[ee] = run;
+      }
     }
     __syncthreads();
-    if (valid) sorted_pairs[wave_cnt[wave * E + e] + rank] = p;
+    if (valid) sorted_pairs[wave_cnt[e * kGroupWaves + wave] + rank] = p;
     __syncthreads();
   }
 }
@@ -353,10 +400,12 @@ hipError_t launch_route_proj(const uint16_t* x, const uint16_t* router_w, const 
 hipError_t launch_group(const int32_t* ids, int P, int E, int32_t* offsets, int32_t* sorted_pairs,
                         const TileTables& tt, hipStream_t stream) {
   constexpr int kThreads = kGroupThreadsMax;
-  const size_t smem = (size_t)(4 + kThreads / 64) * E * sizeof(int);
+  const size_t smem = (size_t)(3 + kThreads / 64) * E * sizeof(int);
+  // one block per chunk of kThreads pairs (one block writes the offsets when P == 0)
+  const unsigned grid = P > kThreads ? (unsigned)((P + kThreads - 1) / kThreads) : 1u;
   ProfileScope prof(kStageGroup, stream);
-  group_kernel<kThreads><<<1, kThreads, smem, stream>>>(nullptr, 0, 1, nullptr, const_cast<int32_t*>(ids), P, E,
-                                                   offsets, sorted_pairs, tt);
+  group_kernel<kThreads><<<grid, kThreads, smem, stream>>>(nullptr, 0, 1, nullptr, const_cast<int32_t*>(ids), P, E,
+                                                      offsets, sorted_pairs, tt);
   return hipGetLastError();
 }
 
@@ -366,10 +415,10 @@ hipError_t launch_route_group(const float* logits, int T, int E, int top_k, int3
   const int P = T * top_k;
   ProfileScope prof(kStageGroup, stream);
   if (P <= 256) {
-    const size_t smem = (size_t)(4 + 4) * E * sizeof(int) + (size_t)P * sizeof(int);
+    const size_t smem = (size_t)(3 + 4) * E * sizeof(int) + (size_t)P * sizeof(int);
     group_kernel<256><<<1, 256, smem, stream>>>(logits, T, top_k, weights, ids, P, E, offsets, sorted_pairs, tt);
   } else {
-    const size_t smem = (size_t)(4 + kGroupThreadsMax / 64) * E * sizeof(int) + (size_t)P * sizeof(int);
+    const size_t smem = (size_t)(3 + kGroupThreadsMax / 64) * E * sizeof(int) + (size_t)P * sizeof(int);
     group_kernel<kGroupThreadsMax><<<1, kGroupThreadsMax, smem, stream>>>(logits, T, top_k, weights, ids, P, E,
                                                                           offsets, sorted_pairs, tt);
   }
