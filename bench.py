@@ -264,7 +264,7 @@ def run_moe(args):
         per_unit = (f"{w13_b} B of packed w13 per expert x {n_exp} + x {rows_in} B + a {rows_out} B")
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = measured_traffic(args.workload, dominant)
-    roof["kernel"] = {"gate_up_wide": ("expert_fp4_kernel" if args.act != "bf16" else "expert_gemm_kernel")
+    roof["kernel"] = {"gate_up_wide": ("expert_fp4_kernel" if args.act != "bf16" else "expert_wide_kernel")
                                        + " (gate_up, full 128-pair tiles)",
                       "gate_up_mid": "expert_mid_kernel (gate_up, tiles of 5..64 pairs)",
                       "gate_up_stream": "expert_stream_kernel (gate_up, tiles of at most 4 pairs)"}[dominant]

@@ -132,23 +132,22 @@ __device__ __forceinline__ bool map_block(int num_tiles, int n_tiles, int& tile,
   return true;
 }
 
-// One 64-wide K chunk of MFMA work for a wave: for each of the four K steps,
-// RN x RM MFMAs.  All LDS reads of the chunk are issued first (the scheduling
-// barrier keeps the compiler from sinking them next to their uses), and the
-// converts producing step s+1's weight fragments, written to the other half
-// of a double buffer, are interleaved with step s's MFMAs so the matrix core
-// does not wait for a burst of conversions.
-template <int RN, int RM>
-__device__ __forceinline__ void chunk_mma(f32x16 (&acc)[RN][RM], const u32x4* __restrict__ xb,
-                                          const u32x4 (&w)[RN], const float (&sc)[RN], int lrow, int half) {
-  bf16x8 b[4][RM];
-#pragma unroll
-  for (int cb = 0; cb < RM; ++cb) {
-    const int row = cb * 32 + lrow;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) b[s][cb] = __builtin_bit_cast(bf16x8, xb[row * 8 + slot_col(row, half * 4 + s)]);
-  }
-  __builtin_amdgcn_sched_barrier(0);
+// One 64-wide K chunk of MFMA work for a wave from operands in registers:
+// for each of the four K steps, RN x RM MFMAs over the token fragments b
+// (step s, token block cb).  The converts producing step s+1's weight
+// fragments, written to the other half of a double buffer, are interleaved
+// with step s's MFMAs so the matrix core does not wait for a burst of
+// conversions.
+struct NoExtra {
+  __device__ void operator()(int) const {}
+};
+
+// `extra(k)` runs right after the k-th MFMA of the chunk (k = 0 .. 4*RN*RM-1),
+// so a caller can spread other instructions between the MFMAs.
+template <int RN, int RM, typename Extra = NoExtra>
+__device__ __forceinline__ void chunk_mma_regs(f32x16 (&acc)[RN][RM], const bf16x8 (&b)[4][RM],
+                                               const u32x4 (&w)[RN], const float (&sc)[RN],
+                                               Extra extra = Extra()) {
   u32x4 a[2][RN];
 #pragma unroll
   for (int rb = 0; rb < RN; ++rb) a[0][rb] = mx::fp4x8_to_bf16x8(w[rb][0], sc[rb]);
@@ -169,6 +168,7 @@ __device__ __forceinline__ void chunk_mma(f32x16 (&acc)[RN][RM], const u32x4* __
       const int rb = i % RN, cb = i / RN;
       acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mx::as_bf16x8(a[s & 1][rb]), b[s][cb], acc[rb][cb], 0, 0, 0);
       if (s + 1 < 4 && i < 4 * RN) convert(s + 1, i);
+      extra(s * RN * RM + i);
     }
     if (s + 1 < 4) {
 #pragma unroll
@@ -177,21 +177,28 @@ __device__ __forceinline__ void chunk_mma(f32x16 (&acc)[RN][RM], const u32x4* __
   }
 }
 
-// The expert GEMM kernel.
-//
-// One wave per SIMD in the wide configuration (several per SIMD in the
-// streaming one), each computing a (32*RN) x (32*RM) tile with its
-// accumulators in registers; WN waves stack along the weight rows, so a block
-// covers (32*RN*WN) weight rows x (32*RM) tokens and every staged token chunk
-// feeds WN waves.  Per 64-wide K chunk a block moves BM*128 bytes of tokens
-// and BN*32 bytes of packed weights from global memory: each thread loads its
-// share of chunk c+kDepth into a register ring while the waves run MFMA on
-// chunk c from LDS; all loads of a wave have the same age, so they complete in
-// order without draining the ring.  Staged chunks are written to the spare of
-// two LDS stages; one barrier per chunk.  The scale bytes of the block's
-// weight rows are staged once.  Tiles always hold RM*32 live tokens except the
-// remainder tiles of the streaming configuration (RM = 1), whose dead token
-// columns are computed and dropped.
+// The token fragments of one chunk from a staged token slab xb (RM blocks of
+// 32 rows, 128 bytes each): lane (r, h) takes row r of block cb, 16-byte slot
+// 4h + s for step s.
+template <int RM>
+__device__ __forceinline__ void read_token_frags(bf16x8 (&b)[4][RM], const u32x4* __restrict__ xb, int lrow,
+                                                 int half) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+#pragma unroll
+    for (int cb = 0; cb < RM; ++cb) {
+      const int row = cb * 32 + lrow;
+      b[s][cb] = __builtin_bit_cast(bf16x8, xb[row * 8 + slot_col(row, half * 4 + s)]);
+    }
+  }
+}
+
+// Full tiles (the wide kernel): one wave per SIMD, each computing a
+// (32*RN) x (32*RM) tile with its accumulators in registers; WN waves stack
+// along the weight rows, so a block covers (32*RN*WN) weight rows x (32*RM)
+// tokens and every staged token chunk feeds WN waves.  Per 64-wide K chunk a
+// block moves BM*128 bytes of tokens and BN*32 bytes of packed weights from
+// global memory.  The scale bytes of the block's weight rows are staged once.
 constexpr int kWideMaxGroups = 128;  // K <= 4096
 
 // Scale bytes of a block's BN weight rows, row-major as in memory: the rows
@@ -302,24 +309,62 @@ __device__ __forceinline__ void store_epilogue(const mxfp4moe::GemmArgs& args, c
   }
 }
 
-template <int WN, int WM, int RN, int RM, int kDepth, int kMinBlocks, bool kGateUp>
-__global__ __launch_bounds__(WN * WM * 64, kMinBlocks) void expert_gemm_kernel(mxfp4moe::GemmArgs args) {
+// 16 bytes per lane from global memory straight into LDS (the load unit
+// writes lane l's bytes at lds + 16 * l; lds is the same for the whole wave).
+__device__ __forceinline__ void load_lds16(const void* src, u32x4* lds) {
+  __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
+}
+
+// Waits until at most kVm of this wave's vector-memory loads are in flight
+// and its LDS operations are done, then joins the block barrier.  The empty
+// asm statements keep the compiler from moving memory accesses across it
+// (the barrier builtin alone is not a memory fence to the compiler).
+template <int kVm>
+__device__ __forceinline__ void wait_loads_then_barrier() {
+  static_assert(kVm >= 0 && kVm < 64, "vmcnt field");
+  __builtin_amdgcn_sched_barrier(0);  // nothing (MFMAs included) is scheduled across the wait
+  asm volatile("" ::: "memory");
+  // s_waitcnt fields: vmcnt bits 3:0 and 15:14, expcnt 6:4 (7: no wait), lgkmcnt 11:8 (0)
+  __builtin_amdgcn_s_waitcnt((kVm & 15) | ((kVm >> 4) << 14) | (7 << 4));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// The wide kernel.  Operand chunks move from global memory to LDS by the
+// load unit itself (global_load_lds_dwordx4: 16 bytes per lane, written at
+// the wave's LDS address + 16 * lane; no staging registers, no LDS stores in
+// the wave's stream), three LDS stages deep, and each wave reads its
+// operands of chunk c+1 (weight groups, scale bytes, token fragments) from
+// LDS into a second register set while chunk c runs on the matrix core.
+// Per chunk c: wait for this wave's loads of chunk c+1 (those of chunk c+2
+// stay in flight) and for its reads of chunk c, barrier (every wave's share
+// of chunk c+1 is in LDS; every wave is done with chunk c's stage), then
+// the 64 MFMAs of chunk c from registers, with the loads of chunk c+3 into
+// chunk c's stage and the reads of chunk c+1 spread between them, one after
+// every other MFMA.  Issued as a burst, 32 memory instructions would stall
+// the wave (and leave the matrix core idle) until the LDS queue drains;
+// spread out, they issue while earlier MFMAs run.  All waits sit at the
+// barrier and cover work issued a whole chunk earlier.  While LDS-DMA loads
+// are in flight the compiler only waits for all LDS reads at once, which
+// this order makes free.
+template <int WN, int WM, int RN, int RM, bool kGateUp>
+__global__ __launch_bounds__(WN * WM * 64, 1) void expert_wide_kernel(mxfp4moe::GemmArgs args) {
   constexpr int kThreads = WN * WM * 64;
   constexpr int BN = WN * RN * 32;
   constexpr int BM = WM * RM * 32;
-  constexpr int kXSlots = BM * 8;  // 16-byte token slots per chunk
-  constexpr int kWSlots = BN * 2;  // 16-byte weight slots per chunk (one 32-code group each)
+  constexpr int kXSlots = BM * 8;
+  constexpr int kWSlots = BN * 2;
   constexpr int kXPer = kXSlots / kThreads;
   constexpr int kWPer = kWSlots / kThreads;
   static_assert(kXSlots % kThreads == 0 && kWSlots % kThreads == 0, "tile / thread mismatch");
-  // One LDS arena: two token stages, two weight stages, the scale rows; after
-  // the loop every wave takes an epilogue region of RM*32*128 bytes of it.
-  constexpr int kArena = 2 * kXSlots * 16 + 2 * kWSlots * 16 + BN * kWideMaxGroups;
+  constexpr int kStages = 3;              // LDS stages: chunk c+3 loads while c+1 is read and c runs
+  constexpr int kLoads = kXPer + kWPer;  // loads per thread per chunk
+  constexpr int kStage = kXSlots + kWSlots;  // 16-byte slots per stage
+  constexpr int kArena = kStages * kStage * 16 + BN * kWideMaxGroups;
   static_assert(WN * WM * RM * 32 * 128 <= kArena, "epilogue regions fit in the arena");
   __shared__ __attribute__((aligned(16))) u32x4 arena[kArena / 16];
-  u32x4 (*const xs)[kXSlots] = reinterpret_cast<u32x4 (*)[kXSlots]>(arena);
-  u32x4 (*const wsm)[kWSlots] = reinterpret_cast<u32x4 (*)[kWSlots]>(arena + 2 * kXSlots);
-  uint8_t* const sst = reinterpret_cast<uint8_t*>(arena + 2 * kXSlots + 2 * kWSlots);
+  uint8_t* const sst = reinterpret_cast<uint8_t*>(arena + kStages * kStage);
 
   const int N = args.N, K = args.K;
   const int n_tiles = (N + BN - 1) / BN;
@@ -331,10 +376,9 @@ __global__ __launch_bounds__(WN * WM * 64, kMinBlocks) void expert_gemm_kernel(m
   const int count = __builtin_amdgcn_readfirstlane(tl.z);
   const int kgroups = K >> 5;
   const int nchunks = (kgroups + 1) >> 1;
-  const int niter = (nchunks + kDepth - 1) / kDepth * kDepth;  // padded: every iteration is branch-free
   const int t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int wn = wave % WN, wm = wave / WN;  // the wave's weight-row block and token block
+  const int wn = wave % WN, wm = wave / WN;
   const int lane = t & 63;
   const int half = lane >> 5;
   const int lrow = lane & 31;
@@ -366,35 +410,30 @@ __global__ __launch_bounds__(WN * WM * 64, kMinBlocks) void expert_gemm_kernel(m
   }
   const int wh = t & 1;
 
-  u32x4 xr[kDepth][kXPer];
-  u32x4 wr[kDepth][kWPer];
-  auto issue = [&](int c, int d) {
-    c = c < nchunks ? c : nchunks - 1;  // padding iterations re-read the last chunk
+  // chunk c (the last chunk again past the end) into stage st; lane l of the
+  // wave lands in slot wave*64 + l (+ i*threads), as the register path stores it
+  auto issue = [&](int c, int st) {
+    c = c < nchunks ? c : nchunks - 1;
+    u32x4* xs = arena + st * kStage + wave * 64;
+    u32x4* ws = xs + kXSlots;
 #pragma unroll
     for (int i = 0; i < kXPer; ++i) {
       // K tail: the missing half chunk re-reads the first half (its weights are zero)
       const int koff = (c * 64 + xcol[i] < K) ? c * 64 : c * 64 - 32;
-      xr[d][i] = *reinterpret_cast<const u32x4*>(xsrc[i] + koff);
+      load_lds16(xsrc[i] + koff, xs + i * kThreads);
     }
     int g = 2 * c + wh;
     g = g < kgroups ? g : g - 1;
 #pragma unroll
-    for (int j = 0; j < kWPer; ++j) wr[d][j] = *reinterpret_cast<const u32x4*>(wsrc[j] + (size_t)g * 16);
-  };
-  auto commit = [&](int d, int st) {
-#pragma unroll
-    for (int i = 0; i < kXPer; ++i) xs[st][t + i * kThreads] = xr[d][i];
-#pragma unroll
-    for (int j = 0; j < kWPer; ++j) wsm[st][t + j * kThreads] = wr[d][j];
+    for (int j = 0; j < kWPer; ++j) load_lds16(wsrc[j] + (size_t)g * 16, ws + j * kThreads);
   };
 
-  // compute-side constants
-  const int n_wave = ntile * BN + wn * RN * 32;
   const int wslot0 = (wn * RN * 32 + lrow) * 2 + half;
   const uint8_t* srow = sst + staged_row(wn * RN * 32 + lrow, min(BN, N - ntile * BN), split) * kgroups;
+  const int n_wave = ntile * BN + wn * RN * 32;
   const int m_wave = wm * RM * 32;
-  const bool live = m_wave < count;  // wave-uniform: token blocks past the tile's pairs skip their MFMAs
-  const int rb_stride = (split ? 16 : 32) * kgroups;  // staged_row(x + 32) = staged_row(x) + 16 when split
+  const bool live = WM == 1 || m_wave < count;  // wave-uniform; a tile holds at least one pair
+  const int rb_stride = (split ? 16 : 32) * kgroups;
 
   f32x16 acc[RN][RM];
 #pragma unroll
@@ -404,51 +443,124 @@ __global__ __launch_bounds__(WN * WM * 64, kMinBlocks) void expert_gemm_kernel(m
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[rb][cb][r] = 0.f;
 
+  // the operands of one chunk in registers, as read (nothing computed from
+  // them until the chunk runs, a chunk later)
+  struct Ops {
+    u32x4 w[RN];
+    uint32_t sb[RN];  // E8M0 scale bytes
+    bf16x8 b[4][RM];
+  };
+  auto read_ops = [&](Ops& o, int c, int st) {
+    c = c < nchunks ? c : nchunks - 1;  // past the end: a harmless re-read
+    const u32x4* xs = arena + st * kStage;
+    const u32x4* wsm = xs + kXSlots;
+    const int g = 2 * c + half;
+    const int gg = g < kgroups ? g : g - 1;
 #pragma unroll
-  for (int d = 0; d < kDepth; ++d) issue(d, d);
-  commit(0, 0);
-  issue(kDepth, 0);
-  __syncthreads();  // also publishes the scale table
-
-  for (int c0 = 0; c0 < niter; c0 += kDepth) {
+    for (int rb = 0; rb < RN; ++rb) {
+      o.w[rb] = wsm[wslot0 + rb * 64];
+      o.sb[rb] = srow[rb * rb_stride + gg];
+    }
+    read_token_frags<RM>(o.b, xs + m_wave * 8, lrow, half);
+  };
+  // load k (0 .. kLoads-1) of chunk c into stage st
+  auto issue_one = [&](int c, int st, int k) {
+    c = c < nchunks ? c : nchunks - 1;
+    u32x4* xs = arena + st * kStage + wave * 64;
+    if (k < kXPer) {
+      const int koff = (c * 64 + xcol[k] < K) ? c * 64 : c * 64 - 32;
+      load_lds16(xsrc[k] + koff, xs + k * kThreads);
+    } else {
+      int g = 2 * c + wh;
+      g = g < kgroups ? g : g - 1;
+      load_lds16(wsrc[k - kXPer] + (size_t)g * 16, xs + kXSlots + (k - kXPer) * kThreads);
+    }
+  };
+  // LDS read j of chunk c's operands (weights, scale bytes, token fragments) from stage st
+  constexpr int kReads = 2 * RN + 4 * RM;
+  auto read_one = [&](Ops& o, int c, int st, int j) {
+    c = c < nchunks ? c : nchunks - 1;
+    const u32x4* xs = arena + st * kStage;
+    const int g = 2 * c + half;
+    const int gg = g < kgroups ? g : g - 1;
+    if (j < RN) {
+      o.w[j] = xs[kXSlots + wslot0 + j * 64];
+    } else if (j < 2 * RN) {
+      o.sb[j - RN] = srow[(j - RN) * rb_stride + gg];
+    } else {
+      const int s = (j - 2 * RN) / RM, cb = (j - 2 * RN) % RM;
+      const int row = cb * 32 + lrow;
+      o.b[s][cb] = __builtin_bit_cast(bf16x8, xs[m_wave * 8 + row * 8 + slot_col(row, half * 4 + s)]);
+    }
+  };
+  // chunk c from registers `cur` (stage st = c % kStages, a constant at every
+  // call site); chunk c+1's operands into `nxt`; chunk c+kStages into
+  // chunk c's stage.  The loads and reads are spread through the chunk's
+  // MFMAs, one after every other MFMA, so the wave never stalls on a burst of
+  // memory instructions while the matrix core idles.
+  auto step = [&](int c, int st, const Ops& cur, Ops& nxt) {
+    // this wave's loads of chunk c+1 are done once at most the loads of the
+    // chunks after it are in flight
+    wait_loads_then_barrier<(kStages - 2) * kLoads>();
+    if (live) {
+      static_assert(2 * (kLoads + kReads) <= 4 * RN * RM, "room between the MFMAs");
+      auto extra = [&](int k) {
+        if (k % 2 != 0) return;
+        const int op = k / 2;
+        if (op < kLoads) issue_one(c + kStages, st, op);
+        else if (op < kLoads + kReads) read_one(nxt, c + 1, (st + 1) % kStages, op - kLoads);
+        else return;
+        __builtin_amdgcn_sched_barrier(0);  // keep the order: the compiler would bunch the MFMAs
+      };
+      // K tail: the group past K multiplies zero weights
+      const bool glive = 2 * c + half < kgroups;
+      u32x4 w[RN];
+      float sc[RN];
 #pragma unroll
-    for (int u = 0; u < kDepth; ++u) {
-      const int c = c0 + u;
-      // stage chunk c+1 (register slot (u+1)%kDepth) into the spare LDS stage,
-      // then refill that slot with chunk c+1+kDepth
-      commit((u + 1) % kDepth, (c + 1) & 1);
-      issue(c + 1 + kDepth, (u + 1) % kDepth);
-      if (c < nchunks && live) {
-        const int st = c & 1;
-        const int g = 2 * c + half;
-        const bool glive = g < kgroups;
-        const int gg = glive ? g : g - 1;
-        u32x4 w[RN];
-        float sc[RN];
-#pragma unroll
-        for (int rb = 0; rb < RN; ++rb) {
-          w[rb] = wsm[st][wslot0 + rb * 64];
-          sc[rb] = mx::e8m0_operand(srow[rb * rb_stride + gg]);
-          if (!glive) w[rb] = u32x4{0u, 0u, 0u, 0u};
-        }
-        chunk_mma<RN, RM>(acc, xs[st] + m_wave * 8, w, sc, lrow, half);
+      for (int rb = 0; rb < RN; ++rb) {
+        w[rb] = glive ? cur.w[rb] : u32x4{0u, 0u, 0u, 0u};
+        sc[rb] = mx::e8m0_operand(cur.sb[rb]);
       }
-      __syncthreads();
+      chunk_mma_regs<RN, RM>(acc, cur.b, w, sc, extra);
+    } else {
+      issue(c + kStages, st);
+    }
+  };
+  Ops ops0, ops1;
+#pragma unroll
+  for (int c = 0; c < kStages; ++c) issue(c, c);
+  wait_loads_then_barrier<(kStages - 1) * kLoads>();  // chunk 0 (and the scale table) landed
+  if (live) read_ops(ops0, 0, 0);
+  // trips of 2*kStages chunks: the register set and the stage of every step
+  // are constants; then the remaining steps one by one
+  constexpr int kTrip = 2 * kStages;
+  const int nfull = nchunks / kTrip * kTrip;
+  for (int c0 = 0; c0 < nfull; c0 += kTrip) {
+#pragma unroll
+    for (int u = 0; u < kTrip; u += 2) {
+      step(c0 + u, u % kStages, ops0, ops1);
+      step(c0 + u + 1, (u + 1) % kStages, ops1, ops0);
     }
   }
-  // every wave has passed the loop's last barrier: the staging buffers are free
+#pragma unroll
+  for (int u = 0; u < kTrip - 1; u += 2) {
+    if (nfull + u < nchunks) step(nfull + u, u % kStages, ops0, ops1);
+    if (nfull + u + 1 < nchunks) step(nfull + u + 1, (u + 1) % kStages, ops1, ops0);
+  }
+  // the chunks issued past the end land before the arena is reused
+  wait_loads_then_barrier<0>();
   uint8_t* region = reinterpret_cast<uint8_t*>(arena) + wave * (RM * 32 * 128);
   if (live) store_epilogue<RN, RM, kGateUp>(args, acc, e, row0 + m_wave, count - m_wave, n_wave, lane, region);
 }
 
-template <int WN, int WM, int RN, int RM, int kDepth, int kMinBlocks, bool kGateUp>
-hipError_t launch_cfg(const mxfp4moe::GemmArgs& a, hipStream_t stream) {
+template <int WN, int WM, int RN, int RM, bool kGateUp>
+hipError_t launch_wide(const mxfp4moe::GemmArgs& a, hipStream_t stream) {
   constexpr int BN = WN * RN * 32;
   const long n_tiles = (a.N + BN - 1) / BN;
   const long blocks = n_tiles * a.max_tiles;
   if (blocks == 0) return hipSuccess;
   const long grid = (blocks + kXcds - 1) / kXcds * kXcds;
-  expert_gemm_kernel<WN, WM, RN, RM, kDepth, kMinBlocks, kGateUp><<<(unsigned)grid, WN * WM * 64, 0, stream>>>(a);
+  expert_wide_kernel<WN, WM, RN, RM, kGateUp><<<(unsigned)grid, WN * WM * 64, 0, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -1136,9 +1248,6 @@ namespace mxfp4moe {
 // panels of MX_MID_PANEL chunks staged in LDS.
 // stream: 16x16x32 MFMA, 4 waves of 16*MX_STREAM_RN weight rows x (at most 4)
 // tokens, weights streamed in batches of MX_STREAM_BATCH chunks of 128 K.
-#ifndef MX_WIDE
-#define MX_WIDE 4, 1, 4, 4, 2, 1
-#endif
 static_assert(kWideTokens == 128 && kStreamTokens == 4, "tile sizes");
 
 template <bool kGateUp>
@@ -1155,7 +1264,7 @@ static hipError_t launch_all(GemmArgs a, const TileTables& tt, const TileBounds&
       w.act = reinterpret_cast<const uint16_t*>(a.act_codes);
       err = launch_fp4<kGateUp>(w, a.act_mode == kActMxfp8Split, stream);
     } else {
-      err = launch_cfg<MX_WIDE, kGateUp>(w, stream);
+      err = launch_wide<4, 1, 4, 4, kGateUp>(w, stream);
     }
   }
   if (err == hipSuccess && tb.max_mid > 0) {
