@@ -200,6 +200,8 @@ __device__ __forceinline__ void read_token_frags(bf16x8 (&b)[4][RM], const u32x4
 // block moves BM*128 bytes of tokens and BN*32 bytes of packed weights from
 // global memory.  The scale bytes of the block's weight rows are staged once.
 constexpr int kWideMaxGroups = 128;  // K <= 4096
+constexpr int kFp4StageBytes = (128 * 8 + 512 * 2) * 16 + 256 * 4;  // one LDS stage of the FP4 kernel
+constexpr int kFp4MaxLds = 160 * 1024;                              // LDS per workgroup on gfx950
 
 // Scale bytes of a block's BN weight rows, row-major as in memory: the rows
 // are one contiguous, 32-byte aligned range (row counts and tile starts are
@@ -564,20 +566,31 @@ hipError_t launch_wide(const mxfp4moe::GemmArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// 4 bytes per lane from global memory straight into LDS (lane l's word at lds + 4 * l).
+__device__ __forceinline__ void load_lds4(const void* src, uint32_t* lds) {
+  __builtin_amdgcn_global_load_lds(src, lds, 4, 0, 0);
+}
+
 // FP4 scaled-MFMA variant of the wide kernel (opt-in): the same 512-row x
-// 128-token tiles, staging and epilogue, with v_mfma_scale_f32_32x32x64_f8f6f4
-// multiplying the packed E2M1 weights, scaled by their E8M0 bytes, with the
-// tokens as MXFP8 E4M3 codes scaled by their own block bytes (the
-// quantizer's chunk-interleaved rows; kSplit adds a second MFMA for the
-// residual codes).  No weight is converted: the checkpoint's 16-byte group is
-// the A operand.  Operand layouts of the 32x32x64 instruction (measured on
-// gfx950): A lane (r, h) holds row r, K [32h, 32h + 32) of the chunk as 32
-// nibbles, low nibble first, with its scale byte; B lane (n, h) holds token
-// n, K [16h, 16h + 16) in bytes 0..15 and K [32 + 16h, 48 + 16h) in bytes
-// 16..31, with the scale of group h; D as the bf16 32x32 MFMA.
-template <bool kGateUp, bool kSplit>
+// 128-token tiles, staging, read-ahead and epilogue, with
+// v_mfma_scale_f32_32x32x64_f8f6f4 multiplying the packed E2M1 weights,
+// scaled by their E8M0 bytes, with the tokens as MXFP8 E4M3 codes scaled by
+// their own block bytes (the quantizer's chunk-interleaved rows; kSplit adds a
+// second MFMA for the residual codes).  No weight is converted: the
+// checkpoint's 16-byte group is the A operand.  Operand layouts of the
+// 32x32x64 instruction (measured on gfx950): A lane (r, h) holds row r, K
+// [32h, 32h + 32) of the chunk as 32 nibbles, low nibble first, with its
+// scale byte; B lane (n, h) holds token n, K [16h, 16h + 16) in bytes 0..15
+// and K [32 + 16h, 48 + 16h) in bytes 16..31, with the scale of group h; D as
+// the bf16 32x32 MFMA.
+// A stage holds the chunk's token codes, weight groups and the tokens' four
+// scale bytes (one word per token).  kStages
+// LDS stages (dynamic LDS: three when they and the scale table fit, else two);
+// two memory instructions follow each MFMA (the MFMAs are twice as long as
+// the bf16 ones and there are no conversions).
+template <bool kGateUp, bool kSplit, int kStages>
 __global__ __launch_bounds__(256, 1) void expert_fp4_kernel(mxfp4moe::GemmArgs args) {
-  constexpr int WN = 4, RN = 4, RM = 4, kDepth = 2;
+  constexpr int WN = 4, RN = 4, RM = 4;
   constexpr int kThreads = 256;
   constexpr int BN = WN * RN * 32;
   constexpr int BM = RM * 32;
@@ -585,11 +598,15 @@ __global__ __launch_bounds__(256, 1) void expert_fp4_kernel(mxfp4moe::GemmArgs a
   constexpr int kWSlots = BN * 2;  // 16-byte weight slots per chunk
   constexpr int kXPer = kXSlots / kThreads;
   constexpr int kWPer = kWSlots / kThreads;
-  static_assert(BM * 128 >= RM * 4096 && BN * 32 >= RM * 4096, "epilogue regions");
-  __shared__ __attribute__((aligned(16))) u32x4 xs[2][kXSlots];
-  __shared__ __attribute__((aligned(16))) u32x4 wsm[2][kWSlots];
-  __shared__ uint32_t xsc[2][BM];
-  __shared__ __attribute__((aligned(16))) uint8_t sst[BN * kWideMaxGroups];
+  constexpr int kLoads = kXPer + kWPer + 1;      // per thread per chunk: token slots, weight slots, a scale word
+  constexpr int kStageBytes = (kXSlots + kWSlots) * 16 + kThreads * 4;
+  static_assert(kStageBytes % 16 == 0 && kThreads % BM == 0, "stage layout");
+  static_assert(kStages * kStageBytes >= 4 * RM * 32 * 128, "epilogue regions fit in the stages");
+  extern __shared__ __attribute__((aligned(16))) u32x4 fp4_arena[];
+  uint8_t* const base = reinterpret_cast<uint8_t*>(fp4_arena);
+  uint8_t* const sst = base + kStages * kStageBytes;
+  auto xs_of = [&](int st) { return reinterpret_cast<u32x4*>(base + st * kStageBytes); };
+  auto xsc_of = [&](int st) { return reinterpret_cast<uint32_t*>(base + st * kStageBytes + (kXSlots + kWSlots) * 16); };
 
   const int N = args.N, K = args.K;
   const int n_tiles = (N + BN - 1) / BN;
@@ -601,7 +618,6 @@ __global__ __launch_bounds__(256, 1) void expert_fp4_kernel(mxfp4moe::GemmArgs a
   const int count = __builtin_amdgcn_readfirstlane(tl.z);
   const int kgroups = K >> 5;
   const int nchunks = (kgroups + 1) >> 1;
-  const int niter = (nchunks + kDepth - 1) / kDepth * kDepth;
   const int t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int lane = t & 63;
@@ -624,9 +640,9 @@ __global__ __launch_bounds__(256, 1) void expert_fp4_kernel(mxfp4moe::GemmArgs a
     const size_t src_row = kGateUp ? (size_t)(args.sorted_pairs[row0 + rr] / args.top_k) : (size_t)(row0 + rr);
     xsrc[i] = q + src_row * qrow + slot_col(r, p & 7) * 16;
   }
-  // the 4 scale bytes of token (t % BM) per chunk
-  const int st_tok = t & (BM - 1);
-  const int st_rr = st_tok < count ? st_tok : 0;
+  // the 4 scale bytes of token t % BM per chunk (threads past BM load copies,
+  // into words nobody reads, so every wave issues the same loads)
+  const int st_rr = (t & (BM - 1)) < count ? (t & (BM - 1)) : 0;
   const uint32_t* ssrc = reinterpret_cast<const uint32_t*>(args.act_scales) +
                          (kGateUp ? (size_t)(args.sorted_pairs[row0 + st_rr] / args.top_k) : (size_t)(row0 + st_rr)) *
                              nchunks;
@@ -639,25 +655,26 @@ __global__ __launch_bounds__(256, 1) void expert_fp4_kernel(mxfp4moe::GemmArgs a
   }
   const int wh = t & 1;
 
-  u32x4 xr[kDepth][kXPer];
-  u32x4 wr[kDepth][kWPer];
-  uint32_t sr[kDepth];
-  auto issue = [&](int c, int d) {
-    c = c < nchunks ? c : nchunks - 1;  // padding iterations re-read the last chunk
-#pragma unroll
-    for (int i = 0; i < kXPer; ++i) xr[d][i] = *reinterpret_cast<const u32x4*>(xsrc[i] + (size_t)c * 128);
-    sr[d] = ssrc[c];
-    int g = 2 * c + wh;
-    g = g < kgroups ? g : g - 1;
-#pragma unroll
-    for (int j = 0; j < kWPer; ++j) wr[d][j] = *reinterpret_cast<const u32x4*>(wsrc[j] + (size_t)g * 16);
+  // load o of chunk c into stage st: o = 0 the scale word, 1..kXPer token
+  // slots, then the weight slots; lane l of the wave lands in slot
+  // wave*64 + l (+ i*threads)
+  constexpr int kLoadOps = kLoads;
+  auto issue_one = [&](int c, int st, int o) {
+    c = c < nchunks ? c : nchunks - 1;  // past the end: the last chunk again
+    u32x4* xs = xs_of(st) + wave * 64;
+    if (o == 0) {
+      load_lds4(ssrc + c, xsc_of(st) + wave * 64);
+    } else if (o <= kXPer) {
+      load_lds16(xsrc[o - 1] + (size_t)c * 128, xs + (o - 1) * kThreads);
+    } else {
+      int g = 2 * c + wh;
+      g = g < kgroups ? g : g - 1;
+      load_lds16(wsrc[o - 1 - kXPer] + (size_t)g * 16, xs + kXSlots + (o - 1 - kXPer) * kThreads);
+    }
   };
-  auto commit = [&](int d, int stg) {
+  auto issue = [&](int c, int st) {
 #pragma unroll
-    for (int i = 0; i < kXPer; ++i) xs[stg][t + i * kThreads] = xr[d][i];
-#pragma unroll
-    for (int j = 0; j < kWPer; ++j) wsm[stg][t + j * kThreads] = wr[d][j];
-    if (t < BM) xsc[stg][t] = sr[d];
+    for (int o = 0; o < kLoadOps; ++o) issue_one(c, st, o);
   };
 
   const int n_wave = ntile * BN + wave * RN * 32;
@@ -673,63 +690,114 @@ __global__ __launch_bounds__(256, 1) void expert_fp4_kernel(mxfp4moe::GemmArgs a
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[rb][cb][r] = 0.f;
 
+  // the operands of one chunk in registers, as read
+  constexpr int kHalves = kSplit ? 2 : 1;  // high codes, and the residual's
+  struct Ops {
+    u32x4 w[RN];
+    uint32_t sa[RN];               // weight E8M0 bytes
+    uint32_t sw[RM];               // token scale words
+    mx::i32x8 x[RM][kHalves];      // token code fragments, as the MFMA's B operand
+  };
+  constexpr int kPerBlock = 1 + 2 * kHalves;  // reads per token block: scale word, code fragments
+  constexpr int kReads = 2 * RN + RM * kPerBlock;
+  // LDS read j of chunk c's operands from stage st
+  auto read_one = [&](Ops& o, int c, int st, int j) {
+    c = c < nchunks ? c : nchunks - 1;
+    const u32x4* xs = xs_of(st);
+    const int g = 2 * c + half;
+    const int gg = g < kgroups ? g : g - 1;
+    if (j < RN) {
+      o.w[j] = xs[kXSlots + wslot0 + j * 64];
+    } else if (j < 2 * RN) {
+      o.sa[j - RN] = srow[(j - RN) * rb_stride + gg];
+    } else {
+      const int cb = (j - 2 * RN) / kPerBlock, k = (j - 2 * RN) % kPerBlock;
+      const int row = cb * 32 + lrow;
+      if (k == 0) {
+        o.sw[cb] = xsc_of(st)[row];
+      } else {
+        const int hh = (k - 1) / 2, f = (k - 1) % 2;  // code half (high / residual), fragment
+        const u32x4 v = xs[row * 8 + slot_col(row, 4 * hh + 2 * f + half)];
 #pragma unroll
-  for (int d = 0; d < kDepth; ++d) issue(d, d);
-  commit(0, 0);
-  issue(kDepth, 0);
-  __syncthreads();
-
-  for (int c0 = 0; c0 < niter; c0 += kDepth) {
+        for (int i = 0; i < 4; ++i) o.x[cb][hh][4 * f + i] = (int)v[i];
+      }
+    }
+  };
+  auto read_ops = [&](Ops& o, int c, int st) {
 #pragma unroll
-    for (int u = 0; u < kDepth; ++u) {
-      const int c = c0 + u;
-      commit((u + 1) % kDepth, (c + 1) & 1);
-      issue(c + 1 + kDepth, (u + 1) % kDepth);
-      if (c < nchunks) {
-        const int stg = c & 1;
-        const int g = 2 * c + half;
-        const bool glive = g < kgroups;
-        const int gg = glive ? g : g - 1;
-        mx::i32x8 a[RN];
-        int sa[RN];
+    for (int j = 0; j < kReads; ++j) read_one(o, c, st, j);
+  };
+  constexpr int kMfma = RN * RM * kHalves;
+  static_assert(2 * kMfma >= kLoadOps + kReads, "room between the MFMAs");
+  // chunk c from registers `cur` (stage st = c % kStages, a constant at every
+  // call site); chunk c+1's operands into `nxt`; chunk c+kStages into chunk
+  // c's stage; two memory instructions after each MFMA
+  auto step = [&](int c, int st, const Ops& cur, Ops& nxt) {
+    wait_loads_then_barrier<(kStages - 2) * kLoads>();
+    auto extra = [&](int o) {
+      if (o < kLoadOps) issue_one(c + kStages, st, o);
+      else if (o < kLoadOps + kReads) read_one(nxt, c + 1, (st + 1) % kStages, o - kLoadOps);
+      else return;
+      __builtin_amdgcn_sched_barrier(0);  // keep the order: the compiler would bunch the MFMAs
+    };
+    const bool glive = 2 * c + half < kgroups;  // K tail: the group past K multiplies zero weights
+    mx::i32x8 a[RN];
+#pragma unroll
+    for (int rb = 0; rb < RN; ++rb) {
+      const u32x4 w = glive ? cur.w[rb] : u32x4{0u, 0u, 0u, 0u};
+      a[rb] = mx::i32x8{(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
+    }
+    int k = 0;
+#pragma unroll
+    for (int cb = 0; cb < RM; ++cb) {
+#pragma unroll
+      for (int hh = 0; hh < kHalves; ++hh) {
+        const mx::i32x8 bx = cur.x[cb][hh];
+        const int sb = (int)((cur.sw[cb] >> (16 * hh + 8 * half)) & 255u);
 #pragma unroll
         for (int rb = 0; rb < RN; ++rb) {
-          const u32x4 w = glive ? wsm[stg][wslot0 + rb * 64] : u32x4{0u, 0u, 0u, 0u};
-          a[rb] = mx::i32x8{(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
-          sa[rb] = srow[rb * rb_stride + gg];
-        }
-#pragma unroll
-        for (int cb = 0; cb < RM; ++cb) {
-          const int row = cb * 32 + lrow;
-          const u32x4* xb = xs[stg] + row * 8;
-          const u32x4 h0 = xb[slot_col(row, half)], h1 = xb[slot_col(row, 2 + half)];
-          const uint32_t sw = xsc[stg][row];
-          const mx::i32x8 bh = {(int)h0[0], (int)h0[1], (int)h0[2], (int)h0[3],
-                                (int)h1[0], (int)h1[1], (int)h1[2], (int)h1[3]};
-          const int sbh = (int)((sw >> (8 * half)) & 255u);
-#pragma unroll
-          for (int rb = 0; rb < RN; ++rb)
-            acc[rb][cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[rb], bh, acc[rb][cb], 4, 0, 0, sa[rb], 0,
-                                                                          sbh);
-          if (kSplit) {
-            const u32x4 l0 = xb[slot_col(row, 4 + half)], l1 = xb[slot_col(row, 6 + half)];
-            const mx::i32x8 bl = {(int)l0[0], (int)l0[1], (int)l0[2], (int)l0[3],
-                                  (int)l1[0], (int)l1[1], (int)l1[2], (int)l1[3]};
-            const int sbl = (int)((sw >> (16 + 8 * half)) & 255u);
-#pragma unroll
-            for (int rb = 0; rb < RN; ++rb)
-              acc[rb][cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[rb], bl, acc[rb][cb], 4, 0, 0, sa[rb],
-                                                                            0, sbl);
-          }
+          acc[rb][cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[rb], bx, acc[rb][cb], 4, 0, 0,
+                                                                        (int)cur.sa[rb], 0, sb);
+          extra(2 * k);
+          extra(2 * k + 1);
+          ++k;
         }
       }
-      __syncthreads();
+    }
+  };
+  Ops ops0, ops1;
+#pragma unroll
+  for (int c = 0; c < kStages; ++c) issue(c, c);
+  wait_loads_then_barrier<(kStages - 1) * kLoads>();  // chunk 0 (and the scale table) landed
+  read_ops(ops0, 0, 0);
+  constexpr int kTrip = 2 * kStages;
+  const int nfull = nchunks / kTrip * kTrip;
+  for (int c0 = 0; c0 < nfull; c0 += kTrip) {
+#pragma unroll
+    for (int u = 0; u < kTrip; u += 2) {
+      step(c0 + u, u % kStages, ops0, ops1);
+      step(c0 + u + 1, (u + 1) % kStages, ops1, ops0);
     }
   }
-  uint8_t* region = wave == 0 ? reinterpret_cast<uint8_t*>(xs[0])
-                  : wave == 1 ? reinterpret_cast<uint8_t*>(xs[1])
-                  : wave == 2 ? reinterpret_cast<uint8_t*>(wsm[0]) : reinterpret_cast<uint8_t*>(wsm[1]);
+#pragma unroll
+  for (int u = 0; u < kTrip - 1; u += 2) {
+    if (nfull + u < nchunks) step(nfull + u, u % kStages, ops0, ops1);
+    if (nfull + u + 1 < nchunks) step(nfull + u + 1, (u + 1) % kStages, ops1, ops0);
+  }
+  // the chunks issued past the end land before the stages are reused
+  wait_loads_then_barrier<0>();
+  uint8_t* region = base + wave * (RM * 32 * 128);
   store_epilogue<RN, RM, kGateUp>(args, acc, e, row0, count, n_wave, lane, region);
+}
+
+template <bool kGateUp, bool kSplit, int kStages>
+hipError_t launch_fp4_cfg(const mxfp4moe::GemmArgs& a, unsigned grid, size_t lds, hipStream_t stream) {
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&expert_fp4_kernel<kGateUp, kSplit, kStages>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, kFp4MaxLds);
+  if (attr != hipSuccess) return attr;
+  expert_fp4_kernel<kGateUp, kSplit, kStages><<<grid, 256, lds, stream>>>(a);
+  return hipGetLastError();
 }
 
 template <bool kGateUp>
@@ -738,12 +806,18 @@ hipError_t launch_fp4(const mxfp4moe::GemmArgs& a, bool split_act, hipStream_t s
   const long n_tiles = (a.N + BN - 1) / BN;
   const long blocks = n_tiles * a.max_tiles;
   if (blocks == 0) return hipSuccess;
-  const long grid = (blocks + kXcds - 1) / kXcds * kXcds;
+  const unsigned grid = (unsigned)((blocks + kXcds - 1) / kXcds * kXcds);
+  const size_t table = (size_t)BN * (a.K >> 5);
+  // three stages when they fit, except for the split down GEMM, whose
+  // three-stage build runs out of registers (reloads from scratch in the
+  // loop; measured 312 against 293 us at the 120b prefill shape)
+  const bool three = 3 * kFp4StageBytes + table <= (size_t)kFp4MaxLds && (kGateUp || !split_act);
+  const size_t lds = (three ? 3 : 2) * kFp4StageBytes + table;
   if (split_act)
-    expert_fp4_kernel<kGateUp, true><<<(unsigned)grid, 256, 0, stream>>>(a);
-  else
-    expert_fp4_kernel<kGateUp, false><<<(unsigned)grid, 256, 0, stream>>>(a);
-  return hipGetLastError();
+    return three ? launch_fp4_cfg<kGateUp, true, 3>(a, grid, lds, stream)
+                 : launch_fp4_cfg<kGateUp, true, 2>(a, grid, lds, stream);
+  return three ? launch_fp4_cfg<kGateUp, false, 3>(a, grid, lds, stream)
+               : launch_fp4_cfg<kGateUp, false, 2>(a, grid, lds, stream);
 }
 
 // Streaming kernel for tiles of at most kStreamTokens pairs: decode batches
