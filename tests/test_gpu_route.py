@@ -48,3 +48,37 @@ def test_route_empty(gpu):
     ids, w, offsets, pairs = gpu.moe_mxfp4_route(logits, 2)
     torch.cuda.synchronize()
     assert np.array_equal(offsets.cpu().numpy(), np.zeros(9, np.int32))
+
+
+@pytest.mark.parametrize("P", [1023, 1024, 1025, 2047, 2048, 2049, 3072])
+@pytest.mark.parametrize("skew", ["uniform", "one_expert", "two_alternating"])
+def test_group_chunk_boundaries(gpu, P, skew):
+    # The grouping splits the pairs into chunks of 1024, one block each; every
+    # block counts the pairs before its chunk itself.  Pair counts on and
+    # around chunk edges, with the pairs spread evenly, all on one expert
+    # (its run crosses every chunk edge) or alternating between two experts.
+    E, k = 24, 1
+    rng = np.random.default_rng(P)
+    logits = rng.standard_normal((P, E)).astype(np.float32)
+    if skew == "one_expert":
+        logits[:, 17] += 50.0
+    elif skew == "two_alternating":
+        logits[0::2, 3] += 50.0
+        logits[1::2, 20] += 50.0
+    _check(gpu, logits, k)
+
+
+def test_group_chunk_boundaries_top_k(gpu):
+    # pairs of one token straddle a chunk edge (P = 3 * 683 = 2049)
+    rng = np.random.default_rng(7)
+    _check(gpu, rng.standard_normal((683, 96)).astype(np.float32), 3)
+
+
+def test_route_signed_zero_ties(gpu):
+    # -0 and +0 compare equal: the lower expert index wins either way round
+    logits = np.full((4, 8), -1.0, dtype=np.float32)
+    logits[0, 2], logits[0, 5] = 0.0, -0.0
+    logits[1, 2], logits[1, 5] = -0.0, 0.0
+    logits[2, 0], logits[2, 7] = -0.0, -0.0
+    logits[3, :] = -0.0
+    _check(gpu, logits, 2)
