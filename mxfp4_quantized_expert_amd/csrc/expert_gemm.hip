@@ -1070,7 +1070,10 @@ hipError_t launch_stream(const mxfp4moe::GemmArgs& a, hipStream_t stream) {
 // lanes per row, 128 bytes per row per load: the pattern HBM streams at full
 // rate) and the tile's token rows as kP*256 bytes each.  The loads of panel
 // p+1 are issued before the MFMAs of panel p and stored after them (single
-// LDS buffer, two barriers per panel); two blocks per CU overlap further.
+// LDS buffer, two barriers per panel); with panels of one chunk a block
+// needs about 39 KB of LDS and 160 registers per lane at K = 2880, so three
+// blocks share a CU and overlap further (panels of two chunks, two blocks
+// per CU: 9 % slower at the 20b prefill shape, 17 % with NVFP4 weights).
 // Token columns past the tile's pairs read its first pair (their outputs are
 // dropped).
 //
@@ -1272,7 +1275,7 @@ __global__ __launch_bounds__(256, 2) void expert_mid_kernel(mxfp4moe::GemmArgs a
 }
 
 #ifndef MX_MID_PANEL
-#define MX_MID_PANEL 2
+#define MX_MID_PANEL 1
 #endif
 
 template <bool kGateUp, bool kNv>
