@@ -91,3 +91,46 @@ def test_dequant_graph_replays(gpu):
         ref = gpu.mxfp4_dequantize(b, sc)
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"replay {rep}"
+
+
+@pytest.mark.parametrize("act", ["bf16", "mxfp8_split"])
+def test_forward_graph_replays_full_tiles(gpu, act):
+    # Experts with several full 128-pair tiles, so the full-tile kernels (LDS
+    # staging by the load unit; the FP4 kernel's dynamic LDS) run inside the
+    # graph; a small hidden size keeps the layer cheap.
+    spec = W.LAYERS["20b_live"].with_(T=1024, H=256, I=192, E=4, top_k=2)
+    L = W.make_layer(spec, seed=11)
+    d = gpu.layer_to_device(L)
+    k = spec.top_k
+    flags = gpu.ACT_FLAGS[act]
+    ws = torch.empty((gpu.workspace_bytes(spec.T, spec.H, spec.I, spec.E, k, flags),), dtype=torch.uint8,
+                     device="cuda")
+    x = d["x"].clone()
+    logits = d["router_logits"].clone()
+    y = torch.empty((spec.T, spec.H), dtype=torch.bfloat16, device="cuda")
+
+    def call(xx, lg, out, workspace=ws):
+        return gpu.moe_mxfp4_forward(xx, lg, d["w13_blocks"], d["w13_scales"], d["w13_bias"], d["w2_blocks"],
+                                     d["w2_scales"], d["w2_bias"], k, out=out, workspace=workspace, act=act)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call(x, logits, y)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(x, logits, y)
+    rng = np.random.default_rng(12)
+    for rep in range(3):
+        xn = _bf16(W.to_bf16_bits(rng.standard_normal((spec.T, spec.H)).astype(np.float32)))
+        ln = torch.from_numpy((rng.standard_normal((spec.T, spec.E)) * 2).astype(np.float32)).cuda()
+        x.copy_(xn)
+        logits.copy_(ln)
+        g.replay()
+        torch.cuda.synchronize()
+        got = bits_u16(y)
+        ref = call(xn, ln, torch.empty_like(y), torch.empty_like(ws))
+        torch.cuda.synchronize()
+        assert np.array_equal(got, bits_u16(ref)), f"replay {rep} differs from the eager call"
