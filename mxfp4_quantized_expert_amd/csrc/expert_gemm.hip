@@ -203,27 +203,41 @@ constexpr int kWideMaxGroups = 128;  // K <= 4096
 constexpr int kFp4StageBytes = (128 * 8 + 512 * 2) * 16 + 256 * 4;  // one LDS stage of the FP4 kernel
 constexpr int kFp4MaxLds = 160 * 1024;                              // LDS per workgroup on gfx950
 
+// 16 bytes per lane from global memory straight into LDS (the load unit
+// writes lane l's bytes at lds + 16 * l; lds is the same for the whole wave).
+__device__ __forceinline__ void load_lds16(const void* src, u32x4* lds) {
+  __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
+}
+
 // Scale bytes of a block's BN weight rows, row-major as in memory: the rows
 // are one contiguous, 32-byte aligned range (row counts and tile starts are
 // multiples of 32), copied with 16-byte loads.  Rows past N are not copied
-// (their outputs are dropped).
-template <int BN, int kThreads>
+// (their outputs are dropped).  kDma: the load unit writes LDS itself
+// (global_load_lds, lane l of a wave at the wave's slot + 16 * l), so the
+// copy flies with the first operand loads instead of waiting to be stored;
+// the caller waits for it (vmcnt) before the first barrier.
+template <int BN, int kThreads, bool kDma = false>
 __device__ __forceinline__ void stage_scales(uint8_t* sst, const mxfp4moe::GemmArgs& args, int e, int ntile,
                                              int kgroups, int t, bool split = false) {
   // kgroups: scale bytes per weight row (K/32 for MXFP4, K/16 for NVFP4)
   const int N = args.N;
   const int nv = min(BN, N - ntile * BN);
   u32x4* dst = reinterpret_cast<u32x4*>(sst);
-  if (!split) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(args.wscales + ((size_t)e * N + ntile * BN) * (size_t)kgroups);
-    for (int i = t; i < (nv * kgroups) >> 4; i += kThreads) dst[i] = src[i];
+  // the block's rows (split layout: its gate rows, then its up rows; each
+  // range contiguous and 16-byte aligned)
+  const int n16 = (nv * kgroups) >> 4;
+  const int h = split ? ((nv >> 1) * kgroups) >> 4 : n16;
+  const u32x4* g = reinterpret_cast<const u32x4*>(
+      args.wscales + ((size_t)e * N + (split ? ntile * BN >> 1 : ntile * BN)) * (size_t)kgroups);
+  const u32x4* u =
+      reinterpret_cast<const u32x4*>(args.wscales + ((size_t)e * N + (N >> 1) + (ntile * BN >> 1)) * (size_t)kgroups);
+  if (kDma) {
+    for (int i0 = 0; i0 < n16; i0 += kThreads) {  // the same trip count in every wave
+      const int i = i0 + t;
+      if (i < n16) load_lds16(i < h ? g + i : u + (i - h), dst + i0 + (t & ~63));
+    }
   } else {
-    // the block's gate rows, then its up rows (each range contiguous, 16-byte aligned)
-    const int h = ((nv >> 1) * kgroups) >> 4;
-    const u32x4* g = reinterpret_cast<const u32x4*>(args.wscales + ((size_t)e * N + (ntile * BN >> 1)) * (size_t)kgroups);
-    const u32x4* u =
-        reinterpret_cast<const u32x4*>(args.wscales + ((size_t)e * N + (N >> 1) + (ntile * BN >> 1)) * (size_t)kgroups);
-    for (int i = t; i < 2 * h; i += kThreads) dst[i] = i < h ? g[i] : u[i - h];
+    for (int i = t; i < n16; i += kThreads) dst[i] = i < h ? g[i] : u[i - h];
   }
 }
 
@@ -311,12 +325,6 @@ __device__ __forceinline__ void store_epilogue(const mxfp4moe::GemmArgs& args, c
   }
 }
 
-// 16 bytes per lane from global memory straight into LDS (the load unit
-// writes lane l's bytes at lds + 16 * l; lds is the same for the whole wave).
-__device__ __forceinline__ void load_lds16(const void* src, u32x4* lds) {
-  __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
-}
-
 // Waits until at most kVm of this wave's vector-memory loads are in flight
 // and its LDS operations are done, then joins the block barrier.  The empty
 // asm statements keep the compiler from moving memory accesses across it
@@ -386,7 +394,7 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void expert_wide_kernel(mxfp4moe::
   const int lrow = lane & 31;
 
   const bool split = kGateUp && args.split_gate_up;  // uniform
-  stage_scales<BN, kThreads>(sst, args, e, ntile, kgroups, t, split);
+  stage_scales<BN, kThreads, true>(sst, args, e, ntile, kgroups, t, split);
 
   // token slot p = t + i*threads -> row p/8, logical column slot_col(row, p%8);
   // rows past `count` re-read the tile's first row (their columns are never stored)
@@ -625,7 +633,7 @@ __global__ __launch_bounds__(256, 1) void expert_fp4_kernel(mxfp4moe::GemmArgs a
   const int lrow = lane & 31;
 
   const bool split = kGateUp && args.split_gate_up;  // uniform
-  stage_scales<BN, kThreads>(sst, args, e, ntile, kgroups, t, split);
+  stage_scales<BN, kThreads, true>(sst, args, e, ntile, kgroups, t, split);
 
   // token slot p = t + i*threads -> row p/8, logical column slot_col(row, p%8);
   // rows past `count` re-read the tile's first row (their columns are never stored)
