@@ -358,7 +358,10 @@ __device__ __forceinline__ void wait_loads_then_barrier() {
 // barrier and cover work issued a whole chunk earlier.  While LDS-DMA loads
 // are in flight the compiler only waits for all LDS reads at once, which
 // this order makes free.
-template <int WN, int WM, int RN, int RM, bool kGateUp>
+// kAhead = false: one operand set per wave, read right after the barrier
+// that makes the chunk visible; meant for two waves per SIMD (WM = 2), where
+// the other wave's MFMAs cover that wait.  Two chunks in flight.
+template <int WN, int WM, int RN, int RM, bool kGateUp, bool kAhead = true>
 __global__ __launch_bounds__(WN * WM * 64, 1) void expert_wide_kernel(mxfp4moe::GemmArgs args) {
   constexpr int kThreads = WN * WM * 64;
   constexpr int BN = WN * RN * 32;
@@ -513,7 +516,7 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void expert_wide_kernel(mxfp4moe::
     // chunks after it are in flight
     wait_loads_then_barrier<(kStages - 2) * kLoads>();
     if (live) {
-      static_assert(2 * (kLoads + kReads) <= 4 * RN * RM, "room between the MFMAs");
+      static_assert(!kAhead || 2 * (kLoads + kReads) <= 4 * RN * RM, "room between the MFMAs");
       auto extra = [&](int k) {
         if (k % 2 != 0) return;
         const int op = k / 2;
@@ -536,26 +539,68 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void expert_wide_kernel(mxfp4moe::
       issue(c + kStages, st);
     }
   };
-  Ops ops0, ops1;
-#pragma unroll
-  for (int c = 0; c < kStages; ++c) issue(c, c);
-  wait_loads_then_barrier<(kStages - 1) * kLoads>();  // chunk 0 (and the scale table) landed
-  if (live) read_ops(ops0, 0, 0);
-  // trips of 2*kStages chunks: the register set and the stage of every step
-  // are constants; then the remaining steps one by one
-  constexpr int kTrip = 2 * kStages;
-  const int nfull = nchunks / kTrip * kTrip;
-  for (int c0 = 0; c0 < nfull; c0 += kTrip) {
-#pragma unroll
-    for (int u = 0; u < kTrip; u += 2) {
-      step(c0 + u, u % kStages, ops0, ops1);
-      step(c0 + u + 1, (u + 1) % kStages, ops1, ops0);
+  if constexpr (kAhead) {
+    Ops ops0, ops1;
+  #pragma unroll
+    for (int c = 0; c < kStages; ++c) issue(c, c);
+    wait_loads_then_barrier<(kStages - 1) * kLoads>();  // chunk 0 (and the scale table) landed
+    if (live) read_ops(ops0, 0, 0);
+    // trips of 2*kStages chunks: the register set and the stage of every step
+    // are constants; then the remaining steps one by one
+    constexpr int kTrip = 2 * kStages;
+    const int nfull = nchunks / kTrip * kTrip;
+    for (int c0 = 0; c0 < nfull; c0 += kTrip) {
+  #pragma unroll
+      for (int u = 0; u < kTrip; u += 2) {
+        step(c0 + u, u % kStages, ops0, ops1);
+        step(c0 + u + 1, (u + 1) % kStages, ops1, ops0);
+      }
     }
-  }
+  #pragma unroll
+    for (int u = 0; u < kTrip - 1; u += 2) {
+      if (nfull + u < nchunks) step(nfull + u, u % kStages, ops0, ops1);
+      if (nfull + u + 1 < nchunks) step(nfull + u + 1, (u + 1) % kStages, ops1, ops0);
+    }
+  } else {
+    // one operand set: chunk c is read after the barrier that makes it
+    // visible (the other wave on the SIMD covers the wait), chunk c+2 goes
+    // to the stage of chunk c-1, its loads spread between the MFMAs
+    auto step1 = [&](int c, int st) {
+      wait_loads_then_barrier<kLoads>();  // chunk c landed; chunk c+1 may be in flight
+      Ops cur;
+      if (live) {
 #pragma unroll
-  for (int u = 0; u < kTrip - 1; u += 2) {
-    if (nfull + u < nchunks) step(nfull + u, u % kStages, ops0, ops1);
-    if (nfull + u + 1 < nchunks) step(nfull + u + 1, (u + 1) % kStages, ops1, ops0);
+        for (int j = 0; j < kReads; ++j) read_one(cur, c, st, j);
+        constexpr int kMfma = 4 * RN * RM;
+        constexpr int kEvery = kMfma / kLoads >= 2 ? 2 : 1;
+        static_assert(kEvery * kLoads <= kMfma, "room between the MFMAs");
+        auto extra = [&](int k) {
+          if (k % kEvery != 0 || k / kEvery >= kLoads) return;
+          issue_one(c + 2, (st + 2) % kStages, k / kEvery);
+          __builtin_amdgcn_sched_barrier(0);
+        };
+        const bool glive = 2 * c + half < kgroups;
+        u32x4 w[RN];
+        float sc[RN];
+#pragma unroll
+        for (int rb = 0; rb < RN; ++rb) {
+          w[rb] = glive ? cur.w[rb] : u32x4{0u, 0u, 0u, 0u};
+          sc[rb] = mx::e8m0_operand(cur.sb[rb]);
+        }
+        chunk_mma_regs<RN, RM>(acc, cur.b, w, sc, extra);
+      } else {
+        issue(c + 2, (st + 2) % kStages);
+      }
+    };
+    issue(0, 0);
+    issue(1, 1);
+    const int nfull = nchunks / kStages * kStages;
+    for (int c0 = 0; c0 < nfull; c0 += kStages) {
+#pragma unroll
+      for (int u = 0; u < kStages; ++u) step1(c0 + u, u);
+    }
+    if (nfull < nchunks) step1(nfull, 0);
+    if (nfull + 1 < nchunks) step1(nfull + 1, 1);
   }
   // the chunks issued past the end land before the arena is reused
   wait_loads_then_barrier<0>();
@@ -563,14 +608,14 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void expert_wide_kernel(mxfp4moe::
   if (live) store_epilogue<RN, RM, kGateUp>(args, acc, e, row0 + m_wave, count - m_wave, n_wave, lane, region);
 }
 
-template <int WN, int WM, int RN, int RM, bool kGateUp>
+template <int WN, int WM, int RN, int RM, bool kGateUp, bool kAhead = true>
 hipError_t launch_wide(const mxfp4moe::GemmArgs& a, hipStream_t stream) {
   constexpr int BN = WN * RN * 32;
   const long n_tiles = (a.N + BN - 1) / BN;
   const long blocks = n_tiles * a.max_tiles;
   if (blocks == 0) return hipSuccess;
   const long grid = (blocks + kXcds - 1) / kXcds * kXcds;
-  expert_wide_kernel<WN, WM, RN, RM, kGateUp><<<(unsigned)grid, WN * WM * 64, 0, stream>>>(a);
+  expert_wide_kernel<WN, WM, RN, RM, kGateUp, kAhead><<<(unsigned)grid, WN * WM * 64, 0, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -1349,7 +1394,15 @@ static hipError_t launch_all(GemmArgs a, const TileTables& tt, const TileBounds&
       w.act = reinterpret_cast<const uint16_t*>(a.act_codes);
       err = launch_fp4<kGateUp>(w, a.act_mode == kActMxfp8Split, stream);
     } else {
-      err = launch_wide<4, 1, 4, 4, kGateUp>(w, stream);
+      // gate_up: four waves of 128 rows x 128 pairs, operands read a chunk
+      // ahead; down: eight waves of 128 rows x 64 pairs (two per SIMD, one
+      // operand set each), whose second wave covers the heavier epilogue and
+      // the LDS waits (measured at the 120b prefill shape: down 264 against
+      // 274 us, gate_up 499 against 478 us the other way round)
+      if (kGateUp)
+        err = launch_wide<4, 1, 4, 4, true>(w, stream);
+      else
+        err = launch_wide<4, 2, 4, 2, false, false>(w, stream);
     }
   }
   if (err == hipSuccess && tb.max_mid > 0) {
