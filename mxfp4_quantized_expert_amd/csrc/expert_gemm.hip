@@ -1032,6 +1032,10 @@ __global__ __launch_bounds__(256, 5) void expert_stream_kernel(mxfp4moe::GemmArg
     for (int c0 = c_begin + kBatch; c0 < c_end; c0 += kBatch) {
       u32x4 w[kBatch][RN];
       load_batch(c0, w);
+      // the whole batch in flight before its first use: left alone, the
+      // scheduler sinks each load next to its MFMAs and only about two of a
+      // wave's loads are ever outstanding
+      __builtin_amdgcn_sched_barrier(0);
       compute_batch(c0, w);
     }
   }
