@@ -1272,10 +1272,15 @@ __global__ __launch_bounds__(256, 2) void expert_mid_kernel(mxfp4moe::GemmArgs a
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
         if (cb < ncb) {  // wave-uniform: column blocks past the tile's pairs are skipped
+          // the block's four token fragments read together, then its MFMAs
+          bf16x8 bb[4];
+#pragma unroll
+          for (int st = 0; st < 4; ++st)
+            bb[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xs + xrd[cb] + jj * 256 + 16 * st));
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int st = 0; st < 4; ++st) {
-            const bf16x8 b =
-                __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xs + xrd[cb] + jj * 256 + 16 * st));
+            const bf16x8 b = bb[st];
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb)
               acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mx::as_bf16x8(a[rb][st]), b, acc[rb][cb], 0, 0, 0);
