@@ -99,6 +99,15 @@ struct GroupScale {
       lo = hi = mx::e8m0_operand(srow[g]);
     }
   }
+  // from the group's scale byte(s) already read (b1 only for NVFP4)
+  __device__ __forceinline__ GroupScale(uint32_t b0, uint32_t b1) {
+    if (kNv) {
+      lo = mx::e4m3_operand(b0);
+      hi = mx::e4m3_operand(b1);
+    } else {
+      lo = hi = mx::e8m0_operand(b0);
+    }
+  }
   __device__ __forceinline__ float step(int s) const { return s < 2 ? lo : hi; }
   // eight codes of step s as bf16
   __device__ __forceinline__ u32x4 convert(uint32_t packed, int s) const {
@@ -1261,11 +1270,20 @@ __global__ __launch_bounds__(256, 2) void expert_mid_kernel(mxfp4moe::GemmArgs a
       const bool glive = g0 < kgroups;
       const int g = glive ? g0 : kgroups - 1;
       u32x4 a[2][4];  // [rb][step] converted A fragments
+      // both row blocks' weight fragments and scale bytes read together
+      u32x4 wr[2];
+      uint32_t sb[2][2];
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
-        const GroupScale<kNv> sc(srow[rb], g);
-        u32x4 wj = *reinterpret_cast<const u32x4*>(ws + wrd[rb] + jj * 64);
-        wj = glive ? wj : u32x4{0u, 0u, 0u, 0u};
+        wr[rb] = *reinterpret_cast<const u32x4*>(ws + wrd[rb] + jj * 64);
+        sb[rb][0] = kNv ? srow[rb][2 * g] : srow[rb][g];
+        sb[rb][1] = kNv ? srow[rb][2 * g + 1] : 0u;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const GroupScale<kNv> sc(sb[rb][0], sb[rb][1]);
+        const u32x4 wj = glive ? wr[rb] : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int st = 0; st < 4; ++st) a[rb][st] = sc.convert(wj[st], st);
       }
