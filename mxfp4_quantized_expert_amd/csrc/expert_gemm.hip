@@ -15,15 +15,17 @@
 // of one token: a gate/up pair sits in one lane (SwiGLU without shuffles) and
 // the down outputs leave as 16-byte stores.
 //
-// K runs in chunks of 64 = two E8M0 groups.  Within a chunk lane half h
-// (lane / 32) takes group h: it loads that group's 16 packed bytes of its
-// weight row with one 128-bit load and converts dword s (eight codes) to the
-// eight bf16 it feeds to MFMA step s.  The tokens' bf16 rows of the chunk are
-// staged in LDS and each lane reads the eight values matching its weight codes.  Any consistent
-// assignment of k to (lane half, step, element) yields the same dot products,
-// and this one needs no reshuffle of the checkpoint layout.  Weights are
-// dequantized exactly (E2M1 x 2^(s-127) is a bf16 value) and MFMA
-// accumulates in fp32.
+// In the full-tile kernels K runs in chunks of 64 = two E8M0 groups.  Within
+// a chunk lane half h (lane / 32) takes group h: it reads that group's 16
+// packed bytes of its weight row (staged in LDS with the chunk) with one
+// 128-bit read and converts dword s (eight codes) to the eight bf16 it feeds
+// to MFMA step s; the tokens' bf16 rows of the chunk are staged beside them
+// and each lane reads the eight values matching its weight codes.  (The mid
+// and streaming kernels use the 16x16x32 MFMA with a lane layout of their
+// own, described with them.)  Any consistent assignment of k to (lane half,
+// step, element) yields the same dot products, and this one needs no
+// reshuffle of the checkpoint layout.  Weights are dequantized exactly
+// (E2M1 x 2^(s-127) is a bf16 value) and MFMA accumulates in fp32.
 #include "internal.h"
 #include "mx_device.h"
 
@@ -1400,9 +1402,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 namespace mxfp4moe {
 
-// wide: 4 waves of 128 weight rows x 128 tokens (block 512 x 128), one wave per SIMD.
-// mid: 16x16x32 MFMA, 4 waves of 32 weight rows x (up to) 64 tokens, token
-// panels of MX_MID_PANEL chunks staged in LDS.
+// wide: blocks of 512 weight rows x 128 tokens; gate_up 4 waves of 128 x 128
+// (one per SIMD, operands read a chunk ahead), down 8 waves of 128 x 64 (two
+// per SIMD).
+// mid: 16x16x32 MFMA, 4 waves of 32 weight rows x (up to) 64 tokens, panels
+// of MX_MID_PANEL chunks of both operands staged in LDS.
 // stream: 16x16x32 MFMA, 4 waves of 16*MX_STREAM_RN weight rows x (at most 4)
 // tokens, weights streamed in batches of MX_STREAM_BATCH chunks of 128 K.
 static_assert(kWideTokens == 128 && kStreamTokens == 4, "tile sizes");
