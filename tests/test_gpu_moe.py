@@ -100,14 +100,16 @@ def test_120b_long_prefill_sampled(gpu):
 @pytest.mark.parametrize("T,H,I,E,k", [(5, 96, 160, 7, 3), (1, 64, 32, 3, 3), (37, 224, 96, 9, 2),
                                        (300, 128, 64, 5, 1), (3, 32, 32, 1, 1), (600, 96, 160, 3, 2),
                                        (700, 4096, 64, 2, 1), (9, 32, 64, 512, 32), (40, 64, 64, 64, 32),
-                                       (64, 64, 64, 64, 32)])
+                                       (64, 64, 64, 64, 32), (300, 96, 288, 2, 1)])
 @pytest.mark.parametrize("path", [None, "stream"])
 def test_ragged_shapes(gpu, T, H, I, E, k, path):
     # K tails (H/32 or I/32 odd), partial weight-row tiles, partial token tiles,
     # top_k = E, a single expert, experts with several full 128-pair tiles plus
     # a remainder, the largest supported hidden size, the most experts and the
     # largest top_k, and batches small enough for the fused routing whose 1280
-    # and 2048 pairs take two chunks of the grouping in one block.  path None: full tiles in
+    # and 2048 pairs take two chunks of the grouping in one block, and gate_up rows
+    # N = 576 = 512 + 64 (full tiles whose second weight-row tile holds 64 live
+    # rows).  path None: full tiles in
     # the wide configuration, remainders streamed; "stream": everything streamed.
     spec = W.LAYERS["tiny"].with_(T=T, H=H, I=I, E=E, top_k=k)
     L = W.make_layer(spec, seed=T + H)
