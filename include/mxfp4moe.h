@@ -130,7 +130,7 @@ int moe_mxfp4_route(const float* router_logits, int64_t T, int64_t E, int64_t to
  *     gate = h[0::2], up = h[1::2]                (interleaved rows)
  *     a    = min(gate,7) * sigmoid(1.702*min(gate,7)) * (clamp(up,-7,7) + 1)
  *     z    = a W2_e^T + b2_e                      (bias before the routing weight)
- *   y[t] = bf16_rne( sum_j w[t, j] * z_(t,j) )
+ *   y[t] = bf16_rne( sum_j bf16_rne(w[t, j] * z_(t,j)) )   (sum in fp32, j ascending)
  *
  * Defined by "feat(gguf): serve gpt-oss gguf checkpoints on gpt_oss"
  * (FreeToken PR #838): "What it does" (alpha 1.702 and limit 7, interleaved
@@ -159,7 +159,8 @@ int moe_mxfp4_route(const float* router_logits, int64_t T, int64_t E, int64_t to
  *
  * Biases are required (a NULL bias is MXFP4MOE_ERR_ARG); there is no mode that
  * applies the routing weight to the input.  Accumulation is fp32; the SwiGLU
- * output is rounded to bf16 before the down GEMM.  T == 0 is a no-op.
+ * output is rounded to bf16 before the down GEMM, and each weighted pair
+ * output w * z to bf16 before the sum over the k pairs.  T == 0 is a no-op.
  * An expert with at least 128 pairs is cut into tiles of 128 (the last one
  * partial), one with 5..127 pairs into tiles of at most 64, one with at most
  * 4 pairs makes one streaming tile; each kind has a GEMM kernel of its own

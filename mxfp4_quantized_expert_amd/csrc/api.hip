@@ -105,7 +105,7 @@ Layout make_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k, bo
   L.mid = off;       off = align_up(off + (size_t)L.max_mid * 16);
   L.small = off;     off = align_up(off + (size_t)L.max_small * 16);
   L.act = off;       off = align_up(off + (size_t)P * (size_t)I * 2);
-  L.zw = off;        off = align_up(off + (size_t)P * (size_t)H * 4);
+  L.zw = off;        off = align_up(off + (size_t)P * (size_t)H * 2);  // bf16 pair outputs
   L.logits = off;    off = align_up(off + (size_t)T * (size_t)E * 4);  // router projection output
   // MXFP8 activations of the FP4 scaled-MFMA path (only with its flag)
   const size_t nx = fp8_act ? (size_t)T : 0, na = fp8_act ? (size_t)P : 0;
@@ -191,7 +191,7 @@ int forward_impl(const uint16_t* x, const float* router_logits, const uint16_t* 
   int32_t* sorted = reinterpret_cast<int32_t*>(ws + L.sorted);
   int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
   uint16_t* act = reinterpret_cast<uint16_t*>(ws + L.act);
-  float* zw = reinterpret_cast<float*>(ws + L.zw);
+  uint16_t* zw = reinterpret_cast<uint16_t*>(ws + L.zw);
 
   const int64_t P = T * top_k;
   TileTables tt;

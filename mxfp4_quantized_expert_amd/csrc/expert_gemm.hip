@@ -252,14 +252,20 @@ __device__ __forceinline__ void stage_scales(uint8_t* sst, const mxfp4moe::GemmA
   }
 }
 
+// Four fp32 values as four bf16 (round to nearest even), low half first.
+__device__ __forceinline__ uint2 pack_bf16x4(const f32x4& v) {
+  return uint2{mx::pack_bf16x2_rne(v[0], v[1]), mx::pack_bf16x2_rne(v[2], v[3])};
+}
+
 // Epilogue, staged through an LDS region of RM*32*128 bytes per wave so
 // that every token's outputs leave as full 128-byte rows: the lane layout of
 // the MFMA results (four consecutive features of one token per lane) is
 // written to LDS as [token][features] (16-byte chunks XOR-swizzled by token),
-// then read back along the features and stored with 16-byte stores.
+// then read back along the features and stored as whole rows.
 // gate_up: bias, clamped SwiGLU, bf16 -> a[pair row][I] (16*RN activations,
-// 32*RN bytes, per token per wave).  down: bias, routing weight, fp32 ->
-// zw[pair][H], one 32-feature slab (128 bytes per token) per pass.
+// 32*RN bytes, per token per wave).  down: bias and routing weight in fp32,
+// rounded to bf16 -> zw[pair][H], one 32-feature slab (staged as 128 bytes,
+// stored as 64 per token) per pass.
 template <int RN, int RM, bool kGateUp>
 __device__ __forceinline__ void store_epilogue(const mxfp4moe::GemmArgs& args, const f32x16 (&acc)[RN][RM], int e,
                                               int row0, int count, int n_wave, int lane, uint8_t* region) {
@@ -329,7 +335,7 @@ __device__ __forceinline__ void store_epilogue(const mxfp4moe::GemmArgs& args, c
         if (m < count && n < N) {
           const f32x4 v = *reinterpret_cast<const f32x4*>(region + chunk_addr(m, chunk));
           const int p = args.sorted_pairs[row0 + m];
-          *reinterpret_cast<f32x4*>(static_cast<float*>(args.out) + (size_t)p * N + n) = v;
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(args.out) + (size_t)p * N + n) = pack_bf16x4(v);
         }
       }
     }
@@ -1090,7 +1096,7 @@ __global__ __launch_bounds__(256, 5) void expert_stream_kernel(mxfp4moe::GemmArg
       v[1] *= wt;
       v[2] *= wt;
       v[3] *= wt;
-      *reinterpret_cast<f32x4*>(static_cast<float*>(args.out) + (size_t)p * N + n) = v;
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(args.out) + (size_t)p * N + n) = pack_bf16x4(v);
     }
   }
 }
@@ -1350,7 +1356,7 @@ __global__ __launch_bounds__(256, 2) void expert_mid_kernel(mxfp4moe::GemmArgs a
         o[1] = wt * (v[1] + b1);
         o[2] = wt * (v[2] + b2);
         o[3] = wt * (v[3] + b3);
-        *reinterpret_cast<f32x4*>(static_cast<float*>(args.out) + (size_t)pr * N + n) = o;
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(args.out) + (size_t)pr * N + n) = pack_bf16x4(o);
       }
     }
   }
@@ -1375,27 +1381,31 @@ hipError_t launch_mid(const mxfp4moe::GemmArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// y[t, n] = bf16(sum_j zw[t*k + j, n]), j ascending; four features per thread.
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ zw, uint16_t* __restrict__ y,
+// y[t, n] = bf16(sum_j zw[t*k + j, n]) summed in fp32, j ascending, over the
+// bf16 pair outputs; eight features per thread.
+__global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ zw, uint16_t* __restrict__ y,
                                                       int T, int H, int top_k) {
-  const int h4 = H >> 2;
+  const int h8 = H >> 3;
   const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (size_t)T * h4) return;
-  const int t = (int)(idx / h4);
-  const int n = (int)(idx - (size_t)t * h4) * 4;
-  const float* src = zw + (size_t)t * top_k * H + n;
-  f32x4 s = *reinterpret_cast<const f32x4*>(src);
-  for (int j = 1; j < top_k; ++j) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(src + (size_t)j * H);
-    s[0] += v[0];
-    s[1] += v[1];
-    s[2] += v[2];
-    s[3] += v[3];
+  if (idx >= (size_t)T * h8) return;
+  const int t = (int)(idx / h8);
+  const int n = (int)(idx - (size_t)t * h8) * 8;
+  const uint16_t* src = zw + (size_t)t * top_k * H + n;
+  float s[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s[i] = 0.f;
+  for (int j = 0; j < top_k; ++j) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(src + (size_t)j * H);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s[2 * i] += mx::bf16_to_f32(v[i] & 0xffffu);
+      s[2 * i + 1] += mx::bf16_to_f32(v[i] >> 16);
+    }
   }
-  uint2 o;
-  o.x = mx::pack_bf16x2_rne(s[0], s[1]);
-  o.y = mx::pack_bf16x2_rne(s[2], s[3]);
-  *reinterpret_cast<uint2*>(y + (size_t)t * H + n) = o;
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = mx::pack_bf16x2_rne(s[2 * i], s[2 * i + 1]);
+  *reinterpret_cast<u32x4*>(y + (size_t)t * H + n) = o;
 }
 
 }  // namespace
@@ -1463,8 +1473,8 @@ hipError_t launch_down(GemmArgs a, const TileTables& tt, const TileBounds& tb, h
   return launch_all<false>(a, tt, tb, stream);
 }
 
-hipError_t launch_combine(const float* zw, uint16_t* y, int T, int H, int top_k, hipStream_t stream) {
-  const size_t n = (size_t)T * (H / 4);
+hipError_t launch_combine(const uint16_t* zw, uint16_t* y, int T, int H, int top_k, hipStream_t stream) {
+  const size_t n = (size_t)T * (H / 8);
   if (n == 0) return hipSuccess;
   ProfileScope prof(kStageCombine, stream);
   combine_kernel<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(zw, y, T, H, top_k);

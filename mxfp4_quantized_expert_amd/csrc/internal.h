@@ -99,7 +99,7 @@ struct GemmArgs {
   const int32_t* tiles;     // [max_tiles][4] = {expert, first sorted row, rows, 0}
   const int32_t* num_tiles;
   const float* topk_weights;  // [P] (down only)
-  void* out;                // gate_up: a [P, N/2] bf16 in expert order; down: zw [P, N] f32 by pair id
+  void* out;                // gate_up: a [P, N/2] bf16 in expert order; down: zw [P, N] bf16 by pair id
   int N, K, top_k, max_tiles;
   int split_gate_up;        // gate_up only: w13 rows stored [I gate rows; I up rows] instead of interleaved
   const float* scale2;      // NVFP4: [E] second-level scale per expert (scales are E4M3 per 16), else nullptr
@@ -115,7 +115,7 @@ enum ActMode : int { kActBf16 = 0, kActMxfp8 = 1, kActMxfp8Split = 2 };
 // tables (each launch skipped when its table has no capacity).
 hipError_t launch_gate_up(GemmArgs a, const TileTables& tt, const TileBounds& tb, hipStream_t stream);
 hipError_t launch_down(GemmArgs a, const TileTables& tt, const TileBounds& tb, hipStream_t stream);
-hipError_t launch_combine(const float* zw, uint16_t* y, int T, int H, int top_k, hipStream_t stream);
+hipError_t launch_combine(const uint16_t* zw, uint16_t* y, int T, int H, int top_k, hipStream_t stream);
 
 // MXFP8 activations (single or split) in the FP4 GEMM's chunk-interleaved
 // layout: per row act_quant_row_bytes(K) code bytes and
