@@ -117,6 +117,34 @@ def test_ragged_shapes(gpu, T, H, I, E, k, path):
     assert_layer_parity(y, O.moe_forward(L, k), f"ragged{(T, H, I, E, k)}/{path}")
 
 
+@pytest.mark.parametrize("T", [1, 4])
+def test_decode_batches_back_to_back_one_workspace(gpu, T):
+    # Nothing of a call survives in the workspace into the next: two different
+    # decode batches through one workspace must each match the oracle (no stale
+    # tile counts, tables or pair outputs), and repeating the first must repeat
+    # its bits.
+    spec = W.LAYERS["20b_live"].with_(T=T)
+    A = W.make_layer(spec, seed=21)
+    B = dict(A)
+    rng = np.random.default_rng(22)
+    B["x"] = W.to_bf16_bits(rng.standard_normal((T, spec.H)).astype(np.float32))
+    B["router_logits"] = (2.0 * rng.standard_normal((T, spec.E))).astype(np.float32)
+    dA, dB = gpu.layer_to_device(A), gpu.layer_to_device(B)
+    ws = torch.empty((gpu.workspace_bytes(T, spec.H, spec.I, spec.E, spec.top_k),), dtype=torch.uint8,
+                     device="cuda")
+
+    def run(d):
+        y = gpu.moe_mxfp4_forward(d["x"], d["router_logits"], d["w13_blocks"], d["w13_scales"], d["w13_bias"],
+                                  d["w2_blocks"], d["w2_scales"], d["w2_bias"], spec.top_k, workspace=ws)
+        torch.cuda.synchronize()
+        return y
+
+    ya, yb, ya2 = run(dA), run(dB), run(dA)
+    assert_layer_parity(ya, O.moe_forward(A, spec.top_k), f"back to back A T={T}")
+    assert_layer_parity(yb, O.moe_forward(B, spec.top_k), f"back to back B T={T}")
+    assert np.array_equal(bits_u16(ya), bits_u16(ya2))
+
+
 def test_empty_batch_is_noop(gpu):
     spec = W.LAYERS["tiny"].with_(T=0)
     L = W.make_layer(spec)
