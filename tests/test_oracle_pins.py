@@ -550,3 +550,61 @@ def test_mxfp8_split_error_bound_and_exact_cases():
     # a single MXFP8 tensor is coarser than the split
     e1 = np.abs(v - O.mxfp8_activations(v, "single")).max()
     assert e1 > 4 * np.abs(v - q).max()
+
+
+def _mxfp8_blocks_scalar(v, mode):
+    """Plain loops over blocks of 32: shared scale 2^(floor(log2 max|v|) - 7) (OCP
+    MX: the block maximum lands in E4M3's top binade), elements rounded to E4M3
+    by torch's float8_e4m3fn; "split" adds the same quantization of the residual."""
+    def one(vals):
+        amax = max(abs(u) for u in vals)
+        if amax == 0.0:
+            return [0.0] * len(vals)
+        s = 2.0 ** (math.floor(math.log2(amax)) - 7)
+        enc = torch.tensor([u / s for u in vals], dtype=torch.float32).to(torch.float8_e4m3fn)
+        return [float(c) * s for c in enc.to(torch.float64)]
+
+    out = []
+    for b0 in range(0, len(v), 32):
+        blk = [float(u) for u in v[b0:b0 + 32]]
+        hi = one(blk)
+        if mode == "split":
+            hi = [h + r for h, r in zip(hi, one([u - h for u, h in zip(blk, hi)]))]
+        out += hi
+    return out
+
+
+@pytest.mark.parametrize("mode", ["split", "single"])
+def test_fp8act_forward_matches_scalar_loops_on_one_token(mode):
+    # The FP4 scaled-MFMA path's oracle (moe_forward_fp8act) against scalar
+    # loops with their own quantizer, on a layer where one of the three experts
+    # keeps exact activations: x quantized per 32-block before the gate_up
+    # GEMM, the SwiGLU output rounded to bf16 (torch) and quantized before the
+    # down GEMM, exact experts untouched.
+    L, spec = _tiny(5, T=3, H=64, I=32, E=3)
+    quantized = np.array([True, False, True])
+    y = O.moe_forward_fp8act(L, spec.top_k, quantized, mode)
+    x = O.bf16_decode(L["x"])
+    ids, w = O.route(L["router_logits"], spec.top_k)
+    t = 1
+    acc = np.zeros(spec.H)
+    for j in range(spec.top_k):
+        e = ids[t, j]
+        W13 = O.dequantize_f64(L["w13_blocks"][e], L["w13_scales"][e])
+        b13 = O.bf16_decode(L["w13_bias"][e])
+        W2 = O.dequantize_f64(L["w2_blocks"][e], L["w2_scales"][e])
+        b2 = O.bf16_decode(L["w2_bias"][e])
+        xq = _mxfp8_blocks_scalar(x[t], mode) if quantized[e] else list(x[t])
+        a = []
+        for i in range(spec.I):
+            hg = sum(W13[2 * i, c] * xq[c] for c in range(spec.H)) + b13[2 * i]
+            hu = sum(W13[2 * i + 1, c] * xq[c] for c in range(spec.H)) + b13[2 * i + 1]
+            a.append(float(O.swiglu_clamped(hg, hu)))
+        if quantized[e]:
+            a = torch.tensor(a, dtype=torch.float32).to(torch.bfloat16).to(torch.float64).tolist()
+            a = _mxfp8_blocks_scalar(a, mode)
+        for n in range(spec.H):
+            acc[n] += w[t, j] * (sum(W2[n, i] * a[i] for i in range(spec.I)) + b2[n])
+    assert np.allclose(acc, y[t], rtol=1e-12, atol=1e-9)
+    # the quantized experts really differ from the exact layer here
+    assert not np.allclose(y[t], O.moe_forward(L, spec.top_k)[t], rtol=1e-6, atol=0)
