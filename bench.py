@@ -232,6 +232,21 @@ def run_moe(args):
     value = T / (ms_per_step / 1e3)
     kms = float(np.mean(dom_ms))
 
+    # Per-call spread (an untimed pass after the timed region): a HIP event
+    # pair around each call (each replay with --graph) on the stream it runs on.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i, (ea, eb) in enumerate(evs):
+        ea.record()
+        if args.graph:
+            graphs[i % copies].replay()
+        else:
+            step(i)
+        eb.record()
+    torch.cuda.synchronize()
+    calls = np.array([ea.elapsed_time(eb) for ea, eb in evs])
+    per_call = {"calls": int(calls.size), "median": float(np.median(calls)), "p10": float(np.percentile(calls, 10)),
+                "p90": float(np.percentile(calls, 90))}
+
     copy_gbs, _ = copy_bandwidth()
 
     flops_total = 6.0 * H * I * P
@@ -272,6 +287,8 @@ def run_moe(args):
     roof["algorithmic"] = per_unit
     layer_tflops = flops_total / (ms_per_step / 1e3) / 1e12
     alg_bytes = active_bytes + T * H * 2 + T * E * 4 + T * H * 2
+    log(f"[bench] per call: median {per_call['median']:.4f} ms, p10 {per_call['p10']:.4f}, "
+        f"p90 {per_call['p90']:.4f} ({per_call['calls']} calls)")
     log(f"[bench] {args.workload}: {ms_per_step:.4f} ms/step, {value:.1f} tokens/s, "
         f"layer {layer_tflops:.1f} TFLOP/s, active experts {n_active}, weight bytes {active_bytes / 1e6:.1f} MB "
         f"-> {alg_bytes / (ms_per_step / 1e3) / 1e9:.1f} GB/s; copies {copies}; copy kernel {copy_gbs:.0f} GB/s")
@@ -312,6 +329,7 @@ def run_moe(args):
             "layer_frac_hbm_peak": alg_bytes / (ms_per_step / 1e3) / 1e9 / PEAK_HBM_GBS,
             "hbm_copy_gbs": copy_gbs,
             "stage_ms": stages,
+            "per_call_ms": per_call,
         },
         "roofline": roof,
     }

@@ -102,7 +102,7 @@ def _check(t: torch.Tensor, name: str, dtype: torch.dtype, shape=None):
         raise ValueError(f"{name} must be a device tensor")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
-    if shape is not None and tuple(t.shape) != tuple(shape):
+    if shape is not None and t.shape != shape:  # torch.Size is a tuple
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
@@ -260,9 +260,8 @@ def moe_mxfp4_forward(x: torch.Tensor, router_logits: torch.Tensor,
         out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
     _check(out, "out", torch.bfloat16, (T, H))
     flags = (1 if gate_up_split else 0) | ACT_FLAGS[act]
-    need = workspace_bytes(T, H, I, E, top_k, flags)
-    if workspace is None:
-        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
+    if workspace is None:  # a caller's workspace is size-checked by the library
+        workspace = torch.empty((max(workspace_bytes(T, H, I, E, top_k, flags), 1),), dtype=torch.uint8, device=x.device)
     _check(workspace, "workspace", torch.uint8)
     n = ctypes.c_size_t(workspace.numel())
     st = lib.moe_mxfp4_forward_ex(x.data_ptr(), router_logits.data_ptr(),
@@ -298,9 +297,8 @@ def moe_mxfp4_forward_router(x: torch.Tensor, router_w: torch.Tensor, router_b: 
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
     _check(out, "out", torch.bfloat16, (T, H))
-    need = workspace_bytes(T, H, I, E, top_k)
-    if workspace is None:
-        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
+    if workspace is None:  # a caller's workspace is size-checked by the library
+        workspace = torch.empty((max(workspace_bytes(T, H, I, E, top_k), 1),), dtype=torch.uint8, device=x.device)
     _check(workspace, "workspace", torch.uint8)
     n = ctypes.c_size_t(workspace.numel())
     st = lib.moe_mxfp4_forward_router(x.data_ptr(), router_w.data_ptr(), router_b.data_ptr(),
@@ -337,9 +335,8 @@ def moe_nvfp4_forward(x: torch.Tensor, router_logits: torch.Tensor,
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
     _check(out, "out", torch.bfloat16, (T, H))
-    need = workspace_bytes(T, H, I, E, top_k)
-    if workspace is None:
-        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
+    if workspace is None:  # a caller's workspace is size-checked by the library
+        workspace = torch.empty((max(workspace_bytes(T, H, I, E, top_k), 1),), dtype=torch.uint8, device=x.device)
     _check(workspace, "workspace", torch.uint8)
     n = ctypes.c_size_t(workspace.numel())
     st = lib.moe_nvfp4_forward(x.data_ptr(), router_logits.data_ptr(), w13_blocks.data_ptr(),
