@@ -115,6 +115,23 @@ def copy_bandwidth(nbytes=1 << 30, reps=10):
     return 2 * nbytes / (ms / 1e3) / 1e9, ms
 
 
+def per_call_spread(call, n):
+    """Median, p10 and p90 (ms) of n calls call(i), each between two HIP events on
+    the current stream; an untimed pass after the timed region."""
+    import numpy as np
+    import torch
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i, (ea, eb) in enumerate(evs):
+        ea.record()
+        call(i)
+        eb.record()
+    torch.cuda.synchronize()
+    t = np.array([ea.elapsed_time(eb) for ea, eb in evs])
+    return {"calls": int(t.size), "median": float(np.median(t)), "p10": float(np.percentile(t, 10)),
+            "p90": float(np.percentile(t, 90))}
+
+
 def run_moe(args):
     import numpy as np
     import torch
@@ -232,20 +249,8 @@ def run_moe(args):
     value = T / (ms_per_step / 1e3)
     kms = float(np.mean(dom_ms))
 
-    # Per-call spread (an untimed pass after the timed region): a HIP event
-    # pair around each call (each replay with --graph) on the stream it runs on.
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for i, (ea, eb) in enumerate(evs):
-        ea.record()
-        if args.graph:
-            graphs[i % copies].replay()
-        else:
-            step(i)
-        eb.record()
-    torch.cuda.synchronize()
-    calls = np.array([ea.elapsed_time(eb) for ea, eb in evs])
-    per_call = {"calls": int(calls.size), "median": float(np.median(calls)), "p10": float(np.percentile(calls, 10)),
-                "p90": float(np.percentile(calls, 90))}
+    # per-call spread of eager calls, or of replays with --graph
+    per_call = per_call_spread((lambda i: graphs[i % copies].replay()) if args.graph else step, args.steps)
 
     copy_gbs, _ = copy_bandwidth()
 
@@ -415,6 +420,7 @@ def run_dequant(args):
     kms = float(np.mean(binding.profile_end(args.steps)))
     ms = (t1 - t0) * 1e3 / args.steps
     nbytes = blocks.nbytes + scales.nbytes + out.numel() * 2
+    per_call = per_call_spread(lambda i: binding.mxfp4_dequantize(b, s, out=out), args.steps)
     res = {
         "metric": "mxfp4_dequantize HBM GB/s",
         "value": nbytes / (ms / 1e3) / 1e9,
@@ -422,7 +428,8 @@ def run_dequant(args):
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "u8->bf16", "data": "synthetic",
-        "config": {"workload": f"dequant of a gpt-oss-120b shaped w13 bank {list(blocks.shape)} -> bf16"},
+        "config": {"workload": f"dequant of a gpt-oss-120b shaped w13 bank {list(blocks.shape)} -> bf16",
+                   "per_call_ms": per_call},
         "roofline": {"bound": "hbm", "achieved": nbytes / (kms / 1e3) / 1e9, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": nbytes / (kms / 1e3) / 1e9 / PEAK_HBM_GBS, "traffic": None,
                      "kernel": "mxfp4_dequant_kernel", "kernel_ms": kms},
