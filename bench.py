@@ -9,11 +9,15 @@ one batch of synthetic tokens whose inputs are already resident in HBM.
 
 Prints one JSON line.  Workloads: 120b_prefill (default: gpt-oss-120b shaped
 layer, T=4096 long prefill with Zipf-skewed routing), 20b_prefill, 20b_decode,
-tiny, dequant_120b (the standalone dequant of a 120b-shaped w13 bank),
-dequant_host_120b (the same bank dequantized on copy from page-locked host
-memory) and copy
-(a plain 1 GiB device copy: the achievable-bandwidth reference that also
-calibrates the HBM byte counters).
+tiny, dequant_120b (the standalone dequant of both 120b-shaped expert banks),
+dequant_host_120b (the w13 bank dequantized on copy from page-locked host
+memory) and copy (a plain 1 GiB device copy: the achievable-bandwidth
+reference that also calibrates the HBM byte counters).
+
+The default run (120b_prefill without --only) also times the 20b decode layer
+(T=4) and the dequant of the 120b banks, each in a timed region of its own
+after the headline one, and reports them under config.decode_20b and
+config.dequant_120b; `value` stays the 120b long prefill's tokens/s.
 """
 
 from __future__ import annotations
@@ -67,32 +71,55 @@ def measured_traffic(workload, kernel_tag):
     return None if ent is None else float(ent["bytes"])
 
 
+def cpu_model():
+    """The host CPU's model name, from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
+
+
 def cpu_baseline_moe(layer, spec, nvfp4=False, router=False, budget_s=15.0):
-    """Time the float64 CPU oracle, single-threaded, on the first tokens of the same layer."""
+    """Time the float64 CPU oracle on the first tokens of the same layer, on one
+    core: the process is pinned to one CPU for the run and BLAS/OpenMP pools
+    are limited to one thread."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
     from oracle import mxfp4_moe as O
 
+    allowed = os.sched_getaffinity(0)
+    core = min(allowed)
+    os.sched_setaffinity(0, {core})
     n = 1
     elapsed = 0.0
-    with threadpool_limits(limits=1):
-        while True:
-            tokens = np.arange(min(n, spec.T))
-            t0 = time.perf_counter()
-            fwd = O.moe_forward_nvfp4 if nvfp4 else O.moe_forward_router if router else O.moe_forward
-            fwd(layer, spec.top_k, tokens=tokens)
-            elapsed = time.perf_counter() - t0
-            if elapsed >= budget_s / 3 or n >= spec.T:
-                break
-            n *= 2
+    try:
+        with threadpool_limits(limits=1):
+            while True:
+                tokens = np.arange(min(n, spec.T))
+                t0 = time.perf_counter()
+                fwd = O.moe_forward_nvfp4 if nvfp4 else O.moe_forward_router if router else O.moe_forward
+                fwd(layer, spec.top_k, tokens=tokens)
+                elapsed = time.perf_counter() - t0
+                if elapsed >= budget_s / 3 or n >= spec.T:
+                    break
+                n *= 2
+    finally:
+        os.sched_setaffinity(0, allowed)
+    flops = 6.0 * spec.H * spec.I * spec.top_k * len(tokens)
     return {
         "value": len(tokens) / elapsed,
         "unit": "tokens/s",
         "cores": 1,
         "kind": "oracle",
+        "gflops": flops / elapsed / 1e9,
+        "cpu": f"1 of {os.cpu_count()} host cores ({cpu_model()}), pinned to core {core}",
         "sample": f"first {len(tokens)} of {spec.T} tokens of the same layer through the float64 numpy "
-                  f"oracle, one BLAS thread, {elapsed:.1f} s (host has {os.cpu_count()} cores)",
+                  f"oracle, one thread, {elapsed:.1f} s",
     }
 
 
@@ -138,6 +165,7 @@ def run_moe(args):
 
     from mxfp4_quantized_expert_amd import binding, workloads
 
+    torch.cuda.synchronize()
     nvfp4 = args.workload.startswith("nvfp4_")
     router = args.workload.startswith("router_")
     base = args.workload[len("nvfp4_"):] if nvfp4 else args.workload[len("router_"):] if router else args.workload
@@ -291,6 +319,7 @@ def run_moe(args):
     roof["kernel_ms"] = kms
     roof["algorithmic"] = per_unit
     layer_tflops = flops_total / (ms_per_step / 1e3) / 1e12
+    # active experts' packed weights, scales and biases + x + logits + y
     alg_bytes = active_bytes + T * H * 2 + T * E * 4 + T * H * 2
     log(f"[bench] per call: median {per_call['median']:.4f} ms, p10 {per_call['p10']:.4f}, "
         f"p90 {per_call['p90']:.4f} ({per_call['calls']} calls)")
@@ -373,6 +402,18 @@ def run_dequant_host(args):
     chunk_rows = N // n_chunks
     kernel_bytes = chunk_rows * (bank.K // 2 + bank.K // 32 + bank.K * 2)
     kmean = float(np.mean(kms))
+    # the plain page-locked host -> device copy of the same packed bytes: the PCIe bound
+    db = torch.empty(hb.shape, dtype=torch.uint8, device="cuda")
+    ds = torch.empty(hs.shape, dtype=torch.uint8, device="cuda")
+    db.copy_(hb, non_blocking=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        db.copy_(hb, non_blocking=True)
+        ds.copy_(hs, non_blocking=True)
+    torch.cuda.synchronize()
+    h2d_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    del db, ds
     return {
         "metric": "mxfp4 dequant-on-copy from host memory, host GB/s",
         "value": host_bytes / (ms / 1e3) / 1e9,
@@ -382,7 +423,10 @@ def run_dequant_host(args):
         "dtype": "u8->bf16", "data": "synthetic",
         "config": {"workload": f"dequant-on-copy of a gpt-oss-120b shaped w13 bank {list(blocks.shape)} from "
                                f"page-locked host memory, {n_chunks} chunks through two staging slots",
-                   "output_gbs": out.numel() * 2 / (ms / 1e3) / 1e9},
+                   "output_gbs": out.numel() * 2 / (ms / 1e3) / 1e9,
+                   "plain_h2d_copy_ms": h2d_ms,
+                   "plain_h2d_copy_gbs": host_bytes / (h2d_ms / 1e3) / 1e9,
+                   "frac_of_plain_h2d": h2d_ms / ms},
         "roofline": {"bound": "hbm", "achieved": kernel_bytes / (kmean / 1e3) / 1e9, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": kernel_bytes / (kmean / 1e3) / 1e9 / PEAK_HBM_GBS, "traffic": None,
                      "kernel": "mxfp4_dequant_kernel (one chunk)", "kernel_ms": kmean},
@@ -398,29 +442,37 @@ def run_copy(args):
 
 
 def run_dequant(args):
+    """mxfp4_dequantize of both gpt-oss-120b shaped expert banks (w13 [128, 5760, 2880]
+    and w2 [128, 2880, 2880]); a step dequantizes both."""
     import numpy as np
     import torch
 
     from mxfp4_quantized_expert_amd import binding, workloads
 
-    bank = workloads.DEQUANT_BANK_120B[0]
-    blocks, scales = workloads.make_bank(bank)
-    b = torch.from_numpy(blocks).cuda()
-    s = torch.from_numpy(scales).cuda()
-    out = torch.empty(blocks.shape[:-1] + (bank.K,), dtype=torch.bfloat16, device="cuda")
+    banks = []
+    for bank in workloads.DEQUANT_BANK_120B:
+        blocks, scales = workloads.make_bank(bank)
+        banks.append((blocks, scales, torch.from_numpy(blocks).cuda(), torch.from_numpy(scales).cuda(),
+                      torch.empty(blocks.shape[:-1] + (bank.K,), dtype=torch.bfloat16, device="cuda")))
+
+    def step(_=None):
+        for _, _, b, s, out in banks:
+            binding.mxfp4_dequantize(b, s, out=out)
+
     for _ in range(args.warmup):
-        binding.mxfp4_dequantize(b, s, out=out)
+        step()
     torch.cuda.synchronize()
-    binding.profile_begin("dequant", args.steps)
+    binding.profile_begin("dequant", 2 * args.steps)
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        binding.mxfp4_dequantize(b, s, out=out)
+        step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    kms = float(np.mean(binding.profile_end(args.steps)))
+    kms = 2 * float(np.mean(binding.profile_end(2 * args.steps)))  # both banks, kernel time
     ms = (t1 - t0) * 1e3 / args.steps
-    nbytes = blocks.nbytes + scales.nbytes + out.numel() * 2
-    per_call = per_call_spread(lambda i: binding.mxfp4_dequantize(b, s, out=out), args.steps)
+    nbytes = sum(bl.nbytes + sc.nbytes + out.numel() * 2 for bl, sc, _, _, out in banks)
+    elements = sum(out.numel() for *_, out in banks)
+    per_call = per_call_spread(step, args.steps)
     res = {
         "metric": "mxfp4_dequantize HBM GB/s",
         "value": nbytes / (ms / 1e3) / 1e9,
@@ -428,24 +480,43 @@ def run_dequant(args):
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "u8->bf16", "data": "synthetic",
-        "config": {"workload": f"dequant of a gpt-oss-120b shaped w13 bank {list(blocks.shape)} -> bf16",
-                   "per_call_ms": per_call},
+        "config": {"workload": "dequant of both gpt-oss-120b shaped expert banks, w13 "
+                               f"{list(banks[0][0].shape)} and w2 {list(banks[1][0].shape)} packed -> bf16",
+                   "elements": elements, "bytes_per_step": nbytes, "per_call_ms": per_call},
         "roofline": {"bound": "hbm", "achieved": nbytes / (kms / 1e3) / 1e9, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": nbytes / (kms / 1e3) / 1e9 / PEAK_HBM_GBS, "traffic": None,
-                     "kernel": "mxfp4_dequant_kernel", "kernel_ms": kms},
+                     "kernel": "mxfp4_dequant_kernel", "kernel_ms": kms,
+                     "algorithmic": "2.53125 B per element (0.5 packed + 1/32 scale + 2 bf16 out) x "
+                                    f"{elements} elements"},
     }
     if not args.no_cpu_baseline:
         from oracle import mxfp4_moe as O
+        blocks, scales = banks[0][0], banks[0][1]
         t0 = time.perf_counter()
         n = 0
-        while time.perf_counter() - t0 < 10.0 and n < bank.E:
+        while time.perf_counter() - t0 < 10.0 and n < blocks.shape[0]:
             O.mxfp4_dequantize(blocks[n], scales[n])
             n += 1
         el = time.perf_counter() - t0
         per = (blocks[0].nbytes + scales[0].nbytes + blocks[0].size * 4)
         res["cpu_baseline"] = {"value": n * per / el / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-                               "sample": f"{n} of {bank.E} experts, numpy oracle, {el:.1f} s"}
+                               "sample": f"{n} of {blocks.shape[0]} w13 experts, numpy oracle, {el:.1f} s"}
     return res
+
+
+def compact(res):
+    """The figures of a secondary workload that go into the headline line's config."""
+    out = {"workload": res["config"]["workload"], "metric": res["metric"], "value": res["value"],
+           "unit": res["unit"], "ms_per_step": res["ms_per_step"], "steps": res["steps"]}
+    for key in ("per_call_ms", "layer_algorithmic_gbs", "layer_frac_hbm_peak", "active_experts", "stage_ms",
+                "weight_copies_rotated"):
+        if key in res["config"]:
+            out[key] = res["config"][key]
+    r = res.get("roofline")
+    if r is not None:
+        out["roofline"] = {k: r[k] for k in ("bound", "achieved", "peak", "unit", "frac", "kernel", "kernel_ms")
+                           if k in r}
+    return out
 
 
 def main():
@@ -458,6 +529,11 @@ def main():
                              "nvfp4_20b_prefill", "nvfp4_120b_prefill", "router_20b_decode", "router_120b_prefill",
                              "dequant_120b", "dequant_host_120b", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", action="store_true",
+                    help="measure the named workload alone (the default run also times the 20b decode layer "
+                         "and the 120b dequant after the 120b long prefill)")
+    ap.add_argument("--decode-steps", type=int, default=400,
+                    help="timed calls of the 20b decode layer in the default run")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of a HIP graph of one layer call instead of eager calls")
     ap.add_argument("--act", default="bf16", choices=["bf16", "mxfp8_split", "mxfp8"],
@@ -483,6 +559,17 @@ def main():
         res = run_copy(args)
     else:
         res = run_moe(args)
+        if args.workload == "120b_prefill" and not args.only and args.act == "bf16" and not args.graph:
+            # the decode half of the metric and the dequant, each in a timed region of its own
+            sub = argparse.Namespace(**vars(args))
+            sub.workload, sub.steps, sub.warmup, sub.no_cpu_baseline = "20b_decode", args.decode_steps, 10, True
+            res["config"]["decode_20b"] = compact(run_moe(sub))
+            sub.workload, sub.steps, sub.warmup = "dequant_120b", 5, 2
+            res["config"]["dequant_120b"] = compact(run_dequant(sub))
+            d = res["config"]["decode_20b"]
+            log(f"[bench] 20b decode: {d['ms_per_step'] * 1e3:.1f} us/call, {d['layer_algorithmic_gbs']:.0f} GB/s "
+                f"({100 * d['layer_frac_hbm_peak']:.1f} % of HBM peak); dequant "
+                f"{res['config']['dequant_120b']['value']:.0f} GB/s")
     print(json.dumps(res), flush=True)
 
 

@@ -34,7 +34,7 @@ extern "C" {
 #define MXFP4MOE_ERR_ARG (-1)       /* NULL pointer or otherwise invalid argument          */
 #define MXFP4MOE_ERR_SHAPE (-2)     /* sizes out of range or not multiples of 32           */
 #define MXFP4MOE_ERR_WORKSPACE (-3) /* workspace smaller than the size the query returned   */
-#define MXFP4MOE_ERR_ALIGN (-4)     /* a pointer is not 16-byte aligned                    */
+#define MXFP4MOE_ERR_ALIGN (-4)     /* a pointer is not aligned as its call requires        */
 #define MXFP4MOE_ERR_HIP (-5)       /* the HIP runtime rejected a launch                   */
 
 /* Largest supported expert count and top_k. */
@@ -145,11 +145,11 @@ int moe_mxfp4_route(const float* router_logits, int64_t T, int64_t E, int64_t to
  *   x             [T, H] bf16, 16-byte aligned
  *   router_logits [T, E] float32
  *   w13_blocks    [E, 2I, H/2] uint8, 16-byte aligned   (row 2i = gate i, row 2i+1 = up i)
- *   w13_scales    [E, 2I, H/32] uint8
- *   w13_bias      [E, 2I] bf16
+ *   w13_scales    [E, 2I, H/32] uint8, 16-byte aligned
+ *   w13_bias      [E, 2I] bf16, 8-byte aligned
  *   w2_blocks     [E, H, I/2] uint8, 16-byte aligned
- *   w2_scales     [E, H, I/32] uint8
- *   w2_bias       [E, H] bf16
+ *   w2_scales     [E, H, I/32] uint8, 16-byte aligned
+ *   w2_bias       [E, H] bf16, 8-byte aligned
  *   y             [T, H] bf16 out, 16-byte aligned, must not alias any input
  *   H, I multiples of 32 in [32, MXFP4MOE_MAX_HIDDEN]; 1 <= E <= MXFP4MOE_MAX_EXPERTS;
  *   1 <= top_k <= min(E, MXFP4MOE_MAX_TOPK); T >= 0.
@@ -165,8 +165,13 @@ int moe_mxfp4_route(const float* router_logits, int64_t T, int64_t E, int64_t to
  * partial), one with 5..127 pairs into tiles of at most 64, one with at most
  * 4 pairs makes one streaming tile; each kind has a GEMM kernel of its own
  * (with T <= 4 every expert has one streaming tile: the decode path).
- * MXFP4MOE_PATH=stream in the environment sends every pair through the
- * streaming kernels, in tiles of 4.
+ *
+ * E8M0 byte 0xFF (NaN) in a weight row makes that row's GEMM output NaN for
+ * every token of the expert: a 0xFF in gate_up row r of expert e gives NaN in
+ * the whole output row of every token routed to e; a 0xFF in down row n gives
+ * NaN in column n of those tokens' outputs.  Nothing else changes.  Scale
+ * bytes 253 and 254 with the largest codes overflow the bf16 weights to inf
+ * (unspecified outputs); 0..252 are exact.
  */
 int moe_mxfp4_forward(const uint16_t* x, const float* router_logits,
                       const uint8_t* w13_blocks, const uint8_t* w13_scales, const uint16_t* w13_bias,
@@ -191,7 +196,8 @@ int moe_mxfp4_forward(const uint16_t* x, const float* router_logits,
  *           (v_mfma_scale_f32_32x32x64_f8f6f4): packed E2M1 weights with their
  *           E8M0 scales times activations quantized to MXFP8 (E4M3 in blocks
  *           of 32, one E8M0 scale per block, shared exponent
- *           floor(log2 max) - 7, round to nearest even) plus the MXFP8
+ *           floor(log2 max) - 7 by this library's own rule, round to
+ *           nearest even) plus the MXFP8
  *           quantization of the residual; about 1e-3 normwise from the
  *           exact layer on the test layers.  The SwiGLU output is rounded to
  *           bf16, then quantized the same way.
@@ -201,11 +207,19 @@ int moe_mxfp4_forward(const uint16_t* x, const float* router_logits,
  * Experts with fewer pairs keep the exact bf16 path.  The two ACT flags are
  * exclusive (SPLIT wins); the workspace query must pass the same flags (the
  * quantized activations live in the workspace).  Not available for NVFP4.
+ * How a 0xFF scale byte acts on the ACT paths is unspecified.
+ *
+ *   flags |= MXFP4MOE_TILES_STREAM   every pair in streaming tiles of at most
+ *           4 pairs, whatever the expert loads (the decode kernels on every
+ *           shape: a check of those kernels, not a faster path).  Same
+ *           results within the tolerance of the layer; with it the ACT
+ *           flags find no full tiles and change nothing.
  * Any other flag bit is MXFP4MOE_ERR_ARG.
  */
 #define MXFP4MOE_GATE_UP_SPLIT 1u
 #define MXFP4MOE_ACT_MXFP8 2u
 #define MXFP4MOE_ACT_MXFP8_SPLIT 4u
+#define MXFP4MOE_TILES_STREAM 8u
 int moe_mxfp4_forward_ex(const uint16_t* x, const float* router_logits,
                          const uint8_t* w13_blocks, const uint8_t* w13_scales, const uint16_t* w13_bias,
                          const uint8_t* w2_blocks, const uint8_t* w2_scales, const uint16_t* w2_bias,
@@ -224,8 +238,10 @@ int moe_mxfp4_forward_ex(const uint16_t* x, const float* router_logits,
  *           E8M0 bytes of groups 2c, 2c+1, then the residual's (127 unless split)
  * A chunk past K (K % 64 == 32) holds zero codes and scale 127.  Encodings
  * (OCP Microscaling Formats v1.0): E4M3 elements in blocks of 32 sharing one
- * E8M0 scale; the shared exponent is floor(log2(max|v|)) - 7 (127 for an
- * all-zero block) and elements round to nearest, ties to even.
+ * E8M0 scale.  The shared exponent floor(log2(max|v|)) - 7 is this library's
+ * own choice (the specification subtracts emax = 8 and clamps at 448; one
+ * more keeps every scaled value below 256); 127 for an all-zero block;
+ * elements round to nearest, ties to even.
  */
 int moe_mxfp8_quantize(const uint16_t* src, int64_t rows, int64_t K, int split, uint8_t* codes,
                        uint8_t* scales, void* stream);
@@ -281,8 +297,10 @@ int moe_mxfp4_forward_router(const uint16_t* x, const uint16_t* router_w, const 
  *
  *   w13_blocks [E, 2I, H/2] uint8, w13_scales [E, 2I, H/16] uint8 (E4M3),
  *   w13_scale2 [E] float32, w2_blocks [E, H, I/2], w2_scales [E, H, I/16],
- *   w2_scale2 [E] float32; everything else as moe_mxfp4_forward (gate/up rows
- *   interleaved), and the same workspace query.
+ *   w2_scale2 [E] float32 (4-byte aligned); everything else as moe_mxfp4_forward
+ *   (gate/up rows interleaved, scales 16-byte and biases 8-byte aligned), and
+ *   the same workspace query.  An E4M3 NaN scale byte (0x7F, 0xFF) makes its
+ *   weights NaN, with the same effect on the outputs as an E8M0 0xFF.
  * Every pair runs in mid-size or streaming tiles.  A NULL second-level scale
  * with a workspace is MXFP4MOE_ERR_ARG.
  */

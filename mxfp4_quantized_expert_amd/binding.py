@@ -21,7 +21,7 @@ STATUS = {
     -1: "invalid argument",
     -2: "unsupported shape",
     -3: "workspace too small",
-    -4: "pointer not 16-byte aligned",
+    -4: "pointer not aligned as required",
     -5: "HIP launch error",
 }
 
@@ -221,7 +221,9 @@ def moe_mxfp4_router(x: torch.Tensor, router_w: torch.Tensor, router_b: torch.Te
     return logits, ids, w
 
 
+FLAG_GATE_UP_SPLIT = 1
 ACT_FLAGS = {"bf16": 0, "mxfp8": 2, "mxfp8_split": 4}
+FLAG_TILES_STREAM = 8
 
 
 def workspace_bytes(T: int, H: int, I: int, E: int, top_k: int, flags: int = 0) -> int:
@@ -239,11 +241,13 @@ def moe_mxfp4_forward(x: torch.Tensor, router_logits: torch.Tensor,
                       w2_blocks: torch.Tensor, w2_scales: torch.Tensor, w2_bias: torch.Tensor,
                       top_k: int, out: Optional[torch.Tensor] = None,
                       workspace: Optional[torch.Tensor] = None, stream=None,
-                      gate_up_split: bool = False, act: str = "bf16") -> torch.Tensor:
+                      gate_up_split: bool = False, act: str = "bf16",
+                      stream_tiles_only: bool = False) -> torch.Tensor:
     """One MXFP4 MoE expert layer; returns y [T, H] bfloat16.  gate_up_split: w13 rows are
     [I gate rows; I up rows] instead of interleaved.  act: "bf16" (exact), or the opt-in
     FP4 scaled-MFMA path for experts with at least 128 pairs over MXFP8 activations,
-    "mxfp8_split" (high part + residual) or "mxfp8" (one tensor)."""
+    "mxfp8_split" (high part + residual) or "mxfp8" (one tensor).  stream_tiles_only:
+    every pair through the streaming kernels (MXFP4MOE_TILES_STREAM)."""
     lib = load()
     T, H = x.shape
     E = router_logits.shape[1]
@@ -259,7 +263,7 @@ def moe_mxfp4_forward(x: torch.Tensor, router_logits: torch.Tensor,
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
     _check(out, "out", torch.bfloat16, (T, H))
-    flags = (1 if gate_up_split else 0) | ACT_FLAGS[act]
+    flags = (FLAG_GATE_UP_SPLIT if gate_up_split else 0) | ACT_FLAGS[act] | (FLAG_TILES_STREAM if stream_tiles_only else 0)
     if workspace is None:  # a caller's workspace is size-checked by the library
         workspace = torch.empty((max(workspace_bytes(T, H, I, E, top_k, flags), 1),), dtype=torch.uint8, device=x.device)
     _check(workspace, "workspace", torch.uint8)

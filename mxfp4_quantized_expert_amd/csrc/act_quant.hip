@@ -1,9 +1,11 @@
 // Block-scaled FP8 activations for the FP4 scaled-MFMA path (opt-in).
 //
-// OCP Microscaling Formats v1.0: MXFP8 E4M3 elements in blocks of 32 along
-// K sharing one E8M0 scale.  The shared exponent is floor(log2(max|v|)) - 7
-// (scaled magnitudes below 256, so no element needs clamping; an all-zero
-// block takes 127) and elements round to nearest, ties to even.  "split"
+// Encodings of the OCP Microscaling Formats v1.0: MXFP8 E4M3 elements in
+// blocks of 32 along K sharing one E8M0 scale.  The shared exponent is this
+// implementation's own choice, floor(log2(max|v|)) - 7, one more than the
+// specification's floor(log2(max|v|)) - emax (emax = 8 for E4M3): scaled
+// magnitudes stay below 256, so no element needs clamping.  An all-zero block
+// takes 127; elements round to nearest, ties to even.  "split"
 // activations add the MXFP8 tensor of the residual v - hi, which brings the
 // product within about 2^-8 of the block maximum of the exact bf16 value.
 //

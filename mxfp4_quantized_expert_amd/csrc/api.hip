@@ -3,8 +3,6 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
-#include <cstdlib>
-#include <cstring>
 #include <mutex>
 #include <vector>
 
@@ -118,15 +116,7 @@ Layout make_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k, bo
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
-
-// Full tiles of kWideTokens pairs go to the wide kernel unless the
-// environment asks for the streaming kernel alone (MXFP4MOE_PATH=stream, used
-// to test that kernel on every shape).
-int big_tile_tokens() {
-  const char* env = std::getenv("MXFP4MOE_PATH");
-  if (env != nullptr && std::strcmp(env, "stream") == 0) return 0;
-  return kWideTokens;
-}
+bool aligned8(const void* p) { return ((uintptr_t)p & 7u) == 0; }
 
 int check_route_shape(int64_t T, int64_t E, int64_t top_k) {
   if (T < 0 || E < 1 || E > MXFP4MOE_MAX_EXPERTS) return MXFP4MOE_ERR_SHAPE;
@@ -143,7 +133,8 @@ using namespace mxfp4moe;
 namespace {
 
 const float kNvQuery = 0.f;  // stands in for the NVFP4 scale pointers of a size query
-constexpr uint32_t kForwardFlags = MXFP4MOE_GATE_UP_SPLIT | MXFP4MOE_ACT_MXFP8 | MXFP4MOE_ACT_MXFP8_SPLIT;
+constexpr uint32_t kForwardFlags =
+    MXFP4MOE_GATE_UP_SPLIT | MXFP4MOE_ACT_MXFP8 | MXFP4MOE_ACT_MXFP8_SPLIT | MXFP4MOE_TILES_STREAM;
 
 // The layer.  scale2_13 / scale2_2 != nullptr selects NVFP4 weights (E4M3
 // block scales per 16 elements, one second-level scale per expert and
@@ -181,6 +172,9 @@ int forward_impl(const uint16_t* x, const float* router_logits, const uint16_t* 
   if (*workspace_bytes < L.total) return MXFP4MOE_ERR_WORKSPACE;
   if (((uintptr_t)workspace & (kAlign - 1)) != 0) return MXFP4MOE_ERR_ALIGN;
   if (!aligned16(w13_blocks) || !aligned16(w2_blocks)) return MXFP4MOE_ERR_ALIGN;
+  // the GEMMs stage scale rows with 16-byte loads and read biases four at a time
+  if (!aligned16(w13_scales) || !aligned16(w2_scales)) return MXFP4MOE_ERR_ALIGN;
+  if (!aligned8(w13_bias) || !aligned8(w2_bias)) return MXFP4MOE_ERR_ALIGN;
   if (T > 0 && (!aligned16(x) || !aligned16(y))) return MXFP4MOE_ERR_ALIGN;
   if (T == 0) return MXFP4MOE_OK;
 
@@ -201,7 +195,9 @@ int forward_impl(const uint16_t* x, const float* router_logits, const uint16_t* 
   tt.num_mid = counts + 1;
   tt.small = reinterpret_cast<int32_t*>(ws + L.small);
   tt.num_small = counts + 2;
-  tt.big_tokens = nv ? 0 : big_tile_tokens();
+  // full tiles of kWideTokens pairs take the wide kernel unless the caller
+  // asked for streaming tiles only (a check of that kernel on every shape)
+  tt.big_tokens = nv || (flags & MXFP4MOE_TILES_STREAM) ? 0 : kWideTokens;
   tt.no_wide = nv ? 1 : 0;
   const TileBounds tb = tile_bounds(T, P, E, nv ? kTilesNoWide : tt.big_tokens > 0 ? kTilesWide : kTilesStreamOnly);
   hipStream_t s = (hipStream_t)stream;
@@ -272,7 +268,7 @@ const char* mxfp4moe_status_string(int status) {
     case MXFP4MOE_ERR_ARG: return "invalid argument (NULL pointer)";
     case MXFP4MOE_ERR_SHAPE: return "unsupported shape";
     case MXFP4MOE_ERR_WORKSPACE: return "workspace too small";
-    case MXFP4MOE_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case MXFP4MOE_ERR_ALIGN: return "pointer not aligned as required";
     case MXFP4MOE_ERR_HIP: return "HIP launch error";
     default: return "unknown status";
   }
@@ -348,6 +344,7 @@ int moe_nvfp4_forward(const uint16_t* x, const float* router_logits, const uint8
                       const uint16_t* w2_bias, uint16_t* y, int64_t T, int64_t H, int64_t I, int64_t E,
                       int64_t top_k, void* workspace, size_t* workspace_bytes, void* stream) {
   if (workspace != nullptr && (w13_scale2 == nullptr || w2_scale2 == nullptr)) return MXFP4MOE_ERR_ARG;
+  if (((uintptr_t)w13_scale2 & 3u) != 0 || ((uintptr_t)w2_scale2 & 3u) != 0) return MXFP4MOE_ERR_ALIGN;
   return forward_impl(x, router_logits, nullptr, nullptr, w13_blocks, w13_scales, w13_scale2 ? w13_scale2 : &kNvQuery,
                       w13_bias,
                       w2_blocks, w2_scales, w2_scale2 ? w2_scale2 : &kNvQuery, w2_bias, y, T, H, I, E, top_k, 0u,
@@ -358,6 +355,7 @@ int moe_mxfp8_quantize(const uint16_t* src, int64_t rows, int64_t K, int split, 
                        void* stream) {
   if (rows < 0 || K <= 0 || (K & 31) != 0 || K > ((int64_t)1 << 30) || rows > ((int64_t)1 << 40) / K)
     return MXFP4MOE_ERR_SHAPE;
+  if (rows > (int64_t)0x7fffffff) return MXFP4MOE_ERR_SHAPE;  // the kernel counts rows in int
   if (rows == 0) return MXFP4MOE_OK;
   if (src == nullptr || codes == nullptr || scales == nullptr) return MXFP4MOE_ERR_ARG;
   if (!aligned16(src) || !aligned16(codes) || ((uintptr_t)scales & 3u) != 0) return MXFP4MOE_ERR_ALIGN;

@@ -48,9 +48,11 @@ __device__ __forceinline__ int slot_col(int row, int part) {
 
 __device__ __forceinline__ float swiglu_clamped(float gate, float up) {
   // gpt-oss family constants: alpha 1.702, limit 7; gate clamped from above,
-  // up clamped on both sides, +1 after the clamp.
-  const float g = fminf(gate, 7.0f);
-  const float u = fminf(fmaxf(up, -7.0f), 7.0f);
+  // up clamped on both sides, +1 after the clamp.  The clamps are selects, not
+  // fminf/fmaxf, so that a NaN input (a weight group with scale byte 0xFF)
+  // stays NaN instead of becoming the limit.
+  const float g = gate > 7.0f ? 7.0f : gate;
+  const float u = up > 7.0f ? 7.0f : (up < -7.0f ? -7.0f : up);
   // sigmoid through the hardware reciprocal (about 1 ulp; the result is
   // rounded to bf16)
   return g * __builtin_amdgcn_rcpf(1.0f + __expf(-1.702f * g)) * (u + 1.0f);
@@ -90,30 +92,34 @@ __device__ __forceinline__ f32x4 load_bias4(const uint16_t* bias, int n, int N, 
 // MXFP4: one E8M0 byte for all 32.  NVFP4: two E4M3 block scales, the first
 // for the codes of steps 0 and 1, the second for steps 2 and 3; the result is
 // exact in bf16 (a code has at most 2 significant bits, an E4M3 value 4).
+// MXFP4: E8M0 byte 0xFF is NaN, so the group's weights are NaN (OCP MX).  A
+// single NaN element is enough to make every dot product over the group NaN,
+// so the NaN is OR-ed into the first two converted elements of the group only
+// (nan_mask: 0x7FC07FC0 for byte 0xFF, else 0).  NVFP4's E4M3 NaN scale
+// reaches the weights through the float32 conversion by itself.
 template <bool kNv>
 struct GroupScale {
   float lo, hi;
-  __device__ __forceinline__ GroupScale(const uint8_t* srow, int g) {
-    if (kNv) {
-      lo = mx::e4m3_operand(srow[2 * g]);
-      hi = mx::e4m3_operand(srow[2 * g + 1]);
-    } else {
-      lo = hi = mx::e8m0_operand(srow[g]);
-    }
-  }
+  uint32_t nan;
+  __device__ __forceinline__ GroupScale(const uint8_t* srow, int g) : GroupScale(kNv ? srow[2 * g] : srow[g],
+                                                                                   kNv ? srow[2 * g + 1] : 0u) {}
   // from the group's scale byte(s) already read (b1 only for NVFP4)
   __device__ __forceinline__ GroupScale(uint32_t b0, uint32_t b1) {
     if (kNv) {
       lo = mx::e4m3_operand(b0);
       hi = mx::e4m3_operand(b1);
+      nan = 0u;
     } else {
       lo = hi = mx::e8m0_operand(b0);
+      nan = mx::e8m0_nan_mask(b0);
     }
   }
   __device__ __forceinline__ float step(int s) const { return s < 2 ? lo : hi; }
   // eight codes of step s as bf16
   __device__ __forceinline__ u32x4 convert(uint32_t packed, int s) const {
-    return kNv ? mx::fp4x8_to_bf16x8_any_scale(packed, step(s)) : mx::fp4x8_to_bf16x8(packed, step(s));
+    u32x4 r = kNv ? mx::fp4x8_to_bf16x8_any_scale(packed, step(s)) : mx::fp4x8_to_bf16x8(packed, step(s));
+    if (!kNv && s == 0) r[0] |= nan;
+    return r;
   }
 };
 
@@ -155,13 +161,18 @@ struct NoExtra {
 
 // `extra(k)` runs right after the k-th MFMA of the chunk (k = 0 .. 4*RN*RM-1),
 // so a caller can spread other instructions between the MFMAs.
+// nanm[rb]: the NaN mask of fragment rb's scale byte (see GroupScale), OR-ed
+// into its first converted elements.
 template <int RN, int RM, typename Extra = NoExtra>
 __device__ __forceinline__ void chunk_mma_regs(f32x16 (&acc)[RN][RM], const bf16x8 (&b)[4][RM],
                                                const u32x4 (&w)[RN], const float (&sc)[RN],
-                                               Extra extra = Extra()) {
+                                               const uint32_t (&nanm)[RN], Extra extra = Extra()) {
   u32x4 a[2][RN];
 #pragma unroll
-  for (int rb = 0; rb < RN; ++rb) a[0][rb] = mx::fp4x8_to_bf16x8(w[rb][0], sc[rb]);
+  for (int rb = 0; rb < RN; ++rb) {
+    a[0][rb] = mx::fp4x8_to_bf16x8(w[rb][0], sc[rb]);
+    a[0][rb][0] |= nanm[rb];
+  }
   auto convert = [&](int s, int i) {  // converts pair i%4 of fragment i/4 for step s
     const int rb = i / 4, sel = i % 4;
     const uint32_t packed = w[rb][s];
@@ -546,12 +557,14 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void expert_wide_kernel(mxfp4moe::
       const bool glive = 2 * c + half < kgroups;
       u32x4 w[RN];
       float sc[RN];
+      uint32_t nanm[RN];
 #pragma unroll
       for (int rb = 0; rb < RN; ++rb) {
         w[rb] = glive ? cur.w[rb] : u32x4{0u, 0u, 0u, 0u};
         sc[rb] = mx::e8m0_operand(cur.sb[rb]);
+        nanm[rb] = mx::e8m0_nan_mask(cur.sb[rb]);
       }
-      chunk_mma_regs<RN, RM>(acc, cur.b, w, sc, extra);
+      chunk_mma_regs<RN, RM>(acc, cur.b, w, sc, nanm, extra);
     } else {
       issue(c + kStages, st);
     }
@@ -599,12 +612,14 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void expert_wide_kernel(mxfp4moe::
         const bool glive = 2 * c + half < kgroups;
         u32x4 w[RN];
         float sc[RN];
+        uint32_t nanm[RN];
 #pragma unroll
         for (int rb = 0; rb < RN; ++rb) {
           w[rb] = glive ? cur.w[rb] : u32x4{0u, 0u, 0u, 0u};
           sc[rb] = mx::e8m0_operand(cur.sb[rb]);
+          nanm[rb] = mx::e8m0_nan_mask(cur.sb[rb]);
         }
-        chunk_mma_regs<RN, RM>(acc, cur.b, w, sc, extra);
+        chunk_mma_regs<RN, RM>(acc, cur.b, w, sc, nanm, extra);
       } else {
         issue(c + 2, (st + 2) % kStages);
       }

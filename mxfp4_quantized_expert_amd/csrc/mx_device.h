@@ -21,6 +21,10 @@ typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
 // 16 codes x 255 finite scale bytes against the exact values.
 __device__ __forceinline__ float e8m0_operand(uint32_t s) { return __uint_as_float(s << 23); }
 
+// E8M0 byte 0xFF is NaN: two quiet-NaN bf16 to OR into converted weights of
+// that group (any bf16 OR 0x7FC0 is a NaN), else 0.
+__device__ __forceinline__ uint32_t e8m0_nan_mask(uint32_t s) { return s == 255u ? 0x7fc07fc0u : 0u; }
+
 // Two E2M1 codes (byte `SEL` of `packed`; low nibble -> low half) times the
 // scale, rounded to bf16.  Exact for finite scales (the products have at most
 // two significant bits and stay inside bf16's range or overflow to +-inf).
@@ -42,7 +46,6 @@ __device__ __forceinline__ u32x4 fp4x8_to_bf16x8(uint32_t packed, float scale) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// float -> bf16 bits, round to nearest, ties to even; NaN -> 0x7FC0.
 // FP8 E4M3 byte (OCP, finite-only: 4 exponent bits with bias 7, 3 mantissa
 // bits, exponent field 0 subnormal, S.1111.111 NaN) -> float, exactly.  The
 // NVFP4 block scale.

@@ -397,11 +397,13 @@ def moe_forward(layer: Dict[str, np.ndarray], top_k: int,
 # accumulation of exact bf16 products only); it is defined here so that the
 # GPU's quantized codes can be checked exactly.  Encodings from the OCP
 # Microscaling Formats v1.0 specification: MXFP8 E4M3 elements in blocks of
-# 32 along K sharing one E8M0 scale.  Reading: the shared exponent is
-# floor(log2(max|v|)) - 7, one below the specification's emax-based choice,
-# so that no element of a block needs clamping (scaled magnitudes stay below
-# 256 <= 448); an all-zero block takes scale byte 127.  "split" activations
-# add a second MXFP8 tensor that quantizes the residual v - hi the same way.
+# 32 along K sharing one E8M0 scale.  The shared exponent is this
+# implementation's own choice, floor(log2(max|v|)) - 7: the specification
+# subtracts the element format's emax (8 for E4M3), which puts the scaled
+# block maximum in [256, 512) and clamps what exceeds 448; subtracting 7 keeps every
+# scaled magnitude below 256, so no element is clamped.  An all-zero block
+# takes scale byte 127.  "split" activations add a second MXFP8 tensor that
+# quantizes the residual v - hi the same way.
 # --------------------------------------------------------------------------
 
 def e4m3_encode_rne(v) -> np.ndarray:

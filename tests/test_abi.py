@@ -75,9 +75,9 @@ def test_dequant_from_host_argument_checks(lib):
 
 
 def _fwd(lib, T=4, H=64, I=64, E=4, k=2, ws=A, ws_bytes=1 << 30, x=A, lg=A, b13=A, b2=A, y=A,
-         wb=A):
+         wb=A, s13=A, s2=A):
     n = ctypes.c_size_t(ws_bytes)
-    return lib.moe_mxfp4_forward(x, lg, wb, A, b13, wb, A, b2, y, T, H, I, E, k, ws,
+    return lib.moe_mxfp4_forward(x, lg, wb, s13, b13, wb, s2, b2, y, T, H, I, E, k, ws,
                                  ctypes.byref(n), None), n.value
 
 
@@ -109,6 +109,10 @@ def test_forward_argument_checks(lib):
     assert _fwd(lib, ws=A + 16)[0] == -4
     assert _fwd(lib, x=A + 2)[0] == -4
     assert _fwd(lib, wb=A + 4)[0] == -4
+    assert _fwd(lib, s13=A + 8)[0] == -4      # scale rows are staged with 16-byte loads
+    assert _fwd(lib, s2=A + 4)[0] == -4
+    assert _fwd(lib, b13=A + 4)[0] == -4      # biases are read four at a time
+    assert _fwd(lib, b2=A + 2)[0] == -4
     n = ctypes.c_size_t(0)
     assert lib.moe_mxfp4_forward(A, A, A, A, A, A, A, A, A, 4, 64, 64, 4, 2, A, None, None) == -1
     assert _fwd(lib, T=0, x=None, lg=None, y=None)[0] == 0  # empty batch: nothing to do
@@ -118,7 +122,8 @@ def test_forward_argument_checks(lib):
 def test_forward_ex_rejects_unknown_flags(lib):
     n = ctypes.c_size_t(0)
     f = lib.moe_mxfp4_forward_ex
-    assert f(A, A, A, A, A, A, A, A, A, 4, 64, 64, 4, 2, 8, None, ctypes.byref(n), None) == -1
+    assert f(A, A, A, A, A, A, A, A, A, 4, 64, 64, 4, 2, 16, None, ctypes.byref(n), None) == -1
+    assert f(A, A, A, A, A, A, A, A, A, 4, 64, 64, 4, 2, 8, None, ctypes.byref(n), None) == 0  # streaming tiles
     assert f(A, A, A, A, A, A, A, A, A, 4, 64, 64, 4, 2, 1, None, ctypes.byref(n), None) == 0 and n.value > 0
     base = n.value
     # the MXFP8 activation flags need room for the quantized activations
@@ -138,6 +143,8 @@ def test_nvfp4_forward_argument_checks(lib):
     assert f(A, A, A, A, None, A, A, A, A, A, A, 4, 64, 64, 4, 2, A, ctypes.byref(big), None) == -1  # no scale2
     assert f(A, A, A, A, A, A, A, A, None, A, A, 4, 64, 64, 4, 2, A, ctypes.byref(big), None) == -1
     assert f(A, A, A, A, A, A, A, A, A, A, A, 4, 48, 64, 4, 2, A, ctypes.byref(big), None) == -2
+    assert f(A, A, A, A, A + 2, A, A, A, A, A, A, 4, 64, 64, 4, 2, A, ctypes.byref(big), None) == -4  # scale2
+    assert f(A, A, A, A + 8, A, A, A, A, A, A, A, 4, 64, 64, 4, 2, A, ctypes.byref(big), None) == -4  # scales
 
 
 def test_route_argument_checks(lib):
@@ -170,7 +177,7 @@ def test_forward_router_argument_checks(lib):
     w = [A] * 6
     assert f(A, None, A, *w, A, 4, 64, 64, 4, 2, 0, A, ctypes.byref(big), None) == -1  # no router weights
     assert f(A, A, None, *w, A, 4, 64, 64, 4, 2, 0, A, ctypes.byref(big), None) == -1  # no router bias
-    assert f(A, A, A, *w, A, 4, 64, 64, 4, 2, 8, A, ctypes.byref(big), None) == -1     # unknown flag
+    assert f(A, A, A, *w, A, 4, 64, 64, 4, 2, 16, A, ctypes.byref(big), None) == -1    # unknown flag
     assert f(A, A + 2, A, *w, A, 4, 64, 64, 4, 2, 0, A, ctypes.byref(big), None) == -4  # misaligned router
     assert f(A, A, A, *w, A, 4, 48, 64, 4, 2, 0, A, ctypes.byref(big), None) == -2
 
@@ -184,3 +191,4 @@ def test_mxfp8_quantize_argument_checks(lib):
     assert f(A + 2, 4, 64, 1, A, A, None) == -4
     assert f(A, 4, 64, 1, A, A + 2, None) == -4  # scale rows are read as 4-byte words
     assert f(None, 0, 64, 1, None, None, None) == 0
+    assert f(A, 1 << 31, 64, 1, A, A, None) == -2  # more rows than the kernel counts

@@ -5,7 +5,6 @@ only while the GEMM source it was measured on is unchanged."""
 import importlib.util
 import json
 import os
-import shutil
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -29,16 +28,25 @@ def test_layer_bytes_at_gpt_oss_shapes():
 
 
 def test_traffic_reported_only_for_the_profiled_source(tmp_path):
+    # A counter record names the source it was measured on by its SHA-256: the
+    # figure is reported while that source is unchanged, and dropped after an edit.
+    import hashlib
+
     b = _bench()
-    rec = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))
-    key = "120b_prefill/gate_up_wide"
-    assert b.measured_traffic("120b_prefill", "gate_up_wide") == float(rec["kernels"][key]["bytes"])
-    assert b.measured_traffic("120b_prefill", "no_such_kernel") is None
-    # the same record next to an edited copy of the source: no figure
-    (tmp_path / "profiles").mkdir()
-    shutil.copy(os.path.join(ROOT, "profiles", "traffic.json"), tmp_path / "profiles" / "traffic.json")
-    src = tmp_path / rec["source"]
+    src = tmp_path / "pkg" / "kernels.hip"
     src.parent.mkdir(parents=True)
-    src.write_bytes(open(os.path.join(ROOT, rec["source"]), "rb").read() + b"\n// edited\n")
+    src.write_bytes(b"// a kernel source\n")
+    rec = {"source": "pkg/kernels.hip", "source_sha256": hashlib.sha256(src.read_bytes()).hexdigest(),
+           "kernels": {"120b_prefill/gate_up_wide": {"bytes": 723238121.0}}}
+    (tmp_path / "profiles").mkdir()
+    (tmp_path / "profiles" / "traffic.json").write_text(json.dumps(rec))
     b.ROOT = str(tmp_path)
+    assert b.measured_traffic("120b_prefill", "gate_up_wide") == 723238121.0
+    assert b.measured_traffic("120b_prefill", "no_such_kernel") is None
+    src.write_bytes(src.read_bytes() + b"// edited\n")
     assert b.measured_traffic("120b_prefill", "gate_up_wide") is None
+    # the committed record, if any, has the same form
+    committed = os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(committed):
+        rec = json.load(open(committed))
+        assert {"source", "source_sha256", "kernels"} <= set(rec)

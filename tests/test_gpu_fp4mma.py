@@ -14,7 +14,7 @@ import torch
 
 from mxfp4_quantized_expert_amd import workloads as W
 from oracle import mxfp4_moe as O
-from tests.helpers import assert_layer_parity, bf16_to_f64
+from tests.helpers import assert_layer_parity, bf16_to_f64, long_prefill_120b
 
 pytestmark = pytest.mark.gpu
 
@@ -77,14 +77,15 @@ def _run(gpu, L, k, act, tokens=None):
     return y
 
 
-def _check(gpu, L, k, act, label, tokens=None):
+def _check(gpu, L, k, act, label, tokens=None, exact=None):
     mode = "split" if act == "mxfp8_split" else "single"
     q = _quantized_experts(L, k)
     assert q.any(), "the case must have experts on the FP4 path"
     y = _run(gpu, L, k, act, tokens)
     ref = O.moe_forward_fp8act(L, k, q, mode, tokens=tokens)
     assert_layer_parity(y, ref, f"{label}/{act} vs its oracle")
-    exact = O.moe_forward(L, k, tokens=tokens)
+    if exact is None:
+        exact = O.moe_forward(L, k, tokens=tokens)
     rel, mx = O.parity_errors(bf16_to_f64(y), exact)
     print(f"[fp4mma] {label}/{act}: vs the exact layer normwise {rel:.3e}, max-element {mx:.3e}", flush=True)
     if act == "mxfp8_split":
@@ -118,8 +119,8 @@ def test_tile_boundaries_split(gpu):
 
 
 @pytest.mark.parametrize("act", ["mxfp8_split", "mxfp8"])
-def test_120b_sampled(gpu, act):
-    spec = W.LAYERS["120b_prefill"]
-    L = W.make_layer(spec)
-    tokens = np.sort(np.random.default_rng(9).choice(spec.T, size=48, replace=False))
-    _check(gpu, L, spec.top_k, act, "120b sampled", tokens=tokens)
+def test_120b_long_prefill(gpu, act):
+    # every output of the 120b long prefill: against the oracle of the same
+    # mode at the bar, and (split) against the exact oracle at the bar
+    spec, L, exact = long_prefill_120b()
+    _check(gpu, L, spec.top_k, act, "120b (all tokens)", exact=exact)

@@ -553,9 +553,11 @@ def test_mxfp8_split_error_bound_and_exact_cases():
 
 
 def _mxfp8_blocks_scalar(v, mode):
-    """Plain loops over blocks of 32: shared scale 2^(floor(log2 max|v|) - 7) (OCP
-    MX: the block maximum lands in E4M3's top binade), elements rounded to E4M3
-    by torch's float8_e4m3fn; "split" adds the same quantization of the residual."""
+    """Plain loops over blocks of 32: shared scale 2^(floor(log2 max|v|) - 7) (the
+    implementation's rule: the block maximum lands in [128, 256), E4M3's top
+    binade but one; the OCP rule would subtract emax = 8), elements rounded to
+    E4M3 by torch's float8_e4m3fn; "split" adds the same quantization of the
+    residual."""
     def one(vals):
         amax = max(abs(u) for u in vals)
         if amax == 0.0:
@@ -608,3 +610,82 @@ def test_fp8act_forward_matches_scalar_loops_on_one_token(mode):
     assert np.allclose(acc, y[t], rtol=1e-12, atol=1e-9)
     # the quantized experts really differ from the exact layer here
     assert not np.allclose(y[t], O.moe_forward(L, spec.top_k)[t], rtol=1e-6, atol=0)
+
+
+# ---------------------------------------------------------------- the acceptance measure
+
+def test_parity_errors_hand_computed():
+    # ||y - y_ref||_2 / ||y_ref||_2 and max|y - y_ref| / max|y_ref|, worked by hand.
+    rel, mx = O.parity_errors(np.array([3.0, 4.5]), np.array([3.0, 4.0]))
+    assert rel == pytest.approx(0.5 / 5.0, abs=1e-15)        # ||(0, .5)|| / ||(3, 4)||
+    assert mx == pytest.approx(0.5 / 4.0, abs=1e-15)
+    # the max-element error is relative to max|y_ref| (2), not max|y| (5)
+    rel, mx = O.parity_errors(np.array([1.0, -5.0]), np.array([1.0, -2.0]))
+    assert rel == pytest.approx(3.0 / math.sqrt(5.0), abs=1e-15)
+    assert mx == pytest.approx(1.5, abs=1e-15)
+    # the norms run over every element of a 2-D output, not a row or a column
+    rel, mx = O.parity_errors(np.array([[1.0, 0.0], [0.0, 2.0]]), np.array([[1.0, 0.0], [0.0, 1.0]]))
+    assert rel == pytest.approx(1.0 / math.sqrt(2.0), abs=1e-15)
+    assert mx == pytest.approx(1.0, abs=1e-15)
+    rel, mx = O.parity_errors(np.array([[2.0, 0.0], [0.0, 0.0]]), np.array([[1.0, 0.0], [0.0, 3.0]]))
+    assert rel == pytest.approx(math.sqrt(10.0) / math.sqrt(10.0), abs=1e-15)  # ||(1, -3)|| / ||(1, 3)||
+    assert mx == pytest.approx(3.0 / 3.0, abs=1e-15)
+    # a sign flip is off by 2 in both measures; equal inputs by 0
+    rel, mx = O.parity_errors(-np.array([0.25, -8.0, 1.0]), np.array([0.25, -8.0, 1.0]))
+    assert (rel, mx) == (pytest.approx(2.0, abs=1e-15), pytest.approx(2.0, abs=1e-15))
+    assert O.parity_errors(np.arange(6.0), np.arange(6.0)) == (0.0, 0.0)
+    # differences below float32 resolution still count (float64 arithmetic)
+    rel, _ = O.parity_errors(np.array([1.0 + 2.0 ** -40]), np.array([1.0]))
+    assert rel == 2.0 ** -40
+
+
+# ---------------------------------------------------------------- E8M0 0xFF inside the layer
+
+def test_nan_scale_byte_poisons_exactly_the_rows_it_reaches():
+    # A 0xFF scale byte makes its 32 weights NaN (OCP MX).  In gate_up row r of
+    # expert e every h[:, r] of e's tokens is NaN, so their whole activation,
+    # down output and routed output rows are NaN; in down row n only column n
+    # of the outputs of that expert's tokens.  Every other element stays finite.
+    L, spec = _tiny(7, T=12, H=64, I=64, E=4)
+    k = spec.top_k
+    ids, _ = O.route(L["router_logits"], k)
+    e_up, e_down, n_bad = 1, 2, 37
+    L["w13_scales"] = L["w13_scales"].copy()
+    L["w2_scales"] = L["w2_scales"].copy()
+    L["w13_scales"][e_up, 5, 1] = 255
+    L["w2_scales"][e_down, n_bad, 0] = 255
+    y = O.moe_forward(L, k)
+    hit_up = (ids == e_up).any(axis=1)
+    hit_down = (ids == e_down).any(axis=1)
+    assert hit_up.any() and (~hit_up).any() and (hit_down & ~hit_up).any()
+    expect = np.zeros(y.shape, dtype=bool)
+    expect[hit_up, :] = True
+    expect[hit_down, n_bad] = True
+    assert np.array_equal(np.isnan(y), expect)
+    # every element the bad bytes cannot reach is the clean layer's, bit for bit
+    clean = O.moe_forward(_tiny(7, T=12, H=64, I=64, E=4)[0], k)
+    assert np.array_equal(y[~expect], clean[~expect])
+
+
+# ---------------------------------------------------------------- MXFP8 codes worked by hand
+
+def test_mxfp8_quantize_hand_derived_codes():
+    # This implementation's rule (not the OCP emax rule): shared exponent
+    # floor(log2 max|v|) - 7.  Block max 3.0 -> exponent 1 - 7 = -6, byte 121.
+    #   3.0 / 2^-6 = 192 = 1.5 * 2^7     -> E4M3 exponent field 14, mantissa 4: 0x74
+    #   0.1 / 2^-6 = 6.4 = 1.6 * 2^2     -> mantissa 4.8 rounds to 5: 0x4D (value 6.5)
+    #  -0.5 / 2^-6 = -32 = -1.0 * 2^5    -> 0x80 | (12 << 3): 0xE0
+    #   2^-16 / 2^-6 = 2^-10 < 2^-9 / 2  -> rounds to zero: 0x00
+    #   0.0703125 / 2^-6 = 4.5 = 1.125*4 -> mantissa 1: 0x49
+    #   0.0546875 / 2^-6 = 3.5 = 1.75*2  -> mantissa 6: 0x46
+    v = np.zeros((1, 32))
+    v[0, :6] = [3.0, 0.1, -0.5, 2.0 ** -16, 0.0703125, 0.0546875]
+    codes, scales = O.mxfp8_quantize(v)
+    assert scales.tolist() == [[121]]
+    assert codes[0, :6].tolist() == [0x74, 0x4D, 0xE0, 0x00, 0x49, 0x46]
+    assert np.all(codes[0, 6:] == 0)
+    # a tie: 0.06640625 / 2^-6 = 4.25, halfway between 4 (mantissa 0) and 4.5
+    # (mantissa 1): ties to even -> 0x48; 4.75 halfway between 4.5 and 5 -> 5 (0x4A)
+    v[0, 1:3] = [0.06640625, 0.07421875]
+    codes, _ = O.mxfp8_quantize(v)
+    assert codes[0, 1:3].tolist() == [0x48, 0x4A]
