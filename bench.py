@@ -308,8 +308,8 @@ def run_moe(args):
         else:
             n_exp, rows_in, rows_out = n_active, T * H * 2, P * I * 2
         work = n_exp * w13_b + rows_in + rows_out
+        per_unit = f"{w13_b} B of packed w13 per expert x {n_exp} + x {rows_in} B + a {rows_out} B"
         roof = {"bound": "hbm", "achieved": work / (kms / 1e3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
-        per_unit = (f"{w13_b} B of packed w13 per expert x {n_exp} + x {rows_in} B + a {rows_out} B")
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = measured_traffic(args.workload, dominant)
     roof["kernel"] = {"gate_up_wide": ("expert_fp4_kernel" if args.act != "bf16" else "expert_wide_kernel")

@@ -26,10 +26,21 @@
 // step, element) yields the same dot products, and this one needs no
 // reshuffle of the checkpoint layout.  Weights are dequantized exactly
 // (E2M1 x 2^(s-127) is a bf16 value) and MFMA accumulates in fp32.
+#include "expert_device.h"
 #include "internal.h"
 #include "mx_device.h"
 
 namespace {
+
+using mxgemm::GroupScale;
+using mxgemm::load_bias4;
+using mxgemm::load_lds16;
+using mxgemm::pack_bf16x4;
+using mxgemm::stage_scales;
+using mxgemm::staged_row;
+using mxgemm::swiglu_clamped;
+using mxgemm::w13_row;
+using mxgemm::wait_loads_then_barrier;
 
 using mx::bf16x8;
 using mx::f32x16;
@@ -45,83 +56,6 @@ __device__ __forceinline__ int slot_col(int row, int part) {
   const int r = row & 31;  // depends only on the row within its 32-row block
   return part ^ ((r ^ (r >> 3)) & 7);
 }
-
-__device__ __forceinline__ float swiglu_clamped(float gate, float up) {
-  // gpt-oss family constants: alpha 1.702, limit 7; gate clamped from above,
-  // up clamped on both sides, +1 after the clamp.  The clamps are selects, not
-  // fminf/fmaxf, so that a NaN input (a weight group with scale byte 0xFF)
-  // stays NaN instead of becoming the limit.
-  const float g = gate > 7.0f ? 7.0f : gate;
-  const float u = up > 7.0f ? 7.0f : (up < -7.0f ? -7.0f : up);
-  // sigmoid through the hardware reciprocal (about 1 ulp; the result is
-  // rounded to bf16)
-  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-1.702f * g)) * (u + 1.0f);
-}
-
-// gate/up row layout of w13.  Logical row 2i is gate i and 2i+1 is up i (the
-// order every kernel computes in).  Interleaved checkpoints store them so;
-// split ones ("feat(gguf): serve gpt-oss gguf checkpoints on gpt_oss",
-// FreeToken PR #838, "What it does": swigluoai is the uninterleaved spelling
-// of the same activation) store the I gate rows first, then the I up rows.
-__device__ __forceinline__ int w13_row(int r, int N, bool split) {
-  return split ? ((r & 1) ? (N >> 1) + (r >> 1) : (r >> 1)) : r;
-}
-// LDS row of block-local logical row rl after stage_scales (split: the block's
-// gate rows, then its up rows).
-__device__ __forceinline__ int staged_row(int rl, int nv, bool split) {
-  return split ? ((rl & 1) ? (nv >> 1) + (rl >> 1) : (rl >> 1)) : rl;
-}
-// Biases of logical rows n..n+3 (n a multiple of 4, below N).
-__device__ __forceinline__ f32x4 load_bias4(const uint16_t* bias, int n, int N, bool split) {
-  uint32_t lo, hi;
-  if (split) {  // gate n/2, up n/2, gate n/2+1, up n/2+1
-    const uint32_t g = *reinterpret_cast<const uint32_t*>(bias + (n >> 1));
-    const uint32_t u = *reinterpret_cast<const uint32_t*>(bias + (N >> 1) + (n >> 1));
-    lo = (g & 0xffffu) | (u << 16);
-    hi = (g >> 16) | (u & 0xffff0000u);
-  } else {
-    const uint2 b = *reinterpret_cast<const uint2*>(bias + n);
-    lo = b.x;
-    hi = b.y;
-  }
-  return f32x4{mx::bf16_to_f32(lo & 0xffffu), mx::bf16_to_f32(lo >> 16), mx::bf16_to_f32(hi & 0xffffu),
-               mx::bf16_to_f32(hi >> 16)};
-}
-
-// Scale operands of the 32 codes a lane converts at once (one 16-byte piece).
-// MXFP4: one E8M0 byte for all 32.  NVFP4: two E4M3 block scales, the first
-// for the codes of steps 0 and 1, the second for steps 2 and 3; the result is
-// exact in bf16 (a code has at most 2 significant bits, an E4M3 value 4).
-// MXFP4: E8M0 byte 0xFF is NaN, so the group's weights are NaN (OCP MX).  A
-// single NaN element is enough to make every dot product over the group NaN,
-// so the NaN is OR-ed into the first two converted elements of the group only
-// (nan_mask: 0x7FC07FC0 for byte 0xFF, else 0).  NVFP4's E4M3 NaN scale
-// reaches the weights through the float32 conversion by itself.
-template <bool kNv>
-struct GroupScale {
-  float lo, hi;
-  uint32_t nan;
-  __device__ __forceinline__ GroupScale(const uint8_t* srow, int g) : GroupScale(kNv ? srow[2 * g] : srow[g],
-                                                                                   kNv ? srow[2 * g + 1] : 0u) {}
-  // from the group's scale byte(s) already read (b1 only for NVFP4)
-  __device__ __forceinline__ GroupScale(uint32_t b0, uint32_t b1) {
-    if (kNv) {
-      lo = mx::e4m3_operand(b0);
-      hi = mx::e4m3_operand(b1);
-      nan = 0u;
-    } else {
-      lo = hi = mx::e8m0_operand(b0);
-      nan = mx::e8m0_nan_mask(b0);
-    }
-  }
-  __device__ __forceinline__ float step(int s) const { return s < 2 ? lo : hi; }
-  // eight codes of step s as bf16
-  __device__ __forceinline__ u32x4 convert(uint32_t packed, int s) const {
-    u32x4 r = kNv ? mx::fp4x8_to_bf16x8_any_scale(packed, step(s)) : mx::fp4x8_to_bf16x8(packed, step(s));
-    if (!kNv && s == 0) r[0] |= nan;
-    return r;
-  }
-};
 
 // Block -> (tile, weight-row tile).  Blocks are dealt to the 8 XCDs round
 // robin (block b runs on XCD b % 8), so the id is first remapped so that each
@@ -225,49 +159,6 @@ constexpr int kWideMaxGroups = 128;  // K <= 4096
 constexpr int kFp4StageBytes = (128 * 8 + 512 * 2) * 16 + 256 * 4;  // one LDS stage of the FP4 kernel
 constexpr int kFp4MaxLds = 160 * 1024;                              // LDS per workgroup on gfx950
 
-// 16 bytes per lane from global memory straight into LDS (the load unit
-// writes lane l's bytes at lds + 16 * l; lds is the same for the whole wave).
-__device__ __forceinline__ void load_lds16(const void* src, u32x4* lds) {
-  __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
-}
-
-// Scale bytes of a block's BN weight rows, row-major as in memory: the rows
-// are one contiguous, 32-byte aligned range (row counts and tile starts are
-// multiples of 32), copied with 16-byte loads.  Rows past N are not copied
-// (their outputs are dropped).  kDma: the load unit writes LDS itself
-// (global_load_lds, lane l of a wave at the wave's slot + 16 * l), so the
-// copy flies with the first operand loads instead of waiting to be stored;
-// the caller waits for it (vmcnt) before the first barrier.
-template <int BN, int kThreads, bool kDma = false>
-__device__ __forceinline__ void stage_scales(uint8_t* sst, const mxfp4moe::GemmArgs& args, int e, int ntile,
-                                             int kgroups, int t, bool split = false) {
-  // kgroups: scale bytes per weight row (K/32 for MXFP4, K/16 for NVFP4)
-  const int N = args.N;
-  const int nv = min(BN, N - ntile * BN);
-  u32x4* dst = reinterpret_cast<u32x4*>(sst);
-  // the block's rows (split layout: its gate rows, then its up rows; each
-  // range contiguous and 16-byte aligned)
-  const int n16 = (nv * kgroups) >> 4;
-  const int h = split ? ((nv >> 1) * kgroups) >> 4 : n16;
-  const u32x4* g = reinterpret_cast<const u32x4*>(
-      args.wscales + ((size_t)e * N + (split ? ntile * BN >> 1 : ntile * BN)) * (size_t)kgroups);
-  const u32x4* u =
-      reinterpret_cast<const u32x4*>(args.wscales + ((size_t)e * N + (N >> 1) + (ntile * BN >> 1)) * (size_t)kgroups);
-  if (kDma) {
-    for (int i0 = 0; i0 < n16; i0 += kThreads) {  // the same trip count in every wave
-      const int i = i0 + t;
-      if (i < n16) load_lds16(i < h ? g + i : u + (i - h), dst + i0 + (t & ~63));
-    }
-  } else {
-    for (int i = t; i < n16; i += kThreads) dst[i] = i < h ? g[i] : u[i - h];
-  }
-}
-
-// Four fp32 values as four bf16 (round to nearest even), low half first.
-__device__ __forceinline__ uint2 pack_bf16x4(const f32x4& v) {
-  return uint2{mx::pack_bf16x2_rne(v[0], v[1]), mx::pack_bf16x2_rne(v[2], v[3])};
-}
-
 // Epilogue, staged through an LDS region of RM*32*128 bytes per wave so
 // that every token's outputs leave as full 128-byte rows: the lane layout of
 // the MFMA results (four consecutive features of one token per lane) is
@@ -353,22 +244,6 @@ __device__ __forceinline__ void store_epilogue(const mxfp4moe::GemmArgs& args, c
   }
 }
 
-// Waits until at most kVm of this wave's vector-memory loads are in flight
-// and its LDS operations are done, then joins the block barrier.  The empty
-// asm statements keep the compiler from moving memory accesses across it
-// (the barrier builtin alone is not a memory fence to the compiler).
-template <int kVm>
-__device__ __forceinline__ void wait_loads_then_barrier() {
-  static_assert(kVm >= 0 && kVm < 64, "vmcnt field");
-  __builtin_amdgcn_sched_barrier(0);  // nothing (MFMAs included) is scheduled across the wait
-  asm volatile("" ::: "memory");
-  // s_waitcnt fields: vmcnt bits 3:0 and 15:14, expcnt 6:4 (7: no wait), lgkmcnt 11:8 (0)
-  __builtin_amdgcn_s_waitcnt((kVm & 15) | ((kVm >> 4) << 14) | (7 << 4));
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
-
 // The wide kernel.  Operand chunks move from global memory to LDS by the
 // load unit itself (global_load_lds_dwordx4: 16 bytes per lane, written at
 // the wave's LDS address + 16 * lane; no staging registers, no LDS stores in
@@ -425,7 +300,7 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void expert_wide_kernel(mxfp4moe::
   const int lrow = lane & 31;
 
   const bool split = kGateUp && args.split_gate_up;  // uniform
-  stage_scales<BN, kThreads, true>(sst, args, e, ntile, kgroups, t, split);
+  stage_scales<BN, kThreads, true>(sst, args.wscales, args.N, e, ntile, kgroups, t, split);
 
   // token slot p = t + i*threads -> row p/8, logical column slot_col(row, p%8);
   // rows past `count` re-read the tile's first row (their columns are never stored)
@@ -710,7 +585,7 @@ __global__ __launch_bounds__(256, 1) void expert_fp4_kernel(mxfp4moe::GemmArgs a
   const int lrow = lane & 31;
 
   const bool split = kGateUp && args.split_gate_up;  // uniform
-  stage_scales<BN, kThreads, true>(sst, args, e, ntile, kgroups, t, split);
+  stage_scales<BN, kThreads, true>(sst, args.wscales, args.N, e, ntile, kgroups, t, split);
 
   // token slot p = t + i*threads -> row p/8, logical column slot_col(row, p%8);
   // rows past `count` re-read the tile's first row (their columns are never stored)
@@ -1017,7 +892,7 @@ __global__ __launch_bounds__(256, 5) void expert_stream_kernel(mxfp4moe::GemmArg
       const size_t base = r == 0 ? xsrc[0] : r == 1 ? xsrc[1] : r == 2 ? xsrc[2] : xsrc[3];
       if (j * kThreads < nx16) xv[j] = reinterpret_cast<const u32x4*>(args.act + base)[p];
     }
-    stage_scales<BN, kThreads>(sl, args, e, ntile, kNv ? 2 * kgroups : kgroups, t, split);
+    stage_scales<BN, kThreads>(sl, args.wscales, args.N, e, ntile, kNv ? 2 * kgroups : kgroups, t, split);
 #pragma unroll
     for (int j = 0; j < 8; ++j)
       if (t + j * kThreads < nx16) reinterpret_cast<u32x4*>(xl)[t + j * kThreads] = xv[j];
@@ -1211,7 +1086,7 @@ __global__ __launch_bounds__(256, 2) void expert_mid_kernel(mxfp4moe::GemmArgs a
   uint8_t* const ws = lds + 64 * kXRow;
   uint8_t* const sl = ws + BN * kWRow;
   const bool split = kGateUp && args.split_gate_up;  // uniform
-  stage_scales<BN, kThreads>(sl, args, e, ntile, kNv ? 2 * kgroups : kgroups, t, split);
+  stage_scales<BN, kThreads>(sl, args.wscales, args.N, e, ntile, kNv ? 2 * kgroups : kgroups, t, split);
 
   // load slots: token piece i = t + j*256 -> token i / kXPieces; weight piece
   // i = t + j*256 -> row i / kWPieces (rows past N re-read row N-1)

@@ -7,68 +7,13 @@
 #include "../../include/mxfp4moe.h"
 #include "internal.h"
 #include "mx_device.h"
+#include "route_device.h"
 
 namespace {
 
+using mxroute::route_row;
+
 constexpr int kRouteThreads = 256;  // four tokens per block, one wave each
-constexpr int kPerLane = MXFP4MOE_MAX_EXPERTS / 64;
-
-// Selection key of logit v of expert e: larger keys for larger logits and,
-// between equal logits, for the lower expert index.  The float bits are
-// mapped to an unsigned order (sign flipped for non-negative values, all
-// bits for negative ones); -0 takes the key of +0 since the two compare
-// equal.  Every real key exceeds 0, the key of an empty slot.
-__device__ __forceinline__ uint64_t route_key(float v, int e) {
-  uint32_t b = __float_as_uint(v);
-  if ((b << 1) == 0u) b = 0u;
-  b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-  return ((uint64_t)b << 32) | (uint32_t)~(uint32_t)e;
-}
-__device__ __forceinline__ float key_logit(uint64_t k) {
-  const uint32_t u = (uint32_t)(k >> 32);
-  return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
-}
-__device__ __forceinline__ int key_expert(uint64_t k) { return (int)~(uint32_t)k; }
-
-// Token t, by one wave (all 64 lanes active).  Lane l holds the keys of
-// experts l, l+64, ...; k rounds of a wave-wide key maximum pick the experts
-// by descending logit (ties to the lower expert index); lane j keeps the
-// j-th pick.  The softmax runs over the picks relative to the largest one.
-__device__ void route_row(const float* row, int t, int E, int top_k, int32_t* __restrict__ ids,
-                          float* __restrict__ weights, int32_t* ids_copy = nullptr) {
-  const int lane = mx::lane_id();
-  uint64_t key[kPerLane];
-#pragma unroll
-  for (int i = 0; i < kPerLane; ++i) {
-    const int e = lane + 64 * i;
-    key[i] = e < E ? route_key(row[e], e) : 0ull;
-  }
-  float my_v = 0.f, v0 = 0.f;
-  int my_e = 0;
-  for (int j = 0; j < top_k; ++j) {
-    uint64_t best = 0;
-#pragma unroll
-    for (int i = 0; i < kPerLane; ++i) best = mx::max_u64(best, key[i]);
-    best = mx::wave_max_u64(best);
-    const int be = key_expert(best);
-#pragma unroll
-    for (int i = 0; i < kPerLane; ++i)
-      if (lane + 64 * i == be) key[i] = 0ull;
-    const float bv = key_logit(best);
-    if (lane == j) {
-      my_v = bv;
-      my_e = be;
-    }
-    if (j == 0) v0 = bv;
-  }
-  const float ex = lane < top_k ? expf(my_v - v0) : 0.f;
-  const float sum = mx::wave_sum_f32(ex);
-  if (lane < top_k) {
-    ids[(size_t)t * top_k + lane] = my_e;
-    weights[(size_t)t * top_k + lane] = ex / sum;
-    if (ids_copy != nullptr) ids_copy[t * top_k + lane] = my_e;
-  }
-}
 
 __device__ __forceinline__ void route_token(const float* __restrict__ logits, int t, int E, int top_k,
                                             int32_t* __restrict__ ids, float* __restrict__ weights) {

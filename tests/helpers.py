@@ -27,7 +27,9 @@ def bits_u16(t: torch.Tensor) -> np.ndarray:
 
 def assert_layer_parity(y_gpu: torch.Tensor, y_ref: np.ndarray, label: str):
     y = bf16_to_f64(y_gpu)
-    assert np.all(np.isfinite(y)), f"{label}: non-finite output"
+    bad = np.argwhere(~np.isfinite(y))
+    assert bad.size == 0, (f"{label}: {len(bad)} non-finite outputs, first at {bad[:4].tolist()}, "
+                           f"rows {np.unique(bad[:, 0])[:8].tolist() if y.ndim == 2 else ''}")
     rel, mx = O.parity_errors(y, y_ref)
     print(f"[parity] {label}: normwise {rel:.3e}, max-element {mx:.3e} over {y.size} elements", flush=True)
     assert rel <= REL_TOL, f"{label}: normwise relative error {rel:.3e} > {REL_TOL}"
