@@ -36,6 +36,7 @@ extern "C" {
 #define MXFP4MOE_ERR_WORKSPACE (-3) /* workspace smaller than the size the query returned   */
 #define MXFP4MOE_ERR_ALIGN (-4)     /* a pointer is not aligned as its call requires        */
 #define MXFP4MOE_ERR_HIP (-5)       /* the HIP runtime rejected a launch                   */
+#define MXFP4MOE_ERR_SCRATCH (-6)   /* the layer needs more than the no-allocation scratch  */
 
 /* Largest supported expert count and top_k. */
 #define MXFP4MOE_MAX_EXPERTS 512
@@ -178,6 +179,33 @@ int moe_mxfp4_forward(const uint16_t* x, const float* router_logits,
                       const uint8_t* w2_blocks, const uint8_t* w2_scales, const uint16_t* w2_bias,
                       uint16_t* y, int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k,
                       void* workspace, size_t* workspace_bytes, void* stream);
+
+/*
+ * moe_mxfp4_forward_noalloc - moe_mxfp4_forward for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): no workspace argument.  Its scratch is a
+ * fixed device array inside the library, MXFP4MOE_NOALLOC_SCRATCH_BYTES bytes
+ * per device, held by every device the library runs on until the process
+ * ends.  The call allocates nothing: no hipMalloc, hipFree or allocating
+ * library routine (the first call on a device looks the array's address up
+ * once).  The caller still passes x, the logits, the weights and y.
+ *
+ * Arguments, checks and results as moe_mxfp4_forward, with the same kernels
+ * (bit-identical outputs).  A layer whose workspace (the size
+ * moe_mxfp4_forward's query returns) exceeds the scratch returns
+ * MXFP4MOE_ERR_SCRATCH before any launch: 32 MiB hold about 700 tokens at
+ * H = I = 2880, top_k = 4.  Every call on one device shares that device's
+ * array, and a call leaves its contents behind for the next (nothing in it is
+ * assumed zero at the start of a call): two calls that overlap on one device
+ * race.  Order them on one stream, or use moe_mxfp4_forward with separate
+ * workspaces.
+ */
+#define MXFP4MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+int moe_mxfp4_forward_noalloc(const uint16_t* x, const float* router_logits,
+                              const uint8_t* w13_blocks, const uint8_t* w13_scales, const uint16_t* w13_bias,
+                              const uint8_t* w2_blocks, const uint8_t* w2_scales, const uint16_t* w2_bias,
+                              uint16_t* y, int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k,
+                              void* stream);
 
 /*
  * moe_mxfp4_forward_ex - moe_mxfp4_forward with layout flags.

@@ -23,6 +23,7 @@ STATUS = {
     -3: "workspace too small",
     -4: "pointer not aligned as required",
     -5: "HIP launch error",
+    -6: "layer needs more than the no-allocation scratch",
 }
 
 STAGES = {"route": 1, "group": 2, "gate_up": 3, "down": 4, "combine": 5, "dequant": 6,
@@ -60,6 +61,9 @@ def load() -> ctypes.CDLL:
                                       _i64, _i64, _i64, _i64, _i64, _vp,
                                       ctypes.POINTER(ctypes.c_size_t), _vp]
     lib.moe_mxfp4_forward.restype = ctypes.c_int
+    lib.moe_mxfp4_forward_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                              _i64, _i64, _i64, _i64, _i64, _vp]
+    lib.moe_mxfp4_forward_noalloc.restype = ctypes.c_int
     lib.moe_mxfp4_forward_ex.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                          _i64, _i64, _i64, _i64, _i64, ctypes.c_uint32, _vp,
                                          ctypes.POINTER(ctypes.c_size_t), _vp]
@@ -274,6 +278,38 @@ def moe_mxfp4_forward(x: torch.Tensor, router_logits: torch.Tensor,
                                   out.data_ptr(), T, H, I, E, top_k, flags,
                                   workspace.data_ptr(), ctypes.byref(n), _stream(stream))
     _raise("moe_mxfp4_forward", st)
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def moe_mxfp4_forward_noalloc(x: torch.Tensor, router_logits: torch.Tensor,
+                              w13_blocks: torch.Tensor, w13_scales: torch.Tensor, w13_bias: torch.Tensor,
+                              w2_blocks: torch.Tensor, w2_scales: torch.Tensor, w2_bias: torch.Tensor,
+                              top_k: int, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """moe_mxfp4_forward through the entry point that takes no workspace (its scratch
+    is a fixed device array of the library); returns y [T, H] bfloat16."""
+    lib = load()
+    T, H = x.shape
+    E = router_logits.shape[1]
+    I = w2_blocks.shape[-1] * 2
+    _check(x, "x", torch.bfloat16, (T, H))
+    _check(router_logits, "router_logits", torch.float32, (T, E))
+    _check(w13_blocks, "w13_blocks", torch.uint8, (E, 2 * I, H // 2))
+    _check(w13_scales, "w13_scales", torch.uint8, (E, 2 * I, H // 32))
+    _check(w13_bias, "w13_bias", torch.bfloat16, (E, 2 * I))
+    _check(w2_blocks, "w2_blocks", torch.uint8, (E, H, I // 2))
+    _check(w2_scales, "w2_scales", torch.uint8, (E, H, I // 32))
+    _check(w2_bias, "w2_bias", torch.bfloat16, (E, H))
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    _check(out, "out", torch.bfloat16, (T, H))
+    st = lib.moe_mxfp4_forward_noalloc(x.data_ptr(), router_logits.data_ptr(),
+                                       w13_blocks.data_ptr(), w13_scales.data_ptr(), w13_bias.data_ptr(),
+                                       w2_blocks.data_ptr(), w2_scales.data_ptr(), w2_bias.data_ptr(),
+                                       out.data_ptr(), T, H, I, E, top_k, _stream(stream))
+    _raise("moe_mxfp4_forward_noalloc", st)
     return out
 
 

@@ -132,6 +132,31 @@ using namespace mxfp4moe;
 
 namespace {
 
+// Scratch of moe_mxfp4_forward_noalloc: a fixed device array, so that callers
+// that cannot allocate (graph capture, tight serving loops) need no
+// workspace.  Each device holds its own copy for the life of the process.  In
+// host code `scratch` only names the symbol; its device address comes from
+// hipGetSymbolAddress, looked up once per device (noalloc_scratch below).
+constexpr size_t kNoAllocScratch = MXFP4MOE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratch];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address, or nullptr if it cannot be had.
+void* noalloc_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
 const float kNvQuery = 0.f;  // stands in for the NVFP4 scale pointers of a size query
 constexpr uint32_t kForwardFlags =
     MXFP4MOE_GATE_UP_SPLIT | MXFP4MOE_ACT_MXFP8 | MXFP4MOE_ACT_MXFP8_SPLIT | MXFP4MOE_TILES_STREAM;
@@ -145,7 +170,7 @@ int forward_impl(const uint16_t* x, const float* router_logits, const uint16_t* 
                  const float* scale2_13, const uint16_t* w13_bias, const uint8_t* w2_blocks,
                  const uint8_t* w2_scales, const float* scale2_2, const uint16_t* w2_bias, uint16_t* y, int64_t T,
                  int64_t H, int64_t I, int64_t E, int64_t top_k, uint32_t flags, void* workspace,
-                 size_t* workspace_bytes, void* stream) {
+                 size_t* workspace_bytes, void* stream, bool check_only = false) {
   const bool nv = scale2_13 != nullptr;
   if (workspace_bytes == nullptr) return MXFP4MOE_ERR_ARG;
   int st = check_route_shape(T, E, top_k);
@@ -176,7 +201,7 @@ int forward_impl(const uint16_t* x, const float* router_logits, const uint16_t* 
   if (!aligned16(w13_scales) || !aligned16(w2_scales)) return MXFP4MOE_ERR_ALIGN;
   if (!aligned8(w13_bias) || !aligned8(w2_bias)) return MXFP4MOE_ERR_ALIGN;
   if (T > 0 && (!aligned16(x) || !aligned16(y))) return MXFP4MOE_ERR_ALIGN;
-  if (T == 0) return MXFP4MOE_OK;
+  if (T == 0 || check_only) return MXFP4MOE_OK;
 
   char* ws = static_cast<char*>(workspace);
   int32_t* ids = reinterpret_cast<int32_t*>(ws + L.ids);
@@ -270,6 +295,7 @@ const char* mxfp4moe_status_string(int status) {
     case MXFP4MOE_ERR_WORKSPACE: return "workspace too small";
     case MXFP4MOE_ERR_ALIGN: return "pointer not aligned as required";
     case MXFP4MOE_ERR_HIP: return "HIP launch error";
+    case MXFP4MOE_ERR_SCRATCH: return "layer needs more than the no-allocation scratch";
     default: return "unknown status";
   }
 }
@@ -326,6 +352,24 @@ int moe_mxfp4_forward(const uint16_t* x, const float* router_logits, const uint8
                       void* stream) {
   return moe_mxfp4_forward_ex(x, router_logits, w13_blocks, w13_scales, w13_bias, w2_blocks, w2_scales, w2_bias, y,
                               T, H, I, E, top_k, 0u, workspace, workspace_bytes, stream);
+}
+
+int moe_mxfp4_forward_noalloc(const uint16_t* x, const float* router_logits, const uint8_t* w13_blocks,
+                              const uint8_t* w13_scales, const uint16_t* w13_bias, const uint8_t* w2_blocks,
+                              const uint8_t* w2_scales, const uint16_t* w2_bias, uint16_t* y, int64_t T, int64_t H,
+                              int64_t I, int64_t E, int64_t top_k, void* stream) {
+  // every host check first, against a stand-in scratch address that nothing
+  // dereferences (the check-only pass launches nothing)
+  size_t have = kNoAllocScratch;
+  int st = forward_impl(x, router_logits, nullptr, nullptr, w13_blocks, w13_scales, nullptr, w13_bias, w2_blocks,
+                        w2_scales, nullptr, w2_bias, y, T, H, I, E, top_k, 0u, reinterpret_cast<void*>(kAlign),
+                        &have, stream, /*check_only=*/true);
+  if (st == MXFP4MOE_ERR_WORKSPACE) return MXFP4MOE_ERR_SCRATCH;
+  if (st != MXFP4MOE_OK || T == 0) return st;
+  void* ws = noalloc_scratch();
+  if (ws == nullptr) return MXFP4MOE_ERR_HIP;
+  return forward_impl(x, router_logits, nullptr, nullptr, w13_blocks, w13_scales, nullptr, w13_bias, w2_blocks,
+                      w2_scales, nullptr, w2_bias, y, T, H, I, E, top_k, 0u, ws, &have, stream);
 }
 
 int moe_mxfp4_forward_ex(const uint16_t* x, const float* router_logits, const uint8_t* w13_blocks,

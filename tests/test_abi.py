@@ -192,3 +192,22 @@ def test_mxfp8_quantize_argument_checks(lib):
     assert f(A, 4, 64, 1, A, A + 2, None) == -4  # scale rows are read as 4-byte words
     assert f(None, 0, 64, 1, None, None, None) == 0
     assert f(A, 1 << 31, 64, 1, A, A, None) == -2  # more rows than the kernel counts
+
+
+def test_forward_noalloc_argument_checks(lib):
+    # Every host check runs before the scratch address is looked up (no GPU here).
+    f = lib.moe_mxfp4_forward_noalloc
+    assert f(A, A, A, A, A, A, A, A, A, 4, 48, 64, 4, 2, None) == -2       # H not a multiple of 32
+    assert f(A, A, A, A, A, A, A, A, A, 4, 64, 64, 4, 5, None) == -2       # top_k > E
+    assert f(A, A, A, A, None, A, A, A, A, 4, 64, 64, 4, 2, None) == -1    # biases are required
+    assert f(A, A, A, A, A, A, A, None, A, 4, 64, 64, 4, 2, None) == -1
+    assert f(A + 2, A, A, A, A, A, A, A, A, 4, 64, 64, 4, 2, None) == -4   # x misaligned
+    assert f(A, A, A, A + 8, A, A, A, A, A, 4, 64, 64, 4, 2, None) == -4   # scales misaligned
+    assert f(None, None, A, A, A, A, A, A, None, 0, 64, 64, 4, 2, None) == 0  # empty batch: nothing to do
+    # more than the fixed scratch: 4096 tokens of the 120b layer need ~190 MB
+    assert f(A, A, A, A, A, A, A, A, A, 4096, 2880, 2880, 128, 4, None) == -6
+    n = ctypes.c_size_t(0)
+    assert lib.moe_mxfp4_forward(None, None, None, None, None, None, None, None, None, 256, 2880, 2880, 32, 4,
+                                 None, ctypes.byref(n), None) == 0
+    assert n.value <= binding.NOALLOC_SCRATCH_BYTES  # the 20b prefill layer fits
+    assert b"scratch" in lib.mxfp4moe_status_string(-6)
