@@ -183,7 +183,9 @@ def run_moe(args):
     _, _, offsets, _ = binding.moe_mxfp4_route(dev["router_logits"], k)
     counts = np.diff(offsets.cpu().numpy().astype(np.int64))
     n_active = int((counts > 0).sum())
-    full_pairs = 0 if nvfp4 else int(counts[counts >= 128].sum())  # pairs of the experts in 128-pair tiles
+    # NVFP4 layers take full tiles only when H and I are multiples of 64
+    wide_tiles = not nvfp4 or (H % 64 == 0 and I % 64 == 0)
+    full_pairs = int(counts[counts >= 128].sum()) if wide_tiles else 0  # pairs of the experts in 128-pair tiles
     w13_b, w2_b = layer_bytes(H, I, nvfp4)
     # Weight copies rotate so that repeated steps cannot be served from the
     # 256 MB Infinity Cache when the active weights would fit in it.
@@ -284,9 +286,9 @@ def run_moe(args):
 
     flops_total = 6.0 * H * I * P
     # Pairs of the experts that go to mid tiles (more than 4 pairs, below the
-    # wide threshold; NVFP4 layers use mid tiles for every such expert).
-    mid_pairs = int(counts[(counts > 4) & ((counts < 128) | nvfp4)].sum())
-    mid_experts = int(((counts > 4) & ((counts < 128) | nvfp4)).sum())
+    # wide threshold; every such expert when there are no full tiles).
+    mid_pairs = int(counts[(counts > 4) & ((counts < 128) | (not wide_tiles))].sum())
+    mid_experts = int(((counts > 4) & ((counts < 128) | (not wide_tiles))).sum())
     # The mid launch is priced against whichever roof is lower for its work:
     # its experts' packed w13 once from HBM, or 2*H*2I MFMA FLOPs per pair.
     mid_mfma = (dominant == "gate_up_mid" and

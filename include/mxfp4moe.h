@@ -329,7 +329,8 @@ int moe_mxfp4_forward_router(const uint16_t* x, const uint16_t* router_w, const 
  *   (gate/up rows interleaved, scales 16-byte and biases 8-byte aligned), and
  *   the same workspace query.  An E4M3 NaN scale byte (0x7F, 0xFF) makes its
  *   weights NaN, with the same effect on the outputs as an E8M0 0xFF.
- * Every pair runs in mid-size or streaming tiles.  A NULL second-level scale
+ * Tiles as moe_mxfp4_forward when H and I are multiples of 64; otherwise
+ * every pair runs in mid-size or streaming tiles.  A NULL second-level scale
  * with a workspace is MXFP4MOE_ERR_ARG.
  */
 int moe_nvfp4_forward(const uint16_t* x, const float* router_logits,

@@ -221,10 +221,14 @@ int forward_impl(const uint16_t* x, const float* router_logits, const uint16_t* 
   tt.small = reinterpret_cast<int32_t*>(ws + L.small);
   tt.num_small = counts + 2;
   // full tiles of kWideTokens pairs take the wide kernel unless the caller
-  // asked for streaming tiles only (a check of that kernel on every shape)
-  tt.big_tokens = nv || (flags & MXFP4MOE_TILES_STREAM) ? 0 : kWideTokens;
-  tt.no_wide = nv ? 1 : 0;
-  const TileBounds tb = tile_bounds(T, P, E, nv ? kTilesNoWide : tt.big_tokens > 0 ? kTilesWide : kTilesStreamOnly);
+  // asked for streaming tiles only (a check of that kernel on every shape);
+  // NVFP4 full tiles read a chunk's scales of a row as one aligned dword, so
+  // they need H and I to be multiples of 64 (else mid tiles take those pairs)
+  const bool nv_no_wide = nv && ((H & 63) != 0 || (I & 63) != 0);
+  tt.big_tokens = nv_no_wide || (flags & MXFP4MOE_TILES_STREAM) ? 0 : kWideTokens;
+  tt.no_wide = nv_no_wide ? 1 : 0;
+  const TileBounds tb =
+      tile_bounds(T, P, E, nv_no_wide ? kTilesNoWide : tt.big_tokens > 0 ? kTilesWide : kTilesStreamOnly);
   hipStream_t s = (hipStream_t)stream;
 
   hipError_t err;

@@ -73,8 +73,9 @@ struct GroupScale {
   // from the group's scale byte(s) already read (b1 only for NVFP4)
   __device__ __forceinline__ GroupScale(uint32_t b0, uint32_t b1) {
     if (kNv) {
-      lo = mx::e4m3_operand(b0);
-      hi = mx::e4m3_operand(b1);
+      const mx::f32x2p v = mx::e4m3x2_operands(b0 | (b1 << 8));
+      lo = v.x;
+      hi = v.y;
       nan = 0u;
     } else {
       lo = hi = mx::e8m0_operand(b0);
@@ -94,6 +95,11 @@ struct GroupScale {
 // writes lane l's bytes at lds + 16 * l; lds is the same for the whole wave).
 __device__ __forceinline__ void load_lds16(const void* src, u32x4* lds) {
   __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
+}
+
+// 4 bytes per lane from global memory straight into LDS (lane l's word at lds + 4 * l).
+__device__ __forceinline__ void load_lds4(const void* src, uint32_t* lds) {
+  __builtin_amdgcn_global_load_lds(src, lds, 4, 0, 0);
 }
 
 // Scale bytes of a block's BN weight rows, row-major as in memory: the rows

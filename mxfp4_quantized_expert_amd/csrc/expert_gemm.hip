@@ -35,6 +35,7 @@ namespace {
 using mxgemm::GroupScale;
 using mxgemm::load_bias4;
 using mxgemm::load_lds16;
+using mxgemm::load_lds4;
 using mxgemm::pack_bf16x4;
 using mxgemm::stage_scales;
 using mxgemm::staged_row;
@@ -95,26 +96,42 @@ struct NoExtra {
 
 // `extra(k)` runs right after the k-th MFMA of the chunk (k = 0 .. 4*RN*RM-1),
 // so a caller can spread other instructions between the MFMAs.
-// nanm[rb]: the NaN mask of fragment rb's scale byte (see GroupScale), OR-ed
-// into its first converted elements.
-template <int RN, int RM, typename Extra = NoExtra>
+// MXFP4 (kNv = false): sc[rb] is fragment rb's E8M0 scale as a convert
+// operand and nanm[rb] the NaN mask of its scale byte (see GroupScale), OR-ed
+// into its first converted elements; sc_hi is unused.  NVFP4: sc[rb] and
+// sc_hi[rb] are the E4M3 block scales of steps 0-1 and 2-3 as floats, applied
+// by the exact float32 conversion; nanm is unused.
+template <int RN, int RM, bool kNv = false, typename Extra = NoExtra>
 __device__ __forceinline__ void chunk_mma_regs(f32x16 (&acc)[RN][RM], const bf16x8 (&b)[4][RM],
                                                const u32x4 (&w)[RN], const float (&sc)[RN],
-                                               const uint32_t (&nanm)[RN], Extra extra = Extra()) {
+                                               const float (&sc_hi)[RN], const uint32_t (&nanm)[RN],
+                                               Extra extra = Extra()) {
   u32x4 a[2][RN];
 #pragma unroll
   for (int rb = 0; rb < RN; ++rb) {
-    a[0][rb] = mx::fp4x8_to_bf16x8(w[rb][0], sc[rb]);
-    a[0][rb][0] |= nanm[rb];
+    if (kNv) {
+      a[0][rb] = mx::fp4x8_to_bf16x8_any_scale(w[rb][0], sc[rb]);
+    } else {
+      a[0][rb] = mx::fp4x8_to_bf16x8(w[rb][0], sc[rb]);
+      a[0][rb][0] |= nanm[rb];
+    }
   }
   auto convert = [&](int s, int i) {  // converts pair i%4 of fragment i/4 for step s
     const int rb = i / 4, sel = i % 4;
     const uint32_t packed = w[rb][s];
     uint32_t v;
-    if (sel == 0) v = mx::fp4x2_to_bf16x2<0>(packed, sc[rb]);
-    else if (sel == 1) v = mx::fp4x2_to_bf16x2<1>(packed, sc[rb]);
-    else if (sel == 2) v = mx::fp4x2_to_bf16x2<2>(packed, sc[rb]);
-    else v = mx::fp4x2_to_bf16x2<3>(packed, sc[rb]);
+    if (kNv) {
+      const float f = s < 2 ? sc[rb] : sc_hi[rb];
+      if (sel == 0) v = mx::fp4x2_to_bf16x2_any_scale<0>(packed, f);
+      else if (sel == 1) v = mx::fp4x2_to_bf16x2_any_scale<1>(packed, f);
+      else if (sel == 2) v = mx::fp4x2_to_bf16x2_any_scale<2>(packed, f);
+      else v = mx::fp4x2_to_bf16x2_any_scale<3>(packed, f);
+    } else {
+      if (sel == 0) v = mx::fp4x2_to_bf16x2<0>(packed, sc[rb]);
+      else if (sel == 1) v = mx::fp4x2_to_bf16x2<1>(packed, sc[rb]);
+      else if (sel == 2) v = mx::fp4x2_to_bf16x2<2>(packed, sc[rb]);
+      else v = mx::fp4x2_to_bf16x2<3>(packed, sc[rb]);
+    }
     a[s & 1][rb][sel] = v;
   };
 #pragma unroll
@@ -167,13 +184,16 @@ constexpr int kFp4MaxLds = 160 * 1024;                              // LDS per w
 // gate_up: bias, clamped SwiGLU, bf16 -> a[pair row][I] (16*RN activations,
 // 32*RN bytes, per token per wave).  down: bias and routing weight in fp32,
 // rounded to bf16 -> zw[pair][H], one 32-feature slab (staged as 128 bytes,
-// stored as 64 per token) per pass.
-template <int RN, int RM, bool kGateUp>
+// stored as 64 per token) per pass.  NVFP4: the sums are first multiplied by
+// the expert's second-level scale (before the bias).
+template <int RN, int RM, bool kGateUp, bool kNv = false>
 __device__ __forceinline__ void store_epilogue(const mxfp4moe::GemmArgs& args, const f32x16 (&acc)[RN][RM], int e,
                                               int row0, int count, int n_wave, int lane, uint8_t* region) {
   const int N = args.N;
   const int half = lane >> 5, lrow = lane & 31;
   const uint16_t* bias = args.bias + (size_t)e * N;
+  const float s2 = kNv ? args.scale2[e] : 1.0f;
+  auto sum = [&](int rb, int cb, int r) { return kNv ? s2 * acc[rb][cb][r] : acc[rb][cb][r]; };
   auto chunk_addr = [](int m, int chunk) { return m * 128 + ((chunk ^ (m & 7)) << 4); };
   if (kGateUp) {
     // stage a[m][q_local], q_local = 0..16*RN-1 for this wave's 32*RN rows of w13
@@ -188,8 +208,8 @@ __device__ __forceinline__ void store_epilogue(const mxfp4moe::GemmArgs& args, c
 #pragma unroll
         for (int cb = 0; cb < RM; ++cb) {
           const int m = cb * 32 + lrow;
-          const float a0 = swiglu_clamped(acc[rb][cb][4 * i + 0] + b0, acc[rb][cb][4 * i + 1] + b1);
-          const float a1 = swiglu_clamped(acc[rb][cb][4 * i + 2] + b2, acc[rb][cb][4 * i + 3] + b3);
+          const float a0 = swiglu_clamped(sum(rb, cb, 4 * i + 0) + b0, sum(rb, cb, 4 * i + 1) + b1);
+          const float a1 = swiglu_clamped(sum(rb, cb, 4 * i + 2) + b2, sum(rb, cb, 4 * i + 3) + b3);
           *reinterpret_cast<uint32_t*>(region + chunk_addr(m, byte >> 4) + (byte & 15)) = mx::pack_bf16x2_rne(a0, a1);
         }
       }
@@ -222,10 +242,10 @@ __device__ __forceinline__ void store_epilogue(const mxfp4moe::GemmArgs& args, c
           const int m = cb * 32 + lrow;
           const float w = m < count ? args.topk_weights[args.sorted_pairs[row0 + m]] : 0.f;
           f32x4 v;
-          v[0] = w * (acc[rb][cb][4 * i + 0] + b0);
-          v[1] = w * (acc[rb][cb][4 * i + 1] + b1);
-          v[2] = w * (acc[rb][cb][4 * i + 2] + b2);
-          v[3] = w * (acc[rb][cb][4 * i + 3] + b3);
+          v[0] = w * (sum(rb, cb, 4 * i + 0) + b0);
+          v[1] = w * (sum(rb, cb, 4 * i + 1) + b1);
+          v[2] = w * (sum(rb, cb, 4 * i + 2) + b2);
+          v[3] = w * (sum(rb, cb, 4 * i + 3) + b3);
           *reinterpret_cast<f32x4*>(region + chunk_addr(m, 2 * i + half)) = v;
         }
       }
@@ -264,20 +284,27 @@ __device__ __forceinline__ void store_epilogue(const mxfp4moe::GemmArgs& args, c
 // kAhead = false: one operand set per wave, read right after the barrier
 // that makes the chunk visible; meant for two waves per SIMD (WM = 2), where
 // the other wave's MFMAs cover that wait.  Two chunks in flight.
-template <int WN, int WM, int RN, int RM, bool kGateUp, bool kAhead = true>
+// kNv: NVFP4 weights (E4M3 block scales per 16 codes, K a multiple of 64).  A
+// chunk's four scale bytes of a row are one aligned dword; each stage holds
+// them for the block's rows (one 4-byte global -> LDS load per row), in place
+// of the MXFP4 path's table of whole scale rows.
+template <int WN, int WM, int RN, int RM, bool kGateUp, bool kAhead = true, bool kNv = false>
 __global__ __launch_bounds__(WN * WM * 64, 1) void expert_wide_kernel(mxfp4moe::GemmArgs args) {
   constexpr int kThreads = WN * WM * 64;
   constexpr int BN = WN * RN * 32;
   constexpr int BM = WM * RM * 32;
   constexpr int kXSlots = BM * 8;
   constexpr int kWSlots = BN * 2;
+  constexpr int kSSlots = kNv ? BN / 4 : 0;  // NVFP4: one scale dword per row
   constexpr int kXPer = kXSlots / kThreads;
   constexpr int kWPer = kWSlots / kThreads;
-  static_assert(kXSlots % kThreads == 0 && kWSlots % kThreads == 0, "tile / thread mismatch");
+  constexpr int kSPer = kNv ? BN / kThreads : 0;
+  static_assert(kXSlots % kThreads == 0 && kWSlots % kThreads == 0 && (!kNv || BN % kThreads == 0),
+                "tile / thread mismatch");
   constexpr int kStages = 3;              // LDS stages: chunk c+3 loads while c+1 is read and c runs
-  constexpr int kLoads = kXPer + kWPer;  // loads per thread per chunk
-  constexpr int kStage = kXSlots + kWSlots;  // 16-byte slots per stage
-  constexpr int kArena = kStages * kStage * 16 + BN * kWideMaxGroups;
+  constexpr int kLoads = kXPer + kWPer + kSPer;  // loads per thread per chunk
+  constexpr int kStage = kXSlots + kWSlots + kSSlots;  // 16-byte slots per stage
+  constexpr int kArena = kStages * kStage * 16 + (kNv ? 0 : BN * kWideMaxGroups);
   static_assert(WN * WM * RM * 32 * 128 <= kArena, "epilogue regions fit in the arena");
   __shared__ __attribute__((aligned(16))) u32x4 arena[kArena / 16];
   uint8_t* const sst = reinterpret_cast<uint8_t*>(arena + kStages * kStage);
@@ -300,7 +327,7 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void expert_wide_kernel(mxfp4moe::
   const int lrow = lane & 31;
 
   const bool split = kGateUp && args.split_gate_up;  // uniform
-  stage_scales<BN, kThreads, true>(sst, args.wscales, args.N, e, ntile, kgroups, t, split);
+  if (!kNv) stage_scales<BN, kThreads, true>(sst, args.wscales, args.N, e, ntile, kgroups, t, split);
 
   // token slot p = t + i*threads -> row p/8, logical column slot_col(row, p%8);
   // rows past `count` re-read the tile's first row (their columns are never stored)
@@ -324,6 +351,14 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void expert_wide_kernel(mxfp4moe::
     wr = w13_row(wr < N ? wr : N - 1, N, split);
     wsrc[j] = args.wblocks + ((size_t)e * N + wr) * (size_t)(K >> 1);
   }
+  // NVFP4 scale slot j: the dword of row t + j*threads (rows past N re-read row N-1)
+  const uint8_t* ssrc[kSPer > 0 ? kSPer : 1];
+#pragma unroll
+  for (int j = 0; j < kSPer; ++j) {
+    int wr = ntile * BN + t + j * kThreads;
+    wr = w13_row(wr < N ? wr : N - 1, N, split);
+    ssrc[j] = args.wscales + ((size_t)e * N + wr) * (size_t)(K >> 4);
+  }
   const int wh = t & 1;
 
   // chunk c (the last chunk again past the end) into stage st; lane l of the
@@ -342,10 +377,16 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void expert_wide_kernel(mxfp4moe::
     g = g < kgroups ? g : g - 1;
 #pragma unroll
     for (int j = 0; j < kWPer; ++j) load_lds16(wsrc[j] + (size_t)g * 16, ws + j * kThreads);
+#pragma unroll
+    for (int j = 0; j < kSPer; ++j)
+      load_lds4(ssrc[j] + 4 * c,
+                reinterpret_cast<uint32_t*>(arena + st * kStage + kXSlots + kWSlots) + wave * 64 + j * kThreads);
   };
 
   const int wslot0 = (wn * RN * 32 + lrow) * 2 + half;
   const uint8_t* srow = sst + staged_row(wn * RN * 32 + lrow, min(BN, N - ntile * BN), split) * kgroups;
+  // NVFP4: byte offset of this lane's two scale bytes (group 2c + half) in a stage's scale dwords
+  const int nvs0 = (wn * RN * 32 + lrow) * 4 + 2 * half;
   const int n_wave = ntile * BN + wn * RN * 32;
   const int m_wave = wm * RM * 32;
   const bool live = WM == 1 || m_wave < count;  // wave-uniform; a tile holds at least one pair
@@ -363,19 +404,25 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void expert_wide_kernel(mxfp4moe::
   // them until the chunk runs, a chunk later)
   struct Ops {
     u32x4 w[RN];
-    uint32_t sb[RN];  // E8M0 scale bytes
+    uint32_t sb[RN];  // E8M0 scale byte (NVFP4: the group's two E4M3 bytes, low byte first)
     bf16x8 b[4][RM];
+  };
+  auto read_scale = [&](int c, int st, int rb) -> uint32_t {
+    if (kNv) {
+      const uint8_t* ss = reinterpret_cast<const uint8_t*>(arena + st * kStage + kXSlots + kWSlots);
+      return *reinterpret_cast<const uint16_t*>(ss + nvs0 + rb * 128);
+    }
+    const int g = 2 * c + half;
+    return srow[rb * rb_stride + (g < kgroups ? g : g - 1)];
   };
   auto read_ops = [&](Ops& o, int c, int st) {
     c = c < nchunks ? c : nchunks - 1;  // past the end: a harmless re-read
     const u32x4* xs = arena + st * kStage;
     const u32x4* wsm = xs + kXSlots;
-    const int g = 2 * c + half;
-    const int gg = g < kgroups ? g : g - 1;
 #pragma unroll
     for (int rb = 0; rb < RN; ++rb) {
       o.w[rb] = wsm[wslot0 + rb * 64];
-      o.sb[rb] = srow[rb * rb_stride + gg];
+      o.sb[rb] = read_scale(c, st, rb);
     }
     read_token_frags<RM>(o.b, xs + m_wave * 8, lrow, half);
   };
@@ -386,10 +433,14 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void expert_wide_kernel(mxfp4moe::
     if (k < kXPer) {
       const int koff = (c * 64 + xcol[k] < K) ? c * 64 : c * 64 - 32;
       load_lds16(xsrc[k] + koff, xs + k * kThreads);
-    } else {
+    } else if (k < kXPer + kWPer) {
       int g = 2 * c + wh;
       g = g < kgroups ? g : g - 1;
       load_lds16(wsrc[k - kXPer] + (size_t)g * 16, xs + kXSlots + (k - kXPer) * kThreads);
+    } else {
+      const int j = k - kXPer - kWPer;
+      load_lds4(ssrc[j] + 4 * c,
+                reinterpret_cast<uint32_t*>(arena + st * kStage + kXSlots + kWSlots) + wave * 64 + j * kThreads);
     }
   };
   // LDS read j of chunk c's operands (weights, scale bytes, token fragments) from stage st
@@ -397,16 +448,26 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void expert_wide_kernel(mxfp4moe::
   auto read_one = [&](Ops& o, int c, int st, int j) {
     c = c < nchunks ? c : nchunks - 1;
     const u32x4* xs = arena + st * kStage;
-    const int g = 2 * c + half;
-    const int gg = g < kgroups ? g : g - 1;
     if (j < RN) {
       o.w[j] = xs[kXSlots + wslot0 + j * 64];
     } else if (j < 2 * RN) {
-      o.sb[j - RN] = srow[(j - RN) * rb_stride + gg];
+      o.sb[j - RN] = read_scale(c, st, j - RN);
     } else {
       const int s = (j - 2 * RN) / RM, cb = (j - 2 * RN) % RM;
       const int row = cb * 32 + lrow;
       o.b[s][cb] = __builtin_bit_cast(bf16x8, xs[m_wave * 8 + row * 8 + slot_col(row, half * 4 + s)]);
+    }
+  };
+  // conversion operands of a fragment's scale byte(s) (see chunk_mma_regs)
+  auto scales_of = [](uint32_t sb, float& lo, float& hi, uint32_t& nanm) {
+    if (kNv) {
+      const mx::f32x2p v = mx::e4m3x2_operands(sb);
+      lo = v.x;
+      hi = v.y;
+      nanm = 0u;
+    } else {
+      lo = hi = mx::e8m0_operand(sb);
+      nanm = mx::e8m0_nan_mask(sb);
     }
   };
   // chunk c from registers `cur` (stage st = c % kStages, a constant at every
@@ -419,10 +480,12 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void expert_wide_kernel(mxfp4moe::
     // chunks after it are in flight
     wait_loads_then_barrier<(kStages - 2) * kLoads>();
     if (live) {
-      static_assert(!kAhead || 2 * (kLoads + kReads) <= 4 * RN * RM, "room between the MFMAs");
+      // one memory instruction after every other MFMA; what does not fit
+      // (NVFP4's scale loads) after the first odd ones
+      constexpr int kSlots = 2 * RN * RM;
+      static_assert(!kAhead || kLoads + kReads <= 2 * kSlots, "room between the MFMAs");
       auto extra = [&](int k) {
-        if (k % 2 != 0) return;
-        const int op = k / 2;
+        const int op = k % 2 == 0 ? k / 2 : kSlots + k / 2;
         if (op < kLoads) issue_one(c + kStages, st, op);
         else if (op < kLoads + kReads) read_one(nxt, c + 1, (st + 1) % kStages, op - kLoads);
         else return;
@@ -431,15 +494,14 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void expert_wide_kernel(mxfp4moe::
       // K tail: the group past K multiplies zero weights
       const bool glive = 2 * c + half < kgroups;
       u32x4 w[RN];
-      float sc[RN];
+      float sc[RN], sc_hi[RN];
       uint32_t nanm[RN];
 #pragma unroll
       for (int rb = 0; rb < RN; ++rb) {
         w[rb] = glive ? cur.w[rb] : u32x4{0u, 0u, 0u, 0u};
-        sc[rb] = mx::e8m0_operand(cur.sb[rb]);
-        nanm[rb] = mx::e8m0_nan_mask(cur.sb[rb]);
+        scales_of(cur.sb[rb], sc[rb], sc_hi[rb], nanm[rb]);
       }
-      chunk_mma_regs<RN, RM>(acc, cur.b, w, sc, nanm, extra);
+      chunk_mma_regs<RN, RM, kNv>(acc, cur.b, w, sc, sc_hi, nanm, extra);
     } else {
       issue(c + kStages, st);
     }
@@ -486,15 +548,14 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void expert_wide_kernel(mxfp4moe::
         };
         const bool glive = 2 * c + half < kgroups;
         u32x4 w[RN];
-        float sc[RN];
+        float sc[RN], sc_hi[RN];
         uint32_t nanm[RN];
 #pragma unroll
         for (int rb = 0; rb < RN; ++rb) {
           w[rb] = glive ? cur.w[rb] : u32x4{0u, 0u, 0u, 0u};
-          sc[rb] = mx::e8m0_operand(cur.sb[rb]);
-          nanm[rb] = mx::e8m0_nan_mask(cur.sb[rb]);
+          scales_of(cur.sb[rb], sc[rb], sc_hi[rb], nanm[rb]);
         }
-        chunk_mma_regs<RN, RM>(acc, cur.b, w, sc, nanm, extra);
+        chunk_mma_regs<RN, RM, kNv>(acc, cur.b, w, sc, sc_hi, nanm, extra);
       } else {
         issue(c + 2, (st + 2) % kStages);
       }
@@ -512,23 +573,19 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void expert_wide_kernel(mxfp4moe::
   // the chunks issued past the end land before the arena is reused
   wait_loads_then_barrier<0>();
   uint8_t* region = reinterpret_cast<uint8_t*>(arena) + wave * (RM * 32 * 128);
-  if (live) store_epilogue<RN, RM, kGateUp>(args, acc, e, row0 + m_wave, count - m_wave, n_wave, lane, region);
+  if (live) store_epilogue<RN, RM, kGateUp, kNv>(args, acc, e, row0 + m_wave, count - m_wave, n_wave, lane, region);
 }
 
-template <int WN, int WM, int RN, int RM, bool kGateUp, bool kAhead = true>
+template <int WN, int WM, int RN, int RM, bool kGateUp, bool kAhead = true, bool kNv = false>
 hipError_t launch_wide(const mxfp4moe::GemmArgs& a, hipStream_t stream) {
   constexpr int BN = WN * RN * 32;
   const long n_tiles = (a.N + BN - 1) / BN;
   const long blocks = n_tiles * a.max_tiles;
   if (blocks == 0) return hipSuccess;
+  if (kNv && (a.K & 63) != 0) return hipErrorInvalidValue;  // NVFP4 full tiles: whole 64-wide chunks only
   const long grid = (blocks + kXcds - 1) / kXcds * kXcds;
-  expert_wide_kernel<WN, WM, RN, RM, kGateUp, kAhead><<<(unsigned)grid, WN * WM * 64, 0, stream>>>(a);
+  expert_wide_kernel<WN, WM, RN, RM, kGateUp, kAhead, kNv><<<(unsigned)grid, WN * WM * 64, 0, stream>>>(a);
   return hipGetLastError();
-}
-
-// 4 bytes per lane from global memory straight into LDS (lane l's word at lds + 4 * l).
-__device__ __forceinline__ void load_lds4(const void* src, uint32_t* lds) {
-  __builtin_amdgcn_global_load_lds(src, lds, 4, 0, 0);
 }
 
 // FP4 scaled-MFMA variant of the wide kernel (opt-in): the same 512-row x
@@ -1314,7 +1371,6 @@ static_assert(kWideTokens == 128 && kStreamTokens == 4, "tile sizes");
 template <bool kGateUp>
 static hipError_t launch_all(GemmArgs a, const TileTables& tt, const TileBounds& tb, hipStream_t stream) {
   hipError_t err = hipSuccess;
-  if (tb.max_big > 0 && a.scale2 != nullptr) return hipErrorInvalidValue;  // NVFP4 runs mid / streaming tiles only
   if (tb.max_big > 0) {
     ProfileScope prof(kGateUp ? kStageGateUpWide : kStageDownWide, stream);
     GemmArgs w = a;
@@ -1330,10 +1386,12 @@ static hipError_t launch_all(GemmArgs a, const TileTables& tt, const TileBounds&
       // operand set each), whose second wave covers the heavier epilogue and
       // the LDS waits (measured at the 120b prefill shape: down 264 against
       // 274 us, gate_up 499 against 478 us the other way round)
+      const bool nv = a.scale2 != nullptr;
       if (kGateUp)
-        err = launch_wide<4, 1, 4, 4, true>(w, stream);
+        err = nv ? launch_wide<4, 1, 4, 4, true, true, true>(w, stream) : launch_wide<4, 1, 4, 4, true>(w, stream);
       else
-        err = launch_wide<4, 2, 4, 2, false, false>(w, stream);
+        err = nv ? launch_wide<4, 2, 4, 2, false, false, true>(w, stream)
+                 : launch_wide<4, 2, 4, 2, false, false>(w, stream);
     }
   }
   if (err == hipSuccess && tb.max_mid > 0) {

@@ -46,14 +46,15 @@ __device__ __forceinline__ u32x4 fp4x8_to_bf16x8(uint32_t packed, float scale) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// FP8 E4M3 byte (OCP, finite-only: 4 exponent bits with bias 7, 3 mantissa
-// bits, exponent field 0 subnormal, S.1111.111 NaN) -> float, exactly.  The
-// NVFP4 block scale.
-__device__ __forceinline__ float e4m3_operand(uint32_t b) {
-  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
-  float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
-  if ((b & 0x7fu) == 0x7fu) v = __builtin_nanf("");
-  return (b & 0x80u) ? -v : v;
+// Two FP8 E4M3 bytes (OCP, finite-only: 4 exponent bits with bias 7, 3
+// mantissa bits, exponent field 0 subnormal, S.1111.111 NaN; bits 0-7 and
+// 8-15 of `two`) -> two floats, exactly, in one v_cvt_pk_f32_fp8: the NVFP4
+// block scales of a 32-code group.  gfx950's conversion follows the OCP
+// encoding; it was checked on gfx950 hardware against the exact decode (sign,
+// subnormals, NaN) for all 256 byte values.
+typedef __attribute__((ext_vector_type(2))) float f32x2p;
+__device__ __forceinline__ f32x2p e4m3x2_operands(uint32_t two) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8((int)two, false);
 }
 
 // Two floats -> two bf16 (round to nearest even) packed low/high, with the
@@ -72,17 +73,18 @@ __device__ __forceinline__ uint32_t pack_bf16x2_rne(float lo, float hi) {
 // codes -> exact floats, times the scale, then bf16 round to nearest even
 // (exact when the product fits in 8 significant bits, as code x E4M3 does).
 typedef __attribute__((ext_vector_type(2))) float f32x2e;
+// Two codes (byte SEL of `packed`, low nibble -> low half) of the above.
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4x2_to_bf16x2_any_scale(uint32_t packed, float scale) {
+  const f32x2e v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, 1.0f, SEL);
+  return pack_bf16x2_rne(v.x * scale, v.y * scale);
+}
 __device__ __forceinline__ u32x4 fp4x8_to_bf16x8_any_scale(uint32_t packed, float scale) {
   u32x4 r;
-  f32x2e v;
-  v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, 1.0f, 0);
-  r[0] = pack_bf16x2_rne(v.x * scale, v.y * scale);
-  v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, 1.0f, 1);
-  r[1] = pack_bf16x2_rne(v.x * scale, v.y * scale);
-  v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, 1.0f, 2);
-  r[2] = pack_bf16x2_rne(v.x * scale, v.y * scale);
-  v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, 1.0f, 3);
-  r[3] = pack_bf16x2_rne(v.x * scale, v.y * scale);
+  r[0] = fp4x2_to_bf16x2_any_scale<0>(packed, scale);
+  r[1] = fp4x2_to_bf16x2_any_scale<1>(packed, scale);
+  r[2] = fp4x2_to_bf16x2_any_scale<2>(packed, scale);
+  r[3] = fp4x2_to_bf16x2_any_scale<3>(packed, scale);
   return r;
 }
 

@@ -62,3 +62,15 @@ def long_prefill_120b():
     ref = O.moe_forward(L, spec.top_k)
     print(f"[oracle] 120b long prefill, all {spec.T} tokens: {time.perf_counter() - t0:.1f} s", flush=True)
     return spec, L, ref
+
+
+@functools.lru_cache(maxsize=None)
+def long_prefill_120b_nvfp4():
+    """The same long-prefill shapes with NVFP4 experts, and the oracle's output
+    on every element."""
+    spec = W.LAYERS["120b_prefill"]
+    L = W.make_nvfp4_layer(spec)
+    t0 = time.perf_counter()
+    ref = O.moe_forward_nvfp4(L, spec.top_k)
+    print(f"[oracle] NVFP4 120b long prefill, all {spec.T} tokens: {time.perf_counter() - t0:.1f} s", flush=True)
+    return spec, L, ref
