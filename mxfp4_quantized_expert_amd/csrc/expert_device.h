@@ -59,15 +59,11 @@ __device__ __forceinline__ f32x4 load_bias4(const uint16_t* bias, int n, int N, 
 // MXFP4: one E8M0 byte for all 32.  NVFP4: two E4M3 block scales, the first
 // for the codes of steps 0 and 1, the second for steps 2 and 3; the result is
 // exact in bf16 (a code has at most 2 significant bits, an E4M3 value 4).
-// MXFP4: E8M0 byte 0xFF is NaN, so the group's weights are NaN (OCP MX).  A
-// single NaN element is enough to make every dot product over the group NaN,
-// so the NaN is OR-ed into the first two converted elements of the group only
-// (nan_mask: 0x7FC07FC0 for byte 0xFF, else 0).  NVFP4's E4M3 NaN scale
-// reaches the weights through the float32 conversion by itself.
+// A NaN scale (E8M0 0xFF, E4M3 S.1111.111) makes every weight of its group
+// NaN through the conversion itself (see e8m0_operand).
 template <bool kNv>
 struct GroupScale {
   float lo, hi;
-  uint32_t nan;
   __device__ __forceinline__ GroupScale(const uint8_t* srow, int g) : GroupScale(kNv ? srow[2 * g] : srow[g],
                                                                                    kNv ? srow[2 * g + 1] : 0u) {}
   // from the group's scale byte(s) already read (b1 only for NVFP4)
@@ -76,18 +72,14 @@ struct GroupScale {
       const mx::f32x2p v = mx::e4m3x2_operands(b0 | (b1 << 8));
       lo = v.x;
       hi = v.y;
-      nan = 0u;
     } else {
       lo = hi = mx::e8m0_operand(b0);
-      nan = mx::e8m0_nan_mask(b0);
     }
   }
   __device__ __forceinline__ float step(int s) const { return s < 2 ? lo : hi; }
   // eight codes of step s as bf16
   __device__ __forceinline__ u32x4 convert(uint32_t packed, int s) const {
-    u32x4 r = kNv ? mx::fp4x8_to_bf16x8_any_scale(packed, step(s)) : mx::fp4x8_to_bf16x8(packed, step(s));
-    if (!kNv && s == 0) r[0] |= nan;
-    return r;
+    return kNv ? mx::fp4x8_to_bf16x8_any_scale(packed, step(s)) : mx::fp4x8_to_bf16x8(packed, step(s));
   }
 };
 

@@ -97,25 +97,17 @@ struct NoExtra {
 // `extra(k)` runs right after the k-th MFMA of the chunk (k = 0 .. 4*RN*RM-1),
 // so a caller can spread other instructions between the MFMAs.
 // MXFP4 (kNv = false): sc[rb] is fragment rb's E8M0 scale as a convert
-// operand and nanm[rb] the NaN mask of its scale byte (see GroupScale), OR-ed
-// into its first converted elements; sc_hi is unused.  NVFP4: sc[rb] and
-// sc_hi[rb] are the E4M3 block scales of steps 0-1 and 2-3 as floats, applied
-// by the exact float32 conversion; nanm is unused.
+// operand; sc_hi is unused.  NVFP4: sc[rb] and sc_hi[rb] are the E4M3 block
+// scales of steps 0-1 and 2-3 as floats, applied by the exact float32
+// conversion.
 template <int RN, int RM, bool kNv = false, typename Extra = NoExtra>
 __device__ __forceinline__ void chunk_mma_regs(f32x16 (&acc)[RN][RM], const bf16x8 (&b)[4][RM],
                                                const u32x4 (&w)[RN], const float (&sc)[RN],
-                                               const float (&sc_hi)[RN], const uint32_t (&nanm)[RN],
-                                               Extra extra = Extra()) {
+                                               const float (&sc_hi)[RN], Extra extra = Extra()) {
   u32x4 a[2][RN];
 #pragma unroll
-  for (int rb = 0; rb < RN; ++rb) {
-    if (kNv) {
-      a[0][rb] = mx::fp4x8_to_bf16x8_any_scale(w[rb][0], sc[rb]);
-    } else {
-      a[0][rb] = mx::fp4x8_to_bf16x8(w[rb][0], sc[rb]);
-      a[0][rb][0] |= nanm[rb];
-    }
-  }
+  for (int rb = 0; rb < RN; ++rb)
+    a[0][rb] = kNv ? mx::fp4x8_to_bf16x8_any_scale(w[rb][0], sc[rb]) : mx::fp4x8_to_bf16x8(w[rb][0], sc[rb]);
   auto convert = [&](int s, int i) {  // converts pair i%4 of fragment i/4 for step s
     const int rb = i / 4, sel = i % 4;
     const uint32_t packed = w[rb][s];
@@ -288,7 +280,10 @@ __device__ __forceinline__ void store_epilogue(const mxfp4moe::GemmArgs& args, c
 // chunk's four scale bytes of a row are one aligned dword; each stage holds
 // them for the block's rows (one 4-byte global -> LDS load per row), in place
 // of the MXFP4 path's table of whole scale rows.
-template <int WN, int WM, int RN, int RM, bool kGateUp, bool kAhead = true, bool kNv = false>
+// kTail: K is not a multiple of 64, so the last chunk holds one group; its
+// missing group re-reads the one before and multiplies zeroed weights.
+// Without it the selects of that case are compiled out.
+template <int WN, int WM, int RN, int RM, bool kGateUp, bool kAhead = true, bool kNv = false, bool kTail = false>
 __global__ __launch_bounds__(WN * WM * 64, 1) void expert_wide_kernel(mxfp4moe::GemmArgs args) {
   constexpr int kThreads = WN * WM * 64;
   constexpr int BN = WN * RN * 32;
@@ -370,11 +365,11 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void expert_wide_kernel(mxfp4moe::
 #pragma unroll
     for (int i = 0; i < kXPer; ++i) {
       // K tail: the missing half chunk re-reads the first half (its weights are zero)
-      const int koff = (c * 64 + xcol[i] < K) ? c * 64 : c * 64 - 32;
+      const int koff = (!kTail || c * 64 + xcol[i] < K) ? c * 64 : c * 64 - 32;
       load_lds16(xsrc[i] + koff, xs + i * kThreads);
     }
     int g = 2 * c + wh;
-    g = g < kgroups ? g : g - 1;
+    if (kTail) g = g < kgroups ? g : g - 1;
 #pragma unroll
     for (int j = 0; j < kWPer; ++j) load_lds16(wsrc[j] + (size_t)g * 16, ws + j * kThreads);
 #pragma unroll
@@ -413,7 +408,7 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void expert_wide_kernel(mxfp4moe::
       return *reinterpret_cast<const uint16_t*>(ss + nvs0 + rb * 128);
     }
     const int g = 2 * c + half;
-    return srow[rb * rb_stride + (g < kgroups ? g : g - 1)];
+    return srow[rb * rb_stride + (!kTail || g < kgroups ? g : g - 1)];
   };
   auto read_ops = [&](Ops& o, int c, int st) {
     c = c < nchunks ? c : nchunks - 1;  // past the end: a harmless re-read
@@ -431,11 +426,11 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void expert_wide_kernel(mxfp4moe::
     c = c < nchunks ? c : nchunks - 1;
     u32x4* xs = arena + st * kStage + wave * 64;
     if (k < kXPer) {
-      const int koff = (c * 64 + xcol[k] < K) ? c * 64 : c * 64 - 32;
+      const int koff = (!kTail || c * 64 + xcol[k] < K) ? c * 64 : c * 64 - 32;
       load_lds16(xsrc[k] + koff, xs + k * kThreads);
     } else if (k < kXPer + kWPer) {
       int g = 2 * c + wh;
-      g = g < kgroups ? g : g - 1;
+      if (kTail) g = g < kgroups ? g : g - 1;
       load_lds16(wsrc[k - kXPer] + (size_t)g * 16, xs + kXSlots + (k - kXPer) * kThreads);
     } else {
       const int j = k - kXPer - kWPer;
@@ -459,15 +454,13 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void expert_wide_kernel(mxfp4moe::
     }
   };
   // conversion operands of a fragment's scale byte(s) (see chunk_mma_regs)
-  auto scales_of = [](uint32_t sb, float& lo, float& hi, uint32_t& nanm) {
+  auto scales_of = [](uint32_t sb, float& lo, float& hi) {
     if (kNv) {
       const mx::f32x2p v = mx::e4m3x2_operands(sb);
       lo = v.x;
       hi = v.y;
-      nanm = 0u;
     } else {
       lo = hi = mx::e8m0_operand(sb);
-      nanm = mx::e8m0_nan_mask(sb);
     }
   };
   // chunk c from registers `cur` (stage st = c % kStages, a constant at every
@@ -492,16 +485,15 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void expert_wide_kernel(mxfp4moe::
         __builtin_amdgcn_sched_barrier(0);  // keep the order: the compiler would bunch the MFMAs
       };
       // K tail: the group past K multiplies zero weights
-      const bool glive = 2 * c + half < kgroups;
+      const bool glive = !kTail || 2 * c + half < kgroups;
       u32x4 w[RN];
       float sc[RN], sc_hi[RN];
-      uint32_t nanm[RN];
 #pragma unroll
       for (int rb = 0; rb < RN; ++rb) {
         w[rb] = glive ? cur.w[rb] : u32x4{0u, 0u, 0u, 0u};
-        scales_of(cur.sb[rb], sc[rb], sc_hi[rb], nanm[rb]);
+        scales_of(cur.sb[rb], sc[rb], sc_hi[rb]);
       }
-      chunk_mma_regs<RN, RM, kNv>(acc, cur.b, w, sc, sc_hi, nanm, extra);
+      chunk_mma_regs<RN, RM, kNv>(acc, cur.b, w, sc, sc_hi, extra);
     } else {
       issue(c + kStages, st);
     }
@@ -546,16 +538,15 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void expert_wide_kernel(mxfp4moe::
           issue_one(c + 2, (st + 2) % kStages, k / kEvery);
           __builtin_amdgcn_sched_barrier(0);
         };
-        const bool glive = 2 * c + half < kgroups;
+        const bool glive = !kTail || 2 * c + half < kgroups;
         u32x4 w[RN];
         float sc[RN], sc_hi[RN];
-        uint32_t nanm[RN];
-#pragma unroll
+  #pragma unroll
         for (int rb = 0; rb < RN; ++rb) {
           w[rb] = glive ? cur.w[rb] : u32x4{0u, 0u, 0u, 0u};
-          scales_of(cur.sb[rb], sc[rb], sc_hi[rb], nanm[rb]);
+          scales_of(cur.sb[rb], sc[rb], sc_hi[rb]);
         }
-        chunk_mma_regs<RN, RM, kNv>(acc, cur.b, w, sc, sc_hi, nanm, extra);
+        chunk_mma_regs<RN, RM, kNv>(acc, cur.b, w, sc, sc_hi, extra);
       } else {
         issue(c + 2, (st + 2) % kStages);
       }
@@ -582,9 +573,13 @@ hipError_t launch_wide(const mxfp4moe::GemmArgs& a, hipStream_t stream) {
   const long n_tiles = (a.N + BN - 1) / BN;
   const long blocks = n_tiles * a.max_tiles;
   if (blocks == 0) return hipSuccess;
-  if (kNv && (a.K & 63) != 0) return hipErrorInvalidValue;  // NVFP4 full tiles: whole 64-wide chunks only
+  const bool tail = (a.K & 63) != 0;
+  if (kNv && tail) return hipErrorInvalidValue;  // NVFP4 full tiles: whole 64-wide chunks only
   const long grid = (blocks + kXcds - 1) / kXcds * kXcds;
-  expert_wide_kernel<WN, WM, RN, RM, kGateUp, kAhead, kNv><<<(unsigned)grid, WN * WM * 64, 0, stream>>>(a);
+  if (!kNv && tail)
+    expert_wide_kernel<WN, WM, RN, RM, kGateUp, kAhead, false, true><<<(unsigned)grid, WN * WM * 64, 0, stream>>>(a);
+  else
+    expert_wide_kernel<WN, WM, RN, RM, kGateUp, kAhead, kNv><<<(unsigned)grid, WN * WM * 64, 0, stream>>>(a);
   return hipGetLastError();
 }
 
