@@ -253,6 +253,7 @@ int forward_impl(const uint16_t* x, const float* router_logits, const uint16_t* 
     g.wscales = w13_scales;
     g.bias = w13_bias;
     g.act = x;
+    g.act_rows = T;
     g.out = act;
     g.N = (int)(2 * I);
     g.K = (int)H;
@@ -270,6 +271,7 @@ int forward_impl(const uint16_t* x, const float* router_logits, const uint16_t* 
     g.wscales = w2_scales;
     g.bias = w2_bias;
     g.act = act;
+    g.act_rows = P;
     g.out = zw;
     g.N = (int)H;
     g.K = (int)I;

@@ -280,9 +280,14 @@ __device__ __forceinline__ void store_epilogue(const mxfp4moe::GemmArgs& args, c
 // chunk's four scale bytes of a row are one aligned dword; each stage holds
 // them for the block's rows (one 4-byte global -> LDS load per row), in place
 // of the MXFP4 path's table of whole scale rows.
-// kTail: K is not a multiple of 64, so the last chunk holds one group; its
-// missing group re-reads the one before and multiplies zeroed weights.
-// Without it the selects of that case are compiled out.
+// kTail: the general form, for any K (a multiple of 32): when K is not a
+// multiple of 64 the last chunk holds one group, whose missing group re-reads
+// the one before and multiplies zeroed weights; operands are addressed by
+// 64-bit pointers.  Without it (K a multiple of 64, every byte offset into the
+// activations and into one expert's weights below 2^31) the selects are
+// compiled out and the loads are buffer loads into LDS: a thread keeps a
+// 32-bit offset per operand row and the chunk's offset moves in a scalar
+// register, so a chunk's loads cost no vector address arithmetic.
 template <int WN, int WM, int RN, int RM, bool kGateUp, bool kAhead = true, bool kNv = false, bool kTail = false>
 __global__ __launch_bounds__(WN * WM * 64, 1) void expert_wide_kernel(mxfp4moe::GemmArgs args) {
   constexpr int kThreads = WN * WM * 64;
@@ -355,6 +360,32 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void expert_wide_kernel(mxfp4moe::
     ssrc[j] = args.wscales + ((size_t)e * N + wr) * (size_t)(K >> 4);
   }
   const int wh = t & 1;
+  // the fast form's buffer resources and per-thread byte offsets (the same
+  // rows as the pointers above); raw buffers, no swizzle, range-checked
+  // against their byte counts
+  constexpr int kRawBuffer = 0x00020000;  // descriptor word 3: 32-bit data format, for untyped loads
+  // (built in the general form too, where nothing uses them)
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(args.act), (short)0, (int)(args.act_rows * K * 2), kRawBuffer);
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(args.wblocks + (size_t)e * N * (K >> 1)), (short)0, N * (K >> 1), kRawBuffer);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(args.wscales + (size_t)e * N * (K >> 4)), (short)0, N * (K >> 4), kRawBuffer);
+  int xoff[kXPer], woff[kWPer], soff[kSPer > 0 ? kSPer : 1];
+  if (!kTail) {
+#pragma unroll
+    for (int i = 0; i < kXPer; ++i) xoff[i] = (int)((xsrc[i] - args.act) * 2);
+#pragma unroll
+    for (int j = 0; j < kWPer; ++j) woff[j] = (int)(wsrc[j] - (args.wblocks + (size_t)e * N * (K >> 1))) + 16 * wh;
+#pragma unroll
+    for (int j = 0; j < kSPer; ++j) soff[j] = (int)(ssrc[j] - (args.wscales + (size_t)e * N * (K >> 4)));
+  }
+  auto buf_lds = [](__amdgpu_buffer_rsrc_t r, void* lds, int bytes, int voff, int soffs) {
+    if (bytes == 16)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soffs, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, voff, soffs, 0, 0);
+  };
 
   // chunk c (the last chunk again past the end) into stage st; lane l of the
   // wave lands in slot wave*64 + l (+ i*threads), as the register path stores it
@@ -362,20 +393,28 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void expert_wide_kernel(mxfp4moe::
     c = c < nchunks ? c : nchunks - 1;
     u32x4* xs = arena + st * kStage + wave * 64;
     u32x4* ws = xs + kXSlots;
+    uint32_t* const ss = reinterpret_cast<uint32_t*>(arena + st * kStage + kXSlots + kWSlots) + wave * 64;
+    if (!kTail) {
+#pragma unroll
+      for (int i = 0; i < kXPer; ++i) buf_lds(rx, xs + i * kThreads, 16, xoff[i], c * 128);
+#pragma unroll
+      for (int j = 0; j < kWPer; ++j) buf_lds(rw, ws + j * kThreads, 16, woff[j], c * 32);
+#pragma unroll
+      for (int j = 0; j < kSPer; ++j) buf_lds(rs, ss + j * kThreads, 4, soff[j], c * 4);
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < kXPer; ++i) {
       // K tail: the missing half chunk re-reads the first half (its weights are zero)
-      const int koff = (!kTail || c * 64 + xcol[i] < K) ? c * 64 : c * 64 - 32;
+      const int koff = c * 64 + xcol[i] < K ? c * 64 : c * 64 - 32;
       load_lds16(xsrc[i] + koff, xs + i * kThreads);
     }
     int g = 2 * c + wh;
-    if (kTail) g = g < kgroups ? g : g - 1;
+    g = g < kgroups ? g : g - 1;
 #pragma unroll
     for (int j = 0; j < kWPer; ++j) load_lds16(wsrc[j] + (size_t)g * 16, ws + j * kThreads);
 #pragma unroll
-    for (int j = 0; j < kSPer; ++j)
-      load_lds4(ssrc[j] + 4 * c,
-                reinterpret_cast<uint32_t*>(arena + st * kStage + kXSlots + kWSlots) + wave * 64 + j * kThreads);
+    for (int j = 0; j < kSPer; ++j) load_lds4(ssrc[j] + 4 * c, ss + j * kThreads);
   };
 
   const int wslot0 = (wn * RN * 32 + lrow) * 2 + half;
@@ -425,17 +464,26 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void expert_wide_kernel(mxfp4moe::
   auto issue_one = [&](int c, int st, int k) {
     c = c < nchunks ? c : nchunks - 1;
     u32x4* xs = arena + st * kStage + wave * 64;
+    uint32_t* const ss = reinterpret_cast<uint32_t*>(arena + st * kStage + kXSlots + kWSlots) + wave * 64;
     if (k < kXPer) {
-      const int koff = (!kTail || c * 64 + xcol[k] < K) ? c * 64 : c * 64 - 32;
-      load_lds16(xsrc[k] + koff, xs + k * kThreads);
+      if (!kTail) {
+        buf_lds(rx, xs + k * kThreads, 16, xoff[k], c * 128);
+      } else {
+        const int koff = c * 64 + xcol[k] < K ? c * 64 : c * 64 - 32;
+        load_lds16(xsrc[k] + koff, xs + k * kThreads);
+      }
     } else if (k < kXPer + kWPer) {
-      int g = 2 * c + wh;
-      if (kTail) g = g < kgroups ? g : g - 1;
-      load_lds16(wsrc[k - kXPer] + (size_t)g * 16, xs + kXSlots + (k - kXPer) * kThreads);
+      if (!kTail) {
+        buf_lds(rw, xs + kXSlots + (k - kXPer) * kThreads, 16, woff[k - kXPer], c * 32);
+      } else {
+        int g = 2 * c + wh;
+        g = g < kgroups ? g : g - 1;
+        load_lds16(wsrc[k - kXPer] + (size_t)g * 16, xs + kXSlots + (k - kXPer) * kThreads);
+      }
     } else {
       const int j = k - kXPer - kWPer;
-      load_lds4(ssrc[j] + 4 * c,
-                reinterpret_cast<uint32_t*>(arena + st * kStage + kXSlots + kWSlots) + wave * 64 + j * kThreads);
+      if (!kTail) buf_lds(rs, ss + j * kThreads, 4, soff[j], c * 4);
+      else load_lds4(ssrc[j] + 4 * c, ss + j * kThreads);
     }
   };
   // LDS read j of chunk c's operands (weights, scale bytes, token fragments) from stage st
@@ -573,13 +621,15 @@ hipError_t launch_wide(const mxfp4moe::GemmArgs& a, hipStream_t stream) {
   const long n_tiles = (a.N + BN - 1) / BN;
   const long blocks = n_tiles * a.max_tiles;
   if (blocks == 0) return hipSuccess;
-  const bool tail = (a.K & 63) != 0;
-  if (kNv && tail) return hipErrorInvalidValue;  // NVFP4 full tiles: whole 64-wide chunks only
+  if (kNv && (a.K & 63) != 0) return hipErrorInvalidValue;  // NVFP4 full tiles: whole 64-wide chunks only
+  // the fast form: whole 64-wide chunks and 32-bit buffer offsets
+  const bool fast = (a.K & 63) == 0 && a.act_rows * a.K * 2 < ((int64_t)1 << 31) &&
+                    (int64_t)a.N * (a.K >> 1) < ((int64_t)1 << 31);
   const long grid = (blocks + kXcds - 1) / kXcds * kXcds;
-  if (!kNv && tail)
-    expert_wide_kernel<WN, WM, RN, RM, kGateUp, kAhead, false, true><<<(unsigned)grid, WN * WM * 64, 0, stream>>>(a);
-  else
+  if (fast)
     expert_wide_kernel<WN, WM, RN, RM, kGateUp, kAhead, kNv><<<(unsigned)grid, WN * WM * 64, 0, stream>>>(a);
+  else
+    expert_wide_kernel<WN, WM, RN, RM, kGateUp, kAhead, kNv, true><<<(unsigned)grid, WN * WM * 64, 0, stream>>>(a);
   return hipGetLastError();
 }
 

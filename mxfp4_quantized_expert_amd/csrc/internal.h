@@ -100,6 +100,7 @@ struct GemmArgs {
   const int32_t* num_tiles;
   const float* topk_weights;  // [P] (down only)
   void* out;                // gate_up: a [P, N/2] bf16 in expert order; down: zw [P, N] bf16 by pair id
+  int64_t act_rows;         // rows of `act` (gate_up: T, down: P)
   int N, K, top_k, max_tiles;
   int split_gate_up;        // gate_up only: w13 rows stored [I gate rows; I up rows] instead of interleaved
   const float* scale2;      // NVFP4: [E] second-level scale per expert (scales are E4M3 per 16), else nullptr
