@@ -301,7 +301,7 @@ def run_moe(args):
         peak = PEAK_FP8_TFLOPS if args.act != "bf16" and dominant == "gate_up_wide" else PEAK_BF16_TFLOPS
         roof = {"bound": "mfma", "achieved": work / (kms / 1e3) / 1e12, "peak": peak, "unit": "TFLOP/s"}
         per_unit = (f"{4 * H * I:,} FLOPs per pair (2*H*2I) x {tile_pairs} pairs in "
-                    + ("128-pair tiles" if dominant == "gate_up_wide" else "mid tiles of at most 64 pairs"))
+                    + ("128-pair tiles" if dominant == "gate_up_wide" else "mid tiles of at most 48 pairs"))
     else:
         # packed w13 (blocks, scales, bias) of every active expert + x rows + a rows out
         # (the streaming or the mid launch carries every expert of a small batch)
@@ -316,7 +316,7 @@ def run_moe(args):
     roof["traffic"] = measured_traffic(args.workload, dominant)
     roof["kernel"] = {"gate_up_wide": ("expert_fp4_kernel" if args.act != "bf16" else "expert_wide_kernel")
                                        + " (gate_up, full 128-pair tiles)",
-                      "gate_up_mid": "expert_mid_kernel (gate_up, tiles of 5..64 pairs)",
+                      "gate_up_mid": "expert_mid_kernel (gate_up, tiles of 3..48 pairs)",
                       "gate_up_stream": "expert_stream_kernel (gate_up, tiles of at most 4 pairs)"}[dominant]
     roof["kernel_ms"] = kms
     roof["algorithmic"] = per_unit

@@ -163,8 +163,9 @@ int moe_mxfp4_route(const float* router_logits, int64_t T, int64_t E, int64_t to
  * output is rounded to bf16 before the down GEMM, and each weighted pair
  * output w * z to bf16 before the sum over the k pairs.  T == 0 is a no-op.
  * An expert with at least 128 pairs is cut into tiles of 128 (the last one
- * partial), one with 5..127 pairs into tiles of at most 64, one with at most
- * 4 pairs makes one streaming tile; each kind has a GEMM kernel of its own
+ * partial), one with 5..127 pairs into ceil(pairs / 48) tiles of near-equal
+ * size, one with at most 4 pairs makes one streaming tile; each kind has a
+ * GEMM kernel of its own
  * (with T <= 4 every expert has one streaming tile: the decode path).
  *
  * E8M0 byte 0xFF (NaN) in a weight row makes that row's GEMM output NaN for

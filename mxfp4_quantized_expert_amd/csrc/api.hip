@@ -62,21 +62,22 @@ struct Layout {
 // Tile table capacities.  An expert gets at most T pairs (a token's k
 // experts are distinct).  An expert with at least kWideTokens pairs makes
 // ceil(c / kWideTokens) wide tiles (at most P / kWideTokens full ones plus one
-// partial per such expert); one with kStreamTokens < c < kWideTokens pairs at
-// most two mid tiles; one with fewer, one streaming tile.  With no wide tiles
-// (NVFP4) an expert with more than kStreamTokens pairs makes ceil(c /
-// kMidTokens) mid tiles.  With streaming tiles only, every pair goes to tiles
-// of kStreamTokens.
+// partial per such expert); one with kStreamTokens < c < kWideTokens pairs
+// ceil(c / kMidTokens) mid tiles (at most kMidPerExpert, and never more than
+// one per kStreamTokens + 1 of its pairs); one with fewer, one streaming tile.
+// With no wide tiles an expert with more than kStreamTokens pairs makes
+// ceil(c / kMidTokens) mid tiles.  With streaming tiles only, every pair goes
+// to tiles of kStreamTokens.
 enum TileMode { kTilesWide, kTilesNoWide, kTilesStreamOnly };
 TileBounds tile_bounds(int64_t T, int64_t P, int64_t E, TileMode mode) {
   const int64_t active = E < P ? E : P;
   const int64_t fulls = P / kWideTokens;
   TileBounds b;
   b.max_big = (mode == kTilesWide && T >= kWideTokens) ? (int)(fulls + (active < fulls ? active : fulls)) : 0;
-  static_assert(2 * kMidTokens >= kWideTokens, "two mid tiles cover an expert below kWideTokens");
-  const int64_t mids = 2 * (P / (kStreamTokens + 1));
+  constexpr int64_t kMidPerExpert = (kWideTokens - 1 + kMidTokens - 1) / kMidTokens;
+  const int64_t mids = P / (kStreamTokens + 1);
   if (mode == kTilesWide)
-    b.max_mid = T > kStreamTokens ? (int)(2 * active < mids ? 2 * active : mids) : 0;
+    b.max_mid = T > kStreamTokens ? (int)(kMidPerExpert * active < mids ? kMidPerExpert * active : mids) : 0;
   else if (mode == kTilesNoWide)
     b.max_mid = T > kStreamTokens ? (int)(P / kMidTokens + active) : 0;
   else

@@ -1126,42 +1126,49 @@ hipError_t launch_stream(const mxfp4moe::GemmArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Mid-size tiles (kStreamTokens < pairs <= kMidTokens): the per-expert
-// remainders of prefill.  16x16x32 MFMA (A: lane (r, q) takes group 4c+q of
-// row r, step s its codes [8s, 8s+8), so K = 128c + 32q + 8s + i; B: the same
-// K values of token l%16).  A block owns 128 weight rows (four waves of
-// 2 x 16 rows) and up to 64 tokens (four 16-token column blocks).  K runs in
-// panels of kP chunks (128 K each); both operands of a panel are staged in
-// LDS: the block's 128 weight rows as kP*64 contiguous bytes per row (eight
-// lanes per row, 128 bytes per row per load: the pattern HBM streams at full
-// rate) and the tile's token rows as kP*256 bytes each.  The loads of panel
-// p+1 are issued before the MFMAs of panel p and stored after them (single
-// LDS buffer, two barriers per panel); with panels of one chunk a block
-// needs about 39 KB of LDS and 160 registers per lane at K = 2880, so three
-// blocks share a CU and overlap further (panels of two chunks, two blocks
-// per CU: 9 % slower at the 20b prefill shape, 17 % with NVFP4 weights).
-// Token columns past the tile's pairs read its first pair (their outputs are
-// dropped).
+// Mid-size tiles (kStreamTokens < pairs, at most kMidTokens = 48 per tile):
+// the per-expert remainders of prefill.  16x16x32 MFMA (A: lane (r, q) takes
+// group 4c+q of row r, step s its codes [8s, 8s+8), so K = 128c + 32q + 8s + i;
+// B: the same K values of token l%16).  A block owns 128 weight rows (four
+// waves of 2 x 16 rows) and up to 48 tokens (three 16-token column blocks).  K
+// runs in panels of one chunk (128 K); both operands of a panel are staged in
+// LDS: the block's 128 weight rows as 64 contiguous bytes per row (four lanes
+// per row: the pattern HBM streams at full rate) and the tile's token rows as
+// 256 bytes each.  A panel's loads go to one of three register slots, so three
+// panels are in flight while one runs from LDS: per panel, after its MFMAs and
+// a barrier, the next panel's slot is stored to the (single) LDS buffer, the
+// slot is refilled with the panel three ahead, and a second barrier makes the
+// stored panel visible.  The token bytes of a panel (at most 12 KB, from L2)
+// are at most 1.5 times its weight bytes (8 KB, from HBM), which is what lets
+// three panels fit in registers at three blocks per CU (with 64-token tiles
+// only two did).  The loop body is
+// three panels of straight-line code with the same loads in flight at entry
+// and at the back edge (the compiler then waits for each slot alone); panels
+// past the last re-read the last one (in bounds, never computed).  Token rows
+// past the tile's pairs re-read its first pair (their outputs are dropped).
 //
-// Dynamic LDS: tokens [64][kP*256 + 16] | weights [128][kP*64 + 16] |
-// scales [128][K/32]  (the 16-byte row pads make the 16-lane column reads
-// conflict-free).
-template <int kP, bool kNv = false>
+// Dynamic LDS: tokens [48][256 + 16] | weights [128][64 + 16] | scales [128][K/32]
+// (the 16-byte row pads make the 16-lane column reads conflict-free).
+template <bool kNv = false>
 __host__ __device__ constexpr size_t mid_lds_bytes(int K) {
-  return (size_t)64 * (kP * 256 + 16) + (size_t)128 * (kP * 64 + 16) + (size_t)128 * (K / (kNv ? 16 : 32));
+  return (size_t)mxfp4moe::kMidTokens * (256 + 16) + (size_t)128 * (64 + 16) + (size_t)128 * (K / (kNv ? 16 : 32));
 }
 
-template <int kP, bool kGateUp, bool kNv>
+template <bool kGateUp, bool kNv>
 __global__ __launch_bounds__(256, 2) void expert_mid_kernel(mxfp4moe::GemmArgs args) {
   constexpr int kThreads = 256;
   constexpr int BN = 128;
-  constexpr int kXRow = kP * 256 + 16;      // LDS bytes per token row of a panel
-  constexpr int kWRow = kP * 64 + 16;       // LDS bytes per weight row of a panel
-  constexpr int kXPieces = kP * 16;         // 16-byte pieces per token row of a panel
-  constexpr int kWPieces = kP * 4;          // 16-byte pieces per weight row of a panel
-  constexpr int kXPer = 64 * kXPieces / kThreads;
+  constexpr int BM = mxfp4moe::kMidTokens;
+  constexpr int kCB = BM / 16;  // 16-token column blocks
+  static_assert(BM % 16 == 0 && kCB <= 4, "16-token column blocks");
+  constexpr int kXRow = 256 + 16;     // LDS bytes per token row of a panel
+  constexpr int kWRow = 64 + 16;      // LDS bytes per weight row of a panel
+  constexpr int kXPieces = 16;        // 16-byte pieces per token row of a panel
+  constexpr int kWPieces = 4;         // 16-byte pieces per weight row of a panel
+  constexpr int kXPer = BM * kXPieces / kThreads;
   constexpr int kWPer = BN * kWPieces / kThreads;
-  static_assert(64 * kXPieces % kThreads == 0 && BN * kWPieces % kThreads == 0, "panel / thread mismatch");
+  constexpr int kSlot = kXPer + kWPer;  // loads per thread per panel
+  static_assert(BM * kXPieces % kThreads == 0 && BN * kWPieces % kThreads == 0, "panel / thread mismatch");
   extern __shared__ u32x4 dyn[];
   uint8_t* const lds = reinterpret_cast<uint8_t*>(dyn);
 
@@ -1174,8 +1181,7 @@ __global__ __launch_bounds__(256, 2) void expert_mid_kernel(mxfp4moe::GemmArgs a
   const int row0 = __builtin_amdgcn_readfirstlane(tl.y);
   const int count = __builtin_amdgcn_readfirstlane(tl.z);
   const int kgroups = K >> 5;
-  const int nchunks = (kgroups + 3) >> 2;
-  const int npanels = (nchunks + kP - 1) / kP;
+  const int npanels = (kgroups + 3) >> 2;
   const int k16 = K >> 3;   // 16-byte pieces of a token row
   const int kg16 = K >> 5;  // 16-byte pieces (groups) of a weight row
   const int t = threadIdx.x;
@@ -1185,13 +1191,13 @@ __global__ __launch_bounds__(256, 2) void expert_mid_kernel(mxfp4moe::GemmArgs a
   const int lr = lane & 15;
 
   uint8_t* const xs = lds;
-  uint8_t* const ws = lds + 64 * kXRow;
+  uint8_t* const ws = lds + BM * kXRow;
   uint8_t* const sl = ws + BN * kWRow;
   const bool split = kGateUp && args.split_gate_up;  // uniform
   stage_scales<BN, kThreads>(sl, args.wscales, args.N, e, ntile, kNv ? 2 * kgroups : kgroups, t, split);
 
-  // load slots: token piece i = t + j*256 -> token i / kXPieces; weight piece
-  // i = t + j*256 -> row i / kWPieces (rows past N re-read row N-1)
+  // load slots: token piece i = t + j*256 -> token i / 16; weight piece
+  // i = t + j*256 -> row i / 4 (rows past N re-read row N-1)
   const u32x4* xsrc[kXPer];
   int xpiece[kXPer], xdst[kXPer];
 #pragma unroll
@@ -1215,23 +1221,25 @@ __global__ __launch_bounds__(256, 2) void expert_mid_kernel(mxfp4moe::GemmArgs a
     wpiece[j] = i - r * kWPieces;
     wdst[j] = r * kWRow + wpiece[j] * 16;
   }
-  // Two register slots hold the next two panels in flight.  Groups / pieces
-  // past the end re-read the last one (finite; the weights of a missing group
-  // are zeroed at use); panels past the last re-read the last panel.
-  u32x4 xv[2][kXPer], wv[2][kWPer];
-  auto issue = [&](int p, int sl2) {
+  // Three register slots of panel loads.  Groups / pieces past the end
+  // re-read the last one (finite; the weights of a missing group are zeroed
+  // at use); panels past the last re-read the last panel.
+  u32x4 xv[3][kXPer], wv[3][kWPer];
+  auto issue = [&](int p, int sl3) {
     p = min(p, npanels - 1);
 #pragma unroll
-    for (int j = 0; j < kWPer; ++j) wv[sl2][j] = wsrc[j][min(p * kWPieces + wpiece[j], kg16 - 1)];
+    for (int j = 0; j < kWPer; ++j) wv[sl3][j] = wsrc[j][min(p * kWPieces + wpiece[j], kg16 - 1)];
 #pragma unroll
-    for (int j = 0; j < kXPer; ++j) xv[sl2][j] = xsrc[j][min(p * kXPieces + xpiece[j], k16 - 1)];
+    for (int j = 0; j < kXPer; ++j) xv[sl3][j] = xsrc[j][min(p * kXPieces + xpiece[j], k16 - 1)];
   };
-  auto commit = [&](int sl2) {
+  // every token row is stored (rows past the tile's pairs hold its first
+  // pair's values, never read for an output): no branch between the loads
+  // and their uses
+  auto commit = [&](int sl3) {
 #pragma unroll
-    for (int j = 0; j < kWPer; ++j) *reinterpret_cast<u32x4*>(ws + wdst[j]) = wv[sl2][j];
+    for (int j = 0; j < kWPer; ++j) *reinterpret_cast<u32x4*>(ws + wdst[j]) = wv[sl3][j];
 #pragma unroll
-    for (int j = 0; j < kXPer; ++j)
-      if (t + j * kThreads < count * kXPieces) *reinterpret_cast<u32x4*>(xs + xdst[j]) = xv[sl2][j];
+    for (int j = 0; j < kXPer; ++j) *reinterpret_cast<u32x4*>(xs + xdst[j]) = xv[sl3][j];
   };
 
   const int n_wave = ntile * BN + wave * 32;
@@ -1243,87 +1251,94 @@ __global__ __launch_bounds__(256, 2) void expert_mid_kernel(mxfp4moe::GemmArgs a
     wrd[rb] = (wave * 32 + rb * 16 + lr) * kWRow + 16 * q;
   }
   const int ncb = (count + 15) >> 4;  // live 16-token column blocks
-  int xrd[4];  // LDS byte offset of this lane's token row for each column block
+  int xrd[kCB];  // LDS byte offset of this lane's token row for each column block
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb) {
+  for (int cb = 0; cb < kCB; ++cb) {
     const int m = cb * 16 + lr;
     xrd[cb] = (m < count ? m : 0) * kXRow + 64 * q;
   }
-  f32x4 acc[2][4];
+  f32x4 acc[2][kCB];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int cb = 0; cb < kCB; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  issue(0, 0);
-  issue(1, 1);
-  commit(0);
-  __syncthreads();  // panel 0 and the scale rows staged
-  issue(2, 0);
-  // iteration p: panel p is in LDS, slot (p+1)&1 holds panel p+1 and slot p&1
-  // panel p+2; after the MFMAs, panel p+1 goes to LDS and its slot is refilled
-  // with panel p+3.  Unrolled by two so the slots are static.
+  // the MFMAs of panel p from LDS
   auto compute = [&](int p) {
+    const int g0 = 4 * p + q;
+    const bool glive = g0 < kgroups;
+    const int g = glive ? g0 : kgroups - 1;
+    u32x4 a[2][4];  // [rb][step] converted A fragments
+    // both row blocks' weight fragments and scale bytes read together
+    u32x4 wr[2];
+    uint32_t sb[2][2];
 #pragma unroll
-    for (int jj = 0; jj < kP; ++jj) {
-      const int g0 = 4 * (p * kP + jj) + q;
-      const bool glive = g0 < kgroups;
-      const int g = glive ? g0 : kgroups - 1;
-      u32x4 a[2][4];  // [rb][step] converted A fragments
-      // both row blocks' weight fragments and scale bytes read together
-      u32x4 wr[2];
-      uint32_t sb[2][2];
+    for (int rb = 0; rb < 2; ++rb) {
+      wr[rb] = *reinterpret_cast<const u32x4*>(ws + wrd[rb]);
+      sb[rb][0] = kNv ? srow[rb][2 * g] : srow[rb][g];
+      sb[rb][1] = kNv ? srow[rb][2 * g + 1] : 0u;
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        wr[rb] = *reinterpret_cast<const u32x4*>(ws + wrd[rb] + jj * 64);
-        sb[rb][0] = kNv ? srow[rb][2 * g] : srow[rb][g];
-        sb[rb][1] = kNv ? srow[rb][2 * g + 1] : 0u;
-      }
-      __builtin_amdgcn_sched_barrier(0);
+    for (int rb = 0; rb < 2; ++rb) {
+      const GroupScale<kNv> sc(sb[rb][0], sb[rb][1]);
+      const u32x4 wj = glive ? wr[rb] : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        const GroupScale<kNv> sc(sb[rb][0], sb[rb][1]);
-        const u32x4 wj = glive ? wr[rb] : u32x4{0u, 0u, 0u, 0u};
+      for (int st = 0; st < 4; ++st) a[rb][st] = sc.convert(wj[st], st);
+    }
 #pragma unroll
-        for (int st = 0; st < 4; ++st) a[rb][st] = sc.convert(wj[st], st);
-      }
+    for (int cb = 0; cb < kCB; ++cb) {
+      if (cb < ncb) {  // wave-uniform: a column block past the tile's pairs is skipped
+        // the block's four token fragments read together, then its MFMAs
+        bf16x8 bb[4];
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        if (cb < ncb) {  // wave-uniform: column blocks past the tile's pairs are skipped
-          // the block's four token fragments read together, then its MFMAs
-          bf16x8 bb[4];
+        for (int st = 0; st < 4; ++st)
+          bb[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xs + xrd[cb] + 16 * st));
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int st = 0; st < 4; ++st)
-            bb[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xs + xrd[cb] + jj * 256 + 16 * st));
-          __builtin_amdgcn_sched_barrier(0);
+        for (int st = 0; st < 4; ++st) {
 #pragma unroll
-          for (int st = 0; st < 4; ++st) {
-            const bf16x8 b = bb[st];
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
-              acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mx::as_bf16x8(a[rb][st]), b, acc[rb][cb], 0, 0, 0);
-          }
+          for (int rb = 0; rb < 2; ++rb)
+            acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mx::as_bf16x8(a[rb][st]), bb[st], acc[rb][cb], 0, 0, 0);
         }
       }
     }
   };
-  for (int p = 0; p < npanels; p += 2) {
-    compute(p);
-    __syncthreads();  // every wave is done with panel p
-    if (p + 1 >= npanels) break;  // uniform
-    commit(1);
-    __syncthreads();  // panel p+1 staged
-    issue(p + 3, 1);
-    compute(p + 1);
+  // after the MFMAs of a panel: every wave is done with the LDS buffer, the
+  // next panel's slot `nx` is stored, refilled with panel `ahead`, and the
+  // stored panel made visible
+  auto advance = [&](int nx, int ahead) {
     __syncthreads();
-    if (p + 2 >= npanels) break;
-    commit(0);
-    __syncthreads();  // panel p+2 staged
-    issue(p + 4, 0);
+    commit(nx);
+    issue(ahead, nx);
+    __syncthreads();
+  };
+
+  issue(0, 0);
+  issue(1, 1);
+  issue(2, 2);
+  commit(0);
+  issue(3, 0);
+  __syncthreads();  // panel 0 and the scale rows staged; panels 1, 2, 3 in flight
+  int p = 0;
+  for (; p + 3 <= npanels; p += 3) {
+    compute(p);
+    advance(1, p + 4);
+    compute(p + 1);
+    advance(2, p + 5);
+    compute(p + 2);
+    advance(0, p + 6);
+  }
+  // the last one or two panels (slots 0 and 1 hold them, in order)
+  if (p < npanels) compute(p);
+  if (p + 1 < npanels) {
+    advance(1, p + 4);
+    compute(p + 1);
   }
 
   if (n_wave >= N) return;
   const uint16_t* bias = args.bias + (size_t)e * N;
+  const float s2 = kNv ? args.scale2[e] : 1.0f;  // second-level scale, before the bias
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
     const int n = n_wave + rb * 16 + 4 * q;  // first of this lane's four rows
@@ -1331,10 +1346,9 @@ __global__ __launch_bounds__(256, 2) void expert_mid_kernel(mxfp4moe::GemmArgs a
     const f32x4 bv = load_bias4(bias, n, N, split);
     const float b0 = bv[0], b1 = bv[1], b2 = bv[2], b3 = bv[3];
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
+    for (int cb = 0; cb < kCB; ++cb) {
       const int m = cb * 16 + lr;
       if (m >= count) continue;
-      const float s2 = kNv ? args.scale2[e] : 1.0f;  // second-level scale, before the bias
       const f32x4 v = f32x4{s2 * acc[rb][cb][0], s2 * acc[rb][cb][1], s2 * acc[rb][cb][2], s2 * acc[rb][cb][3]};
       if (kGateUp) {
         const int I = N >> 1;
@@ -1354,22 +1368,17 @@ __global__ __launch_bounds__(256, 2) void expert_mid_kernel(mxfp4moe::GemmArgs a
   }
 }
 
-#ifndef MX_MID_PANEL
-#define MX_MID_PANEL 1
-#endif
-
 template <bool kGateUp, bool kNv>
 hipError_t launch_mid(const mxfp4moe::GemmArgs& a, hipStream_t stream) {
-  constexpr int kP = MX_MID_PANEL;
   const long n_tiles = (a.N + 127) / 128;
   const long blocks = n_tiles * a.max_tiles;
   if (blocks == 0) return hipSuccess;
   const long grid = (blocks + kXcds - 1) / kXcds * kXcds;
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&expert_mid_kernel<kP, kGateUp, kNv>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, (int)mid_lds_bytes<kP, kNv>(mxfp4moe::kMaxHidden));
+  static const hipError_t attr =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&expert_mid_kernel<kGateUp, kNv>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)mid_lds_bytes<kNv>(mxfp4moe::kMaxHidden));
   if (attr != hipSuccess) return attr;
-  expert_mid_kernel<kP, kGateUp, kNv><<<(unsigned)grid, 256, mid_lds_bytes<kP, kNv>(a.K), stream>>>(a);
+  expert_mid_kernel<kGateUp, kNv><<<(unsigned)grid, 256, mid_lds_bytes<kNv>(a.K), stream>>>(a);
   return hipGetLastError();
 }
 
@@ -1407,8 +1416,8 @@ namespace mxfp4moe {
 // wide: blocks of 512 weight rows x 128 tokens; gate_up 4 waves of 128 x 128
 // (one per SIMD, operands read a chunk ahead), down 8 waves of 128 x 64 (two
 // per SIMD).
-// mid: 16x16x32 MFMA, 4 waves of 32 weight rows x (up to) 64 tokens, panels
-// of MX_MID_PANEL chunks of both operands staged in LDS.
+// mid: 16x16x32 MFMA, 4 waves of 32 weight rows x (up to) 48 tokens, panels
+// of one chunk of both operands staged in LDS, three panels in flight.
 // stream: 16x16x32 MFMA, 4 waves of 16*MX_STREAM_RN weight rows x (at most 4)
 // tokens, weights streamed in batches of MX_STREAM_BATCH chunks of 128 K.
 static_assert(kWideTokens == 128 && kStreamTokens == 4, "tile sizes");

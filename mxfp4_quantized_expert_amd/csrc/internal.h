@@ -43,15 +43,15 @@ int device_cu_count();
 
 // Token tiles of the expert GEMMs.  An expert with at least kWideTokens pairs
 // is cut into tiles of kWideTokens pairs, the last one partial (wide kernel);
-// one with more than kStreamTokens pairs into mid tiles of at most
-// kMidTokens pairs (mid kernel); one with at most kStreamTokens pairs makes a
-// single streaming tile (streaming kernel, which is also the whole path for
-// decode-sized batches).  Every expert's weights are streamed by one kernel.
-// With big_tokens == 0 every pair goes to the streaming kernel in tiles of
-// kStreamTokens.
+// one with more than kStreamTokens pairs into ceil(pairs / kMidTokens) mid
+// tiles of near-equal size (mid kernel); one with at most kStreamTokens pairs
+// makes a single streaming tile (streaming kernel, which is also the whole
+// path for decode-sized batches).  Every expert's weights are streamed by one
+// kernel.  With big_tokens == 0 every pair goes to the streaming kernel in
+// tiles of kStreamTokens.
 constexpr int kWideTokens = 128;
 constexpr int kStreamTokens = 4;
-constexpr int kMidTokens = 64;
+constexpr int kMidTokens = 48;
 constexpr int kMaxHidden = 4096;  // bound on H and I (the GEMMs stage scale rows in LDS)
 
 struct TileTables {

@@ -240,9 +240,9 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(const float* __res
       if (tables) {
         // an expert with at least bt pairs: all its pairs in tiles of bt (the
         // last one partial), so its weights are streamed by one kernel only;
-        // fewer than bt, more than st: mid tiles of at most mt pairs; at most
-        // st: one streaming tile; without full tiles (bt == 0) every pair in
-        // streaming tiles of st
+        // fewer than bt, more than st: ceil(c / mt) mid tiles of near-equal
+        // size (the first c % nm one pair larger); at most st: one streaming
+        // tile; without full tiles (bt == 0) every pair in streaming tiles of st
         const int nb = (wide_on && c >= bt) ? (c + bt - 1) / bt : 0;
         const int nm = (mid_on && c > st && (tt.no_wide || c < bt)) ? (c + mt - 1) / mt : 0;
         const int ns = mid_on ? (c > 0 && c <= st ? 1 : 0) : (c + st - 1) / st;
@@ -252,7 +252,10 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(const float* __res
         int4* big = reinterpret_cast<int4*>(tt.big) + tb + ib - nb;
         for (int i = 0; i < nb; ++i) big[i] = int4{e, start + i * bt, min(bt, c - i * bt), 0};
         int4* mid = reinterpret_cast<int4*>(tt.mid) + tm + im - nm;
-        for (int i = 0; i < nm; ++i) mid[i] = int4{e, start + i * mt, min(mt, c - i * mt), 0};
+        if (nm > 0) {
+          const int mq = c / nm, mr = c - mq * nm;
+          for (int i = 0; i < nm; ++i) mid[i] = int4{e, start + i * mq + min(i, mr), mq + (i < mr ? 1 : 0), 0};
+        }
         int4* small = reinterpret_cast<int4*>(tt.small) + ts + is - ns;
         for (int i = 0; i < ns; ++i) small[i] = int4{e, start + i * st, min(st, c - i * st), 0};
         tb += __builtin_amdgcn_readlane(ib, 63);

@@ -164,10 +164,11 @@ def test_bias_after_scale_identity(gpu):
 def test_tile_boundaries(gpu, path):
     # Expert loads on every side of the tile limits: 128 (one full wide tile),
     # 127 / 129 / 259 (mid tiles, wide tiles with a partial last one), 4 / 5
-    # (largest streaming tile, smallest mid tile), 16 / 17 / 32 / 33 (one or
-    # several 16-token column blocks of a mid tile), 64 / 65 (one or two mid
-    # tiles), 1 and 0.  k = 1 with one dominant logit per token forces them.
-    counts = [128, 127, 129, 4, 5, 16, 17, 32, 33, 64, 65, 1, 0, 259]
+    # (largest streaming tile, smallest mid tile), 16 / 17 / 32 / 33 (one to
+    # three 16-token column blocks of a mid tile), 48 / 49 / 96 / 97 (one,
+    # two or three mid tiles of at most 48), 64 / 65, 1 and 0.  k = 1 with one
+    # dominant logit per token forces them.
+    counts = [128, 127, 129, 4, 5, 16, 17, 32, 33, 48, 49, 64, 65, 96, 97, 1, 0, 259]
     E = len(counts)
     T = sum(counts)
     spec = W.LAYERS["tiny"].with_(T=T, H=64, I=96, E=E, top_k=1)

@@ -76,8 +76,8 @@ def _owned_layer(counts, H, I, seed):
 
 def test_tile_boundaries(gpu):
     # experts on both sides of the 128-pair full-tile threshold, the 4-pair
-    # streaming limit and the 64-pair mid-tile size
-    counts = [128, 127, 129, 4, 5, 16, 17, 32, 33, 64, 65, 1, 0, 259, 256]
+    # streaming limit and the 48-pair mid-tile size
+    counts = [128, 127, 129, 4, 5, 16, 17, 32, 33, 48, 49, 64, 65, 96, 97, 1, 0, 259, 256]
     L = _owned_layer(counts, H=128, I=192, seed=51)
     assert_layer_parity(_forward(gpu, L, 1), O.moe_forward_nvfp4(L, 1), "nvfp4 tile boundaries")
 
