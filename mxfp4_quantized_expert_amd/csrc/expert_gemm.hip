@@ -1167,7 +1167,6 @@ __global__ __launch_bounds__(256, 2) void expert_mid_kernel(mxfp4moe::GemmArgs a
   constexpr int kWPieces = 4;         // 16-byte pieces per weight row of a panel
   constexpr int kXPer = BM * kXPieces / kThreads;
   constexpr int kWPer = BN * kWPieces / kThreads;
-  constexpr int kSlot = kXPer + kWPer;  // loads per thread per panel
   static_assert(BM * kXPieces % kThreads == 0 && BN * kWPieces % kThreads == 0, "panel / thread mismatch");
   extern __shared__ u32x4 dyn[];
   uint8_t* const lds = reinterpret_cast<uint8_t*>(dyn);
