@@ -38,21 +38,25 @@ __device__ __forceinline__ int w13_row(int r, int N, bool split) {
 __device__ __forceinline__ int staged_row(int rl, int nv, bool split) {
   return split ? ((rl & 1) ? (nv >> 1) + (rl >> 1) : (rl >> 1)) : rl;
 }
-// Biases of logical rows n..n+3 (n a multiple of 4, below N).
-__device__ __forceinline__ f32x4 load_bias4(const uint16_t* bias, int n, int N, bool split) {
-  uint32_t lo, hi;
-  if (split) {  // gate n/2, up n/2, gate n/2+1, up n/2+1
-    const uint32_t g = *reinterpret_cast<const uint32_t*>(bias + (n >> 1));
-    const uint32_t u = *reinterpret_cast<const uint32_t*>(bias + (N >> 1) + (n >> 1));
-    lo = (g & 0xffffu) | (u << 16);
-    hi = (g >> 16) | (u & 0xffff0000u);
-  } else {
-    const uint2 b = *reinterpret_cast<const uint2*>(bias + n);
-    lo = b.x;
-    hi = b.y;
-  }
+// The two dwords of bf16 biases that hold logical rows n..n+3 (n a multiple
+// of 4, below N), as loaded: interleaved rows n, n+1 | n+2, n+3; split: gate
+// n/2, n/2+1 | up n/2, n/2+1.  Branch-free (the same two loads either way),
+// so a caller can issue many of them before the first use.
+__device__ __forceinline__ uint2 load_bias4_raw(const uint16_t* bias, int n, int N, bool split) {
+  const int a0 = split ? (n >> 1) : n;
+  const int a1 = split ? (N >> 1) + (n >> 1) : n + 2;
+  return uint2{*reinterpret_cast<const uint32_t*>(bias + a0), *reinterpret_cast<const uint32_t*>(bias + a1)};
+}
+// ... and the four biases of rows n..n+3 in order.
+__device__ __forceinline__ f32x4 bias4_of(uint2 d, bool split) {
+  const uint32_t lo = split ? (d.x & 0xffffu) | (d.y << 16) : d.x;
+  const uint32_t hi = split ? (d.x >> 16) | (d.y & 0xffff0000u) : d.y;
   return f32x4{mx::bf16_to_f32(lo & 0xffffu), mx::bf16_to_f32(lo >> 16), mx::bf16_to_f32(hi & 0xffffu),
                mx::bf16_to_f32(hi >> 16)};
+}
+// Biases of logical rows n..n+3 (n a multiple of 4, below N).
+__device__ __forceinline__ f32x4 load_bias4(const uint16_t* bias, int n, int N, bool split) {
+  return bias4_of(load_bias4_raw(bias, n, N, split), split);
 }
 
 // Scale operands of the 32 codes a lane converts at once (one 16-byte piece).

@@ -33,7 +33,9 @@
 namespace {
 
 using mxgemm::GroupScale;
+using mxgemm::bias4_of;
 using mxgemm::load_bias4;
+using mxgemm::load_bias4_raw;
 using mxgemm::load_lds16;
 using mxgemm::load_lds4;
 using mxgemm::pack_bf16x4;
@@ -187,14 +189,25 @@ __device__ __forceinline__ void store_epilogue(const mxfp4moe::GemmArgs& args, c
   const float s2 = kNv ? args.scale2[e] : 1.0f;
   auto sum = [&](int rb, int cb, int r) { return kNv ? s2 * acc[rb][cb][r] : acc[rb][cb][r]; };
   auto chunk_addr = [](int m, int chunk) { return m * 128 + ((chunk ^ (m & 7)) << 4); };
+  const bool split = kGateUp && args.split_gate_up != 0;
+  // Every global value the epilogue reads (this lane's biases, and for down
+  // its pairs' routing weights and pair ids) is loaded in one batch before
+  // the first use: loaded where used, each would be a round trip of its own.
+  uint2 braw[RN][4];
+#pragma unroll
+  for (int rb = 0; rb < RN; ++rb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int n = n_wave + rb * 32 + 8 * i + 4 * half;
+      braw[rb][i] = load_bias4_raw(bias, n < N ? n : N - 4, N, split);
+    }
   if (kGateUp) {
     // stage a[m][q_local], q_local = 0..16*RN-1 for this wave's 32*RN rows of w13
 #pragma unroll
     for (int rb = 0; rb < RN; ++rb) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        int n = n_wave + rb * 32 + 8 * i + 4 * half;
-        const f32x4 bv = load_bias4(bias, n < N ? n : N - 4, N, args.split_gate_up != 0);
+        const f32x4 bv = bias4_of(braw[rb][i], split);
         const float b0 = bv[0], b1 = bv[1], b2 = bv[2], b3 = bv[3];
         const int byte = rb * 32 + 8 * i + 4 * half;  // 2 * q_local
 #pragma unroll
@@ -220,19 +233,29 @@ __device__ __forceinline__ void store_epilogue(const mxfp4moe::GemmArgs& args, c
       }
     }
   } else {
+    // token m = cb*32 + lrow of each column block: its routing weight (0 past
+    // the tile's pairs); store pass j: the pair of token (j*64 + lane) / 8
+    constexpr int kStores = RM * 32 * 8 / 64;
+    const int last = count - 1;
+    int spw[RM], pid[kStores];
+#pragma unroll
+    for (int cb = 0; cb < RM; ++cb) spw[cb] = args.sorted_pairs[row0 + min(cb * 32 + lrow, last)];
+#pragma unroll
+    for (int j = 0; j < kStores; ++j) pid[j] = args.sorted_pairs[row0 + min((j * 64 + lane) >> 3, last)];
+    float wt[RM];
+#pragma unroll
+    for (int cb = 0; cb < RM; ++cb) wt[cb] = cb * 32 + lrow < count ? args.topk_weights[spw[cb]] : 0.f;
 #pragma unroll
     for (int rb = 0; rb < RN; ++rb) {
       // stage zw[m][32 features of block rb]
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        int n = n_wave + rb * 32 + 8 * i + 4 * half;
-        const uint2 bb = *reinterpret_cast<const uint2*>(bias + (n < N ? n : N - 4));
-        const float b0 = mx::bf16_to_f32(bb.x & 0xffffu), b1 = mx::bf16_to_f32(bb.x >> 16);
-        const float b2 = mx::bf16_to_f32(bb.y & 0xffffu), b3 = mx::bf16_to_f32(bb.y >> 16);
+        const f32x4 bv = bias4_of(braw[rb][i], false);
+        const float b0 = bv[0], b1 = bv[1], b2 = bv[2], b3 = bv[3];
 #pragma unroll
         for (int cb = 0; cb < RM; ++cb) {
           const int m = cb * 32 + lrow;
-          const float w = m < count ? args.topk_weights[args.sorted_pairs[row0 + m]] : 0.f;
+          const float w = wt[cb];
           f32x4 v;
           v[0] = w * (sum(rb, cb, 4 * i + 0) + b0);
           v[1] = w * (sum(rb, cb, 4 * i + 1) + b1);
@@ -241,15 +264,14 @@ __device__ __forceinline__ void store_epilogue(const mxfp4moe::GemmArgs& args, c
           *reinterpret_cast<f32x4*>(region + chunk_addr(m, 2 * i + half)) = v;
         }
       }
-#pragma unroll 4
-      for (int j = 0; j < RM * 32 * 8 / 64; ++j) {
+#pragma unroll
+      for (int j = 0; j < kStores; ++j) {
         const int idx = j * 64 + lane;
         const int m = idx >> 3, chunk = idx & 7;
         const int n = n_wave + rb * 32 + chunk * 4;
         if (m < count && n < N) {
           const f32x4 v = *reinterpret_cast<const f32x4*>(region + chunk_addr(m, chunk));
-          const int p = args.sorted_pairs[row0 + m];
-          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(args.out) + (size_t)p * N + n) = pack_bf16x4(v);
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(args.out) + (size_t)pid[j] * N + n) = pack_bf16x4(v);
         }
       }
     }
