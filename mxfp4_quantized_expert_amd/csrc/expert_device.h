@@ -15,14 +15,17 @@ using mx::u32x4;
 
 __device__ __forceinline__ float swiglu_clamped(float gate, float up) {
   // gpt-oss family constants: alpha 1.702, limit 7; gate clamped from above,
-  // up clamped on both sides, +1 after the clamp.  The clamps are selects, not
-  // fminf/fmaxf, so that a NaN input (a weight group with scale byte 0xFF)
-  // stays NaN instead of becoming the limit.
-  const float g = gate > 7.0f ? 7.0f : gate;
-  const float u = up > 7.0f ? 7.0f : (up < -7.0f ? -7.0f : up);
-  // sigmoid through the hardware reciprocal (about 1 ulp; the result is
-  // rounded to bf16)
-  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-1.702f * g)) * (u + 1.0f);
+  // up clamped on both sides, +1 after the clamp.  The clamps are IEEE 754-2019
+  // minimum / maximum (gfx950's v_minimum3_f32 / v_maximum3_f32), which keep a
+  // NaN input (a weight group with a NaN scale) NaN instead of turning it into
+  // the limit, and equal the plain clamp for every other input (+-inf
+  // included): one instruction each instead of a compare and a select.
+  const float g = __builtin_elementwise_minimum(gate, 7.0f);
+  const float u = __builtin_elementwise_maximum(__builtin_elementwise_minimum(up, 7.0f), -7.0f);
+  // sigmoid(alpha g) = 1 / (1 + 2^(-alpha log2(e) g)) through the hardware
+  // exp2 and reciprocal (about 1 ulp each; the result is rounded to bf16)
+  constexpr float kNegAlphaLog2e = -1.702f * 1.4426950408889634f;
+  return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(kNegAlphaLog2e * g)) * (u + 1.0f);
 }
 
 // gate/up row layout of w13.  Logical row 2i is gate i and 2i+1 is up i (the
