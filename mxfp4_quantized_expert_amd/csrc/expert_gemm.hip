@@ -69,8 +69,7 @@ __device__ __forceinline__ int slot_col(int row, int part) {
 constexpr int kXcds = 8;
 constexpr int kGroup = 4;
 
-__device__ __forceinline__ bool map_block(int num_tiles, int n_tiles, int& tile, int& ntile) {
-  const int b = blockIdx.x;
+__device__ __forceinline__ bool map_job(int b, int num_tiles, int n_tiles, int& tile, int& ntile) {
   const int total = num_tiles * n_tiles;
   const int per = (total + kXcds - 1) / kXcds;
   const int local = b / kXcds;
@@ -84,6 +83,9 @@ __device__ __forceinline__ bool map_block(int num_tiles, int n_tiles, int& tile,
   tile = g * kGroup + rem % gm;
   ntile = rem / gm;
   return true;
+}
+__device__ __forceinline__ bool map_block(int num_tiles, int n_tiles, int& tile, int& ntile) {
+  return map_job(blockIdx.x, num_tiles, n_tiles, tile, ntile);
 }
 
 // One 64-wide K chunk of MFMA work for a wave from operands in registers:
@@ -333,12 +335,14 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void expert_wide_kernel(mxfp4moe::
 
   const int N = args.N, K = args.K;
   const int n_tiles = (N + BN - 1) / BN;
+  const int num_tiles = *args.num_tiles;
+  // this block's jobs: virtual block ids blockIdx.x + j * gridDim.x (gridDim.x
+  // a multiple of 8, so every one is on this block's XCD), in the order the
+  // dispatcher would hand them out
+  int vb = blockIdx.x;
   int tile, ntile;
-  if (!map_block(*args.num_tiles, n_tiles, tile, ntile)) return;  // uniform per block
-  const int4 tl = reinterpret_cast<const int4*>(args.tiles)[tile];
-  const int e = __builtin_amdgcn_readfirstlane(tl.x);
-  const int row0 = __builtin_amdgcn_readfirstlane(tl.y);
-  const int count = __builtin_amdgcn_readfirstlane(tl.z);
+  if (!map_job(vb, num_tiles, n_tiles, tile, ntile)) return;  // uniform per block
+  int e, row0, count;
   const int kgroups = K >> 5;
   const int nchunks = (kgroups + 1) >> 1;
   const int t = threadIdx.x;
@@ -349,59 +353,67 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void expert_wide_kernel(mxfp4moe::
   const int lrow = lane & 31;
 
   const bool split = kGateUp && args.split_gate_up;  // uniform
-  if (!kNv) stage_scales<BN, kThreads, true>(sst, args.wscales, args.N, e, ntile, kgroups, t, split);
-
-  // token slot p = t + i*threads -> row p/8, logical column slot_col(row, p%8);
-  // rows past `count` re-read the tile's first row (their columns are never stored)
-  const uint16_t* xsrc[kXPer];
-  int xcol[kXPer];
-#pragma unroll
-  for (int i = 0; i < kXPer; ++i) {
-    const int p = t + i * kThreads;
-    const int r = p >> 3;
-    const int part = slot_col(r, p & 7);
-    const int rr = r < count ? r : 0;
-    const size_t src_row = kGateUp ? (size_t)(args.sorted_pairs[row0 + rr] / args.top_k) : (size_t)(row0 + rr);
-    xsrc[i] = args.act + src_row * (size_t)K + part * 8;
-    xcol[i] = part * 8;
-  }
-  // weight slot q = t + j*threads: row q/2 of the block, group 2c + (q&1) of chunk c
-  const uint8_t* wsrc[kWPer];
-#pragma unroll
-  for (int j = 0; j < kWPer; ++j) {
-    int wr = ntile * BN + ((t + j * kThreads) >> 1);
-    wr = w13_row(wr < N ? wr : N - 1, N, split);
-    wsrc[j] = args.wblocks + ((size_t)e * N + wr) * (size_t)(K >> 1);
-  }
-  // NVFP4 scale slot j: the dword of row t + j*threads (rows past N re-read row N-1)
-  const uint8_t* ssrc[kSPer > 0 ? kSPer : 1];
-#pragma unroll
-  for (int j = 0; j < kSPer; ++j) {
-    int wr = ntile * BN + t + j * kThreads;
-    wr = w13_row(wr < N ? wr : N - 1, N, split);
-    ssrc[j] = args.wscales + ((size_t)e * N + wr) * (size_t)(K >> 4);
-  }
   const int wh = t & 1;
   // the fast form's buffer resources and per-thread byte offsets (the same
-  // rows as the pointers above); raw buffers, no swizzle, range-checked
-  // against their byte counts
+  // rows as the pointers); raw buffers, no swizzle, range-checked against
+  // their byte counts (built in the general form too, where nothing uses them)
   constexpr int kRawBuffer = 0x00020000;  // descriptor word 3: 32-bit data format, for untyped loads
-  // (built in the general form too, where nothing uses them)
   const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(args.act), (short)0, (int)(args.act_rows * K * 2), kRawBuffer);
-  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(args.wblocks + (size_t)e * N * (K >> 1)), (short)0, N * (K >> 1), kRawBuffer);
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(args.wscales + (size_t)e * N * (K >> 4)), (short)0, N * (K >> 4), kRawBuffer);
+  __amdgpu_buffer_rsrc_t rw, rs;
+  const uint16_t* xsrc[kXPer];
+  int xcol[kXPer];
+  const uint8_t* wsrc[kWPer];
+  const uint8_t* ssrc[kSPer > 0 ? kSPer : 1];
   int xoff[kXPer], woff[kWPer], soff[kSPer > 0 ? kSPer : 1];
-  if (!kTail) {
+  // one job's operand addresses: the fast form keeps 32-bit offsets only, the
+  // general form 64-bit pointers (and the column of each token slot)
+  auto setup = [&]() {
+    const int4 tl = reinterpret_cast<const int4*>(args.tiles)[tile];
+    e = __builtin_amdgcn_readfirstlane(tl.x);
+    row0 = __builtin_amdgcn_readfirstlane(tl.y);
+    count = __builtin_amdgcn_readfirstlane(tl.z);
+    // token slot p = t + i*threads -> row p/8, logical column slot_col(row, p%8);
+    // rows past `count` re-read the tile's first row (their columns are never stored)
 #pragma unroll
-    for (int i = 0; i < kXPer; ++i) xoff[i] = (int)((xsrc[i] - args.act) * 2);
+    for (int i = 0; i < kXPer; ++i) {
+      const int p = t + i * kThreads;
+      const int r = p >> 3;
+      const int part = slot_col(r, p & 7);
+      const int rr = r < count ? r : 0;
+      const int src_row = kGateUp ? args.sorted_pairs[row0 + rr] / args.top_k : row0 + rr;
+      if constexpr (kTail) {
+        xsrc[i] = args.act + (size_t)src_row * (size_t)K + part * 8;
+        xcol[i] = part * 8;
+      } else {
+        xoff[i] = (src_row * K + part * 8) * 2;
+      }
+    }
+    // weight slot q = t + j*threads: row q/2 of the block, group 2c + (q&1) of chunk c
 #pragma unroll
-    for (int j = 0; j < kWPer; ++j) woff[j] = (int)(wsrc[j] - (args.wblocks + (size_t)e * N * (K >> 1))) + 16 * wh;
+    for (int j = 0; j < kWPer; ++j) {
+      int wr = ntile * BN + ((t + j * kThreads) >> 1);
+      wr = w13_row(wr < N ? wr : N - 1, N, split);
+      if constexpr (kTail) wsrc[j] = args.wblocks + ((size_t)e * N + wr) * (size_t)(K >> 1);
+      else woff[j] = wr * (K >> 1) + 16 * wh;
+    }
+    // NVFP4 scale slot j: the dword of row t + j*threads (rows past N re-read row N-1)
 #pragma unroll
-    for (int j = 0; j < kSPer; ++j) soff[j] = (int)(ssrc[j] - (args.wscales + (size_t)e * N * (K >> 4)));
-  }
+    for (int j = 0; j < kSPer; ++j) {
+      int wr = ntile * BN + t + j * kThreads;
+      wr = w13_row(wr < N ? wr : N - 1, N, split);
+      if constexpr (kTail) ssrc[j] = args.wscales + ((size_t)e * N + wr) * (size_t)(K >> 4);
+      else soff[j] = wr * (K >> 4);
+    }
+    if constexpr (!kTail) {
+      rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(args.wblocks + (size_t)e * N * (K >> 1)), (short)0,
+                                             N * (K >> 1), kRawBuffer);
+      if (kNv)
+        rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(args.wscales + (size_t)e * N * (K >> 4)),
+                                               (short)0, N * (K >> 4), kRawBuffer);
+    }
+  };
+  setup();
   auto buf_lds = [](__amdgpu_buffer_rsrc_t r, void* lds, int bytes, int voff, int soffs) {
     if (bytes == 16)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soffs, 0, 0);
@@ -440,21 +452,30 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void expert_wide_kernel(mxfp4moe::
   };
 
   const int wslot0 = (wn * RN * 32 + lrow) * 2 + half;
-  const uint8_t* srow = sst + staged_row(wn * RN * 32 + lrow, min(BN, N - ntile * BN), split) * kgroups;
+  const uint8_t* srow;
   // NVFP4: byte offset of this lane's two scale bytes (group 2c + half) in a stage's scale dwords
   const int nvs0 = (wn * RN * 32 + lrow) * 4 + 2 * half;
-  const int n_wave = ntile * BN + wn * RN * 32;
+  int n_wave;
   const int m_wave = wm * RM * 32;
-  const bool live = WM == 1 || m_wave < count;  // wave-uniform; a tile holds at least one pair
+  bool live;
+  auto setup_rows = [&]() {
+    srow = sst + staged_row(wn * RN * 32 + lrow, min(BN, N - ntile * BN), split) * kgroups;
+    n_wave = ntile * BN + wn * RN * 32;
+    live = WM == 1 || m_wave < count;  // wave-uniform; a tile holds at least one pair
+  };
+  setup_rows();
   const int rb_stride = (split ? 16 : 32) * kgroups;
 
   f32x16 acc[RN][RM];
+  auto clear_acc = [&]() {
 #pragma unroll
-  for (int rb = 0; rb < RN; ++rb)
+    for (int rb = 0; rb < RN; ++rb)
 #pragma unroll
-    for (int cb = 0; cb < RM; ++cb)
+      for (int cb = 0; cb < RM; ++cb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[rb][cb][r] = 0.f;
+        for (int r = 0; r < 16; ++r) acc[rb][cb][r] = 0.f;
+  };
+  clear_acc();
 
   // the operands of one chunk in registers, as read (nothing computed from
   // them until the chunk runs, a chunk later)
@@ -568,73 +589,105 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void expert_wide_kernel(mxfp4moe::
       issue(c + kStages, st);
     }
   };
-  if constexpr (kAhead) {
-    Ops ops0, ops1;
-  #pragma unroll
-    for (int c = 0; c < kStages; ++c) issue(c, c);
-    wait_loads_then_barrier<(kStages - 1) * kLoads>();  // chunk 0 (and the scale table) landed
-    if (live) read_ops(ops0, 0, 0);
-    // trips of 2*kStages chunks: the register set and the stage of every step
-    // are constants; then the remaining steps one by one
-    constexpr int kTrip = 2 * kStages;
-    const int nfull = nchunks / kTrip * kTrip;
-    for (int c0 = 0; c0 < nfull; c0 += kTrip) {
-  #pragma unroll
-      for (int u = 0; u < kTrip; u += 2) {
-        step(c0 + u, u % kStages, ops0, ops1);
-        step(c0 + u + 1, (u + 1) % kStages, ops1, ops0);
-      }
-    }
-  #pragma unroll
-    for (int u = 0; u < kTrip - 1; u += 2) {
-      if (nfull + u < nchunks) step(nfull + u, u % kStages, ops0, ops1);
-      if (nfull + u + 1 < nchunks) step(nfull + u + 1, (u + 1) % kStages, ops1, ops0);
-    }
-  } else {
-    // one operand set: chunk c is read after the barrier that makes it
-    // visible (the other wave on the SIMD covers the wait), chunk c+2 goes
-    // to the stage of chunk c-1, its loads spread between the MFMAs
-    auto step1 = [&](int c, int st) {
-      wait_loads_then_barrier<kLoads>();  // chunk c landed; chunk c+1 may be in flight
-      Ops cur;
-      if (live) {
+  // Chunk c sits in LDS stage (c + 2) % 3, so that chunk 0 of the next job
+  // goes to stage 2: the epilogue's regions use only stages 0 and 1 (and the
+  // scale table is no longer read then), so the next job's scale table and
+  // first chunk load while this job's epilogue runs; its other chunks follow
+  // once the epilogue is done with stages 0 and 1.
+  constexpr int kNext = 2;  // stage of chunk 0
+  constexpr bool kPersist = !kTail && !kGateUp;  // this block walks several jobs
+  static_assert(WN * WM * RM * 32 * 128 <= kNext * kStage * 16, "the epilogue regions stay below stage 2");
+  if (!kNv) stage_scales<BN, kThreads, true>(sst, args.wscales, args.N, e, ntile, kgroups, t, split);
+  issue(0, kNext);
+  auto issue_rest = [&]() {  // chunks 1 .. (loads in flight at the first step) of the job
+    issue(1, (1 + kNext) % kStages);
+    if (kAhead) issue(2, (2 + kNext) % kStages);
+  };
+  issue_rest();
+  while (true) {
+    if constexpr (kAhead) {
+      Ops ops0, ops1;
+      wait_loads_then_barrier<(kStages - 1) * kLoads>();  // chunk 0 (and the scale table) landed
+      if (live) read_ops(ops0, 0, kNext);
+      // trips of 2*kStages chunks: the register set and the stage of every step
+      // are constants; then the remaining steps one by one
+      constexpr int kTrip = 2 * kStages;
+      const int nfull = nchunks / kTrip * kTrip;
+      for (int c0 = 0; c0 < nfull; c0 += kTrip) {
 #pragma unroll
-        for (int j = 0; j < kReads; ++j) read_one(cur, c, st, j);
-        constexpr int kMfma = 4 * RN * RM;
-        constexpr int kEvery = kMfma / kLoads >= 2 ? 2 : 1;
-        static_assert(kEvery * kLoads <= kMfma, "room between the MFMAs");
-        auto extra = [&](int k) {
-          if (k % kEvery != 0 || k / kEvery >= kLoads) return;
-          issue_one(c + 2, (st + 2) % kStages, k / kEvery);
-          __builtin_amdgcn_sched_barrier(0);
-        };
-        const bool glive = !kTail || 2 * c + half < kgroups;
-        u32x4 w[RN];
-        float sc[RN], sc_hi[RN];
-  #pragma unroll
-        for (int rb = 0; rb < RN; ++rb) {
-          w[rb] = glive ? cur.w[rb] : u32x4{0u, 0u, 0u, 0u};
-          scales_of(cur.sb[rb], sc[rb], sc_hi[rb]);
+        for (int u = 0; u < kTrip; u += 2) {
+          step(c0 + u, (u + kNext) % kStages, ops0, ops1);
+          step(c0 + u + 1, (u + 1 + kNext) % kStages, ops1, ops0);
         }
-        chunk_mma_regs<RN, RM, kNv>(acc, cur.b, w, sc, sc_hi, extra);
-      } else {
-        issue(c + 2, (st + 2) % kStages);
       }
-    };
-    issue(0, 0);
-    issue(1, 1);
-    const int nfull = nchunks / kStages * kStages;
-    for (int c0 = 0; c0 < nfull; c0 += kStages) {
 #pragma unroll
-      for (int u = 0; u < kStages; ++u) step1(c0 + u, u);
+      for (int u = 0; u < kTrip - 1; u += 2) {
+        if (nfull + u < nchunks) step(nfull + u, (u + kNext) % kStages, ops0, ops1);
+        if (nfull + u + 1 < nchunks) step(nfull + u + 1, (u + 1 + kNext) % kStages, ops1, ops0);
+      }
+    } else {
+      // one operand set: chunk c is read after the barrier that makes it
+      // visible (the other wave on the SIMD covers the wait), chunk c+2 goes
+      // to the stage of chunk c-1, its loads spread between the MFMAs
+      auto step1 = [&](int c, int st) {
+        wait_loads_then_barrier<kLoads>();  // chunk c landed; chunk c+1 may be in flight
+        Ops cur;
+        if (live) {
+#pragma unroll
+          for (int j = 0; j < kReads; ++j) read_one(cur, c, st, j);
+          constexpr int kMfma = 4 * RN * RM;
+          constexpr int kEvery = kMfma / kLoads >= 2 ? 2 : 1;
+          static_assert(kEvery * kLoads <= kMfma, "room between the MFMAs");
+          auto extra = [&](int k) {
+            if (k % kEvery != 0 || k / kEvery >= kLoads) return;
+            issue_one(c + 2, (st + 2) % kStages, k / kEvery);
+            __builtin_amdgcn_sched_barrier(0);
+          };
+          const bool glive = !kTail || 2 * c + half < kgroups;
+          u32x4 w[RN];
+          float sc[RN], sc_hi[RN];
+#pragma unroll
+          for (int rb = 0; rb < RN; ++rb) {
+            w[rb] = glive ? cur.w[rb] : u32x4{0u, 0u, 0u, 0u};
+            scales_of(cur.sb[rb], sc[rb], sc_hi[rb]);
+          }
+          chunk_mma_regs<RN, RM, kNv>(acc, cur.b, w, sc, sc_hi, extra);
+        } else {
+          issue(c + 2, (st + 2) % kStages);
+        }
+      };
+      const int nfull = nchunks / kStages * kStages;
+      for (int c0 = 0; c0 < nfull; c0 += kStages) {
+#pragma unroll
+        for (int u = 0; u < kStages; ++u) step1(c0 + u, (u + kNext) % kStages);
+      }
+      if (nfull < nchunks) step1(nfull, kNext % kStages);
+      if (nfull + 1 < nchunks) step1(nfull + 1, (1 + kNext) % kStages);
     }
-    if (nfull < nchunks) step1(nfull, 0);
-    if (nfull + 1 < nchunks) step1(nfull + 1, 1);
+    // the chunks issued past the end land before the arena is reused
+    wait_loads_then_barrier<0>();
+    // this job's epilogue values; the next job (if any) is set up and its
+    // scale table and first chunk requested before the epilogue runs
+    const int e_j = e, row0_j = row0, count_j = count, n_wave_j = n_wave;
+    const bool live_j = live;
+    vb += gridDim.x;
+    // (gate_up and the general form take one job per block: their next job's
+    // state does not fit beside the epilogue's registers)
+    const bool more = kPersist && map_job(vb, num_tiles, n_tiles, tile, ntile);
+    if (more) {
+      setup();
+      setup_rows();
+      if (!kNv) stage_scales<BN, kThreads, true>(sst, args.wscales, args.N, e, ntile, kgroups, t, split);
+      issue(0, kNext);
+    }
+    uint8_t* region = reinterpret_cast<uint8_t*>(arena) + wave * (RM * 32 * 128);
+    if (live_j)
+      store_epilogue<RN, RM, kGateUp, kNv>(args, acc, e_j, row0_j + m_wave, count_j - m_wave, n_wave_j, lane, region);
+    if (!more) break;
+    __syncthreads();  // every wave is done with the epilogue regions (stages 0 and 1)
+    issue_rest();
+    clear_acc();
   }
-  // the chunks issued past the end land before the arena is reused
-  wait_loads_then_barrier<0>();
-  uint8_t* region = reinterpret_cast<uint8_t*>(arena) + wave * (RM * 32 * 128);
-  if (live) store_epilogue<RN, RM, kGateUp, kNv>(args, acc, e, row0 + m_wave, count - m_wave, n_wave, lane, region);
 }
 
 template <int WN, int WM, int RN, int RM, bool kGateUp, bool kAhead = true, bool kNv = false>
@@ -647,7 +700,12 @@ hipError_t launch_wide(const mxfp4moe::GemmArgs& a, hipStream_t stream) {
   // the fast form: whole 64-wide chunks and 32-bit buffer offsets
   const bool fast = (a.K & 63) == 0 && a.act_rows * a.K * 2 < ((int64_t)1 << 31) &&
                     (int64_t)a.N * (a.K >> 1) < ((int64_t)1 << 31);
-  const long grid = (blocks + kXcds - 1) / kXcds * kXcds;
+  // one block per job; the down GEMM's fast form instead runs one block per
+  // CU (a multiple of the XCD count), each walking its jobs, so that a job's
+  // first loads fly during the previous job's epilogue
+  long grid = (blocks + kXcds - 1) / kXcds * kXcds;
+  const long cus = (long)mxfp4moe::device_cu_count() / kXcds * kXcds;
+  if (fast && !kGateUp && cus >= kXcds && grid > cus) grid = cus;
   if (fast)
     expert_wide_kernel<WN, WM, RN, RM, kGateUp, kAhead, kNv><<<(unsigned)grid, WN * WM * 64, 0, stream>>>(a);
   else
