@@ -349,8 +349,6 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void expert_wide_kernel(mxfp4moe::
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wn = wave % WN, wm = wave / WN;
   const int lane = t & 63;
-  const int half = lane >> 5;
-  const int lrow = lane & 31;
 
   const bool split = kGateUp && args.split_gate_up;  // uniform
   const int wh = t & 1;
@@ -369,6 +367,11 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void expert_wide_kernel(mxfp4moe::
   // one job's operand addresses: the fast form keeps 32-bit offsets only, the
   // general form 64-bit pointers (and the column of each token slot)
   auto setup = [&]() {
+    // the thread index through an opaque copy: what is derived from it is
+    // recomputed per job instead of hoisted out of the job loop and held in
+    // registers through the K loop and the epilogue
+    int t = threadIdx.x;
+    asm volatile("" : "+v"(t));
     const int4 tl = reinterpret_cast<const int4*>(args.tiles)[tile];
     e = __builtin_amdgcn_readfirstlane(tl.x);
     row0 = __builtin_amdgcn_readfirstlane(tl.y);
@@ -451,19 +454,26 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void expert_wide_kernel(mxfp4moe::
     for (int j = 0; j < kSPer; ++j) load_lds4(ssrc[j] + 4 * c, ss + j * kThreads);
   };
 
-  const int wslot0 = (wn * RN * 32 + lrow) * 2 + half;
+  // a job's lane quantities and LDS read positions, derived at the top of
+  // every job from an opaque copy of the lane (as in setup()), so that they are
+  // not held through the epilogue
+  int half, lrow, wslot0, nvs0;
   const uint8_t* srow;
-  // NVFP4: byte offset of this lane's two scale bytes (group 2c + half) in a stage's scale dwords
-  const int nvs0 = (wn * RN * 32 + lrow) * 4 + 2 * half;
   int n_wave;
   const int m_wave = wm * RM * 32;
   bool live;
   auto setup_rows = [&]() {
+    int l = lane;
+    asm volatile("" : "+v"(l));
+    half = l >> 5;
+    lrow = l & 31;
+    wslot0 = (wn * RN * 32 + lrow) * 2 + half;
+    // NVFP4: byte offset of this lane's two scale bytes (group 2c + half) in a stage's scale dwords
+    nvs0 = (wn * RN * 32 + lrow) * 4 + 2 * half;
     srow = sst + staged_row(wn * RN * 32 + lrow, min(BN, N - ntile * BN), split) * kgroups;
     n_wave = ntile * BN + wn * RN * 32;
     live = WM == 1 || m_wave < count;  // wave-uniform; a tile holds at least one pair
   };
-  setup_rows();
   const int rb_stride = (split ? 16 : 32) * kgroups;
 
   f32x16 acc[RN][RM];
@@ -605,6 +615,7 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void expert_wide_kernel(mxfp4moe::
   };
   issue_rest();
   while (true) {
+    setup_rows();
     if constexpr (kAhead) {
       Ops ops0, ops1;
       wait_loads_then_barrier<(kStages - 1) * kLoads>();  // chunk 0 (and the scale table) landed
@@ -668,21 +679,22 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void expert_wide_kernel(mxfp4moe::
     wait_loads_then_barrier<0>();
     // this job's epilogue values; the next job (if any) is set up and its
     // scale table and first chunk requested before the epilogue runs
-    const int e_j = e, row0_j = row0, count_j = count, n_wave_j = n_wave;
-    const bool live_j = live;
+    const int e_j = e, row0_j = row0, count_j = count;
     vb += gridDim.x;
-    // (gate_up and the general form take one job per block: their next job's
-    // state does not fit beside the epilogue's registers)
+    // (gate_up and the general form take one job per block: beside the next
+    // job's state the compiler moves gate_up's 256 accumulators out of the
+    // accumulator registers for the epilogue and spills half of them)
     const bool more = kPersist && map_job(vb, num_tiles, n_tiles, tile, ntile);
     if (more) {
       setup();
-      setup_rows();
       if (!kNv) stage_scales<BN, kThreads, true>(sst, args.wscales, args.N, e, ntile, kgroups, t, split);
       issue(0, kNext);
     }
     uint8_t* region = reinterpret_cast<uint8_t*>(arena) + wave * (RM * 32 * 128);
-    if (live_j)
-      store_epilogue<RN, RM, kGateUp, kNv>(args, acc, e_j, row0_j + m_wave, count_j - m_wave, n_wave_j, lane, region);
+    int lane_j = lane;  // opaque copy, as in setup()
+    asm volatile("" : "+v"(lane_j));
+    if (live)
+      store_epilogue<RN, RM, kGateUp, kNv>(args, acc, e_j, row0_j + m_wave, count_j - m_wave, n_wave, lane_j, region);
     if (!more) break;
     __syncthreads();  // every wave is done with the epilogue regions (stages 0 and 1)
     issue_rest();
