@@ -1530,7 +1530,8 @@ static hipError_t launch_all(GemmArgs a, const TileTables& tt, const TileBounds&
       // ahead; down: eight waves of 128 rows x 64 pairs (two per SIMD, one
       // operand set each), whose second wave covers the heavier epilogue and
       // the LDS waits (measured at the 120b prefill shape: down 264 against
-      // 274 us, gate_up 499 against 478 us the other way round)
+      // 274 us; gate_up in eight waves 473 against 450 us, 470 with the
+      // down GEMM's persistent blocks)
       const bool nv = a.scale2 != nullptr;
       if (kGateUp)
         err = nv ? launch_wide<4, 1, 4, 4, true, true, true>(w, stream) : launch_wide<4, 1, 4, 4, true>(w, stream);
