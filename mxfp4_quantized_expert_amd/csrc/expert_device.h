@@ -23,9 +23,12 @@ __device__ __forceinline__ float swiglu_clamped(float gate, float up) {
   const float g = __builtin_elementwise_minimum(gate, 7.0f);
   const float u = __builtin_elementwise_maximum(__builtin_elementwise_minimum(up, 7.0f), -7.0f);
   // sigmoid(alpha g) = 1 / (1 + 2^(-alpha log2(e) g)) through the hardware
-  // exp2 and reciprocal (about 1 ulp each; the result is rounded to bf16)
+  // exp2 and reciprocal (about 1 ulp each; the result is rounded to bf16).
+  // g * sigmoid first (a very negative gate gives -0, not an overflow), then
+  // times (u + 1) as one fused multiply-add.
   constexpr float kNegAlphaLog2e = -1.702f * 1.4426950408889634f;
-  return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(kNegAlphaLog2e * g)) * (u + 1.0f);
+  const float gs = g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(kNegAlphaLog2e * g));
+  return __builtin_fmaf(gs, u, gs);
 }
 
 // gate/up row layout of w13.  Logical row 2i is gate i and 2i+1 is up i (the

@@ -172,6 +172,11 @@ constexpr int kWideMaxGroups = 128;  // K <= 4096
 constexpr int kFp4StageBytes = (128 * 8 + 512 * 2) * 16 + 256 * 4;  // one LDS stage of the FP4 kernel
 constexpr int kFp4MaxLds = 160 * 1024;                              // LDS per workgroup on gfx950
 
+template <bool kValue>
+struct Flag {
+  static constexpr bool value = kValue;
+};
+
 // Epilogue, staged through an LDS region of RM*32*128 bytes per wave so
 // that every token's outputs leave as full 128-byte rows: the lane layout of
 // the MFMA results (four consecutive features of one token per lane) is
@@ -184,7 +189,8 @@ constexpr int kFp4MaxLds = 160 * 1024;                              // LDS per w
 // the expert's second-level scale (before the bias).
 template <int RN, int RM, bool kGateUp, bool kNv = false>
 __device__ __forceinline__ void store_epilogue(const mxfp4moe::GemmArgs& args, const f32x16 (&acc)[RN][RM], int e,
-                                              int row0, int count, int n_wave, int lane, uint8_t* region) {
+                                              int row0, int count, int n_wave, int lane, uint8_t* region,
+                                              bool add_bias = true) {
   const int N = args.N;
   const int half = lane >> 5, lrow = lane & 31;
   const uint16_t* bias = args.bias + (size_t)e * N;
@@ -195,32 +201,42 @@ __device__ __forceinline__ void store_epilogue(const mxfp4moe::GemmArgs& args, c
   // Every global value the epilogue reads (this lane's biases, and for down
   // its pairs' routing weights and pair ids) is loaded in one batch before
   // the first use: loaded where used, each would be a round trip of its own.
+  // (add_bias = false: gate_up sums that started at their biases)
   uint2 braw[RN][4];
+  if (add_bias) {
 #pragma unroll
-  for (int rb = 0; rb < RN; ++rb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int n = n_wave + rb * 32 + 8 * i + 4 * half;
-      braw[rb][i] = load_bias4_raw(bias, n < N ? n : N - 4, N, split);
-    }
-  if (kGateUp) {
-    // stage a[m][q_local], q_local = 0..16*RN-1 for this wave's 32*RN rows of w13
-#pragma unroll
-    for (int rb = 0; rb < RN; ++rb) {
+    for (int rb = 0; rb < RN; ++rb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const f32x4 bv = bias4_of(braw[rb][i], split);
-        const float b0 = bv[0], b1 = bv[1], b2 = bv[2], b3 = bv[3];
-        const int byte = rb * 32 + 8 * i + 4 * half;  // 2 * q_local
+        const int n = n_wave + rb * 32 + 8 * i + 4 * half;
+        braw[rb][i] = load_bias4_raw(bias, n < N ? n : N - 4, N, split);
+      }
+  }
+  if (kGateUp) {
+    // stage a[m][q_local], q_local = 0..16*RN-1 for this wave's 32*RN rows of w13
+    auto stage = [&](auto with_bias) {
+      constexpr bool kB = decltype(with_bias)::value;
 #pragma unroll
-        for (int cb = 0; cb < RM; ++cb) {
-          const int m = cb * 32 + lrow;
-          const float a0 = swiglu_clamped(sum(rb, cb, 4 * i + 0) + b0, sum(rb, cb, 4 * i + 1) + b1);
-          const float a1 = swiglu_clamped(sum(rb, cb, 4 * i + 2) + b2, sum(rb, cb, 4 * i + 3) + b3);
-          *reinterpret_cast<uint32_t*>(region + chunk_addr(m, byte >> 4) + (byte & 15)) = mx::pack_bf16x2_rne(a0, a1);
+      for (int rb = 0; rb < RN; ++rb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f32x4 bv = kB ? bias4_of(braw[rb][i], split) : f32x4{};
+          const int byte = rb * 32 + 8 * i + 4 * half;  // 2 * q_local
+#pragma unroll
+          for (int cb = 0; cb < RM; ++cb) {
+            const int m = cb * 32 + lrow;
+            float h[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) h[j] = kB ? sum(rb, cb, 4 * i + j) + bv[j] : sum(rb, cb, 4 * i + j);
+            const float a0 = swiglu_clamped(h[0], h[1]);
+            const float a1 = swiglu_clamped(h[2], h[3]);
+            *reinterpret_cast<uint32_t*>(region + chunk_addr(m, byte >> 4) + (byte & 15)) = mx::pack_bf16x2_rne(a0, a1);
+          }
         }
       }
-    }
+    };
+    if (add_bias) stage(Flag<true>{});
+    else stage(Flag<false>{});
     const int I = N >> 1;
     const int q0 = n_wave >> 1;
     constexpr int kChunks = 2 * RN;  // 16-byte chunks of a per token (RN*16 activations)
@@ -330,6 +346,7 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void expert_wide_kernel(mxfp4moe::
   constexpr int kStage = kXSlots + kWSlots + kSSlots;  // 16-byte slots per stage
   constexpr int kArena = kStages * kStage * 16 + (kNv ? 0 : BN * kWideMaxGroups);
   static_assert(WN * WM * RM * 32 * 128 <= kArena, "epilogue regions fit in the arena");
+  constexpr bool kPersist = !kTail && !kGateUp;  // this block walks several jobs (the down GEMM's fast form)
   __shared__ __attribute__((aligned(16))) u32x4 arena[kArena / 16];
   uint8_t* const sst = reinterpret_cast<uint8_t*>(arena + kStages * kStage);
 
@@ -454,9 +471,10 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void expert_wide_kernel(mxfp4moe::
     for (int j = 0; j < kSPer; ++j) load_lds4(ssrc[j] + 4 * c, ss + j * kThreads);
   };
 
-  // a job's lane quantities and LDS read positions, derived at the top of
-  // every job from an opaque copy of the lane (as in setup()), so that they are
-  // not held through the epilogue
+  // a job's lane quantities and LDS read positions, derived for every job
+  // (before its first loads, or after the previous job's epilogue) from an
+  // opaque copy of the lane (as in setup()), so that they are not held
+  // through the epilogue
   int half, lrow, wslot0, nvs0;
   const uint8_t* srow;
   int n_wave;
@@ -485,7 +503,43 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void expert_wide_kernel(mxfp4moe::
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[rb][cb][r] = 0.f;
   };
-  clear_acc();
+  // MXFP4 gate_up: the sums start at their rows' biases (nothing scales them
+  // afterwards), so the epilogue adds none.  The block's biases travel to LDS
+  // behind its scale rows with the scale table (bias rows as in memory: the
+  // block's rows, or its gate rows then its up rows), and each wave starts
+  // its accumulators from them once the first chunk has landed.  Loaded into
+  // registers instead, they would make the compiler wait for every load in
+  // flight before their first use.  They need K <= 4032 (room behind the
+  // scale rows) and a 16-byte aligned bias array; otherwise the sums start at
+  // zero and the epilogue adds the biases.
+  constexpr bool kBiasInAcc = kGateUp && !kNv && !kPersist;
+  const bool bias_lds = kBiasInAcc && kgroups + 2 <= kWideMaxGroups && (reinterpret_cast<uintptr_t>(args.bias) & 15) == 0;
+  uint8_t* const sbias = sst + BN * kgroups;
+  auto stage_bias = [&]() {
+    const int nv = min(BN, N - ntile * BN);
+    const int n16 = nv >> 3;  // 16-byte pieces, at most 64: wave 0's lanes
+    const int h = split ? n16 >> 1 : n16;
+    const u32x4* g = reinterpret_cast<const u32x4*>(args.bias + (size_t)e * N + (split ? ntile * BN / 2 : ntile * BN));
+    const u32x4* u = reinterpret_cast<const u32x4*>(args.bias + (size_t)e * N + N / 2 + ntile * BN / 2);
+    if (t < n16) load_lds16(t < h ? g + t : u + (t - h), reinterpret_cast<u32x4*>(sbias));
+  };
+  auto init_acc_from_lds = [&]() {
+    const int nv = min(BN, N - ntile * BN);
+#pragma unroll
+    for (int rb = 0; rb < RN; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int n = wn * RN * 32 + rb * 32 + 8 * i + 4 * (lane >> 5);  // block-local, a multiple of 4
+        const int a0 = split ? n : 2 * n, a1 = split ? nv + n : 2 * n + 4;
+        const uint2 raw{*reinterpret_cast<const uint32_t*>(sbias + a0), *reinterpret_cast<const uint32_t*>(sbias + a1)};
+        const f32x4 bv = bias4_of(raw, split);
+#pragma unroll
+        for (int cb = 0; cb < RM; ++cb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[rb][cb][4 * i + j] = bv[j];
+      }
+  };
+  if (!bias_lds) clear_acc();
 
   // the operands of one chunk in registers, as read (nothing computed from
   // them until the chunk runs, a chunk later)
@@ -605,9 +659,10 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void expert_wide_kernel(mxfp4moe::
   // first chunk load while this job's epilogue runs; its other chunks follow
   // once the epilogue is done with stages 0 and 1.
   constexpr int kNext = 2;  // stage of chunk 0
-  constexpr bool kPersist = !kTail && !kGateUp;  // this block walks several jobs
   static_assert(WN * WM * RM * 32 * 128 <= kNext * kStage * 16, "the epilogue regions stay below stage 2");
+  setup_rows();
   if (!kNv) stage_scales<BN, kThreads, true>(sst, args.wscales, args.N, e, ntile, kgroups, t, split);
+  if (bias_lds) stage_bias();
   issue(0, kNext);
   auto issue_rest = [&]() {  // chunks 1 .. (loads in flight at the first step) of the job
     issue(1, (1 + kNext) % kStages);
@@ -615,10 +670,10 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void expert_wide_kernel(mxfp4moe::
   };
   issue_rest();
   while (true) {
-    setup_rows();
     if constexpr (kAhead) {
       Ops ops0, ops1;
       wait_loads_then_barrier<(kStages - 1) * kLoads>();  // chunk 0 (and the scale table) landed
+      if (bias_lds) init_acc_from_lds();
       if (live) read_ops(ops0, 0, kNext);
       // trips of 2*kStages chunks: the register set and the stage of every step
       // are constants; then the remaining steps one by one
@@ -694,9 +749,11 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void expert_wide_kernel(mxfp4moe::
     int lane_j = lane;  // opaque copy, as in setup()
     asm volatile("" : "+v"(lane_j));
     if (live)
-      store_epilogue<RN, RM, kGateUp, kNv>(args, acc, e_j, row0_j + m_wave, count_j - m_wave, n_wave, lane_j, region);
+      store_epilogue<RN, RM, kGateUp, kNv>(args, acc, e_j, row0_j + m_wave, count_j - m_wave, n_wave, lane_j, region,
+                                           !bias_lds);
     if (!more) break;
     __syncthreads();  // every wave is done with the epilogue regions (stages 0 and 1)
+    setup_rows();
     issue_rest();
     clear_acc();
   }
