@@ -76,6 +76,35 @@ def test_120b_long_prefill(gpu):
     assert_layer_parity(y, ref, "120b_prefill (all tokens)")
 
 
+@pytest.mark.parametrize("split", [False, True])
+def test_bias_arrays_at_8_byte_offsets(gpu, split):
+    # Bias arrays 8-byte but not 16-byte aligned (the boundary asks for 8): the
+    # full-tile gate_up then adds its biases in the epilogue instead of starting
+    # its sums from them.  The output must meet the bar either way, on a layer
+    # whose biases move the output (unsaturated SwiGLU), in both w13 layouts.
+    spec = W.LAYERS["20b_live"].with_(T=300, H=128, I=96, E=2, top_k=1)
+    L = W.make_layer(spec, seed=51)
+    ids, _ = O.route(L["router_logits"], 1)
+    assert np.bincount(ids.ravel(), minlength=2).max() >= 128  # full tiles take part
+    ref = O.moe_forward(L, 1)
+    Lg = dict(L, w13_blocks=_split_rows(L["w13_blocks"]), w13_scales=_split_rows(L["w13_scales"]),
+              w13_bias=_split_rows(L["w13_bias"])) if split else L
+    d = gpu.layer_to_device(Lg)
+
+    def at_8_bytes(t):  # the same values, 8 bytes into a larger buffer
+        buf = torch.empty(t.numel() + 4, dtype=t.dtype, device=t.device)
+        v = buf[4:].view(t.shape)
+        v.copy_(t)
+        return v
+
+    b13, b2 = at_8_bytes(d["w13_bias"]), at_8_bytes(d["w2_bias"])
+    assert b13.data_ptr() % 16 == 8 and b2.data_ptr() % 16 == 8
+    y = gpu.moe_mxfp4_forward(d["x"], d["router_logits"], d["w13_blocks"], d["w13_scales"], b13,
+                              d["w2_blocks"], d["w2_scales"], b2, 1, gate_up_split=split)
+    torch.cuda.synchronize()
+    assert_layer_parity(y, ref, f"biases at 8-byte offsets/split={split}")
+
+
 @pytest.mark.parametrize("T,H,I,E,k", [(5, 96, 160, 7, 3), (1, 64, 32, 3, 3), (37, 224, 96, 9, 2),
                                        (300, 128, 64, 5, 1), (3, 32, 32, 1, 1), (600, 96, 160, 3, 2),
                                        (700, 4096, 64, 2, 1), (9, 32, 64, 512, 32), (40, 64, 64, 64, 32),
