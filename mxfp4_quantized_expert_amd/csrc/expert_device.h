@@ -158,4 +158,17 @@ __device__ __forceinline__ void wait_loads_then_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Waits until this wave's LDS reads are done (vector-memory loads may stay in
+// flight), then joins the block barrier: after it no wave still reads what a
+// load issued afterwards will overwrite.
+__device__ __forceinline__ void lds_reads_then_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  // s_waitcnt fields: vmcnt 63 (no wait), expcnt 7 (no wait), lgkmcnt 0
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 }  // namespace mxgemm

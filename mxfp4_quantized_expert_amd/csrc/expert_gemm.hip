@@ -37,6 +37,7 @@ using mxgemm::bias4_of;
 using mxgemm::load_bias4;
 using mxgemm::load_bias4_raw;
 using mxgemm::load_lds16;
+using mxgemm::lds_reads_then_barrier;
 using mxgemm::load_lds4;
 using mxgemm::pack_bf16x4;
 using mxgemm::stage_scales;
@@ -299,23 +300,18 @@ __device__ __forceinline__ void store_epilogue(const mxfp4moe::GemmArgs& args, c
 // The wide kernel.  Operand chunks move from global memory to LDS by the
 // load unit itself (global_load_lds_dwordx4: 16 bytes per lane, written at
 // the wave's LDS address + 16 * lane; no staging registers, no LDS stores in
-// the wave's stream), three LDS stages deep, and each wave reads its
-// operands of chunk c+1 (weight groups, scale bytes, token fragments) from
-// LDS into a second register set while chunk c runs on the matrix core.
-// Per chunk c: wait for this wave's loads of chunk c+1 (those of chunk c+2
-// stay in flight) and for its reads of chunk c, barrier (every wave's share
-// of chunk c+1 is in LDS; every wave is done with chunk c's stage), then
-// the 64 MFMAs of chunk c from registers, with the loads of chunk c+3 into
-// chunk c's stage and the reads of chunk c+1 spread between them, one after
-// every other MFMA.  Issued as a burst, 32 memory instructions would stall
-// the wave (and leave the matrix core idle) until the LDS queue drains;
-// spread out, they issue while earlier MFMAs run.  All waits sit at the
-// barrier and cover work issued a whole chunk earlier.  While LDS-DMA loads
-// are in flight the compiler only waits for all LDS reads at once, which
-// this order makes free.
-// kAhead = false: one operand set per wave, read right after the barrier
-// that makes the chunk visible; meant for two waves per SIMD (WM = 2), where
-// the other wave's MFMAs cover that wait.  Two chunks in flight.
+// the wave's stream), two or three LDS stages deep.  Per chunk c: wait for
+// this wave's loads of chunk c (those of chunk c+1 stay in flight), barrier
+// (every wave's share is in LDS), read the chunk's operands (weight groups,
+// scale bytes, token fragments) into registers, then its MFMAs with the
+// loads of chunk c+2 spread between them, one after every other MFMA (issued
+// as a burst they would stall the wave with the matrix core idle).  With
+// three stages chunk c+2 goes to the stage of chunk c-1; with two, to chunk
+// c's own stage, after a second barrier that every wave reaches once it has
+// read chunk c.  The wait for a chunk's loads is covered by the other wave
+// on the SIMD: blocks run two waves per SIMD, either as eight waves of one
+// block or as two blocks of four waves per CU, whose epilogues, barriers
+// and conversions then also run beside the other block's MFMAs.
 // kNv: NVFP4 weights (E4M3 block scales per 16 codes, K a multiple of 64).  A
 // chunk's four scale bytes of a row are one aligned dword; each stage holds
 // them for the block's rows (one 4-byte global -> LDS load per row), in place
@@ -328,8 +324,9 @@ __device__ __forceinline__ void store_epilogue(const mxfp4moe::GemmArgs& args, c
 // compiled out and the loads are buffer loads into LDS: a thread keeps a
 // 32-bit offset per operand row and the chunk's offset moves in a scalar
 // register, so a chunk's loads cost no vector address arithmetic.
-template <int WN, int WM, int RN, int RM, bool kGateUp, bool kAhead = true, bool kNv = false, bool kTail = false>
-__global__ __launch_bounds__(WN * WM * 64, 1) void expert_wide_kernel(mxfp4moe::GemmArgs args) {
+template <int WN, int WM, int RN, int RM, bool kGateUp, bool kNv = false, bool kTail = false, int kStageCount = 3,
+          int kBlocksPerCu = 1>
+__global__ __launch_bounds__(WN * WM * 64, kBlocksPerCu) void expert_wide_kernel(mxfp4moe::GemmArgs args) {
   constexpr int kThreads = WN * WM * 64;
   constexpr int BN = WN * RN * 32;
   constexpr int BM = WM * RM * 32;
@@ -341,12 +338,13 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void expert_wide_kernel(mxfp4moe::
   constexpr int kSPer = kNv ? BN / kThreads : 0;
   static_assert(kXSlots % kThreads == 0 && kWSlots % kThreads == 0 && (!kNv || BN % kThreads == 0),
                 "tile / thread mismatch");
-  constexpr int kStages = 3;              // LDS stages: chunk c+3 loads while c+1 is read and c runs
+  constexpr int kStages = kStageCount;  // LDS stages (see above)
+  static_assert(kStages == 2 || kStages == 3, "two or three stages");
   constexpr int kLoads = kXPer + kWPer + kSPer;  // loads per thread per chunk
   constexpr int kStage = kXSlots + kWSlots + kSSlots;  // 16-byte slots per stage
   constexpr int kArena = kStages * kStage * 16 + (kNv ? 0 : BN * kWideMaxGroups);
   static_assert(WN * WM * RM * 32 * 128 <= kArena, "epilogue regions fit in the arena");
-  constexpr bool kPersist = !kTail && !kGateUp;  // this block walks several jobs (the down GEMM's fast form)
+  constexpr bool kPersist = !kTail && !kGateUp && kBlocksPerCu == 1;  // this block walks several jobs (the down GEMM's fast form)
   __shared__ __attribute__((aligned(16))) u32x4 arena[kArena / 16];
   uint8_t* const sst = reinterpret_cast<uint8_t*>(arena + kStages * kStage);
 
@@ -556,17 +554,6 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void expert_wide_kernel(mxfp4moe::
     const int g = 2 * c + half;
     return srow[rb * rb_stride + (!kTail || g < kgroups ? g : g - 1)];
   };
-  auto read_ops = [&](Ops& o, int c, int st) {
-    c = c < nchunks ? c : nchunks - 1;  // past the end: a harmless re-read
-    const u32x4* xs = arena + st * kStage;
-    const u32x4* wsm = xs + kXSlots;
-#pragma unroll
-    for (int rb = 0; rb < RN; ++rb) {
-      o.w[rb] = wsm[wslot0 + rb * 64];
-      o.sb[rb] = read_scale(c, st, rb);
-    }
-    read_token_frags<RM>(o.b, xs + m_wave * 8, lrow, half);
-  };
   // load k (0 .. kLoads-1) of chunk c into stage st
   auto issue_one = [&](int c, int st, int k) {
     c = c < nchunks ? c : nchunks - 1;
@@ -618,127 +605,73 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void expert_wide_kernel(mxfp4moe::
       lo = hi = mx::e8m0_operand(sb);
     }
   };
-  // chunk c from registers `cur` (stage st = c % kStages, a constant at every
-  // call site); chunk c+1's operands into `nxt`; chunk c+kStages into
-  // chunk c's stage.  The loads and reads are spread through the chunk's
-  // MFMAs, one after every other MFMA, so the wave never stalls on a burst of
-  // memory instructions while the matrix core idles.
-  auto step = [&](int c, int st, const Ops& cur, Ops& nxt) {
-    // this wave's loads of chunk c+1 are done once at most the loads of the
-    // chunks after it are in flight
-    wait_loads_then_barrier<(kStages - 2) * kLoads>();
-    if (live) {
-      // one memory instruction after every other MFMA; what does not fit
-      // (NVFP4's scale loads) after the first odd ones
-      constexpr int kSlots = 2 * RN * RM;
-      static_assert(!kAhead || kLoads + kReads <= 2 * kSlots, "room between the MFMAs");
-      auto extra = [&](int k) {
-        const int op = k % 2 == 0 ? k / 2 : kSlots + k / 2;
-        if (op < kLoads) issue_one(c + kStages, st, op);
-        else if (op < kLoads + kReads) read_one(nxt, c + 1, (st + 1) % kStages, op - kLoads);
-        else return;
-        __builtin_amdgcn_sched_barrier(0);  // keep the order: the compiler would bunch the MFMAs
-      };
-      // K tail: the group past K multiplies zero weights
-      const bool glive = !kTail || 2 * c + half < kgroups;
-      u32x4 w[RN];
-      float sc[RN], sc_hi[RN];
-#pragma unroll
-      for (int rb = 0; rb < RN; ++rb) {
-        w[rb] = glive ? cur.w[rb] : u32x4{0u, 0u, 0u, 0u};
-        scales_of(cur.sb[rb], sc[rb], sc_hi[rb]);
-      }
-      chunk_mma_regs<RN, RM, kNv>(acc, cur.b, w, sc, sc_hi, extra);
-    } else {
-      issue(c + kStages, st);
-    }
-  };
-  // Chunk c sits in LDS stage (c + 2) % 3, so that chunk 0 of the next job
-  // goes to stage 2: the epilogue's regions use only stages 0 and 1 (and the
-  // scale table is no longer read then), so the next job's scale table and
-  // first chunk load while this job's epilogue runs; its other chunks follow
-  // once the epilogue is done with stages 0 and 1.
-  constexpr int kNext = 2;  // stage of chunk 0
-  static_assert(WN * WM * RM * 32 * 128 <= kNext * kStage * 16, "the epilogue regions stay below stage 2");
+  // Chunk c sits in LDS stage (c + kStages - 1) % kStages, so that chunk 0 of
+  // a persistent block's next job goes to the last stage: the epilogue's
+  // regions use only the stages below it (and the scale table is no longer
+  // read then), so the next job's scale table and first chunk load while this
+  // job's epilogue runs; its second chunk follows once the epilogue is done.
+  constexpr int kNext = kStages - 1;  // stage of chunk 0
+  static_assert(!kPersist || WN * WM * RM * 32 * 128 <= kNext * kStage * 16,
+                "the epilogue regions stay below the next job's first stage");
   setup_rows();
   if (!kNv) stage_scales<BN, kThreads, true>(sst, args.wscales, args.N, e, ntile, kgroups, t, split);
   if (bias_lds) stage_bias();
   issue(0, kNext);
-  auto issue_rest = [&]() {  // chunks 1 .. (loads in flight at the first step) of the job
-    issue(1, (1 + kNext) % kStages);
-    if (kAhead) issue(2, (2 + kNext) % kStages);
-  };
+  auto issue_rest = [&]() { issue(1, (1 + kNext) % kStages); };  // the job's second chunk
   issue_rest();
   while (true) {
-    if constexpr (kAhead) {
-      Ops ops0, ops1;
-      wait_loads_then_barrier<(kStages - 1) * kLoads>();  // chunk 0 (and the scale table) landed
-      if (bias_lds) init_acc_from_lds();
-      if (live) read_ops(ops0, 0, kNext);
-      // trips of 2*kStages chunks: the register set and the stage of every step
-      // are constants; then the remaining steps one by one
-      constexpr int kTrip = 2 * kStages;
-      const int nfull = nchunks / kTrip * kTrip;
-      for (int c0 = 0; c0 < nfull; c0 += kTrip) {
+    // chunk c from stage st: read after the barrier that makes it visible
+    // (the other wave on the SIMD covers the wait); chunk c+2 into stage
+    // (st + 2) % kStages, its loads spread between the MFMAs
+    auto step1 = [&](int c, int st) {
+      wait_loads_then_barrier<kLoads>();  // chunk c landed; chunk c+1 may be in flight
+      Ops cur;
+      if (live) {
 #pragma unroll
-        for (int u = 0; u < kTrip; u += 2) {
-          step(c0 + u, (u + kNext) % kStages, ops0, ops1);
-          step(c0 + u + 1, (u + 1 + kNext) % kStages, ops1, ops0);
+        for (int j = 0; j < kReads; ++j) read_one(cur, c, st, j);
+      }
+      if constexpr (kStages == 2) lds_reads_then_barrier();  // chunk c+2 overwrites chunk c
+      if (live) {
+        constexpr int kMfma = 4 * RN * RM;
+        constexpr int kEvery = kMfma / kLoads >= 2 ? 2 : 1;
+        static_assert(kEvery * kLoads <= kMfma, "room between the MFMAs");
+        auto extra = [&](int k) {
+          if (k % kEvery != 0 || k / kEvery >= kLoads) return;
+          issue_one(c + 2, (st + 2) % kStages, k / kEvery);
+          __builtin_amdgcn_sched_barrier(0);
+        };
+        const bool glive = !kTail || 2 * c + half < kgroups;
+        u32x4 w[RN];
+        float sc[RN], sc_hi[RN];
+#pragma unroll
+        for (int rb = 0; rb < RN; ++rb) {
+          w[rb] = glive ? cur.w[rb] : u32x4{0u, 0u, 0u, 0u};
+          scales_of(cur.sb[rb], sc[rb], sc_hi[rb]);
         }
+        chunk_mma_regs<RN, RM, kNv>(acc, cur.b, w, sc, sc_hi, extra);
+      } else {
+        issue(c + 2, (st + 2) % kStages);
       }
-#pragma unroll
-      for (int u = 0; u < kTrip - 1; u += 2) {
-        if (nfull + u < nchunks) step(nfull + u, (u + kNext) % kStages, ops0, ops1);
-        if (nfull + u + 1 < nchunks) step(nfull + u + 1, (u + 1 + kNext) % kStages, ops1, ops0);
-      }
-    } else {
-      // one operand set: chunk c is read after the barrier that makes it
-      // visible (the other wave on the SIMD covers the wait), chunk c+2 goes
-      // to the stage of chunk c-1, its loads spread between the MFMAs
-      auto step1 = [&](int c, int st) {
-        wait_loads_then_barrier<kLoads>();  // chunk c landed; chunk c+1 may be in flight
-        Ops cur;
-        if (live) {
-#pragma unroll
-          for (int j = 0; j < kReads; ++j) read_one(cur, c, st, j);
-          constexpr int kMfma = 4 * RN * RM;
-          constexpr int kEvery = kMfma / kLoads >= 2 ? 2 : 1;
-          static_assert(kEvery * kLoads <= kMfma, "room between the MFMAs");
-          auto extra = [&](int k) {
-            if (k % kEvery != 0 || k / kEvery >= kLoads) return;
-            issue_one(c + 2, (st + 2) % kStages, k / kEvery);
-            __builtin_amdgcn_sched_barrier(0);
-          };
-          const bool glive = !kTail || 2 * c + half < kgroups;
-          u32x4 w[RN];
-          float sc[RN], sc_hi[RN];
-#pragma unroll
-          for (int rb = 0; rb < RN; ++rb) {
-            w[rb] = glive ? cur.w[rb] : u32x4{0u, 0u, 0u, 0u};
-            scales_of(cur.sb[rb], sc[rb], sc_hi[rb]);
-          }
-          chunk_mma_regs<RN, RM, kNv>(acc, cur.b, w, sc, sc_hi, extra);
-        } else {
-          issue(c + 2, (st + 2) % kStages);
-        }
-      };
-      const int nfull = nchunks / kStages * kStages;
-      for (int c0 = 0; c0 < nfull; c0 += kStages) {
-#pragma unroll
-        for (int u = 0; u < kStages; ++u) step1(c0 + u, (u + kNext) % kStages);
-      }
-      if (nfull < nchunks) step1(nfull, kNext % kStages);
-      if (nfull + 1 < nchunks) step1(nfull + 1, (1 + kNext) % kStages);
+    };
+    if (bias_lds) {
+      wait_loads_then_barrier<kLoads>();  // chunk 0 (and the biases) landed
+      init_acc_from_lds();
     }
+    const int nfull = nchunks / kStages * kStages;
+    for (int c0 = 0; c0 < nfull; c0 += kStages) {
+#pragma unroll
+      for (int u = 0; u < kStages; ++u) step1(c0 + u, (u + kNext) % kStages);
+    }
+#pragma unroll
+    for (int u = 0; u < kStages - 1; ++u)
+      if (nfull + u < nchunks) step1(nfull + u, (u + kNext) % kStages);
     // the chunks issued past the end land before the arena is reused
     wait_loads_then_barrier<0>();
     // this job's epilogue values; the next job (if any) is set up and its
     // scale table and first chunk requested before the epilogue runs
     const int e_j = e, row0_j = row0, count_j = count;
     vb += gridDim.x;
-    // (gate_up and the general form take one job per block: beside the next
-    // job's state the compiler moves gate_up's 256 accumulators out of the
-    // accumulator registers for the epilogue and spills half of them)
+    // (only a down GEMM fast form at one block per CU walks several jobs)
     const bool more = kPersist && map_job(vb, num_tiles, n_tiles, tile, ntile);
     if (more) {
       setup();
@@ -759,7 +692,7 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void expert_wide_kernel(mxfp4moe::
   }
 }
 
-template <int WN, int WM, int RN, int RM, bool kGateUp, bool kAhead = true, bool kNv = false>
+template <int WN, int WM, int RN, int RM, bool kGateUp, bool kNv = false, int kStageCount = 3, int kBlocksPerCu = 1>
 hipError_t launch_wide(const mxfp4moe::GemmArgs& a, hipStream_t stream) {
   constexpr int BN = WN * RN * 32;
   const long n_tiles = (a.N + BN - 1) / BN;
@@ -774,11 +707,14 @@ hipError_t launch_wide(const mxfp4moe::GemmArgs& a, hipStream_t stream) {
   // first loads fly during the previous job's epilogue
   long grid = (blocks + kXcds - 1) / kXcds * kXcds;
   const long cus = (long)mxfp4moe::device_cu_count() / kXcds * kXcds;
-  if (fast && !kGateUp && cus >= kXcds && grid > cus) grid = cus;
+  constexpr bool kPersistent = !kGateUp && kBlocksPerCu == 1;  // as the kernel's fast form decides
+  if (fast && kPersistent && cus >= kXcds && grid > cus) grid = cus;
   if (fast)
-    expert_wide_kernel<WN, WM, RN, RM, kGateUp, kAhead, kNv><<<(unsigned)grid, WN * WM * 64, 0, stream>>>(a);
+    expert_wide_kernel<WN, WM, RN, RM, kGateUp, kNv, false, kStageCount, kBlocksPerCu>
+        <<<(unsigned)grid, WN * WM * 64, 0, stream>>>(a);
   else
-    expert_wide_kernel<WN, WM, RN, RM, kGateUp, kAhead, kNv, true><<<(unsigned)grid, WN * WM * 64, 0, stream>>>(a);
+    expert_wide_kernel<WN, WM, RN, RM, kGateUp, kNv, true, kStageCount, kBlocksPerCu>
+        <<<(unsigned)grid, WN * WM * 64, 0, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -1583,17 +1519,21 @@ static hipError_t launch_all(GemmArgs a, const TileTables& tt, const TileBounds&
       w.act = reinterpret_cast<const uint16_t*>(a.act_codes);
       err = launch_fp4<kGateUp>(w, a.act_mode == kActMxfp8Split, stream);
     } else {
-      // gate_up: four waves of 128 rows x 128 pairs, operands read a chunk
-      // ahead; down: eight waves of 128 rows x 64 pairs (two per SIMD, one
-      // operand set each), whose second wave covers the heavier epilogue and
-      // the LDS waits (measured at the 120b prefill shape: down 264 against
-      // 274 us; gate_up in eight waves 473 against 450 us, 470 with the
-      // down GEMM's persistent blocks)
+      // Two waves per SIMD, so that one wave's conversions, waits and
+      // epilogue run beside the other's MFMAs.  gate_up (MXFP4 and NVFP4) and
+      // the NVFP4 down GEMM: two blocks per CU of four waves x (64 rows x 128
+      // pairs) (MXFP4 gate_up: two LDS stages beside its scale table, within
+      // half the LDS).  MXFP4 down: one persistent block per CU of eight waves
+      // x (128 rows x 64 pairs).  Measured at the 120b long prefill: gate_up
+      // 444 against 454 us for four waves of 128 x 128 with operands read a
+      // chunk ahead (NVFP4 547 against 560); down 221 (persistent) against
+      // 229 us in two blocks (NVFP4 297 against 305 the other way round).
       const bool nv = a.scale2 != nullptr;
       if (kGateUp)
-        err = nv ? launch_wide<4, 1, 4, 4, true, true, true>(w, stream) : launch_wide<4, 1, 4, 4, true>(w, stream);
+        err = nv ? launch_wide<4, 1, 2, 4, true, true, 3, 2>(w, stream)
+                 : launch_wide<4, 1, 2, 4, true, false, 2, 2>(w, stream);
       else
-        err = nv ? launch_wide<4, 2, 4, 2, false, false, true>(w, stream)
+        err = nv ? launch_wide<4, 1, 2, 4, false, true, 3, 2>(w, stream)
                  : launch_wide<4, 2, 4, 2, false, false>(w, stream);
     }
   }
