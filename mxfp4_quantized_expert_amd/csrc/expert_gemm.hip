@@ -324,6 +324,15 @@ __device__ __forceinline__ void store_epilogue(const mxfp4moe::GemmArgs& args, c
 // compiled out and the loads are buffer loads into LDS: a thread keeps a
 // 32-bit offset per operand row and the chunk's offset moves in a scalar
 // register, so a chunk's loads cost no vector address arithmetic.
+// Whether a wide-kernel configuration's fast form is persistent (one block
+// per CU walking its jobs, the next job's first chunk loading during the
+// epilogue): the down GEMM at one block per CU whose epilogue regions stay
+// below the last LDS stage.  The launcher sizes the grid by the same rule.
+template <int WN, int WM, int RN, int RM, bool kGateUp, int kBlocksPerCu, int kStage16>
+constexpr bool wide_persistent() {
+  return !kGateUp && kBlocksPerCu == 1 && WN * WM * RM * 32 * 128 <= 2 * kStage16 * 16;
+}
+
 template <int WN, int WM, int RN, int RM, bool kGateUp, bool kNv = false, bool kTail = false, int kStageCount = 3,
           int kBlocksPerCu = 1>
 __global__ __launch_bounds__(WN * WM * 64, kBlocksPerCu) void expert_wide_kernel(mxfp4moe::GemmArgs args) {
@@ -344,7 +353,7 @@ __global__ __launch_bounds__(WN * WM * 64, kBlocksPerCu) void expert_wide_kernel
   constexpr int kStage = kXSlots + kWSlots + kSSlots;  // 16-byte slots per stage
   constexpr int kArena = kStages * kStage * 16 + (kNv ? 0 : BN * kWideMaxGroups);
   static_assert(WN * WM * RM * 32 * 128 <= kArena, "epilogue regions fit in the arena");
-  constexpr bool kPersist = !kTail && !kGateUp && kBlocksPerCu == 1;  // this block walks several jobs (the down GEMM's fast form)
+  constexpr bool kPersist = !kTail && wide_persistent<WN, WM, RN, RM, kGateUp, kBlocksPerCu, kStage>();
   __shared__ __attribute__((aligned(16))) u32x4 arena[kArena / 16];
   uint8_t* const sst = reinterpret_cast<uint8_t*>(arena + kStages * kStage);
 
@@ -707,7 +716,8 @@ hipError_t launch_wide(const mxfp4moe::GemmArgs& a, hipStream_t stream) {
   // first loads fly during the previous job's epilogue
   long grid = (blocks + kXcds - 1) / kXcds * kXcds;
   const long cus = (long)mxfp4moe::device_cu_count() / kXcds * kXcds;
-  constexpr bool kPersistent = !kGateUp && kBlocksPerCu == 1;  // as the kernel's fast form decides
+  constexpr int kStage16 = (WM * RM * 32) * 8 + BN * 2 + (kNv ? BN / 4 : 0);  // the kernel's kStage
+  constexpr bool kPersistent = wide_persistent<WN, WM, RN, RM, kGateUp, kBlocksPerCu, kStage16>();
   if (fast && kPersistent && cus >= kXcds && grid > cus) grid = cus;
   if (fast)
     expert_wide_kernel<WN, WM, RN, RM, kGateUp, kNv, false, kStageCount, kBlocksPerCu>
