@@ -105,19 +105,41 @@ struct NoExtra {
 // operand; sc_hi is unused.  NVFP4: sc[rb] and sc_hi[rb] are the E4M3 block
 // scales of steps 0-1 and 2-3 as floats, applied by the exact float32
 // conversion.
-template <int RN, int RM, bool kNv = false, typename Extra = NoExtra>
+// kF16 (NVFP4 only): the tokens are f16; each E4M3 block scale comes as its
+// power of two (sc, sc_hi) and its significand as an f16 pair (mt, mt_hi),
+// the codes are converted to f16 by the scaled convert and one packed
+// multiply, and the MFMAs are f16.
+template <int RN, int RM, bool kNv = false, bool kF16 = false, typename Extra = NoExtra>
 __device__ __forceinline__ void chunk_mma_regs(f32x16 (&acc)[RN][RM], const bf16x8 (&b)[4][RM],
                                                const u32x4 (&w)[RN], const float (&sc)[RN],
-                                               const float (&sc_hi)[RN], Extra extra = Extra()) {
+                                               const float (&sc_hi)[RN], Extra extra = Extra(),
+                                               const uint32_t* mt = nullptr, const uint32_t* mt_hi = nullptr) {
+  static_assert(!kF16 || kNv, "f16 operands for NVFP4 weights");
+  auto f16_pair = [&](uint32_t packed, int sel, float pow2, uint32_t mant2) {
+    uint32_t v;
+    if (sel == 0) v = mx::fp4x2_to_f16x2<0>(packed, pow2);
+    else if (sel == 1) v = mx::fp4x2_to_f16x2<1>(packed, pow2);
+    else if (sel == 2) v = mx::fp4x2_to_f16x2<2>(packed, pow2);
+    else v = mx::fp4x2_to_f16x2<3>(packed, pow2);
+    return mx::mul_f16x2(v, mant2);
+  };
   u32x4 a[2][RN];
 #pragma unroll
-  for (int rb = 0; rb < RN; ++rb)
-    a[0][rb] = kNv ? mx::fp4x8_to_bf16x8_any_scale(w[rb][0], sc[rb]) : mx::fp4x8_to_bf16x8(w[rb][0], sc[rb]);
+  for (int rb = 0; rb < RN; ++rb) {
+    if constexpr (kF16) {
+#pragma unroll
+      for (int sel = 0; sel < 4; ++sel) a[0][rb][sel] = f16_pair(w[rb][0], sel, sc[rb], mt[rb]);
+    } else {
+      a[0][rb] = kNv ? mx::fp4x8_to_bf16x8_any_scale(w[rb][0], sc[rb]) : mx::fp4x8_to_bf16x8(w[rb][0], sc[rb]);
+    }
+  }
   auto convert = [&](int s, int i) {  // converts pair i%4 of fragment i/4 for step s
     const int rb = i / 4, sel = i % 4;
     const uint32_t packed = w[rb][s];
     uint32_t v;
-    if (kNv) {
+    if (kF16) {
+      v = s < 2 ? f16_pair(packed, sel, sc[rb], mt[rb]) : f16_pair(packed, sel, sc_hi[rb], mt_hi[rb]);
+    } else if (kNv) {
       const float f = s < 2 ? sc[rb] : sc_hi[rb];
       if (sel == 0) v = mx::fp4x2_to_bf16x2_any_scale<0>(packed, f);
       else if (sel == 1) v = mx::fp4x2_to_bf16x2_any_scale<1>(packed, f);
@@ -136,7 +158,11 @@ __device__ __forceinline__ void chunk_mma_regs(f32x16 (&acc)[RN][RM], const bf16
 #pragma unroll
     for (int i = 0; i < RN * RM; ++i) {
       const int rb = i % RN, cb = i / RN;
-      acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mx::as_bf16x8(a[s & 1][rb]), b[s][cb], acc[rb][cb], 0, 0, 0);
+      if constexpr (kF16)
+        acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(mx::f16x8, a[s & 1][rb]),
+                                                             __builtin_bit_cast(mx::f16x8, b[s][cb]), acc[rb][cb], 0, 0, 0);
+      else
+        acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mx::as_bf16x8(a[s & 1][rb]), b[s][cb], acc[rb][cb], 0, 0, 0);
       if (s + 1 < 4 && i < 4 * RN) convert(s + 1, i);
       extra(s * RN * RM + i);
     }
@@ -188,7 +214,7 @@ struct Flag {
 // rounded to bf16 -> zw[pair][H], one 32-feature slab (staged as 128 bytes,
 // stored as 64 per token) per pass.  NVFP4: the sums are first multiplied by
 // the expert's second-level scale (before the bias).
-template <int RN, int RM, bool kGateUp, bool kNv = false>
+template <int RN, int RM, bool kGateUp, bool kNv = false, bool kF16Out = false>
 __device__ __forceinline__ void store_epilogue(const mxfp4moe::GemmArgs& args, const f32x16 (&acc)[RN][RM], int e,
                                               int row0, int count, int n_wave, int lane, uint8_t* region,
                                               bool add_bias = true) {
@@ -231,7 +257,8 @@ __device__ __forceinline__ void store_epilogue(const mxfp4moe::GemmArgs& args, c
             for (int j = 0; j < 4; ++j) h[j] = kB ? sum(rb, cb, 4 * i + j) + bv[j] : sum(rb, cb, 4 * i + j);
             const float a0 = swiglu_clamped(h[0], h[1]);
             const float a1 = swiglu_clamped(h[2], h[3]);
-            *reinterpret_cast<uint32_t*>(region + chunk_addr(m, byte >> 4) + (byte & 15)) = mx::pack_bf16x2_rne(a0, a1);
+            *reinterpret_cast<uint32_t*>(region + chunk_addr(m, byte >> 4) + (byte & 15)) =
+                kF16Out ? mx::pack_f16x2_rne(a0, a1) : mx::pack_bf16x2_rne(a0, a1);
           }
         }
       }
@@ -354,6 +381,12 @@ __global__ __launch_bounds__(WN * WM * 64, kBlocksPerCu) void expert_wide_kernel
   constexpr int kArena = kStages * kStage * 16 + (kNv ? 0 : BN * kWideMaxGroups);
   static_assert(WN * WM * RM * 32 * 128 <= kArena, "epilogue regions fit in the arena");
   constexpr bool kPersist = !kTail && wide_persistent<WN, WM, RN, RM, kGateUp, kBlocksPerCu, kStage>();
+  // NVFP4 full tiles pass the gate_up output to the down GEMM in f16 (|a| <=
+  // 56: the clamps bound it): gate_up stores it so, the down GEMM converts
+  // its weights to f16 (two instructions per pair of codes instead of four)
+  // and multiplies in f16
+  constexpr bool kF16Out = kNv && kGateUp;
+  constexpr bool kF16In = kNv && !kGateUp;
   __shared__ __attribute__((aligned(16))) u32x4 arena[kArena / 16];
   uint8_t* const sst = reinterpret_cast<uint8_t*>(arena + kStages * kStage);
 
@@ -652,12 +685,17 @@ __global__ __launch_bounds__(WN * WM * 64, kBlocksPerCu) void expert_wide_kernel
         const bool glive = !kTail || 2 * c + half < kgroups;
         u32x4 w[RN];
         float sc[RN], sc_hi[RN];
+        uint32_t mt[RN], mt_hi[RN];
 #pragma unroll
         for (int rb = 0; rb < RN; ++rb) {
           w[rb] = glive ? cur.w[rb] : u32x4{0u, 0u, 0u, 0u};
           scales_of(cur.sb[rb], sc[rb], sc_hi[rb]);
+          if constexpr (kF16In) {
+            mx::split_scale_f16(sc[rb], sc[rb], mt[rb]);
+            mx::split_scale_f16(sc_hi[rb], sc_hi[rb], mt_hi[rb]);
+          }
         }
-        chunk_mma_regs<RN, RM, kNv>(acc, cur.b, w, sc, sc_hi, extra);
+        chunk_mma_regs<RN, RM, kNv, kF16In>(acc, cur.b, w, sc, sc_hi, extra, mt, mt_hi);
       } else {
         issue(c + 2, (st + 2) % kStages);
       }
@@ -691,8 +729,8 @@ __global__ __launch_bounds__(WN * WM * 64, kBlocksPerCu) void expert_wide_kernel
     int lane_j = lane;  // opaque copy, as in setup()
     asm volatile("" : "+v"(lane_j));
     if (live)
-      store_epilogue<RN, RM, kGateUp, kNv>(args, acc, e_j, row0_j + m_wave, count_j - m_wave, n_wave, lane_j, region,
-                                           !bias_lds);
+      store_epilogue<RN, RM, kGateUp, kNv, kF16Out>(args, acc, e_j, row0_j + m_wave, count_j - m_wave, n_wave, lane_j,
+                                                    region, !bias_lds);
     if (!more) break;
     __syncthreads();  // every wave is done with the epilogue regions (stages 0 and 1)
     setup_rows();

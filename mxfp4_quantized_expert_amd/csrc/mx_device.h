@@ -90,6 +90,35 @@ __device__ __forceinline__ u32x4 fp4x8_to_bf16x8_any_scale(uint32_t packed, floa
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
+// f16 forms, for NVFP4 weights: E2M1 x an E4M3 block scale has at most six
+// significant bits and lies in [2^-10, 2688], so it is exact in f16.  The
+// scaled convert applies the scale's power of two (only its exponent field
+// counts, as for the bf16 convert), one packed f16 multiply its mantissa.
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2v;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4x2_to_f16x2(uint32_t packed, float pow2) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, pow2, SEL));
+}
+__device__ __forceinline__ uint32_t mul_f16x2(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2v, a) * __builtin_bit_cast(f16x2v, b));
+}
+// Two floats -> two f16 (round to nearest even), low half first.
+__device__ __forceinline__ uint32_t pack_f16x2_rne(float lo, float hi) {
+  const f32x2v v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2v));
+}
+// An E4M3 scale as a float split into its power of two (the convert's scale
+// operand) and its significand in [1, 2) with the sign, as an f16 pair (a NaN
+// scale gives a NaN significand, so every product of its group is NaN).
+__device__ __forceinline__ void split_scale_f16(float s, float& pow2, uint32_t& mant2) {
+  const uint32_t b = __float_as_uint(s);
+  pow2 = __uint_as_float(b & 0x7F800000u);
+  const float m = s != s ? s : __uint_as_float((b & 0x807FFFFFu) | 0x3F800000u);
+  const f32x2v mm = {m, m};
+  mant2 = __builtin_bit_cast(uint32_t, __builtin_convertvector(mm, f16x2v));
+}
+
 // Number of set bits of `mask` below this lane (wave64).
 __device__ __forceinline__ int lanes_below(uint64_t mask) {
   return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
