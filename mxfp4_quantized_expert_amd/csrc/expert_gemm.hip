@@ -368,19 +368,24 @@ __global__ __launch_bounds__(WN * WM * 64, kBlocksPerCu) void expert_wide_kernel
   constexpr int BM = WM * RM * 32;
   constexpr int kXSlots = BM * 8;
   constexpr int kWSlots = BN * 2;
-  constexpr int kSSlots = kNv ? BN / 4 : 0;  // NVFP4: one scale dword per row
   constexpr int kXPer = kXSlots / kThreads;
   constexpr int kWPer = kWSlots / kThreads;
-  constexpr int kSPer = kNv ? BN / kThreads : 0;
-  static_assert(kXSlots % kThreads == 0 && kWSlots % kThreads == 0 && (!kNv || BN % kThreads == 0),
-                "tile / thread mismatch");
+  static_assert(kXSlots % kThreads == 0 && kWSlots % kThreads == 0, "tile / thread mismatch");
+  // NVFP4 scales: a row's four scale bytes of a chunk are one dword, and the
+  // dwords of four chunks in a row are 16 contiguous bytes.  They travel in
+  // groups of four chunks into a ring of two slots of BN rows x 16 bytes,
+  // four lanes per row (one 16-byte piece per row and line, instead of one
+  // line per row and chunk), one quarter of the next group with each chunk.
+  static_assert(!kNv || BN * 4 == 4 * kThreads, "NVFP4: one scale dword per thread and chunk");
+  constexpr int kRing = kNv ? 2 * BN * 16 : 0;
   constexpr int kStages = kStageCount;  // LDS stages (see above)
   static_assert(kStages == 2 || kStages == 3, "two or three stages");
-  constexpr int kLoads = kXPer + kWPer + kSPer;  // loads per thread per chunk
-  constexpr int kStage = kXSlots + kWSlots + kSSlots;  // 16-byte slots per stage
-  constexpr int kArena = kStages * kStage * 16 + (kNv ? 0 : BN * kWideMaxGroups);
+  constexpr int kLoads = kXPer + kWPer;  // operand loads per thread per chunk
+  constexpr int kStage = kXSlots + kWSlots;  // 16-byte slots per stage
+  constexpr int kArena = kStages * kStage * 16 + (kNv ? kRing : BN * kWideMaxGroups);
   static_assert(WN * WM * RM * 32 * 128 <= kArena, "epilogue regions fit in the arena");
   constexpr bool kPersist = !kTail && wide_persistent<WN, WM, RN, RM, kGateUp, kBlocksPerCu, kStage>();
+  static_assert(!(kNv && kPersist), "the NVFP4 scale ring is per job");
   // NVFP4 full tiles pass the gate_up output to the down GEMM in f16 (|a| <=
   // 56: the clamps bound it): gate_up stores it so, the down GEMM converts
   // its weights to f16 (two instructions per pair of codes instead of four)
@@ -419,8 +424,8 @@ __global__ __launch_bounds__(WN * WM * 64, kBlocksPerCu) void expert_wide_kernel
   const uint16_t* xsrc[kXPer];
   int xcol[kXPer];
   const uint8_t* wsrc[kWPer];
-  const uint8_t* ssrc[kSPer > 0 ? kSPer : 1];
-  int xoff[kXPer], woff[kWPer], soff[kSPer > 0 ? kSPer : 1];
+  int xoff[kXPer], woff[kWPer];
+  int sq0 = 0, sdw = 0;  // NVFP4: this thread's scale row (logical, part 0) and dword in the group
   // one job's operand addresses: the fast form keeps 32-bit offsets only, the
   // general form 64-bit pointers (and the column of each token slot)
   auto setup = [&]() {
@@ -457,13 +462,12 @@ __global__ __launch_bounds__(WN * WM * 64, kBlocksPerCu) void expert_wide_kernel
       if constexpr (kTail) wsrc[j] = args.wblocks + ((size_t)e * N + wr) * (size_t)(K >> 1);
       else woff[j] = wr * (K >> 1) + 16 * wh;
     }
-    // NVFP4 scale slot j: the dword of row t + j*threads (rows past N re-read row N-1)
-#pragma unroll
-    for (int j = 0; j < kSPer; ++j) {
-      int wr = ntile * BN + t + j * kThreads;
-      wr = w13_row(wr < N ? wr : N - 1, N, split);
-      if constexpr (kTail) ssrc[j] = args.wscales + ((size_t)e * N + wr) * (size_t)(K >> 4);
-      else soff[j] = wr * (K >> 4);
+    // NVFP4 scale part j of a group: row t/4 + j*threads/4 of the block,
+    // dword t%4 of the group's four (fewer than four chunks: the dwords past
+    // the row's last re-read it)
+    if constexpr (kNv) {
+      sq0 = ntile * BN + (t >> 2);
+      sdw = min(t & 3, nchunks - 1);
     }
     if constexpr (!kTail) {
       rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(args.wblocks + (size_t)e * N * (K >> 1)), (short)0,
@@ -487,14 +491,11 @@ __global__ __launch_bounds__(WN * WM * 64, kBlocksPerCu) void expert_wide_kernel
     c = c < nchunks ? c : nchunks - 1;
     u32x4* xs = arena + st * kStage + wave * 64;
     u32x4* ws = xs + kXSlots;
-    uint32_t* const ss = reinterpret_cast<uint32_t*>(arena + st * kStage + kXSlots + kWSlots) + wave * 64;
     if (!kTail) {
 #pragma unroll
       for (int i = 0; i < kXPer; ++i) buf_lds(rx, xs + i * kThreads, 16, xoff[i], c * 128);
 #pragma unroll
       for (int j = 0; j < kWPer; ++j) buf_lds(rw, ws + j * kThreads, 16, woff[j], c * 32);
-#pragma unroll
-      for (int j = 0; j < kSPer; ++j) buf_lds(rs, ss + j * kThreads, 4, soff[j], c * 4);
       return;
     }
 #pragma unroll
@@ -507,8 +508,25 @@ __global__ __launch_bounds__(WN * WM * 64, kBlocksPerCu) void expert_wide_kernel
     g = g < kgroups ? g : g - 1;
 #pragma unroll
     for (int j = 0; j < kWPer; ++j) load_lds16(wsrc[j] + (size_t)g * 16, ws + j * kThreads);
-#pragma unroll
-    for (int j = 0; j < kSPer; ++j) load_lds4(ssrc[j] + 4 * c, ss + j * kThreads);
+  };
+  // NVFP4: first chunk of scale group g in the ring (the last group re-reads
+  // earlier chunks so that its four dwords stay in the row)
+  auto group_start = [&](int g) { return max(0, min(4 * g, nchunks - 4)); };
+  // part j of scale group g into its ring slot (g & 1); lane l of the wave
+  // lands at dword wave*64 + l (+ j*threads) of the slot: row (that index)/4
+  auto issue_scales = [&](int g, int j) {
+    uint32_t* const dst = reinterpret_cast<uint32_t*>(sst + (g & 1) * (BN * 16)) + j * kThreads + wave * 64;
+    const int c0 = group_start(g);
+    if constexpr (!kTail) {
+      // rows past N read past the expert's scale range (zero; their outputs
+      // are dropped) or another of its rows (split layout)
+      const int step = (split ? kThreads / 8 : kThreads / 4) * (K >> 4);  // part j+1: rows kThreads/4 further
+      buf_lds(rs, dst, 4, w13_row(sq0, N, split) * (K >> 4) + 4 * sdw, j * step + 4 * c0);
+    } else {
+      const int r = sq0 + j * (kThreads / 4);
+      const int wr = w13_row(r < N ? r : N - 1, N, split);
+      load_lds4(args.wscales + ((size_t)e * N + wr) * (size_t)(K >> 4) + 4 * (c0 + sdw), dst);
+    }
   };
 
   // a job's lane quantities and LDS read positions, derived for every job
@@ -526,8 +544,9 @@ __global__ __launch_bounds__(WN * WM * 64, kBlocksPerCu) void expert_wide_kernel
     half = l >> 5;
     lrow = l & 31;
     wslot0 = (wn * RN * 32 + lrow) * 2 + half;
-    // NVFP4: byte offset of this lane's two scale bytes (group 2c + half) in a stage's scale dwords
-    nvs0 = (wn * RN * 32 + lrow) * 4 + 2 * half;
+    // NVFP4: byte offset in a ring slot of this lane's two scale bytes (group 2c + half) of its
+    // first row, chunk 0 of the slot's group
+    nvs0 = (wn * RN * 32 + lrow) * 16 + 2 * half;
     srow = sst + staged_row(wn * RN * 32 + lrow, min(BN, N - ntile * BN), split) * kgroups;
     n_wave = ntile * BN + wn * RN * 32;
     live = WM == 1 || m_wave < count;  // wave-uniform; a tile holds at least one pair
@@ -590,8 +609,9 @@ __global__ __launch_bounds__(WN * WM * 64, kBlocksPerCu) void expert_wide_kernel
   };
   auto read_scale = [&](int c, int st, int rb) -> uint32_t {
     if (kNv) {
-      const uint8_t* ss = reinterpret_cast<const uint8_t*>(arena + st * kStage + kXSlots + kWSlots);
-      return *reinterpret_cast<const uint16_t*>(ss + nvs0 + rb * 128);
+      const int g = c >> 2;
+      const uint8_t* ss = sst + (g & 1) * (BN * 16) + 4 * (c - group_start(g));
+      return *reinterpret_cast<const uint16_t*>(ss + nvs0 + rb * 512);
     }
     const int g = 2 * c + half;
     return srow[rb * rb_stride + (!kTail || g < kgroups ? g : g - 1)];
@@ -600,7 +620,6 @@ __global__ __launch_bounds__(WN * WM * 64, kBlocksPerCu) void expert_wide_kernel
   auto issue_one = [&](int c, int st, int k) {
     c = c < nchunks ? c : nchunks - 1;
     u32x4* xs = arena + st * kStage + wave * 64;
-    uint32_t* const ss = reinterpret_cast<uint32_t*>(arena + st * kStage + kXSlots + kWSlots) + wave * 64;
     if (k < kXPer) {
       if (!kTail) {
         buf_lds(rx, xs + k * kThreads, 16, xoff[k], c * 128);
@@ -608,7 +627,7 @@ __global__ __launch_bounds__(WN * WM * 64, kBlocksPerCu) void expert_wide_kernel
         const int koff = c * 64 + xcol[k] < K ? c * 64 : c * 64 - 32;
         load_lds16(xsrc[k] + koff, xs + k * kThreads);
       }
-    } else if (k < kXPer + kWPer) {
+    } else {
       if (!kTail) {
         buf_lds(rw, xs + kXSlots + (k - kXPer) * kThreads, 16, woff[k - kXPer], c * 32);
       } else {
@@ -616,10 +635,6 @@ __global__ __launch_bounds__(WN * WM * 64, kBlocksPerCu) void expert_wide_kernel
         g = g < kgroups ? g : g - 1;
         load_lds16(wsrc[k - kXPer] + (size_t)g * 16, xs + kXSlots + (k - kXPer) * kThreads);
       }
-    } else {
-      const int j = k - kXPer - kWPer;
-      if (!kTail) buf_lds(rs, ss + j * kThreads, 4, soff[j], c * 4);
-      else load_lds4(ssrc[j] + 4 * c, ss + j * kThreads);
     }
   };
   // LDS read j of chunk c's operands (weights, scale bytes, token fragments) from stage st
@@ -658,6 +673,10 @@ __global__ __launch_bounds__(WN * WM * 64, kBlocksPerCu) void expert_wide_kernel
   setup_rows();
   if (!kNv) stage_scales<BN, kThreads, true>(sst, args.wscales, args.N, e, ntile, kgroups, t, split);
   if (bias_lds) stage_bias();
+  if constexpr (kNv) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) issue_scales(0, j);
+  }
   issue(0, kNext);
   auto issue_rest = [&]() { issue(1, (1 + kNext) % kStages); };  // the job's second chunk
   issue_rest();
@@ -674,12 +693,17 @@ __global__ __launch_bounds__(WN * WM * 64, kBlocksPerCu) void expert_wide_kernel
       }
       if constexpr (kStages == 2) lds_reads_then_barrier();  // chunk c+2 overwrites chunk c
       if (live) {
+        // NVFP4: part c%4 of the next scale group first, so that the
+        // waits, which leave the last kLoads loads in flight, cover it
+        constexpr int kIssue = kLoads + (kNv ? 1 : 0);
         constexpr int kMfma = 4 * RN * RM;
-        constexpr int kEvery = kMfma / kLoads >= 2 ? 2 : 1;
-        static_assert(kEvery * kLoads <= kMfma, "room between the MFMAs");
+        constexpr int kEvery = kMfma / kIssue >= 2 ? 2 : 1;
+        static_assert(kEvery * kIssue <= kMfma, "room between the MFMAs");
         auto extra = [&](int k) {
-          if (k % kEvery != 0 || k / kEvery >= kLoads) return;
-          issue_one(c + 2, (st + 2) % kStages, k / kEvery);
+          if (k % kEvery != 0 || k / kEvery >= kIssue) return;
+          const int i = k / kEvery;
+          if (kNv && i == 0) issue_scales((c >> 2) + 1, c & 3);
+          else issue_one(c + 2, (st + 2) % kStages, i - (kNv ? 1 : 0));
           __builtin_amdgcn_sched_barrier(0);
         };
         const bool glive = !kTail || 2 * c + half < kgroups;
@@ -697,6 +721,7 @@ __global__ __launch_bounds__(WN * WM * 64, kBlocksPerCu) void expert_wide_kernel
         }
         chunk_mma_regs<RN, RM, kNv, kF16In>(acc, cur.b, w, sc, sc_hi, extra, mt, mt_hi);
       } else {
+        if constexpr (kNv) issue_scales((c >> 2) + 1, c & 3);
         issue(c + 2, (st + 2) % kStages);
       }
     };
@@ -754,7 +779,7 @@ hipError_t launch_wide(const mxfp4moe::GemmArgs& a, hipStream_t stream) {
   // first loads fly during the previous job's epilogue
   long grid = (blocks + kXcds - 1) / kXcds * kXcds;
   const long cus = (long)mxfp4moe::device_cu_count() / kXcds * kXcds;
-  constexpr int kStage16 = (WM * RM * 32) * 8 + BN * 2 + (kNv ? BN / 4 : 0);  // the kernel's kStage
+  constexpr int kStage16 = (WM * RM * 32) * 8 + BN * 2;  // the kernel's kStage
   constexpr bool kPersistent = wide_persistent<WN, WM, RN, RM, kGateUp, kBlocksPerCu, kStage16>();
   if (fast && kPersistent && cus >= kXcds && grid > cus) grid = cus;
   if (fast)
