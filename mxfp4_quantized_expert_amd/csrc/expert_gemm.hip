@@ -371,14 +371,16 @@ __global__ __launch_bounds__(WN * WM * 64, kBlocksPerCu) void expert_wide_kernel
   constexpr int kXPer = kXSlots / kThreads;
   constexpr int kWPer = kWSlots / kThreads;
   static_assert(kXSlots % kThreads == 0 && kWSlots % kThreads == 0, "tile / thread mismatch");
-  // NVFP4 scales: a row's four scale bytes of a chunk are one dword, and the
-  // dwords of four chunks in a row are 16 contiguous bytes.  They travel in
-  // groups of four chunks into a ring of two slots of BN rows x 16 bytes,
-  // four lanes per row (one 16-byte piece per row and line, instead of one
-  // line per row and chunk), one quarter of the next group with each chunk.
-  static_assert(!kNv || BN * 4 == 4 * kThreads, "NVFP4: one scale dword per thread and chunk");
-  constexpr int kRing = kNv ? 2 * BN * 16 : 0;
   constexpr int kStages = kStageCount;  // LDS stages (see above)
+  // NVFP4 scales: a row's four scale bytes of a chunk are one dword, and the
+  // dwords of consecutive chunks in a row are contiguous.  They travel in
+  // groups of kSG chunks (4 beside three stages, 8 beside two) into a ring of
+  // two slots of BN rows x 4*kSG bytes, kSG lanes per row (one 4*kSG-byte
+  // piece per row and line, instead of one line per row and chunk), one
+  // kSG-th of the next group with each chunk.
+  constexpr int kSG = kStages == 2 ? 8 : 4;
+  static_assert(!kNv || BN == kThreads, "NVFP4: one scale dword per thread and chunk");
+  constexpr int kRing = kNv ? 2 * BN * 4 * kSG : 0;
   static_assert(kStages == 2 || kStages == 3, "two or three stages");
   constexpr int kLoads = kXPer + kWPer;  // operand loads per thread per chunk
   constexpr int kStage = kXSlots + kWSlots;  // 16-byte slots per stage
@@ -462,12 +464,12 @@ __global__ __launch_bounds__(WN * WM * 64, kBlocksPerCu) void expert_wide_kernel
       if constexpr (kTail) wsrc[j] = args.wblocks + ((size_t)e * N + wr) * (size_t)(K >> 1);
       else woff[j] = wr * (K >> 1) + 16 * wh;
     }
-    // NVFP4 scale part j of a group: row t/4 + j*threads/4 of the block,
-    // dword t%4 of the group's four (fewer than four chunks: the dwords past
-    // the row's last re-read it)
+    // NVFP4 scale part j of a group: row t/kSG + j*threads/kSG of the
+    // block, dword t%kSG of the group's kSG (fewer than kSG chunks: the
+    // dwords past the row's last re-read it)
     if constexpr (kNv) {
-      sq0 = ntile * BN + (t >> 2);
-      sdw = min(t & 3, nchunks - 1);
+      sq0 = ntile * BN + t / kSG;
+      sdw = min(t % kSG, nchunks - 1);
     }
     if constexpr (!kTail) {
       rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(args.wblocks + (size_t)e * N * (K >> 1)), (short)0,
@@ -510,20 +512,21 @@ __global__ __launch_bounds__(WN * WM * 64, kBlocksPerCu) void expert_wide_kernel
     for (int j = 0; j < kWPer; ++j) load_lds16(wsrc[j] + (size_t)g * 16, ws + j * kThreads);
   };
   // NVFP4: first chunk of scale group g in the ring (the last group re-reads
-  // earlier chunks so that its four dwords stay in the row)
-  auto group_start = [&](int g) { return max(0, min(4 * g, nchunks - 4)); };
+  // earlier chunks so that its kSG dwords stay in the row)
+  auto group_start = [&](int g) { return max(0, min(kSG * g, nchunks - kSG)); };
   // part j of scale group g into its ring slot (g & 1); lane l of the wave
-  // lands at dword wave*64 + l (+ j*threads) of the slot: row (that index)/4
+  // lands at dword wave*64 + l (+ j*threads) of the slot: row (that index)/kSG
   auto issue_scales = [&](int g, int j) {
-    uint32_t* const dst = reinterpret_cast<uint32_t*>(sst + (g & 1) * (BN * 16)) + j * kThreads + wave * 64;
+    uint32_t* const dst =
+        reinterpret_cast<uint32_t*>(sst + (g & 1) * (BN * 4 * kSG)) + j * kThreads + wave * 64;
     const int c0 = group_start(g);
     if constexpr (!kTail) {
       // rows past N read past the expert's scale range (zero; their outputs
       // are dropped) or another of its rows (split layout)
-      const int step = (split ? kThreads / 8 : kThreads / 4) * (K >> 4);  // part j+1: rows kThreads/4 further
+      const int step = (split ? kThreads / (2 * kSG) : kThreads / kSG) * (K >> 4);  // part j+1's rows
       buf_lds(rs, dst, 4, w13_row(sq0, N, split) * (K >> 4) + 4 * sdw, j * step + 4 * c0);
     } else {
-      const int r = sq0 + j * (kThreads / 4);
+      const int r = sq0 + j * (kThreads / kSG);
       const int wr = w13_row(r < N ? r : N - 1, N, split);
       load_lds4(args.wscales + ((size_t)e * N + wr) * (size_t)(K >> 4) + 4 * (c0 + sdw), dst);
     }
@@ -546,7 +549,7 @@ __global__ __launch_bounds__(WN * WM * 64, kBlocksPerCu) void expert_wide_kernel
     wslot0 = (wn * RN * 32 + lrow) * 2 + half;
     // NVFP4: byte offset in a ring slot of this lane's two scale bytes (group 2c + half) of its
     // first row, chunk 0 of the slot's group
-    nvs0 = (wn * RN * 32 + lrow) * 16 + 2 * half;
+    nvs0 = (wn * RN * 32 + lrow) * (4 * kSG) + 2 * half;
     srow = sst + staged_row(wn * RN * 32 + lrow, min(BN, N - ntile * BN), split) * kgroups;
     n_wave = ntile * BN + wn * RN * 32;
     live = WM == 1 || m_wave < count;  // wave-uniform; a tile holds at least one pair
@@ -609,9 +612,9 @@ __global__ __launch_bounds__(WN * WM * 64, kBlocksPerCu) void expert_wide_kernel
   };
   auto read_scale = [&](int c, int st, int rb) -> uint32_t {
     if (kNv) {
-      const int g = c >> 2;
-      const uint8_t* ss = sst + (g & 1) * (BN * 16) + 4 * (c - group_start(g));
-      return *reinterpret_cast<const uint16_t*>(ss + nvs0 + rb * 512);
+      const int g = c / kSG;
+      const uint8_t* ss = sst + (g & 1) * (BN * 4 * kSG) + 4 * (c - group_start(g));
+      return *reinterpret_cast<const uint16_t*>(ss + nvs0 + rb * (32 * 4 * kSG));
     }
     const int g = 2 * c + half;
     return srow[rb * rb_stride + (!kTail || g < kgroups ? g : g - 1)];
@@ -675,7 +678,7 @@ __global__ __launch_bounds__(WN * WM * 64, kBlocksPerCu) void expert_wide_kernel
   if (bias_lds) stage_bias();
   if constexpr (kNv) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) issue_scales(0, j);
+    for (int j = 0; j < kSG; ++j) issue_scales(0, j);
   }
   issue(0, kNext);
   auto issue_rest = [&]() { issue(1, (1 + kNext) % kStages); };  // the job's second chunk
@@ -693,7 +696,7 @@ __global__ __launch_bounds__(WN * WM * 64, kBlocksPerCu) void expert_wide_kernel
       }
       if constexpr (kStages == 2) lds_reads_then_barrier();  // chunk c+2 overwrites chunk c
       if (live) {
-        // NVFP4: part c%4 of the next scale group first, so that the
+        // NVFP4: part c%kSG of the next scale group first, so that the
         // waits, which leave the last kLoads loads in flight, cover it
         constexpr int kIssue = kLoads + (kNv ? 1 : 0);
         constexpr int kMfma = 4 * RN * RM;
@@ -702,7 +705,7 @@ __global__ __launch_bounds__(WN * WM * 64, kBlocksPerCu) void expert_wide_kernel
         auto extra = [&](int k) {
           if (k % kEvery != 0 || k / kEvery >= kIssue) return;
           const int i = k / kEvery;
-          if (kNv && i == 0) issue_scales((c >> 2) + 1, c & 3);
+          if (kNv && i == 0) issue_scales(c / kSG + 1, c % kSG);
           else issue_one(c + 2, (st + 2) % kStages, i - (kNv ? 1 : 0));
           __builtin_amdgcn_sched_barrier(0);
         };
@@ -721,7 +724,7 @@ __global__ __launch_bounds__(WN * WM * 64, kBlocksPerCu) void expert_wide_kernel
         }
         chunk_mma_regs<RN, RM, kNv, kF16In>(acc, cur.b, w, sc, sc_hi, extra, mt, mt_hi);
       } else {
-        if constexpr (kNv) issue_scales((c >> 2) + 1, c & 3);
+        if constexpr (kNv) issue_scales(c / kSG + 1, c % kSG);
         issue(c + 2, (st + 2) % kStages);
       }
     };
