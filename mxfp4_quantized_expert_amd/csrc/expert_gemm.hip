@@ -340,9 +340,9 @@ __device__ __forceinline__ void store_epilogue(const mxfp4moe::GemmArgs& args, c
 // block or as two blocks of four waves per CU, whose epilogues, barriers
 // and conversions then also run beside the other block's MFMAs.
 // kNv: NVFP4 weights (E4M3 block scales per 16 codes, K a multiple of 64).  A
-// chunk's four scale bytes of a row are one aligned dword; each stage holds
-// them for the block's rows (one 4-byte global -> LDS load per row), in place
-// of the MXFP4 path's table of whole scale rows.
+// chunk's four scale bytes of a row are one aligned dword; they reach LDS
+// through a two-slot ring in groups of consecutive chunks (described in the
+// kernel), in place of the MXFP4 path's table of whole scale rows.
 // kTail: the general form, for any K (a multiple of 32): when K is not a
 // multiple of 64 the last chunk holds one group, whose missing group re-reads
 // the one before and multiplies zeroed weights; operands are addressed by
@@ -552,7 +552,12 @@ __global__ __launch_bounds__(WN * WM * 64, kBlocksPerCu) void expert_wide_kernel
     nvs0 = (wn * RN * 32 + lrow) * (4 * kSG) + 2 * half;
     srow = sst + staged_row(wn * RN * 32 + lrow, min(BN, N - ntile * BN), split) * kgroups;
     n_wave = ntile * BN + wn * RN * 32;
-    live = WM == 1 || m_wave < count;  // wave-uniform; a tile holds at least one pair
+    // wave-uniform: the wave holds some of the tile's pairs (a tile holds at
+    // least one) and some rows below N (the last row tile of a GEMM leaves
+    // whole waves past N: they issue their share of the loads but convert
+    // and multiply nothing; 3-5 us less for the down GEMM's full tiles of a
+    // 4096-token gpt-oss-120b prefill)
+    live = (WM == 1 || m_wave < count) && n_wave < N;
   };
   const int rb_stride = (split ? 16 : 32) * kgroups;
 
