@@ -1297,27 +1297,30 @@ hipError_t launch_stream(const mxfp4moe::GemmArgs& a, hipStream_t stream) {
 // group 4c+q of row r, step s its codes [8s, 8s+8), so K = 128c + 32q + 8s + i;
 // B: the same K values of token l%16).  A block owns 128 weight rows (four
 // waves of 2 x 16 rows) and up to 48 tokens (three 16-token column blocks).  K
-// runs in panels of one chunk (128 K); both operands of a panel are staged in
-// LDS: the block's 128 weight rows as 64 contiguous bytes per row (four lanes
-// per row: the pattern HBM streams at full rate) and the tile's token rows as
-// 256 bytes each.  A panel's loads go to one of three register slots, so three
-// panels are in flight while one runs from LDS: per panel, after its MFMAs and
-// a barrier, the next panel's slot is stored to the (single) LDS buffer, the
-// slot is refilled with the panel three ahead, and a second barrier makes the
-// stored panel visible.  The token bytes of a panel (at most 12 KB, from L2)
-// are at most 1.5 times its weight bytes (8 KB, from HBM), which is what lets
-// three panels fit in registers at three blocks per CU (with 64-token tiles
-// only two did).  The loop body is
-// three panels of straight-line code with the same loads in flight at entry
-// and at the back edge (the compiler then waits for each slot alone); panels
-// past the last re-read the last one (in bounds, never computed).  Token rows
-// past the tile's pairs re-read its first pair (their outputs are dropped).
+// runs in panels of one chunk (128 K).  Each wave loads its own weights
+// straight into the A operand's registers (lane (r, q) the 16 bytes of group
+// 4c+q of its row: the four lanes of a row read its 64 contiguous bytes of
+// the panel, the pattern HBM streams at full rate); the tile's token rows
+// (256 bytes each per panel) are shared by the four waves through LDS.  Three
+// register slots each hold the loads of one panel's weights (used by that
+// panel's MFMAs, then refilled with the panel three ahead) and one panel's
+// tokens (stored to the single LDS token buffer a panel before they are
+// used, then refilled): per panel, after its MFMAs and a barrier, the next
+// panel's tokens are stored, their slot refilled, and a second barrier makes
+// them visible.  The token bytes of a panel (at most 12 KB, from L2) are at
+// most 1.5 times its weight bytes (8 KB, from HBM), which is what lets three
+// panels fit in registers at three blocks per CU (with 64-token tiles only
+// two did).  The loop body is three panels of straight-line code with the
+// same loads in flight at entry and at the back edge (the compiler then waits
+// for each slot alone); panels past the last re-read the last one (in
+// bounds, never computed).  Token rows past the tile's pairs re-read its
+// first pair (their outputs are dropped).
 //
-// Dynamic LDS: tokens [48][256 + 16] | weights [128][64 + 16] | scales [128][K/32]
-// (the 16-byte row pads make the 16-lane column reads conflict-free).
+// Dynamic LDS: tokens [48][256 + 16] | scales [128][K/32] (the 16-byte row
+// pad makes the 16-lane column reads conflict-free).
 template <bool kNv = false>
 __host__ __device__ constexpr size_t mid_lds_bytes(int K) {
-  return (size_t)mxfp4moe::kMidTokens * (256 + 16) + (size_t)128 * (64 + 16) + (size_t)128 * (K / (kNv ? 16 : 32));
+  return (size_t)mxfp4moe::kMidTokens * (256 + 16) + (size_t)128 * (K / (kNv ? 16 : 32));
 }
 
 template <bool kGateUp, bool kNv>
@@ -1328,12 +1331,9 @@ __global__ __launch_bounds__(256, 2) void expert_mid_kernel(mxfp4moe::GemmArgs a
   constexpr int kCB = BM / 16;  // 16-token column blocks
   static_assert(BM % 16 == 0 && kCB <= 4, "16-token column blocks");
   constexpr int kXRow = 256 + 16;     // LDS bytes per token row of a panel
-  constexpr int kWRow = 64 + 16;      // LDS bytes per weight row of a panel
   constexpr int kXPieces = 16;        // 16-byte pieces per token row of a panel
-  constexpr int kWPieces = 4;         // 16-byte pieces per weight row of a panel
   constexpr int kXPer = BM * kXPieces / kThreads;
-  constexpr int kWPer = BN * kWPieces / kThreads;
-  static_assert(BM * kXPieces % kThreads == 0 && BN * kWPieces % kThreads == 0, "panel / thread mismatch");
+  static_assert(BM * kXPieces % kThreads == 0 && BN == 4 * 32, "panel / thread mismatch");
   extern __shared__ u32x4 dyn[];
   uint8_t* const lds = reinterpret_cast<uint8_t*>(dyn);
 
@@ -1356,8 +1356,7 @@ __global__ __launch_bounds__(256, 2) void expert_mid_kernel(mxfp4moe::GemmArgs a
   const int lr = lane & 15;
 
   uint8_t* const xs = lds;
-  uint8_t* const ws = lds + BM * kXRow;
-  uint8_t* const sl = ws + BN * kWRow;
+  uint8_t* const sl = lds + BM * kXRow;
   const bool split = kGateUp && args.split_gate_up;  // uniform
   stage_scales<BN, kThreads>(sl, args.wscales, args.N, e, ntile, kNv ? 2 * kgroups : kgroups, t, split);
 
@@ -1375,25 +1374,28 @@ __global__ __launch_bounds__(256, 2) void expert_mid_kernel(mxfp4moe::GemmArgs a
     xpiece[j] = i - r * kXPieces;
     xdst[j] = r * kXRow + xpiece[j] * 16;
   }
-  const u32x4* wsrc[kWPer];
-  int wpiece[kWPer], wdst[kWPer];
+  // weights straight into the MFMA's A operand: lane (lr, q) of row block rb
+  // loads group 4p + q of its row (the four lanes of a row read its 64
+  // contiguous bytes of the panel; rows past N re-read row N-1)
+  const u32x4* wsrc[2];
 #pragma unroll
-  for (int j = 0; j < kWPer; ++j) {
-    const int i = t + j * kThreads;
-    const int r = i / kWPieces;
-    const int gr = w13_row(min(ntile * BN + r, N - 1), N, split);
-    wsrc[j] = reinterpret_cast<const u32x4*>(args.wblocks + ((size_t)e * N + gr) * (size_t)(K >> 1));
-    wpiece[j] = i - r * kWPieces;
-    wdst[j] = r * kWRow + wpiece[j] * 16;
+  for (int rb = 0; rb < 2; ++rb) {
+    const int gr = w13_row(min(ntile * BN + wave * 32 + rb * 16 + lr, N - 1), N, split);
+    wsrc[rb] = reinterpret_cast<const u32x4*>(args.wblocks + ((size_t)e * N + gr) * (size_t)(K >> 1)) + q;
   }
-  // Three register slots of panel loads.  Groups / pieces past the end
-  // re-read the last one (finite; the weights of a missing group are zeroed
-  // at use); panels past the last re-read the last panel.
-  u32x4 xv[3][kXPer], wv[3][kWPer];
-  auto issue = [&](int p, int sl3) {
+  // Three register slots of panel loads each for the weights (consumed by a
+  // panel's MFMAs) and the tokens (consumed when stored to LDS, a panel
+  // earlier).  Groups / pieces past the end re-read the last one (finite;
+  // the weights of a missing group are zeroed at use); panels past the last
+  // re-read the last panel.
+  u32x4 xv[3][kXPer], wv[3][2];
+  auto issue_w = [&](int p, int sl3) {
     p = min(p, npanels - 1);
 #pragma unroll
-    for (int j = 0; j < kWPer; ++j) wv[sl3][j] = wsrc[j][min(p * kWPieces + wpiece[j], kg16 - 1)];
+    for (int rb = 0; rb < 2; ++rb) wv[sl3][rb] = wsrc[rb][min(4 * p, kg16 - 1 - q)];
+  };
+  auto issue_x = [&](int p, int sl3) {
+    p = min(p, npanels - 1);
 #pragma unroll
     for (int j = 0; j < kXPer; ++j) xv[sl3][j] = xsrc[j][min(p * kXPieces + xpiece[j], k16 - 1)];
   };
@@ -1402,19 +1404,14 @@ __global__ __launch_bounds__(256, 2) void expert_mid_kernel(mxfp4moe::GemmArgs a
   // and their uses
   auto commit = [&](int sl3) {
 #pragma unroll
-    for (int j = 0; j < kWPer; ++j) *reinterpret_cast<u32x4*>(ws + wdst[j]) = wv[sl3][j];
-#pragma unroll
     for (int j = 0; j < kXPer; ++j) *reinterpret_cast<u32x4*>(xs + xdst[j]) = xv[sl3][j];
   };
 
   const int n_wave = ntile * BN + wave * 32;
   const uint8_t* srow[2];
-  int wrd[2];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < 2; ++rb)
     srow[rb] = sl + staged_row(wave * 32 + rb * 16 + lr, min(BN, N - ntile * BN), split) * (kNv ? 2 : 1) * kgroups;
-    wrd[rb] = (wave * 32 + rb * 16 + lr) * kWRow + 16 * q;
-  }
   const int ncb = (count + 15) >> 4;  // live 16-token column blocks
   int xrd[kCB];  // LDS byte offset of this lane's token row for each column block
 #pragma unroll
@@ -1428,18 +1425,17 @@ __global__ __launch_bounds__(256, 2) void expert_mid_kernel(mxfp4moe::GemmArgs a
 #pragma unroll
     for (int cb = 0; cb < kCB; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // the MFMAs of panel p from LDS
-  auto compute = [&](int p) {
+  // the MFMAs of panel p: weights from register slot sl3, tokens from LDS
+  auto compute = [&](int p, int sl3) {
     const int g0 = 4 * p + q;
     const bool glive = g0 < kgroups;
     const int g = glive ? g0 : kgroups - 1;
     u32x4 a[2][4];  // [rb][step] converted A fragments
-    // both row blocks' weight fragments and scale bytes read together
-    u32x4 wr[2];
+    // both row blocks' scale bytes read together
+    const u32x4* const wr = wv[sl3];
     uint32_t sb[2][2];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-      wr[rb] = *reinterpret_cast<const u32x4*>(ws + wrd[rb]);
       sb[rb][0] = kNv ? srow[rb][2 * g] : srow[rb][g];
       sb[rb][1] = kNv ? srow[rb][2 * g + 1] : 0u;
     }
@@ -1469,36 +1465,40 @@ __global__ __launch_bounds__(256, 2) void expert_mid_kernel(mxfp4moe::GemmArgs a
       }
     }
   };
-  // after the MFMAs of a panel: every wave is done with the LDS buffer, the
-  // next panel's slot `nx` is stored, refilled with panel `ahead`, and the
+  // after the MFMAs of panel p (weights from slot p % 3, now free: refilled
+  // with panel p + 3): every wave is done with the LDS buffer, the next
+  // panel's token slot `nx` is stored, refilled with panel `ahead`, and the
   // stored panel made visible
-  auto advance = [&](int nx, int ahead) {
+  auto advance = [&](int p, int nx, int ahead) {
+    issue_w(p + 3, p % 3);
     __syncthreads();
     commit(nx);
-    issue(ahead, nx);
+    issue_x(ahead, nx);
     __syncthreads();
   };
 
-  issue(0, 0);
-  issue(1, 1);
-  issue(2, 2);
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    issue_w(j, j);
+    issue_x(j, j);
+  }
   commit(0);
-  issue(3, 0);
-  __syncthreads();  // panel 0 and the scale rows staged; panels 1, 2, 3 in flight
+  issue_x(3, 0);
+  __syncthreads();  // panel 0's tokens and the scale rows staged; panels 1, 2, 3 in flight
   int p = 0;
   for (; p + 3 <= npanels; p += 3) {
-    compute(p);
-    advance(1, p + 4);
-    compute(p + 1);
-    advance(2, p + 5);
-    compute(p + 2);
-    advance(0, p + 6);
+    compute(p, 0);
+    advance(p, 1, p + 4);
+    compute(p + 1, 1);
+    advance(p + 1, 2, p + 5);
+    compute(p + 2, 2);
+    advance(p + 2, 0, p + 6);
   }
   // the last one or two panels (slots 0 and 1 hold them, in order)
-  if (p < npanels) compute(p);
+  if (p < npanels) compute(p, 0);
   if (p + 1 < npanels) {
-    advance(1, p + 4);
-    compute(p + 1);
+    advance(p, 1, p + 4);
+    compute(p + 1, 1);
   }
 
   if (n_wave >= N) return;
