@@ -1381,7 +1381,7 @@ __global__ __launch_bounds__(256, 2) void expert_mid_kernel(mxfp4moe::GemmArgs a
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
     const int gr = w13_row(min(ntile * BN + wave * 32 + rb * 16 + lr, N - 1), N, split);
-    wsrc[rb] = reinterpret_cast<const u32x4*>(args.wblocks + ((size_t)e * N + gr) * (size_t)(K >> 1)) + q;
+    wsrc[rb] = reinterpret_cast<const u32x4*>(args.wblocks + ((size_t)e * N + gr) * (size_t)(K >> 1));
   }
   // Three register slots of panel loads each for the weights (consumed by a
   // panel's MFMAs) and the tokens (consumed when stored to LDS, a panel
@@ -1392,7 +1392,7 @@ __global__ __launch_bounds__(256, 2) void expert_mid_kernel(mxfp4moe::GemmArgs a
   auto issue_w = [&](int p, int sl3) {
     p = min(p, npanels - 1);
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) wv[sl3][rb] = wsrc[rb][min(4 * p, kg16 - 1 - q)];
+    for (int rb = 0; rb < 2; ++rb) wv[sl3][rb] = wsrc[rb][min(4 * p + q, kg16 - 1)];
   };
   auto issue_x = [&](int p, int sl3) {
     p = min(p, npanels - 1);
