@@ -82,6 +82,20 @@ def test_tile_boundaries(gpu):
     assert_layer_parity(_forward(gpu, L, 1), O.moe_forward_nvfp4(L, 1), "nvfp4 tile boundaries")
 
 
+def test_scale_bytes_full_range(gpu):
+    # every finite E4M3 value as a block scale (both signs, the subnormals and
+    # zero) on experts with full, mid and streaming tiles: the full tiles' f16
+    # down GEMM builds code x scale from the scale's power of two and its
+    # significand, exact for all of them, as the bf16 tiles' float32 product is
+    counts = [259, 128, 130, 60, 17, 3, 1, 0]
+    L = _owned_layer(counts, H=128, I=192, seed=71)
+    rng = np.random.default_rng(72)
+    finite = np.array([b for b in range(256) if b & 0x7F != 0x7F], dtype=np.uint8)
+    for k in ("w13_scales", "w2_scales"):
+        L[k] = rng.choice(finite, size=L[k].shape)
+    assert_layer_parity(_forward(gpu, L, 1), O.moe_forward_nvfp4(L, 1), "nvfp4 full-range scale bytes")
+
+
 def test_nan_scale_byte(gpu):
     # E4M3 NaN scale bytes (0x7F, 0xFF) in one block of a gate_up row and of a
     # down row of an expert on each kind of tile (full, mid, streaming): the
