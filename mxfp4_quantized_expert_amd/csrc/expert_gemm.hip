@@ -615,7 +615,7 @@ __global__ __launch_bounds__(WN * WM * 64, kBlocksPerCu) void expert_wide_kernel
     uint32_t sb[RN];  // E8M0 scale byte (NVFP4: the group's two E4M3 bytes, low byte first)
     bf16x8 b[4][RM];
   };
-  auto read_scale = [&](int c, int st, int rb) -> uint32_t {
+  auto read_scale = [&](int c, int rb) -> uint32_t {
     if (kNv) {
       const int g = c / kSG;
       const uint8_t* ss = sst + (g & 1) * (BN * 4 * kSG) + 4 * (c - group_start(g));
@@ -653,7 +653,7 @@ __global__ __launch_bounds__(WN * WM * 64, kBlocksPerCu) void expert_wide_kernel
     if (j < RN) {
       o.w[j] = xs[kXSlots + wslot0 + j * 64];
     } else if (j < 2 * RN) {
-      o.sb[j - RN] = read_scale(c, st, j - RN);
+      o.sb[j - RN] = read_scale(c, j - RN);
     } else {
       const int s = (j - 2 * RN) / RM, cb = (j - 2 * RN) % RM;
       const int row = cb * 32 + lrow;
