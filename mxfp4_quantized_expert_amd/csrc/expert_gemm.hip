@@ -1548,7 +1548,9 @@ hipError_t launch_mid(const mxfp4moe::GemmArgs& a, hipStream_t stream) {
 }
 
 // y[t, n] = bf16(sum_j zw[t*k + j, n]) summed in fp32, j ascending, over the
-// bf16 pair outputs; eight features per thread.
+// bf16 pair outputs; eight features per thread.  kK > 0: top_k == kK, all k
+// rows loaded before the sum (one round trip instead of k); kK == 0: any k.
+template <int kK>
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ zw, uint16_t* __restrict__ y,
                                                       int T, int H, int top_k) {
   const int h8 = H >> 3;
@@ -1560,13 +1562,21 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
   float s[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) s[i] = 0.f;
-  for (int j = 0; j < top_k; ++j) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(src + (size_t)j * H);
+  auto add = [&](const u32x4& v) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       s[2 * i] += mx::bf16_to_f32(v[i] & 0xffffu);
       s[2 * i + 1] += mx::bf16_to_f32(v[i] >> 16);
     }
+  };
+  if constexpr (kK > 0) {
+    u32x4 v[kK];
+#pragma unroll
+    for (int j = 0; j < kK; ++j) v[j] = *reinterpret_cast<const u32x4*>(src + (size_t)j * H);
+#pragma unroll
+    for (int j = 0; j < kK; ++j) add(v[j]);
+  } else {
+    for (int j = 0; j < top_k; ++j) add(*reinterpret_cast<const u32x4*>(src + (size_t)j * H));
   }
   u32x4 o;
 #pragma unroll
@@ -1649,7 +1659,14 @@ hipError_t launch_combine(const uint16_t* zw, uint16_t* y, int T, int H, int top
   const size_t n = (size_t)T * (H / 8);
   if (n == 0) return hipSuccess;
   ProfileScope prof(kStageCombine, stream);
-  combine_kernel<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(zw, y, T, H, top_k);
+  const unsigned grid = (unsigned)((n + 255) / 256);
+  switch (top_k) {
+    case 1: combine_kernel<1><<<grid, 256, 0, stream>>>(zw, y, T, H, top_k); break;
+    case 2: combine_kernel<2><<<grid, 256, 0, stream>>>(zw, y, T, H, top_k); break;
+    case 4: combine_kernel<4><<<grid, 256, 0, stream>>>(zw, y, T, H, top_k); break;
+    case 8: combine_kernel<8><<<grid, 256, 0, stream>>>(zw, y, T, H, top_k); break;
+    default: combine_kernel<0><<<grid, 256, 0, stream>>>(zw, y, T, H, top_k); break;
+  }
   return hipGetLastError();
 }
 
