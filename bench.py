@@ -53,6 +53,28 @@ def layer_bytes(H, I, nvfp4=False):
     return w13, w2
 
 
+def tile_kinds(counts, T, H, I, E, k, nvfp4=False, act="bf16"):
+    """Which pairs each GEMM kernel takes, by the library's tile policy.
+
+    Returns (full_pairs, mid_pairs, mid_experts): pairs of the experts in
+    128-pair tiles, and pairs / experts on mid tiles.  Experts with at least
+    128 pairs take full tiles; the rest with more than 4 pairs mid tiles; the
+    rest one streaming tile.  Batches of 5..256 tokens with exact bf16
+    activations take no full tiles, and when they average at least 16 pairs
+    per expert no streaming tiles either; NVFP4 layers take full tiles only
+    when H and I are multiples of 64.
+    """
+    import numpy as np
+
+    counts = np.asarray(counts)
+    small = act == "bf16" and 4 < T <= 256
+    mid_only = small and T * k >= 16 * E
+    wide_tiles = (not nvfp4 or (H % 64 == 0 and I % 64 == 0)) and not small
+    full_pairs = int(counts[counts >= 128].sum()) if wide_tiles else 0
+    sel = (counts > 0) if mid_only else (counts > 4) & ((counts < 128) | (not wide_tiles))
+    return full_pairs, int(counts[sel].sum()), int(sel.sum())
+
+
 def measured_traffic(workload, kernel_tag):
     """HBM bytes per launch of a kernel from the committed rocprofv3 counter runs
     (FETCH_SIZE and WRITE_SIZE, each scaled by what it reads for a plain copy of
@@ -183,9 +205,7 @@ def run_moe(args):
     _, _, offsets, _ = binding.moe_mxfp4_route(dev["router_logits"], k)
     counts = np.diff(offsets.cpu().numpy().astype(np.int64))
     n_active = int((counts > 0).sum())
-    # NVFP4 layers take full tiles only when H and I are multiples of 64
-    wide_tiles = not nvfp4 or (H % 64 == 0 and I % 64 == 0)
-    full_pairs = int(counts[counts >= 128].sum()) if wide_tiles else 0  # pairs of the experts in 128-pair tiles
+    full_pairs, mid_pairs, mid_experts = tile_kinds(counts, T, H, I, E, k, nvfp4, args.act)
     w13_b, w2_b = layer_bytes(H, I, nvfp4)
     # Weight copies rotate so that repeated steps cannot be served from the
     # 256 MB Infinity Cache when the active weights would fit in it.
@@ -285,10 +305,6 @@ def run_moe(args):
     copy_gbs, _ = copy_bandwidth()
 
     flops_total = 6.0 * H * I * P
-    # Pairs of the experts that go to mid tiles (more than 4 pairs, below the
-    # wide threshold; every such expert when there are no full tiles).
-    mid_pairs = int(counts[(counts > 4) & ((counts < 128) | (not wide_tiles))].sum())
-    mid_experts = int(((counts > 4) & ((counts < 128) | (not wide_tiles))).sum())
     # The mid launch is priced against whichever roof is lower for its work:
     # its experts' packed w13 once from HBM, or 2*H*2I MFMA FLOPs per pair.
     mid_mfma = (dominant == "gate_up_mid" and
@@ -316,7 +332,7 @@ def run_moe(args):
     roof["traffic"] = measured_traffic(args.workload, dominant)
     roof["kernel"] = {"gate_up_wide": ("expert_fp4_kernel" if args.act != "bf16" else "expert_wide_kernel")
                                        + " (gate_up, full 128-pair tiles)",
-                      "gate_up_mid": "expert_mid_kernel (gate_up, tiles of 3..48 pairs)",
+                      "gate_up_mid": "expert_mid_kernel (gate_up, tiles of at most 48 pairs)",
                       "gate_up_stream": "expert_stream_kernel (gate_up, tiles of at most 4 pairs)"}[dominant]
     roof["kernel_ms"] = kms
     roof["algorithmic"] = per_unit

@@ -68,7 +68,7 @@ struct Layout {
 // With no wide tiles an expert with more than kStreamTokens pairs makes
 // ceil(c / kMidTokens) mid tiles.  With streaming tiles only, every pair goes
 // to tiles of kStreamTokens.
-enum TileMode { kTilesWide, kTilesNoWide, kTilesStreamOnly };
+enum TileMode { kTilesWide, kTilesNoWide, kTilesStreamOnly, kTilesMidOnly };
 TileBounds tile_bounds(int64_t T, int64_t P, int64_t E, TileMode mode) {
   const int64_t active = E < P ? E : P;
   const int64_t fulls = P / kWideTokens;
@@ -78,11 +78,11 @@ TileBounds tile_bounds(int64_t T, int64_t P, int64_t E, TileMode mode) {
   const int64_t mids = P / (kStreamTokens + 1);
   if (mode == kTilesWide)
     b.max_mid = T > kStreamTokens ? (int)(kMidPerExpert * active < mids ? kMidPerExpert * active : mids) : 0;
-  else if (mode == kTilesNoWide)
+  else if (mode == kTilesNoWide || mode == kTilesMidOnly)
     b.max_mid = T > kStreamTokens ? (int)(P / kMidTokens + active) : 0;
   else
     b.max_mid = 0;
-  b.max_small = mode == kTilesStreamOnly ? (int)(P / kStreamTokens + active) : (int)active;
+  b.max_small = mode == kTilesStreamOnly ? (int)(P / kStreamTokens + active) : mode == kTilesMidOnly ? 0 : (int)active;
   return b;
 }
 
@@ -226,10 +226,25 @@ int forward_impl(const uint16_t* x, const float* router_logits, const uint16_t* 
   // NVFP4 full tiles read a chunk's scales of a row as one aligned dword, so
   // they need H and I to be multiples of 64 (else mid tiles take those pairs)
   const bool nv_no_wide = nv && ((H & 63) != 0 || (I & 63) != 0);
-  tt.big_tokens = nv_no_wide || (flags & MXFP4MOE_TILES_STREAM) ? 0 : kWideTokens;
-  tt.no_wide = nv_no_wide ? 1 : 0;
-  const TileBounds tb =
-      tile_bounds(T, P, E, nv_no_wide ? kTilesNoWide : tt.big_tokens > 0 ? kTilesWide : kTilesStreamOnly);
+  // Small prefill batches (kStreamTokens < T <= kMidOnlyTokens, exact bf16
+  // activations): no full tiles, since an expert then holds at most two
+  // (its pairs take mid tiles of at most kMidTokens instead), and when the
+  // batch averages at least kMidOnlyPairsPerExpert pairs per expert no
+  // streaming tiles either (an expert with 1..kStreamTokens pairs takes one
+  // mid tile).  A launch whose table turns out empty still costs about as
+  // much as a launch of a few tiles, and the host cannot know the counts, so
+  // the kinds of tile a batch of this size seldom has get no launch at all.
+  const bool stream_only = (flags & MXFP4MOE_TILES_STREAM) != 0;
+  const bool small = act_mode == kActBf16 && !stream_only && T > kStreamTokens && T <= kMidOnlyTokens;
+  const bool mid_only = small && P >= kMidOnlyPairsPerExpert * E;
+  tt.no_wide = nv_no_wide || small ? 1 : 0;
+  tt.big_tokens = tt.no_wide || stream_only ? 0 : kWideTokens;
+  tt.no_stream = mid_only ? 1 : 0;
+  const TileBounds tb = tile_bounds(T, P, E,
+                                    mid_only             ? kTilesMidOnly
+                                    : tt.no_wide         ? kTilesNoWide
+                                    : tt.big_tokens > 0  ? kTilesWide
+                                                         : kTilesStreamOnly);
   hipStream_t s = (hipStream_t)stream;
 
   hipError_t err;

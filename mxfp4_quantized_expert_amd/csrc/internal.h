@@ -52,6 +52,11 @@ int device_cu_count();
 constexpr int kWideTokens = 128;
 constexpr int kStreamTokens = 4;
 constexpr int kMidTokens = 48;
+// Batches of kStreamTokens < T <= kMidOnlyTokens take no full tiles, and no
+// streaming tiles either when they average at least kMidOnlyPairsPerExpert
+// pairs per expert.
+constexpr int kMidOnlyTokens = 256;
+constexpr int kMidOnlyPairsPerExpert = 16;
 constexpr int kMaxHidden = 4096;  // bound on H and I (the GEMMs stage scale rows in LDS)
 
 struct TileTables {
@@ -63,6 +68,7 @@ struct TileTables {
   int32_t* num_small;
   int big_tokens;      // kWideTokens, or 0 (then: every pair in streaming tiles unless no_wide)
   int no_wide;         // no wide tiles: more than kStreamTokens pairs -> mid tiles, whatever the count
+  int no_stream;       // with no_wide: every expert with pairs -> mid tiles (no streaming tiles)
 };
 
 // Capacities of the tile tables (bounds the GEMM grids).

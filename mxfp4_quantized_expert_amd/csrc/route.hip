@@ -243,9 +243,10 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(const float* __res
         // fewer than bt, more than st: ceil(c / mt) mid tiles of near-equal
         // size (the first c % nm one pair larger); at most st: one streaming
         // tile; without full tiles (bt == 0) every pair in streaming tiles of st
+        // (no_stream: mid tiles for every expert with pairs)
         const int nb = (wide_on && c >= bt) ? (c + bt - 1) / bt : 0;
-        const int nm = (mid_on && c > st && (tt.no_wide || c < bt)) ? (c + mt - 1) / mt : 0;
-        const int ns = mid_on ? (c > 0 && c <= st ? 1 : 0) : (c + st - 1) / st;
+        const int nm = (mid_on && c > (tt.no_stream ? 0 : st) && (tt.no_wide || c < bt)) ? (c + mt - 1) / mt : 0;
+        const int ns = tt.no_stream ? 0 : mid_on ? (c > 0 && c <= st ? 1 : 0) : (c + st - 1) / st;
         const int ib = mx::wave_inclusive_sum(nb);
         const int im = mx::wave_inclusive_sum(nm);
         const int is = mx::wave_inclusive_sum(ns);

@@ -50,3 +50,24 @@ def test_traffic_reported_only_for_the_profiled_source(tmp_path):
     if os.path.exists(committed):
         rec = json.load(open(committed))
         assert {"source", "source_sha256", "kernels"} <= set(rec)
+
+
+def test_tile_kinds_follow_the_library_policy():
+    # Full 128-pair tiles for experts with >= 128 pairs in large batches; mid
+    # tiles for 5..127 pairs; one streaming tile for 1..4.  Batches of 5..256
+    # tokens take no full tiles, and no streaming tiles when they average at
+    # least 16 pairs per expert; NVFP4 needs H and I multiples of 64 for full tiles.
+    tk = _bench().tile_kinds
+    c = [200, 127, 5, 4, 0]
+    assert tk(c, 4096, 2880, 2880, 128, 4) == (200, 132, 2)
+    assert tk(c, 4096, 2880, 2880, 128, 4, act="mxfp8_split") == (200, 132, 2)
+    assert tk(c, 4096, 96, 2880, 128, 4, nvfp4=True) == (0, 332, 3)
+    assert tk(c, 4096, 128, 2880, 128, 4, nvfp4=True) == (200, 132, 2)
+    # 256 tokens x 4 over 32 experts: 32 pairs per expert on average -> mid tiles only
+    assert tk([130, 3, 0], 256, 2880, 2880, 32, 4) == (0, 133, 2)
+    # the same batch over 128 experts: 8 per expert -> streaming tiles stay
+    assert tk([130, 3, 0], 256, 2880, 2880, 128, 4) == (0, 130, 1)
+    # with MXFP8 activations small batches keep the full-tile launch
+    assert tk([130, 3, 0], 256, 2880, 2880, 32, 4, act="mxfp8") == (130, 0, 0)
+    # decode: streaming tiles only
+    assert tk([1, 2, 1], 4, 2880, 2880, 32, 4) == (0, 0, 0)

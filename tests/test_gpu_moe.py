@@ -214,6 +214,28 @@ def test_tile_boundaries(gpu, path):
     assert_layer_parity(y, O.moe_forward(L, 1), f"tile boundaries/{path}")
 
 
+@pytest.mark.parametrize("E,counts", [(8, [200, 4, 1, 17, 30, 3, 1, 0]), (16, [20, 49, 30, 16, 4, 5, 1, 0] * 2)])
+def test_small_batch_mid_tiles(gpu, E, counts):
+    # Batches of 5..256 tokens take no full tiles; averaging at least 16 pairs
+    # per expert they take no streaming tiles either, so an expert with 200
+    # pairs becomes five mid tiles and one with 1..4 pairs one mid tile.  The
+    # second case (under 16 pairs per expert on average) keeps its streaming
+    # tiles beside the mid tiles.
+    T = sum(counts)
+    assert T <= 256 and len(counts) == E
+    spec = W.LAYERS["20b_live"].with_(T=T, H=64, I=96, E=E, top_k=1)
+    L = W.make_layer(spec, seed=31 + E)
+    rng = np.random.default_rng(32 + E)
+    owner = rng.permutation(np.repeat(np.arange(E), counts))
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    logits[np.arange(T), owner] += 20.0
+    L["router_logits"] = logits
+    ids, _ = O.route(logits, 1)
+    assert np.array_equal(np.bincount(ids.ravel(), minlength=E), counts)
+    y = _forward(gpu, L, 1)
+    assert_layer_parity(y, O.moe_forward(L, 1), f"small batch mid tiles E={E}")
+
+
 def _split_rows(a: np.ndarray) -> np.ndarray:
     """Interleaved w13 rows (2i gate i, 2i+1 up i) -> [I gate rows; I up rows] along axis 1."""
     return np.concatenate([a[:, 0::2], a[:, 1::2]], axis=1)
