@@ -33,15 +33,17 @@ __device__ __forceinline__ float key_logit(uint64_t k) {
 __device__ __forceinline__ int key_expert(uint64_t k) { return (int)~(uint32_t)k; }
 
 // Token t, by one wave (all 64 lanes active).  Lane l holds the keys of
-// experts l, l+64, ...; k rounds of a wave-wide key maximum pick the experts
-// by descending logit (ties to the lower expert index); lane j keeps the
-// j-th pick.  The softmax runs over the picks relative to the largest one.
-__device__ inline void route_row(const float* row, int t, int E, int top_k, int32_t* __restrict__ ids,
-                          float* __restrict__ weights, int32_t* ids_copy = nullptr) {
+// experts l, l+64, ... (kPL of them, kPL * 64 >= E); k rounds of a wave-wide
+// key maximum pick the experts by descending logit (ties to the lower expert
+// index); lane j keeps the j-th pick.  The softmax runs over the picks
+// relative to the largest one.
+template <int kPL>
+__device__ inline void route_row_keys(const float* row, int t, int E, int top_k, int32_t* __restrict__ ids,
+                                      float* __restrict__ weights, int32_t* ids_copy) {
   const int lane = mx::lane_id();
-  uint64_t key[kPerLane];
+  uint64_t key[kPL];
 #pragma unroll
-  for (int i = 0; i < kPerLane; ++i) {
+  for (int i = 0; i < kPL; ++i) {
     const int e = lane + 64 * i;
     key[i] = e < E ? route_key(row[e], e) : 0ull;
   }
@@ -50,11 +52,11 @@ __device__ inline void route_row(const float* row, int t, int E, int top_k, int3
   for (int j = 0; j < top_k; ++j) {
     uint64_t best = 0;
 #pragma unroll
-    for (int i = 0; i < kPerLane; ++i) best = mx::max_u64(best, key[i]);
+    for (int i = 0; i < kPL; ++i) best = mx::max_u64(best, key[i]);
     best = mx::wave_max_u64(best);
     const int be = key_expert(best);
 #pragma unroll
-    for (int i = 0; i < kPerLane; ++i)
+    for (int i = 0; i < kPL; ++i)
       if (lane + 64 * i == be) key[i] = 0ull;
     const float bv = key_logit(best);
     if (lane == j) {
@@ -70,6 +72,19 @@ __device__ inline void route_row(const float* row, int t, int E, int top_k, int3
     weights[(size_t)t * top_k + lane] = ex / sum;
     if (ids_copy != nullptr) ids_copy[t * top_k + lane] = my_e;
   }
+}
+
+// route_row_keys with as few keys per lane as E needs (E is uniform).
+__device__ inline void route_row(const float* row, int t, int E, int top_k, int32_t* __restrict__ ids,
+                                 float* __restrict__ weights, int32_t* ids_copy = nullptr) {
+  if (E <= 64)
+    route_row_keys<1>(row, t, E, top_k, ids, weights, ids_copy);
+  else if (E <= 128)
+    route_row_keys<2>(row, t, E, top_k, ids, weights, ids_copy);
+  else if (E <= 256)
+    route_row_keys<4>(row, t, E, top_k, ids, weights, ids_copy);
+  else
+    route_row_keys<kPerLane>(row, t, E, top_k, ids, weights, ids_copy);
 }
 
 }  // namespace mxroute

@@ -31,8 +31,10 @@ def test_route_layers(gpu, name):
 
 
 @pytest.mark.parametrize("T,E,k", [(1, 1, 1), (3, 7, 7), (77, 512, 32), (5000, 64, 1), (2048, 128, 8),
-                                   (1, 65, 4)])
+                                   (1, 65, 4), (40, 64, 4), (300, 129, 4), (100, 200, 2), (64, 256, 8),
+                                   (33, 257, 16)])
 def test_route_shapes(gpu, T, E, k):
+    # every keys-per-lane form of the top-k (E up to 64, 128, 256, 512) and its edges
     rng = np.random.default_rng(T + E + k)
     _check(gpu, rng.standard_normal((T, E)).astype(np.float32), k)
 
