@@ -8,6 +8,7 @@
 
 #include "../../include/mxfp4moe.h"
 #include "internal.h"
+#include "route_device.h"
 
 namespace mxfp4moe {
 
@@ -247,8 +248,14 @@ int forward_impl(const uint16_t* x, const float* router_logits, const uint16_t* 
                                                          : kTilesStreamOnly);
   hipStream_t s = (hipStream_t)stream;
 
-  hipError_t err;
-  if (router_w != nullptr) {
+  // A decode batch is routed and grouped inside the gate_up launch (every
+  // block of it does so alike; one writes the data the later launches read).
+  const bool route_in_gate_up = router_w == nullptr && act_mode == kActBf16 &&
+                                T <= mxroute::kSmallRouteTokens && P <= mxroute::kSmallRoutePairs;
+  hipError_t err = hipSuccess;
+  if (route_in_gate_up) {
+    // nothing before the gate_up launch
+  } else if (router_w != nullptr) {
     err = launch_route_proj(x, router_w, router_b, (int)T, (int)H, (int)E, (int)top_k,
                             reinterpret_cast<float*>(ws + L.logits), ids, weights, s);
     if (err == hipSuccess) err = launch_group(ids, (int)P, (int)E, offsets, sorted, tt, s);
@@ -280,7 +287,19 @@ int forward_impl(const uint16_t* x, const float* router_logits, const uint16_t* 
       err = launch_act_quant(x, (int)T, (int)H, act_mode == kActMxfp8Split, reinterpret_cast<uint8_t*>(ws + L.xq),
                              reinterpret_cast<uint8_t*>(ws + L.xqs), s);
     }
+    if (route_in_gate_up) {
+      g.route_logits = router_logits;
+      g.route_T = (int)T;
+      g.route_E = (int)E;
+      g.route_ids = ids;
+      g.route_weights = weights;
+      g.route_offsets = offsets;
+      g.route_sorted = sorted;
+      g.route_tiles = tt.small;
+      g.route_counts = counts;
+    }
     if (err == hipSuccess) err = launch_gate_up(g, tt, tb, s);
+    g.route_logits = nullptr;
   }
   if (err == hipSuccess) {
     g.wblocks = w2_blocks;

@@ -29,6 +29,7 @@
 #include "expert_device.h"
 #include "internal.h"
 #include "mx_device.h"
+#include "route_device.h"
 
 namespace {
 
@@ -1084,19 +1085,38 @@ __host__ __device__ constexpr size_t stream_lds_bytes(int K) {
          (kKSplit == 2 ? (size_t)2 * RN * 64 * 16 : 0);
 }
 
-template <int RN, int kBatch, bool kGateUp, bool kNv, int kKSplit = 1>
+// kRoute (gate_up of a decode batch): the block routes and groups the batch
+// itself before it knows its tile (route_group_small, in LDS past the
+// regions above), so no routing launch runs before this one.
+template <int RN, bool kNv = false, int kKSplit = 1>
+__host__ __device__ constexpr size_t stream_route_offset(int K) {
+  return (stream_lds_bytes<RN, kNv, kKSplit>(K) + 15) / 16 * 16;
+}
+
+template <int RN, int kBatch, bool kGateUp, bool kNv, int kKSplit = 1, bool kRoute = false>
 __global__ __launch_bounds__(256, 5) void expert_stream_kernel(mxfp4moe::GemmArgs args) {
   constexpr int kThreads = 256;
   constexpr int BN = 64 * RN / kKSplit;
   static_assert(kKSplit == 1 || kKSplit == 2, "one or two K parts");
+  static_assert(!kRoute || kGateUp, "routing in the gate_up launch only");
   extern __shared__ u32x4 dyn[];
   uint8_t* const lds = reinterpret_cast<uint8_t*>(dyn);
 
   const int N = args.N, K = args.K;
   const int n_tiles = (N + BN - 1) / BN;
   int tile, ntile;
-  if (!map_block(*args.num_tiles, n_tiles, tile, ntile)) return;  // uniform per block
-  const int4 tl = reinterpret_cast<const int4*>(args.tiles)[tile];
+  int4 tl;
+  mxroute::SmallRoute* const sr = reinterpret_cast<mxroute::SmallRoute*>(lds + stream_route_offset<RN, kNv, kKSplit>(K));
+  if constexpr (kRoute) {
+    mxroute::route_group_small(*sr, args.route_logits, args.route_T, args.route_E, args.top_k, blockIdx.x == 0,
+                               args.route_ids, args.route_weights, args.route_offsets, args.route_sorted,
+                               reinterpret_cast<int4*>(args.route_tiles), args.route_counts);
+    if (!map_block(sr->num_active, n_tiles, tile, ntile)) return;  // uniform per block
+    tl = sr->tiles[tile];
+  } else {
+    if (!map_block(*args.num_tiles, n_tiles, tile, ntile)) return;  // uniform per block
+    tl = reinterpret_cast<const int4*>(args.tiles)[tile];
+  }
   const int e = __builtin_amdgcn_readfirstlane(tl.x);
   const int row0 = __builtin_amdgcn_readfirstlane(tl.y);
   const int count = __builtin_amdgcn_readfirstlane(tl.z);
@@ -1148,7 +1168,8 @@ __global__ __launch_bounds__(256, 5) void expert_stream_kernel(mxfp4moe::GemmArg
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int rr = r < count ? r : 0;
-      xsrc[r] = (kGateUp ? (size_t)(args.sorted_pairs[row0 + rr] / args.top_k) : (size_t)(row0 + rr)) * (size_t)K;
+      const int pr = kRoute ? sr->sorted[row0 + rr] : kGateUp ? args.sorted_pairs[row0 + rr] : 0;
+      xsrc[r] = (kGateUp ? (size_t)(pr / args.top_k) : (size_t)(row0 + rr)) * (size_t)K;
     }
     const int k16 = K >> 3;
     const int nx16 = count * k16;
@@ -1283,6 +1304,19 @@ hipError_t launch_stream(const mxfp4moe::GemmArgs& a, hipStream_t stream) {
   const long blocks = n_tiles * a.max_tiles;
   if (blocks == 0) return hipSuccess;
   const long grid = (blocks + kXcds - 1) / kXcds * kXcds;
+  if constexpr (kGateUp) {
+    if (a.route_logits != nullptr) {  // the decode batch routed inside the launch
+      constexpr size_t kRouteLds = sizeof(mxroute::SmallRoute);
+      static const hipError_t attr_r = hipFuncSetAttribute(
+          reinterpret_cast<const void*>(&expert_stream_kernel<RN, kBatch, kGateUp, kNv, kKSplit, true>),
+          hipFuncAttributeMaxDynamicSharedMemorySize,
+          (int)(stream_route_offset<RN, kNv, kKSplit>(mxfp4moe::kMaxHidden) + kRouteLds));
+      if (attr_r != hipSuccess) return attr_r;
+      expert_stream_kernel<RN, kBatch, kGateUp, kNv, kKSplit, true>
+          <<<(unsigned)grid, 256, stream_route_offset<RN, kNv, kKSplit>(a.K) + kRouteLds, stream>>>(a);
+      return hipGetLastError();
+    }
+  }
   const size_t lds = stream_lds_bytes<RN, kNv, kKSplit>(a.K);
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&expert_stream_kernel<RN, kBatch, kGateUp, kNv, kKSplit>),

@@ -115,6 +115,19 @@ struct GemmArgs {
   int act_mode;             // kActBf16, kActMxfp8 or kActMxfp8Split
   const uint8_t* act_codes;
   const uint8_t* act_scales;
+  // Decode batches (gate_up streaming launch only): route_logits != nullptr
+  // makes every block route and group the batch itself (route_T tokens,
+  // route_E experts); block 0 writes the routing data and the tile table
+  // that the down and combine launches read: ids, weights (topk_weights),
+  // offsets, sorted pairs (sorted_pairs), tiles and the three tile counts.
+  const float* route_logits;
+  int route_T, route_E;
+  int32_t* route_ids;
+  float* route_weights;
+  int32_t* route_offsets;
+  int32_t* route_sorted;
+  int32_t* route_tiles;
+  int32_t* route_counts;
 };
 enum ActMode : int { kActBf16 = 0, kActMxfp8 = 1, kActMxfp8Split = 2 };
 

@@ -87,4 +87,74 @@ __device__ inline void route_row(const float* row, int t, int E, int top_k, int3
     route_row_keys<kPerLane>(row, t, E, top_k, ids, weights, ids_copy);
 }
 
+// Routing and grouping of a decode batch (T <= 4 tokens, P = T * top_k <= 64
+// pairs: an expert then has at most 4 pairs, one streaming tile) inside one
+// block, computed alike in every block of the launch that consumes it, so
+// that no launch has to run before that one: wave t routes token t (as
+// route_row), then wave 0 groups the pairs.  Lane p takes pair p and, in one
+// pass over the pairs, counts the pairs of lower experts (its expert's first
+// sorted row), the earlier pairs of its own expert (its place among them) and
+// the expert's pairs; in a second pass the distinct lower experts (its
+// expert's tile index).  The same ids, weights, stable expert order, offsets
+// and tile table as the grouping kernel; block 0 (write) also stores them to
+// global memory for the launches that follow.
+struct SmallRoute {
+  int32_t ids[64];
+  float weights[64];
+  int32_t sorted[64];
+  int4 tiles[64];  // {expert, first sorted row, rows, 0} per active expert, in expert order
+  int32_t num_active;
+};
+constexpr int kSmallRouteTokens = 4;
+constexpr int kSmallRoutePairs = 64;
+
+__device__ __forceinline__ void route_group_small(SmallRoute& s, const float* logits, int T, int E, int top_k, bool write,
+                                         int32_t* ids, float* weights, int32_t* offsets, int32_t* sorted,
+                                         int4* tiles, int32_t* counts) {
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int P = T * top_k;
+  if (wave < T) route_row(logits + (size_t)wave * E, wave, E, top_k, s.ids, s.weights);  // uniform per wave
+  __syncthreads();
+  if (wave == 0) {
+    const bool valid = lane < P;
+    const int e = valid ? s.ids[lane] : 0x7fffffff;
+    int below = 0, before = 0, cnt = 0;
+    for (int q = 0; q < P; ++q) {
+      const int eq = __builtin_amdgcn_readlane(e, q);
+      below += eq < e ? 1 : 0;
+      before += (eq == e && q < lane) ? 1 : 0;
+      cnt += eq == e ? 1 : 0;
+    }
+    const bool first = valid && before == 0;
+    const uint64_t firsts = __ballot(first);
+    int dbelow = 0;
+    for (int q = 0; q < P; ++q) {
+      const int eq = __builtin_amdgcn_readlane(e, q);
+      dbelow += (((firsts >> q) & 1ull) != 0 && eq < e) ? 1 : 0;
+    }
+    const int na = __popcll(firsts);
+    if (valid) s.sorted[below + before] = lane;
+    if (first) s.tiles[dbelow] = int4{e, below, cnt, 0};
+    if (lane == 0) s.num_active = na;
+    if (write) {
+      if (valid) {
+        ids[lane] = e;
+        weights[lane] = s.weights[lane];
+        sorted[below + before] = lane;
+      }
+      if (first) tiles[dbelow] = int4{e, below, cnt, 0};
+      if (lane < 3) counts[lane] = lane == 2 ? na : 0;  // full, mid, streaming tiles
+    }
+  }
+  __syncthreads();
+  if (write) {
+    for (int i = (int)threadIdx.x; i <= E; i += (int)blockDim.x) {
+      int n = 0;
+      for (int q = 0; q < P; ++q) n += s.ids[q] < i ? 1 : 0;
+      offsets[i] = n;
+    }
+  }
+}
+
 }  // namespace mxroute

@@ -108,7 +108,8 @@ def test_bias_arrays_at_8_byte_offsets(gpu, split):
 @pytest.mark.parametrize("T,H,I,E,k", [(5, 96, 160, 7, 3), (1, 64, 32, 3, 3), (37, 224, 96, 9, 2),
                                        (300, 128, 64, 5, 1), (3, 32, 32, 1, 1), (600, 96, 160, 3, 2),
                                        (700, 4096, 64, 2, 1), (9, 32, 64, 512, 32), (40, 64, 64, 64, 32),
-                                       (64, 64, 64, 64, 32), (300, 96, 288, 2, 1), (50, 64, 96, 16, 8)])
+                                       (64, 64, 64, 64, 32), (300, 96, 288, 2, 1), (50, 64, 96, 16, 8),
+                                       (4, 64, 64, 512, 16), (2, 64, 96, 200, 32), (3, 96, 64, 65, 5)])
 @pytest.mark.parametrize("path", [None, "stream"])
 def test_ragged_shapes(gpu, T, H, I, E, k, path):
     # K tails (H/32 or I/32 odd), partial weight-row tiles, partial token tiles,
@@ -118,7 +119,8 @@ def test_ragged_shapes(gpu, T, H, I, E, k, path):
     # and 2048 pairs take two chunks of the grouping in one block, and gate_up rows
     # N = 576 = 512 + 64 (full tiles whose second weight-row tile holds 64 live
     # rows), and top_k = 8 (each combine specialisation: k = 1, 2, 8 and the
-    # general loop for 3 and 32).  path None: full tiles in
+    # general loop for 3 and 32); decode batches routed inside the gate_up
+    # launch with 64 pairs over 512 and 200 experts, and 15 over 65.  path None: full tiles in
     # the wide configuration, remainders streamed; "stream": everything streamed.
     spec = W.LAYERS["tiny"].with_(T=T, H=H, I=I, E=E, top_k=k)
     L = W.make_layer(spec, seed=T + H)
