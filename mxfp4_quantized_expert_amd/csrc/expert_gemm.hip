@@ -26,6 +26,8 @@
 // step, element) yields the same dot products, and this one needs no
 // reshuffle of the checkpoint layout.  Weights are dequantized exactly
 // (E2M1 x 2^(s-127) is a bf16 value) and MFMA accumulates in fp32.
+#include <type_traits>
+
 #include "expert_device.h"
 #include "internal.h"
 #include "mx_device.h"
@@ -110,7 +112,9 @@ struct NoExtra {
 // power of two (sc, sc_hi) and its significand as an f16 pair (mt, mt_hi),
 // the codes are converted to f16 by the scaled convert and one packed
 // multiply, and the MFMAs are f16.
-template <int RN, int RM, bool kNv = false, bool kF16 = false, typename Extra = NoExtra>
+// RML <= RM: only the first RML token blocks hold pairs of the tile (the
+// others are neither read nor multiplied); extra(k) runs for k < 4*RN*RML.
+template <int RN, int RM, bool kNv = false, bool kF16 = false, int RML = RM, typename Extra = NoExtra>
 __device__ __forceinline__ void chunk_mma_regs(f32x16 (&acc)[RN][RM], const bf16x8 (&b)[4][RM],
                                                const u32x4 (&w)[RN], const float (&sc)[RN],
                                                const float (&sc_hi)[RN], Extra extra = Extra(),
@@ -154,10 +158,11 @@ __device__ __forceinline__ void chunk_mma_regs(f32x16 (&acc)[RN][RM], const bf16
     }
     a[s & 1][rb][sel] = v;
   };
+  static_assert(RML >= 1 && RML <= RM, "live token blocks");
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
 #pragma unroll
-    for (int i = 0; i < RN * RM; ++i) {
+    for (int i = 0; i < RN * RML; ++i) {
       const int rb = i % RN, cb = i / RN;
       if constexpr (kF16)
         acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(mx::f16x8, a[s & 1][rb]),
@@ -165,11 +170,11 @@ __device__ __forceinline__ void chunk_mma_regs(f32x16 (&acc)[RN][RM], const bf16
       else
         acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mx::as_bf16x8(a[s & 1][rb]), b[s][cb], acc[rb][cb], 0, 0, 0);
       if (s + 1 < 4 && i < 4 * RN) convert(s + 1, i);
-      extra(s * RN * RM + i);
+      extra(s * RN * RML + i);
     }
     if (s + 1 < 4) {
 #pragma unroll
-      for (int i = RN * RM; i < 4 * RN; ++i) convert(s + 1, i);
+      for (int i = RN * RML; i < 4 * RN; ++i) convert(s + 1, i);
     }
   }
 }
@@ -693,19 +698,23 @@ __global__ __launch_bounds__(WN * WM * 64, kBlocksPerCu) void expert_wide_kernel
     // chunk c from stage st: read after the barrier that makes it visible
     // (the other wave on the SIMD covers the wait); chunk c+2 into stage
     // (st + 2) % kStages, its loads spread between the MFMAs
-    auto step1 = [&](int c, int st) {
+    // rml_c: the wave's live token blocks (RML of RM; see live_blocks below)
+    auto step1 = [&](int c, int st, auto rml_c) {
+      constexpr int RML = decltype(rml_c)::value;
       wait_loads_then_barrier<kLoads>();  // chunk c landed; chunk c+1 may be in flight
       Ops cur;
       if (live) {
 #pragma unroll
-        for (int j = 0; j < kReads; ++j) read_one(cur, c, st, j);
+        for (int j = 0; j < 2 * RN; ++j) read_one(cur, c, st, j);
+#pragma unroll
+        for (int j = 0; j < 4 * RML; ++j) read_one(cur, c, st, 2 * RN + (j / RML) * RM + j % RML);
       }
       if constexpr (kStages == 2) lds_reads_then_barrier();  // chunk c+2 overwrites chunk c
       if (live) {
         // NVFP4: part c%kSG of the next scale group first, so that the
         // waits, which leave the last kLoads loads in flight, cover it
         constexpr int kIssue = kLoads + (kNv ? 1 : 0);
-        constexpr int kMfma = 4 * RN * RM;
+        constexpr int kMfma = 4 * RN * RML;
         constexpr int kEvery = kMfma / kIssue >= 2 ? 2 : 1;
         static_assert(kEvery * kIssue <= kMfma, "room between the MFMAs");
         auto extra = [&](int k) {
@@ -728,24 +737,35 @@ __global__ __launch_bounds__(WN * WM * 64, kBlocksPerCu) void expert_wide_kernel
             mx::split_scale_f16(sc_hi[rb], sc_hi[rb], mt_hi[rb]);
           }
         }
-        chunk_mma_regs<RN, RM, kNv, kF16In>(acc, cur.b, w, sc, sc_hi, extra, mt, mt_hi);
+        chunk_mma_regs<RN, RM, kNv, kF16In, RML>(acc, cur.b, w, sc, sc_hi, extra, mt, mt_hi);
       } else {
         if constexpr (kNv) issue_scales(c / kSG + 1, c % kSG);
         issue(c + 2, (st + 2) % kStages);
       }
     };
-    if (bias_lds) {
-      wait_loads_then_barrier<kLoads>();  // chunk 0 (and the biases) landed
-      init_acc_from_lds();
-    }
+    // The K loop, in one form per count of live token blocks: in a tile's
+    // last, partial job the blocks past its pairs are neither read nor
+    // multiplied (wave-uniform, chosen once per job; every form runs the
+    // same loads and barriers).
     const int nfull = nchunks / kStages * kStages;
-    for (int c0 = 0; c0 < nfull; c0 += kStages) {
+    auto k_loop = [&](auto rml_c) {
+      if (bias_lds) {
+        wait_loads_then_barrier<kLoads>();  // chunk 0 (and the biases) landed
+        init_acc_from_lds();
+      }
+      for (int c0 = 0; c0 < nfull; c0 += kStages) {
 #pragma unroll
-      for (int u = 0; u < kStages; ++u) step1(c0 + u, (u + kNext) % kStages);
-    }
+        for (int u = 0; u < kStages; ++u) step1(c0 + u, (u + kNext) % kStages, rml_c);
+      }
 #pragma unroll
-    for (int u = 0; u < kStages - 1; ++u)
-      if (nfull + u < nchunks) step1(nfull + u, (u + kNext) % kStages);
+      for (int u = 0; u < kStages - 1; ++u)
+        if (nfull + u < nchunks) step1(nfull + u, (u + kNext) % kStages, rml_c);
+    };
+    const int live_blocks = __builtin_amdgcn_readfirstlane(min(RM, max(0, (count - m_wave + 31) >> 5)));
+    if (RM >= 4 && live_blocks == 3) k_loop(std::integral_constant<int, (RM >= 4 ? 3 : RM)>{});
+    else if (RM >= 3 && live_blocks == 2) k_loop(std::integral_constant<int, (RM >= 3 ? 2 : RM)>{});
+    else if (RM >= 2 && live_blocks == 1) k_loop(std::integral_constant<int, 1>{});
+    else k_loop(std::integral_constant<int, RM>{});
     // the chunks issued past the end land before the arena is reused
     wait_loads_then_barrier<0>();
     // this job's epilogue values; the next job (if any) is set up and its
