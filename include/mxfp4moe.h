@@ -166,7 +166,11 @@ int moe_mxfp4_route(const float* router_logits, int64_t T, int64_t E, int64_t to
  * partial), one with 5..127 pairs into ceil(pairs / 48) tiles of near-equal
  * size, one with at most 4 pairs makes one streaming tile; each kind has a
  * GEMM kernel of its own
- * (with T <= 4 every expert has one streaming tile: the decode path).
+ * (with T <= 4 every expert has one streaming tile: the decode path, whose
+ * routing runs inside the gate_up launch).  Batches of 5..256 tokens take no
+ * full tiles (their experts' pairs take mid tiles), and no streaming tiles
+ * either when T * top_k >= 16 * E.  The tiling changes which kernel computes
+ * a pair, not what is computed.
  *
  * E8M0 byte 0xFF (NaN) in a weight row makes that row's GEMM output NaN for
  * every token of the expert: a 0xFF in gate_up row r of expert e gives NaN in
