@@ -250,15 +250,17 @@ int forward_impl(const uint16_t* x, const float* router_logits, const uint16_t* 
 
   // A decode batch is routed and grouped inside the gate_up launch (every
   // block of it does so alike; one writes the data the later launches read).
-  const bool route_in_gate_up = router_w == nullptr && act_mode == kActBf16 &&
-                                T <= mxroute::kSmallRouteTokens && P <= mxroute::kSmallRoutePairs;
+  // (With the router projection, from the logits it leaves in the workspace.)
+  const bool route_in_gate_up =
+      act_mode == kActBf16 && T <= mxroute::kSmallRouteTokens && P <= mxroute::kSmallRoutePairs;
+  const float* logits = router_w != nullptr ? reinterpret_cast<const float*>(ws + L.logits) : router_logits;
   hipError_t err = hipSuccess;
-  if (route_in_gate_up) {
-    // nothing before the gate_up launch
-  } else if (router_w != nullptr) {
+  if (router_w != nullptr) {
     err = launch_route_proj(x, router_w, router_b, (int)T, (int)H, (int)E, (int)top_k,
                             reinterpret_cast<float*>(ws + L.logits), ids, weights, s);
-    if (err == hipSuccess) err = launch_group(ids, (int)P, (int)E, offsets, sorted, tt, s);
+    if (err == hipSuccess && !route_in_gate_up) err = launch_group(ids, (int)P, (int)E, offsets, sorted, tt, s);
+  } else if (route_in_gate_up) {
+    // nothing before the gate_up launch
   } else if (T <= kFusedRouteTokens) {
     err = launch_route_group(router_logits, (int)T, (int)E, (int)top_k, ids, weights, offsets, sorted, tt, s);
   } else {
@@ -288,7 +290,7 @@ int forward_impl(const uint16_t* x, const float* router_logits, const uint16_t* 
                              reinterpret_cast<uint8_t*>(ws + L.xqs), s);
     }
     if (route_in_gate_up) {
-      g.route_logits = router_logits;
+      g.route_logits = logits;
       g.route_T = (int)T;
       g.route_E = (int)E;
       g.route_ids = ids;

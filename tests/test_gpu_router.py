@@ -123,11 +123,13 @@ def test_forward_router_120b(gpu):
                         f"forward_router 120b ({tokens.size} unambiguous tokens)")
 
 
-def test_forward_router_matches_logits_entry(gpu):
+@pytest.mark.parametrize("T", [64, 4, 1])
+def test_forward_router_matches_logits_entry(gpu, T):
     # The same layer through moe_mxfp4_forward with the logits the router
     # entry returned gives the same bits (the projection only replaces the
-    # logits input).
-    spec = W.LAYERS["20b_prefill"].with_(T=64)
+    # logits input; decode batches are routed inside the gate_up launch from
+    # the projected logits).
+    spec = W.LAYERS["20b_prefill"].with_(T=T)
     L = _layer(spec)
     d = gpu.layer_to_device(L)
     y = gpu.moe_mxfp4_forward_router(d["x"], d["router_w"], d["router_b"], d["w13_blocks"], d["w13_scales"],
