@@ -128,6 +128,23 @@ def test_ragged_shapes(gpu, T, H, I, E, k, path):
     assert_layer_parity(y, O.moe_forward(L, k), f"ragged{(T, H, I, E, k)}/{path}")
 
 
+@pytest.mark.parametrize("E,k", [(8, 3), (64, 16), (3, 3)])
+def test_decode_routing_ties(gpu, E, k):
+    # Decode batches are routed inside the gate_up launch: logits with many
+    # exact ties (and signed zeros) must pick the same experts as the oracle
+    # (descending logit, lower expert index first) in every block.
+    T = 4
+    spec = W.LAYERS["20b_live"].with_(T=T, H=64, I=96, E=E, top_k=k)
+    L = W.make_layer(spec, seed=51 + E)
+    rng = np.random.default_rng(52 + E)
+    logits = np.round(rng.standard_normal((T, E)) * 1.5).astype(np.float32)
+    logits[0, : min(E, 4)] = 0.0
+    logits[1, : min(E, 4)] = -0.0
+    L["router_logits"] = logits
+    y = _forward(gpu, L, k)
+    assert_layer_parity(y, O.moe_forward(L, k), f"decode routing ties E={E} k={k}")
+
+
 @pytest.mark.parametrize("T", [1, 4])
 def test_decode_batches_back_to_back_one_workspace(gpu, T):
     # Nothing of a call survives in the workspace into the next: two different
