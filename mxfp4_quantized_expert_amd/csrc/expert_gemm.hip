@@ -1355,20 +1355,21 @@ hipError_t launch_stream(const mxfp4moe::GemmArgs& a, hipStream_t stream) {
 // straight into the A operand's registers (lane (r, q) the 16 bytes of group
 // 4c+q of its row: the four lanes of a row read its 64 contiguous bytes of
 // the panel, the pattern HBM streams at full rate); the tile's token rows
-// (256 bytes each per panel) are shared by the four waves through LDS.  Three
-// register slots each hold the loads of one panel's weights (used by that
-// panel's MFMAs, then refilled with the panel three ahead) and one panel's
-// tokens (stored to the single LDS token buffer a panel before they are
-// used, then refilled): per panel, after its MFMAs and a barrier, the next
-// panel's tokens are stored, their slot refilled, and a second barrier makes
-// them visible.  The token bytes of a panel (at most 12 KB, from L2) are at
-// most 1.5 times its weight bytes (8 KB, from HBM), which is what lets three
-// panels fit in registers at three blocks per CU (with 64-token tiles only
-// two did).  The loop body is three panels of straight-line code with the
-// same loads in flight at entry and at the back edge (the compiler then waits
-// for each slot alone); panels past the last re-read the last one (in
-// bounds, never computed).  Token rows past the tile's pairs re-read its
-// first pair (their outputs are dropped).
+// (256 bytes each per panel) are shared by the four waves through LDS.  kS
+// register slots (three; two for the MXFP4 down GEMM, see mid_slots) each
+// hold the loads of one panel's weights (used by that panel's MFMAs, then
+// refilled with the panel kS ahead) and one panel's tokens (stored to the
+// single LDS token buffer a panel before they are used, then refilled): per
+// panel, after its MFMAs and a barrier, the next panel's tokens are stored,
+// their slot refilled, and a second barrier makes them visible.  The token
+// bytes of a panel (at most 12 KB, from L2) are at most 1.5 times its weight
+// bytes (8 KB, from HBM), which is what lets three panels fit in registers
+// at three blocks per CU (with 64-token tiles only two did).  The loop body
+// is kS panels of straight-line code with the same loads in flight at entry
+// and at the back edge (the compiler then waits for each slot alone); panels
+// past the last re-read the last one (in bounds, never computed).  Token
+// rows past the tile's pairs re-read its first pair (their outputs are
+// dropped).
 //
 // Dynamic LDS: tokens [48][256 + 16] | scales [128][K/32] (the 16-byte row
 // pad makes the 16-lane column reads conflict-free).
@@ -1377,8 +1378,15 @@ __host__ __device__ constexpr size_t mid_lds_bytes(int K) {
   return (size_t)mxfp4moe::kMidTokens * (256 + 16) + (size_t)128 * (K / (kNv ? 16 : 32));
 }
 
+// Register slots of panel loads: three (at three blocks per CU), or for the
+// MXFP4 down GEMM two at four blocks per CU (128 registers; the others spill
+// inside the loop at that occupancy).  Measured at the 120b long prefill: mid
+// down 74.4-74.8 against 76.6-76.9 us.
 template <bool kGateUp, bool kNv>
-__global__ __launch_bounds__(256, 2) void expert_mid_kernel(mxfp4moe::GemmArgs args) {
+constexpr int mid_slots() { return !kGateUp && !kNv ? 2 : 3; }
+template <bool kGateUp, bool kNv>
+__global__ __launch_bounds__(256, (mid_slots<kGateUp, kNv>() == 2 ? 4 : 2)) void expert_mid_kernel(mxfp4moe::GemmArgs args) {
+  constexpr int kS = mid_slots<kGateUp, kNv>();
   constexpr int kThreads = 256;
   constexpr int BN = 128;
   constexpr int BM = mxfp4moe::kMidTokens;
@@ -1442,7 +1450,7 @@ __global__ __launch_bounds__(256, 2) void expert_mid_kernel(mxfp4moe::GemmArgs a
   // earlier).  Groups / pieces past the end re-read the last one (finite;
   // the weights of a missing group are zeroed at use); panels past the last
   // re-read the last panel.
-  u32x4 xv[3][kXPer], wv[3][2];
+  u32x4 xv[kS][kXPer], wv[kS][2];
   auto issue_w = [&](int p, int sl3) {
     p = min(p, npanels - 1);
 #pragma unroll
@@ -1524,7 +1532,7 @@ __global__ __launch_bounds__(256, 2) void expert_mid_kernel(mxfp4moe::GemmArgs a
   // panel's token slot `nx` is stored, refilled with panel `ahead`, and the
   // stored panel made visible
   auto advance = [&](int p, int nx, int ahead) {
-    issue_w(p + 3, p % 3);
+    issue_w(p + kS, p % kS);
     __syncthreads();
     commit(nx);
     issue_x(ahead, nx);
@@ -1532,27 +1540,26 @@ __global__ __launch_bounds__(256, 2) void expert_mid_kernel(mxfp4moe::GemmArgs a
   };
 
 #pragma unroll
-  for (int j = 0; j < 3; ++j) {
+  for (int j = 0; j < kS; ++j) {
     issue_w(j, j);
     issue_x(j, j);
   }
   commit(0);
-  issue_x(3, 0);
-  __syncthreads();  // panel 0's tokens and the scale rows staged; panels 1, 2, 3 in flight
+  issue_x(kS, 0);
+  __syncthreads();  // panel 0's tokens and the scale rows staged; the next panels in flight
   int p = 0;
-  for (; p + 3 <= npanels; p += 3) {
-    compute(p, 0);
-    advance(p, 1, p + 4);
-    compute(p + 1, 1);
-    advance(p + 1, 2, p + 5);
-    compute(p + 2, 2);
-    advance(p + 2, 0, p + 6);
+  for (; p + kS <= npanels; p += kS) {
+#pragma unroll
+    for (int u = 0; u < kS; ++u) {
+      compute(p + u, u);
+      advance(p + u, (u + 1) % kS, p + u + kS + 1);
+    }
   }
-  // the last one or two panels (slots 0 and 1 hold them, in order)
+  // the last kS - 1 panels at most (slots 0, 1, ... hold them, in order)
   if (p < npanels) compute(p, 0);
-  if (p + 1 < npanels) {
+  if (kS == 3 && p + 1 < npanels) {
     advance(p, 1, p + 4);
-    compute(p + 1, 1);
+    compute(p + 1, 1 % kS);
   }
 
   if (n_wave >= N) return;
