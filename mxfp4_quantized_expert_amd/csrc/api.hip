@@ -251,8 +251,10 @@ int forward_impl(const uint16_t* x, const float* router_logits, const uint16_t* 
   // A decode batch is routed and grouped inside the gate_up launch (every
   // block of it does so alike; one writes the data the later launches read).
   // (With the router projection, from the logits it leaves in the workspace.)
-  const bool route_in_gate_up =
-      act_mode == kActBf16 && T <= mxroute::kSmallRouteTokens && P <= mxroute::kSmallRoutePairs;
+  // (Such a batch has streaming tiles only: its gate_up is one streaming launch.)
+  const bool route_in_gate_up = act_mode == kActBf16 && T <= mxroute::kSmallRouteTokens &&
+                                P <= mxroute::kSmallRoutePairs && tb.max_big == 0 && tb.max_mid == 0 &&
+                                tb.max_small > 0;
   const float* logits = router_w != nullptr ? reinterpret_cast<const float*>(ws + L.logits) : router_logits;
   hipError_t err = hipSuccess;
   if (router_w != nullptr) {
