@@ -1356,15 +1356,15 @@ hipError_t launch_stream(const mxfp4moe::GemmArgs& a, hipStream_t stream) {
 // 4c+q of its row: the four lanes of a row read its 64 contiguous bytes of
 // the panel, the pattern HBM streams at full rate); the tile's token rows
 // (256 bytes each per panel) are shared by the four waves through LDS.  kS
-// register slots (three; two for the MXFP4 down GEMM, see mid_slots) each
+// register slots (see mid_slots) each
 // hold the loads of one panel's weights (used by that panel's MFMAs, then
 // refilled with the panel kS ahead) and one panel's tokens (stored to the
 // single LDS token buffer a panel before they are used, then refilled): per
 // panel, after its MFMAs and a barrier, the next panel's tokens are stored,
 // their slot refilled, and a second barrier makes them visible.  The token
 // bytes of a panel (at most 12 KB, from L2) are at most 1.5 times its weight
-// bytes (8 KB, from HBM), which is what lets three panels fit in registers
-// at three blocks per CU (with 64-token tiles only two did).  The loop body
+// bytes (8 KB, from HBM), which is what lets the slots fit in registers
+// at three or four blocks per CU (with 64-token tiles they did not).  The loop body
 // is kS panels of straight-line code with the same loads in flight at entry
 // and at the back edge (the compiler then waits for each slot alone); panels
 // past the last re-read the last one (in bounds, never computed).  Token
@@ -1378,12 +1378,13 @@ __host__ __device__ constexpr size_t mid_lds_bytes(int K) {
   return (size_t)mxfp4moe::kMidTokens * (256 + 16) + (size_t)128 * (K / (kNv ? 16 : 32));
 }
 
-// Register slots of panel loads: three (at three blocks per CU), or for the
-// MXFP4 down GEMM two at four blocks per CU (128 registers; the others spill
-// inside the loop at that occupancy).  Measured at the 120b long prefill: mid
-// down 74.4-74.8 against 76.6-76.9 us.
+// Register slots of panel loads: two, at four blocks per CU (126-128
+// registers).  Measured against three slots at three blocks per CU: 20b
+// prefill 0.156 against 0.159 ms (mid gate_up 98 against 102 us), NVFP4 0.167
+// against 0.171 ms, the 120b long prefill within noise (MXFP4 mid down 74.4-
+// 74.8 against 76.6-76.9 us when it alone changed).
 template <bool kGateUp, bool kNv>
-constexpr int mid_slots() { return !kGateUp && !kNv ? 2 : 3; }
+constexpr int mid_slots() { return 2; }
 template <bool kGateUp, bool kNv>
 __global__ __launch_bounds__(256, (mid_slots<kGateUp, kNv>() == 2 ? 4 : 2)) void expert_mid_kernel(mxfp4moe::GemmArgs args) {
   constexpr int kS = mid_slots<kGateUp, kNv>();
@@ -1475,12 +1476,9 @@ __global__ __launch_bounds__(256, (mid_slots<kGateUp, kNv>() == 2 ? 4 : 2)) void
   for (int rb = 0; rb < 2; ++rb)
     srow[rb] = sl + staged_row(wave * 32 + rb * 16 + lr, min(BN, N - ntile * BN), split) * (kNv ? 2 : 1) * kgroups;
   const int ncb = (count + 15) >> 4;  // live 16-token column blocks
-  int xrd[kCB];  // LDS byte offset of this lane's token row for each column block
-#pragma unroll
-  for (int cb = 0; cb < kCB; ++cb) {
-    const int m = cb * 16 + lr;
-    xrd[cb] = (m < count ? m : 0) * kXRow + 64 * q;
-  }
+  // LDS byte offset of this lane's token row in column block 0 (block cb adds
+  // a constant; rows past the tile's pairs hold its first pair, finite)
+  const int xrd = lr * kXRow + 64 * q;
   f32x4 acc[2][kCB];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
@@ -1516,7 +1514,7 @@ __global__ __launch_bounds__(256, (mid_slots<kGateUp, kNv>() == 2 ? 4 : 2)) void
         bf16x8 bb[4];
 #pragma unroll
         for (int st = 0; st < 4; ++st)
-          bb[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xs + xrd[cb] + 16 * st));
+          bb[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xs + xrd + cb * 16 * kXRow + 16 * st));
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
